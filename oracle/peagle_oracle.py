@@ -1,0 +1,471 @@
+"""CPU oracle for the P-EAGLE parallel-drafter hot path (NumPy, float64).
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  It shares no code with the HIP
+library and imports nothing from it; it is slow and plain on purpose, so that
+each step can be checked against the pages by eye.
+
+Sources (cited by page title and section):
+  [RH] "Speeding LLM inference with P-EAGLE in vLLM Speculators"
+       (Red Hat Developer): sections "COD sampling", "A learnable mask
+       parameter", "Flex-attention mask", "Example model".
+  [TD] "P-EAGLE: A Technical Deep Dive into Parallel Speculative Decoding":
+       section "2. The P-EAGLE Parallel Drafter", "Memory and Training
+       Complexity".
+  [PN] "P-EAGLE: Parallel-Drafting EAGLE with Scalable Training" (notes on
+       arXiv:2602.01469): section 2 (architecture), 3.1 (amortized mask
+       construction), 3.2 (sequence partitioning), appendix B (RoPE).
+  [E4] "EAGLE-4" (lightseek.org): "EAGLE-4 overview" (accepted prefix plus one
+       bonus token).
+
+Readings where the pages leave a step open (each is listed with its reason in
+the design notes): fusion of token embedding and projected hidden state is an
+addition; h_shared is 3H wide and goes through the same fc; RMSNorm eps 1e-5;
+rotate-half RoPE with frequencies theta^(-2i/hd); a final RMSNorm before an
+untied LM head; ties in argmax go to the lowest index; COD keeps a child with
+conditional probability r given its parent (marginal r^d, floored at 0.2).
+
+Every function here is pinned by tests in tests/ against closed forms,
+invariants, brute force or values the pages print; see each docstring.
+"""
+from __future__ import annotations
+
+import math
+import numpy as np
+
+F64 = np.float64
+
+# ---------------------------------------------------------------------------
+# Elementary pieces of a LLaMA-3 style decoder layer ([PN] section 2 names the
+# layer family; the formulas are the standard ones).
+# ---------------------------------------------------------------------------
+
+
+def rmsnorm(x, gain, eps):
+    """x / sqrt(mean(x^2) + eps) * gain over the last axis."""
+    x = np.asarray(x, dtype=F64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(gain, dtype=F64)
+
+
+def rope_inv_freq(head_dim, theta):
+    """Angular frequency of each rotated pair: theta^(-2i/head_dim)."""
+    i = np.arange(head_dim // 2, dtype=F64)
+    return np.power(F64(theta), -2.0 * i / head_dim)
+
+
+def rope(a, pos, theta):
+    """Rotate-half RoPE of vectors ``a`` [..., hd] at position(s) ``pos``.
+
+    Pair (i, i + hd/2) is rotated by angle pos * theta^(-2i/hd).  ``pos`` may
+    be a scalar or broadcast against a[..., 0].
+    """
+    a = np.asarray(a, dtype=F64)
+    hd = a.shape[-1]
+    half = hd // 2
+    phi = np.asarray(pos, dtype=F64)[..., None] * rope_inv_freq(hd, theta)
+    c, s = np.cos(phi), np.sin(phi)
+    lo, hi = a[..., :half], a[..., half:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+def silu(z):
+    """z * sigmoid(z)."""
+    z = np.asarray(z, dtype=F64)
+    return z / (1.0 + np.exp(-z))
+
+
+def softmax(s):
+    """Max-subtracted softmax over the last axis."""
+    s = np.asarray(s, dtype=F64)
+    e = np.exp(s - np.max(s, axis=-1, keepdims=True))
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def linear(x, w, chunk_rows=16384):
+    """x @ w.T in float64 for w in [out, in] layout.
+
+    The weight is upcast a block of output rows at a time so that very large
+    matrices (the 201088-row LM head) never need a full float64 copy; every
+    output element is still one dot product over the full input width.
+    """
+    x = np.asarray(x, dtype=F64)
+    out_dim = w.shape[0]
+    y = np.empty(x.shape[:-1] + (out_dim,), dtype=F64)
+    for r0 in range(0, out_dim, chunk_rows):
+        r1 = min(out_dim, r0 + chunk_rows)
+        y[..., r0:r1] = x @ np.asarray(w[r0:r1], dtype=F64).T
+    return y
+
+
+def argmax_lowest(logits):
+    """Index of the largest logit, the lowest index among equal maxima."""
+    return np.argmax(np.asarray(logits), axis=-1)  # NumPy returns the first maximum
+
+
+def top2_margin(logits):
+    """Largest minus second-largest logit along the last axis."""
+    part = np.partition(np.asarray(logits, dtype=F64), -2, axis=-1)
+    return part[..., -1] - part[..., -2]
+
+
+# ---------------------------------------------------------------------------
+# Input fusion ([TD] "2. The P-EAGLE Parallel Drafter"; [PN] section 2;
+# [RH] "A learnable mask parameter").
+# ---------------------------------------------------------------------------
+
+
+def fuse_inputs(w, hidden3, token_ids, mask_emb, h_shared, K):
+    """Layer-0 inputs of the K-position block, shape [B, K, H].
+
+    The next-token position uses the new token's embedding plus the
+    fc-projected concatenation of three target hidden states.  Every later
+    position uses the shared mask-token embedding plus the fc projection of
+    the shared hidden state h_shared (3H wide, as the learnable mask_hidden).
+    """
+    hidden3 = np.asarray(hidden3, dtype=F64)
+    B = hidden3.shape[0]
+    H = w["fc"].shape[0]
+    x = np.empty((B, K, H), dtype=F64)
+    ntp = linear(hidden3, w["fc"])                      # [B, H]
+    mtp = linear(np.asarray(h_shared, F64)[None], w["fc"])[0]  # [H]
+    for b in range(B):
+        x[b, 0] = np.asarray(w["embed_rows"][b], dtype=F64) + ntp[b]
+        for k in range(1, K):
+            x[b, k] = np.asarray(mask_emb, dtype=F64) + mtp
+    return x
+
+
+# ---------------------------------------------------------------------------
+# Decode forward ([TD] "2. The P-EAGLE Parallel Drafter"; [PN] section 2;
+# attention visibility from [RH] "Flex-attention mask" restricted to one
+# rollout: the block's query k sees the whole cached context and block rows
+# 0..k).
+# ---------------------------------------------------------------------------
+
+
+def _layer_qkv(x, lw, cfg):
+    u = rmsnorm(x, lw["attn_norm"], cfg.rms_eps)
+    hd = cfg.head_dim
+    q = linear(u, lw["wq"]).reshape(x.shape[:-1] + (cfg.n_q_heads, hd))
+    k = linear(u, lw["wk"]).reshape(x.shape[:-1] + (cfg.n_kv_heads, hd))
+    v = linear(u, lw["wv"]).reshape(x.shape[:-1] + (cfg.n_kv_heads, hd))
+    return q, k, v
+
+
+def _layer_finish(x, attn, lw, cfg):
+    """O projection with residual, then the SwiGLU MLP with residual."""
+    x = x + linear(attn, lw["wo"])
+    u = rmsnorm(x, lw["mlp_norm"], cfg.rms_eps)
+    return x + linear(silu(linear(u, lw["w_gate"])) * linear(u, lw["w_up"]), lw["w_down"])
+
+
+def attend(q, keys, vals, scale):
+    """softmax(q . keys^T * scale) @ vals for q [G, hd], keys/vals [n, hd]."""
+    p = softmax((np.asarray(q, F64) @ np.asarray(keys, F64).T) * scale)
+    return p @ np.asarray(vals, F64)
+
+
+def draft_forward(w, cfg, hidden3, token_ids, mask_emb, h_shared, ctx_lens,
+                  k_cache, v_cache, K, N=None, return_hidden=False):
+    """Logits [B, K, V] of one parallel-drafting forward.
+
+    ``w["embed_rows"]`` holds E[token_ids[b]] (the only embedding rows read).
+    k_cache[l] / v_cache[l]: [B, n_kv, C, hd], keys already rotated.
+    N layers are run (default: all of them).
+    """
+    N = cfg.n_layers if N is None else N
+    B = len(token_ids)
+    nq, nkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    G = nq // nkv
+    scale = 1.0 / math.sqrt(hd)
+    x = fuse_inputs(w, hidden3, token_ids, mask_emb, h_shared, K)
+    pos = np.asarray(ctx_lens, dtype=F64)[:, None] + np.arange(K)[None, :]  # [B, K]
+    for l in range(N):
+        lw = w["layers"][l]
+        q, k, v = _layer_qkv(x, lw, cfg)
+        q = rope(q, pos[:, :, None], cfg.rope_theta)
+        k = rope(k, pos[:, :, None], cfg.rope_theta)
+        attn = np.empty((B, K, nq, hd), dtype=F64)
+        for b in range(B):
+            C = int(ctx_lens[b])
+            for g in range(nkv):
+                ck = np.asarray(k_cache[l][b, g, :C], dtype=F64)
+                cv = np.asarray(v_cache[l][b, g, :C], dtype=F64)
+                for kp in range(K):
+                    keys = np.concatenate([ck, k[b, :kp + 1, g]], axis=0)
+                    vals = np.concatenate([cv, v[b, :kp + 1, g]], axis=0)
+                    attn[b, kp, g * G:(g + 1) * G] = attend(q[b, kp, g * G:(g + 1) * G],
+                                                            keys, vals, scale)
+        x = _layer_finish(x, attn.reshape(B, K, nq * hd), lw, cfg)
+    z = rmsnorm(x, w["final_norm"], cfg.rms_eps)
+    logits = linear(z, w["lm_head"])
+    if return_hidden:
+        return logits, z
+    return logits
+
+
+def eagle3_step(w, cfg, hidden3_b, token_id, ctx_len, k_cache_b, v_cache_b, N=None):
+    """One autoregressive EAGLE-3 drafter step for a single sequence.
+
+    Written separately from ``draft_forward`` (explicit per-head loops) so
+    that the K = 1 case of the parallel drafter, which the pages describe as
+    plain EAGLE-3 next-token prediction, can be checked against it.
+    k_cache_b[l]: [n_kv, C, hd].  Returns the logits [V].
+    """
+    N = cfg.n_layers if N is None else N
+    nq, nkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    x = (np.asarray(w["embed_rows"][0], F64)
+         + np.asarray(w["fc"], F64) @ np.asarray(hidden3_b, F64))
+    for l in range(N):
+        lw = w["layers"][l]
+        ms = float(np.dot(x, x)) / x.shape[0]
+        u = x * (1.0 / math.sqrt(ms + cfg.rms_eps)) * np.asarray(lw["attn_norm"], F64)
+        q = (np.asarray(lw["wq"], F64) @ u).reshape(nq, hd)
+        kk = (np.asarray(lw["wk"], F64) @ u).reshape(nkv, hd)
+        vv = (np.asarray(lw["wv"], F64) @ u).reshape(nkv, hd)
+        half = hd // 2
+        for h in range(nq):
+            q[h] = _rotate_once(q[h], ctx_len, cfg.rope_theta, half)
+        for g in range(nkv):
+            kk[g] = _rotate_once(kk[g], ctx_len, cfg.rope_theta, half)
+        out = np.zeros(nq * hd)
+        for h in range(nq):
+            g = h // (nq // nkv)
+            keys = list(np.asarray(k_cache_b[l][g, :ctx_len], F64)) + [kk[g]]
+            vals = list(np.asarray(v_cache_b[l][g, :ctx_len], F64)) + [vv[g]]
+            sc = np.array([np.dot(q[h], kv) / math.sqrt(hd) for kv in keys])
+            e = np.exp(sc - sc.max())
+            e /= e.sum()
+            out[h * hd:(h + 1) * hd] = sum(ei * vi for ei, vi in zip(e, vals))
+        x = x + np.asarray(lw["wo"], F64) @ out
+        ms = float(np.dot(x, x)) / x.shape[0]
+        u = x * (1.0 / math.sqrt(ms + cfg.rms_eps)) * np.asarray(lw["mlp_norm"], F64)
+        gt = np.asarray(lw["w_gate"], F64) @ u
+        up = np.asarray(lw["w_up"], F64) @ u
+        x = x + np.asarray(lw["w_down"], F64) @ (gt / (1.0 + np.exp(-gt)) * up)
+    ms = float(np.dot(x, x)) / x.shape[0]
+    z = x * (1.0 / math.sqrt(ms + cfg.rms_eps)) * np.asarray(w["final_norm"], F64)
+    return linear(z[None], w["lm_head"])[0]
+
+
+def _rotate_once(a, pos, theta, half):
+    out = np.array(a, dtype=F64)
+    for i in range(half):
+        ang = pos * theta ** (-2.0 * i / (2 * half))
+        c, s = math.cos(ang), math.sin(ang)
+        out[i] = a[i] * c - a[i + half] * s
+        out[i + half] = a[i + half] * c + a[i] * s
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Greedy acceptance ([RH] introduction: the verifier accepts the correct
+# prefix; [E4] "EAGLE-4 overview": longest agreeing path plus one bonus token).
+# ---------------------------------------------------------------------------
+
+
+def accept(draft, target):
+    """accept_len [B] and emitted tokens [B, K+1] (entries past a+1 are -1).
+
+    accept_len = the number of leading draft tokens equal to the target's;
+    the round emits target[0..accept_len] (the accepted prefix plus the
+    target's own next token).
+    """
+    draft = np.asarray(draft)
+    target = np.asarray(target)
+    B, K = draft.shape
+    alen = np.zeros(B, dtype=np.int32)
+    out = np.full((B, K + 1), -1, dtype=np.int32)
+    for b in range(B):
+        a = 0
+        while a < K and draft[b, a] == target[b, a]:
+            a += 1
+        alen[b] = a
+        out[b, :a + 1] = target[b, :a + 1]
+    return alen, out
+
+
+# ---------------------------------------------------------------------------
+# COD sampling ([RH] "COD sampling"; [PN] section 3 challenge analysis and
+# 3.2: geometric decay rate r = 0.8 in the paper's setup).
+# ---------------------------------------------------------------------------
+
+
+def cod_keep(n, K, U, r=0.8, floor=0.2):
+    """Boolean keep grid [n, K] over (position p, depth d).
+
+    Depth 0 keeps every position.  A depth-d cell (p, d), d >= 1, needs its
+    parent (p-1, d-1) kept and is then kept when U[p, d] < r_d, where
+    r_d = max(r^d, floor) / max(r^(d-1), floor), so that the marginal keep
+    rate of depth d is max(r^d, floor).  Cells with p < d have no anchor.
+    """
+    keep = np.zeros((n, K), dtype=bool)
+    keep[:, 0] = True
+
+    def marginal(d):
+        return max(r ** d, floor)
+
+    for d in range(1, K):
+        rate = marginal(d) / marginal(d - 1)
+        for p in range(d, n):
+            keep[p, d] = keep[p - 1, d - 1] and U[p, d] < rate
+    return keep
+
+
+def cod_rows(keep):
+    """Retained grid indices p*K + d in ascending (position-major) order."""
+    n, K = keep.shape
+    return np.array([p * K + d for p in range(n) for d in range(K) if keep[p, d]],
+                    dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Attention visibility ([RH] "Flex-attention mask"; chain structure of
+# [PN] 3.2).  A cell (p, d) belongs to the rollout anchored at a = p - d.
+# ---------------------------------------------------------------------------
+
+
+def mask_allowed(p, d, pk, dk):
+    """May query cell (p, d) attend to key cell (pk, dk)?
+
+    Depth-0 keys are visible up to and including the query's anchor; a
+    deeper key is visible when it lies on the query's own rollout chain at a
+    depth not beyond the query's.
+    """
+    a = p - d
+    if dk == 0:
+        return pk <= a
+    return (pk - dk == a) and dk <= d
+
+
+def mask_fresh(rows, K):
+    """Mask over retained grid rows built cell by cell from the predicate."""
+    rows = np.asarray(rows)
+    L = len(rows)
+    m = np.zeros((L, L), dtype=bool)
+    for i in range(L):
+        p, d = divmod(int(rows[i]), K)
+        for j in range(L):
+            pk, dk = divmod(int(rows[j]), K)
+            m[i, j] = mask_allowed(p, d, pk, dk)
+    return m
+
+
+def mask_precompute(n_max, K):
+    """Full position-major grid mask for the longest sequence, built once
+    ([PN] 3.1: precompute at the maximum length, then slice)."""
+    return mask_fresh(np.arange(n_max * K), K)
+
+
+def mask_slice(m_pre, n, K, rows):
+    """Top-left [nK, nK] slice of the precomputed mask, then the retained
+    rows and columns of one COD sample ([PN] 3.1)."""
+    s = m_pre[:n * K, :n * K]
+    rows = np.asarray(rows)
+    return s[np.ix_(rows, rows)]
+
+
+# ---------------------------------------------------------------------------
+# Sequence partitioning ([PN] 3.2 and its invariant
+# Chunk(p, d) = Chunk(p-1, d-1) for d >= 2).
+# ---------------------------------------------------------------------------
+
+
+def partition(n, K, S, rows):
+    """Chunk of every retained row and the depth-0 completion of each chunk.
+
+    Segments are equal-width index ranges b_s = floor(s n / S).  Depth-0 and
+    depth-1 cells go to the segment of their position; a deeper cell goes to
+    the chunk of its parent (p-1, d-1).  Chunk s is completed with every
+    depth-0 row whose position lies before the end of segment s.
+    Returns (chunk_of_row [L], bounds [S+1], completion list of position
+    arrays).
+    """
+    bounds = [(s * n) // S for s in range(S + 1)]
+
+    def seg(p):
+        for s in range(S):
+            if bounds[s] <= p < bounds[s + 1]:
+                return s
+        raise ValueError(p)
+
+    chunk = {}
+    for r in sorted(int(x) for x in rows):   # position-major: parents come first
+        p, d = divmod(r, K)
+        if d <= 1:
+            chunk[(p, d)] = seg(p)
+        else:
+            chunk[(p, d)] = chunk[(p - 1, d - 1)]
+    chunk_of_row = np.array([chunk[divmod(int(r), K)] for r in rows], dtype=np.int64)
+    completion = [np.arange(0, bounds[s + 1]) for s in range(S)]
+    return chunk_of_row, np.array(bounds), completion
+
+
+# ---------------------------------------------------------------------------
+# Training-shape forward over a COD layout ([TD] "Memory and Training
+# Complexity"; [PN] 3 and 3.2; visibility from [RH] "Flex-attention mask").
+# ---------------------------------------------------------------------------
+
+
+def train_forward(w, cfg, hidden3, token_ids, mask_emb, h_shared, rows, K, N=None,
+                  lm_rows=None, return_kv=False):
+    """Logits of retained grid rows of one sequence.
+
+    Row (p, d) takes E[x_p] + fc(h_p) at depth 0 and mask_emb + fc(h_shared)
+    deeper, sits at RoPE position p, and attends to the retained rows the
+    predicate allows (its anchor's depth-0 prefix and its own chain).
+    ``w["embed_rows"]`` holds E[token_ids[p]] for every position p.
+    ``lm_rows`` optionally restricts the LM head to those indices into
+    ``rows`` (the layers always run on every row).  Returns logits
+    [len(lm_rows) or L, V]; with ``return_kv`` also the per-layer rotated
+    keys and values [L, n_kv, hd].
+    """
+    N = cfg.n_layers if N is None else N
+    rows = np.asarray(rows, dtype=np.int64)
+    L = len(rows)
+    P, D = rows // K, rows % K
+    nq, nkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    G = nq // nkv
+    scale = 1.0 / math.sqrt(hd)
+    hid = np.asarray(hidden3, F64)
+    ntp = linear(hid, w["fc"])
+    mtp = linear(np.asarray(h_shared, F64)[None], w["fc"])[0]
+    x = np.empty((L, cfg.hidden), dtype=F64)
+    for i in range(L):
+        if D[i] == 0:
+            x[i] = np.asarray(w["embed_rows"][P[i]], F64) + ntp[P[i]]
+        else:
+            x[i] = np.asarray(mask_emb, F64) + mtp
+    # Keys each row may see: depth-0 rows of positions <= anchor, then the
+    # row's own chain (depths 1..d at the same anchor).
+    index = {(int(P[i]), int(D[i])): i for i in range(L)}
+    depth0 = np.array([index[(p, 0)] for p in range(int(P.max()) + 1)]) if L else np.zeros(0, int)
+    kv_out = []
+    for l in range(N):
+        lw = w["layers"][l]
+        q, k, v = _layer_qkv(x, lw, cfg)
+        q = rope(q, P[:, None].astype(F64), cfg.rope_theta)
+        k = rope(k, P[:, None].astype(F64), cfg.rope_theta)
+        kv_out.append((k.copy(), v.copy()))
+        attn = np.zeros((L, nq, hd), dtype=F64)
+        # With one layer and a restricted LM head, rows outside lm_rows feed
+        # nothing but their keys and values, so their attention is skipped.
+        need = range(L) if (lm_rows is None or l + 1 < N) else [int(t) for t in lm_rows]
+        for i in need:
+            a = int(P[i] - D[i])
+            keys_idx = list(depth0[:a + 1]) + [index[(a + dd, dd)] for dd in range(1, int(D[i]) + 1)]
+            for g in range(nkv):
+                attn[i, g * G:(g + 1) * G] = attend(q[i, g * G:(g + 1) * G],
+                                                    k[keys_idx, g], v[keys_idx, g], scale)
+        if l + 1 == N and lm_rows is not None:
+            sel = np.asarray(lm_rows)
+            x = x[sel]
+            attn = attn[sel]
+        x = _layer_finish(x, attn.reshape(len(x), nq * hd), lw, cfg)
+    z = rmsnorm(x, w["final_norm"], cfg.rms_eps)
+    sel = np.arange(len(z)) if (lm_rows is None or N > 0) else np.asarray(lm_rows)
+    logits = linear(z[sel], w["lm_head"])
+    if return_kv:
+        return logits, kv_out
+    return logits
