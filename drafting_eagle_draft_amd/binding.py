@@ -1,0 +1,167 @@
+"""ctypes binding of libpeagle.so: the C ABI of include/peagle.h, one Python
+function per entry point with the same name.  Argument marshalling only --
+every step of the drafter runs in the library's HIP kernels.
+
+Device pointers are passed as integers (e.g. ``tensor.data_ptr()``); streams
+as the integer HIP stream handle (``torch.cuda.current_stream().cuda_stream``).
+A missing or unloadable library raises immediately: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpeagle.so")
+
+PE_OK = 0
+PE_ERR_INVALID_ARGUMENT = -1
+PE_ERR_UNSUPPORTED = -2
+PE_ERR_WORKSPACE = -3
+PE_ERR_HIP = -4
+PE_F32 = 0
+PE_BF16 = 1
+PE_K_MAX = 16
+PE_DECODE_ROWS_MAX = 64
+
+EXPORTS = (
+    "pe_model_create", "pe_model_destroy", "pe_draft_workspace_size", "pe_workspace_init",
+    "pe_draft_forward", "pe_accept", "pe_last_error", "pe_version", "pe_profile_enable",
+    "pe_profile_read",
+)
+
+
+class PeConfig(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("intermediate", ctypes.c_int32), ("vocab", ctypes.c_int32),
+        ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
+    ]
+
+
+class PeLayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")]
+
+
+class PeWeights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("fc", ctypes.c_void_p),
+                ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(PeLayerWeights))]
+
+
+class PeagleError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} returned {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libpeagle.so once and declare the signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m drafting_eagle_draft_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "pe_model_create": [ctypes.POINTER(PeConfig), ctypes.POINTER(PeWeights), vp,
+                            ctypes.POINTER(vp)],
+        "pe_model_destroy": [vp],
+        "pe_draft_workspace_size": [vp, i32, i32, i64, ctypes.POINTER(sz)],
+        "pe_workspace_init": [vp, sz, vp],
+        "pe_draft_forward": [vp, i32, i32, i32, vp, vp, vp, vp, vp, i64, ctypes.POINTER(vp),
+                             ctypes.POINTER(vp), vp, vp, vp, sz, vp],
+        "pe_accept": [i32, i32, vp, vp, vp, vp, vp],
+        "pe_profile_enable": [vp, i32],
+        "pe_profile_read": [vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    L.pe_last_error.argtypes = []
+    L.pe_last_error.restype = ctypes.c_char_p
+    L.pe_version.argtypes = []
+    L.pe_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int):
+    if status != PE_OK:
+        raise PeagleError(fn, status, pe_last_error())
+
+
+def pe_last_error() -> str:
+    return load().pe_last_error().decode()
+
+
+def pe_version() -> str:
+    return load().pe_version().decode()
+
+
+def pe_model_create(cfg: PeConfig, weights: PeWeights, stream: int = 0) -> int:
+    out = ctypes.c_void_p()
+    _check("pe_model_create",
+           load().pe_model_create(ctypes.byref(cfg), ctypes.byref(weights), stream, ctypes.byref(out)))
+    return out.value
+
+
+def pe_model_destroy(model: int) -> None:
+    _check("pe_model_destroy", load().pe_model_destroy(model))
+
+
+def pe_draft_workspace_size(model: int, B: int, K: int, ctx_stride: int) -> int:
+    n = ctypes.c_size_t()
+    _check("pe_draft_workspace_size",
+           load().pe_draft_workspace_size(model, B, K, ctx_stride, ctypes.byref(n)))
+    return n.value
+
+
+def pe_workspace_init(workspace: int, ws_bytes: int, stream: int = 0) -> None:
+    _check("pe_workspace_init", load().pe_workspace_init(workspace, ws_bytes, stream))
+
+
+def _ptr_array(ptrs):
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p
+    return arr
+
+
+def pe_draft_forward(model: int, N: int, B: int, K: int, hidden3: int, token_ids: int,
+                     mask_emb: int, h_shared: int, ctx_lens: int, ctx_stride: int,
+                     k_cache, v_cache, draft_out: int, logits_out: int | None,
+                     workspace: int, ws_bytes: int, stream: int = 0) -> None:
+    """k_cache / v_cache: sequences of N device pointers (one per layer)."""
+    kc = _ptr_array(list(k_cache)) if k_cache is not None else None
+    vc = _ptr_array(list(v_cache)) if v_cache is not None else None
+    _check("pe_draft_forward", load().pe_draft_forward(
+        model, N, B, K, hidden3, token_ids, mask_emb, h_shared, ctx_lens, ctx_stride,
+        ctypes.cast(kc, ctypes.POINTER(ctypes.c_void_p)) if kc is not None else None,
+        ctypes.cast(vc, ctypes.POINTER(ctypes.c_void_p)) if vc is not None else None,
+        draft_out, logits_out, workspace, ws_bytes, stream))
+
+
+def pe_accept(B: int, K: int, draft: int, target: int, accept_len: int,
+              out_tokens: int | None = None, stream: int = 0) -> None:
+    _check("pe_accept", load().pe_accept(B, K, draft, target, accept_len, out_tokens, stream))
+
+
+def pe_profile_enable(model: int, enable: bool) -> None:
+    _check("pe_profile_enable", load().pe_profile_enable(model, 1 if enable else 0))
+
+
+def pe_profile_read(model: int):
+    """(launch count, mean LM-head launch duration in ms) since enable/last read."""
+    n = ctypes.c_int32()
+    ms = ctypes.c_double()
+    _check("pe_profile_read", load().pe_profile_read(model, ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value

@@ -1,0 +1,549 @@
+// api.hip -- the C ABI (include/peagle.h): argument validation, weight
+// tiling, workspace planning and the launch sequence of the draft forward.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/peagle.h"
+#include "pe_internal.hpp"
+
+using namespace pe;
+
+namespace {
+
+thread_local std::string g_err;
+
+pe_status fail(pe_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+pe_status hip_fail(hipError_t e, const char *what) {
+  return fail(PE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int env_int(const char *name, int dflt) {
+  const char *v = getenv(name);
+  if (!v || !*v) return dflt;
+  return atoi(v);
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int kPipe = 8;  // tile loads in flight per GEMM wave (kernel constant)
+
+struct Tiled {
+  u32x4 *ptr = nullptr;
+  int N = 0, K = 0, NT = 0, KT = 0;
+};
+
+struct LayerT {
+  Tiled qkv, o, gateup, down;
+  float *attn_norm = nullptr, *mlp_norm = nullptr;
+};
+
+struct GemmPlan {
+  long T;
+  int U;
+  int wpb;
+};
+
+}  // namespace
+
+struct pe_model {
+  pe_config cfg;
+  int ktile = 32;      // contraction elements per tile
+  size_t esz = 2;      // bytes per dtype element
+  int num_cus = 256;
+  int wpc = 16;        // GEMM waves per CU
+  int min_tiles = 8;   // minimum tiles per GEMM wave
+  int lm_wpc = 16;     // LM-head waves per CU
+  int attn_blocks_per_cu = 1;
+  Tiled fc, lm;
+  std::vector<LayerT> layers;
+  float *final_norm = nullptr;
+  double *inv_freq = nullptr;
+  const void *embed = nullptr;
+  std::vector<void *> allocs;
+  // optional LM-head timing
+  mutable bool prof = false;
+  mutable std::vector<hipEvent_t> ev0, ev1;
+  mutable int nrec = 0;
+};
+
+namespace {
+
+GemmPlan plan_gemm(const pe_model *m, const Tiled &t, bool lm) {
+  GemmPlan p;
+  p.T = (long)t.NT * t.KT;
+  const long cap = (long)m->num_cus * (lm ? m->lm_wpc : m->wpc);
+  long u = (p.T + m->min_tiles - 1) / m->min_tiles;
+  if (u > cap) u = cap;
+  if (u < 1) u = 1;
+  p.U = (int)u;
+  p.wpb = lm ? 8 : 4;
+  return p;
+}
+
+struct AttnPlan {
+  int L, S;
+};
+
+AttnPlan plan_attn(const pe_model *m, int B, int K, long C) {
+  const int bg = B * m->cfg.n_kv_heads;
+  long target = ((long)m->num_cus * m->attn_blocks_per_cu + bg - 1) / bg;
+  if (target < 1) target = 1;
+  const long keys = C + K;
+  long tiles = (keys + 63) / 64;
+  long per = (tiles + target - 1) / target;
+  if (per < 1) per = 1;
+  AttnPlan a;
+  a.L = (int)(per * 64);
+  a.S = (int)((keys + a.L - 1) / a.L);
+  if (a.S < 1) a.S = 1;
+  return a;
+}
+
+struct WsLayout {
+  size_t xres, xg, ssq, q, kb, vb, attn_out, mlp_h, gpart, gctr, apart, actr, blk, done, total;
+  int RP;
+  AttnPlan ap;
+  GemmPlan lm;
+};
+
+WsLayout layout(const pe_model *m, int B, int K, long C) {
+  const pe_config &c = m->cfg;
+  WsLayout w;
+  const int G = c.n_q_heads / c.n_kv_heads;
+  const int R = K * G;
+  w.RP = (R + 15) / 16 * 16;
+  w.ap = plan_attn(m, B, K, C);
+  w.lm = plan_gemm(m, m->lm, true);
+  // Largest GEMM plan (partials) and largest strip count (counters).
+  long umax = w.lm.U;
+  int ntmax = m->lm.NT;
+  auto upd = [&](const Tiled &t) {
+    GemmPlan g = plan_gemm(m, t, false);
+    if (g.U > umax) umax = g.U;
+    if (t.NT > ntmax) ntmax = t.NT;
+  };
+  upd(m->fc);
+  for (const LayerT &L : m->layers) {
+    upd(L.qkv); upd(L.o); upd(L.gateup); upd(L.down);
+  }
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  const size_t H = c.hidden, esz = m->esz;
+  w.xres = take((size_t)kMaxRows * H * 4);
+  w.xg = take((size_t)kMaxRows * H * esz);
+  w.ssq = take((size_t)(H / 16) * kMaxRows * 4);
+  w.q = take((size_t)B * c.n_kv_heads * w.RP * c.head_dim * esz);
+  w.kb = take((size_t)B * c.n_kv_heads * K * c.head_dim * esz);
+  w.vb = take((size_t)B * c.n_kv_heads * K * c.head_dim * esz);
+  w.attn_out = take((size_t)kMaxRows * c.n_q_heads * c.head_dim * esz);
+  w.mlp_h = take((size_t)kMaxRows * c.intermediate * esz);
+  w.gpart = take((size_t)2 * umax * 4 * 64 * 16);
+  w.gctr = take((size_t)ntmax * 4);
+  const size_t qparts = (size_t)(w.RP + 63) / 64;
+  w.apart = take((size_t)B * c.n_kv_heads * qparts * w.ap.S * (64 * (size_t)c.head_dim + 128) * 4);
+  w.actr = take((size_t)B * c.n_kv_heads * qparts * 4);
+  const int lm_blocks = (w.lm.U + w.lm.wpb - 1) / w.lm.wpb;
+  w.blk = take((size_t)lm_blocks * kMaxRows * 8);
+  w.done = take(64);
+  w.total = off;
+  return w;
+}
+
+pe_status tile_matrix(pe_model *m, Tiled &t, const void *const *srcs, const int *rows, int nsrc,
+                      int N, int K, int map, hipStream_t s) {
+  t.N = N;
+  t.K = K;
+  t.NT = (N + 15) / 16;
+  t.KT = (K + m->ktile - 1) / m->ktile;
+  const size_t bytes = (size_t)t.NT * t.KT * 1024;
+  hipError_t e = hipMalloc(&t.ptr, bytes);
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(weight tiles)");
+  m->allocs.push_back(t.ptr);
+  RepackParams rp{};
+  for (int i = 0; i < 3; ++i) {
+    rp.src[i] = i < nsrc ? srcs[i] : nullptr;
+    rp.src_rows[i] = i < nsrc ? rows[i] : 0x7FFFFFFF;
+  }
+  rp.N = N; rp.K = K; rp.NT = t.NT; rp.KT = t.KT; rp.map = map;
+  rp.hd = m->cfg.head_dim; rp.nq = m->cfg.n_q_heads; rp.nkv = m->cfg.n_kv_heads;
+  rp.I = m->cfg.intermediate; rp.dst = t.ptr;
+  e = launch_repack(m->cfg.dtype, rp, s);
+  if (e != hipSuccess) return hip_fail(e, "weight tiling launch");
+  return PE_OK;
+}
+
+pe_status gain_copy(pe_model *m, const void *src, float *&dst, hipStream_t s) {
+  hipError_t e = hipMalloc(&dst, (size_t)m->cfg.hidden * 4);
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(gain)");
+  m->allocs.push_back(dst);
+  e = launch_gain_to_f32(m->cfg.dtype, src, dst, m->cfg.hidden, s);
+  if (e != hipSuccess) return hip_fail(e, "gain conversion launch");
+  return PE_OK;
+}
+
+void destroy(pe_model *m) {
+  if (!m) return;
+  for (void *p : m->allocs) (void)hipFree(p);
+  for (hipEvent_t ev : m->ev0) (void)hipEventDestroy(ev);
+  for (hipEvent_t ev : m->ev1) (void)hipEventDestroy(ev);
+  delete m;
+}
+
+pe_status check_cfg(const pe_config *c) {
+  if (c->dtype != PE_F32 && c->dtype != PE_BF16)
+    return fail(PE_ERR_INVALID_ARGUMENT, "dtype %d is neither PE_F32 nor PE_BF16", c->dtype);
+  const int ktile = c->dtype == PE_BF16 ? 32 : 16;
+  const int kmin = kPipe * ktile;  // each contraction spans at least kPipe tiles
+  if (c->hidden <= 0 || c->n_layers < 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->head_dim <= 0 || c->intermediate <= 0 || c->vocab <= 0)
+    return fail(PE_ERR_INVALID_ARGUMENT, "config sizes must be positive (n_layers >= 0)");
+  if (c->n_q_heads % c->n_kv_heads)
+    return fail(PE_ERR_INVALID_ARGUMENT, "n_q_heads %d is not a multiple of n_kv_heads %d",
+                c->n_q_heads, c->n_kv_heads);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PE_ERR_UNSUPPORTED, "head_dim %d: supported 64, 128", c->head_dim);
+  if (c->dtype == PE_F32 && c->head_dim != 64)
+    return fail(PE_ERR_UNSUPPORTED, "fp32 models support head_dim 64 only");
+  if (c->hidden % 16 || c->vocab % 16 || c->intermediate % 8)
+    return fail(PE_ERR_UNSUPPORTED, "hidden and vocab must be multiples of 16, intermediate of 8");
+  if (c->hidden < kmin || c->intermediate < kmin || c->n_q_heads * c->head_dim < kmin)
+    return fail(PE_ERR_UNSUPPORTED, "hidden, intermediate and n_q_heads*head_dim must be >= %d",
+                kmin);
+  if (c->n_q_heads / c->n_kv_heads * PE_K_MAX > 256)
+    return fail(PE_ERR_UNSUPPORTED, "query heads per kv head must be <= 16");
+  if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f))
+    return fail(PE_ERR_INVALID_ARGUMENT, "rope_theta must be > 0 and rms_eps >= 0");
+  return PE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pe_last_error(void) { return g_err.c_str(); }
+
+const char *pe_version(void) {
+  return "peagle-gfx950 stream-K MFMA GEMM + MFMA split-KV decode attention";
+}
+
+pe_status pe_model_create(const pe_config *cfg, const pe_weights *w, void *stream, pe_model **out) {
+  if (!cfg || !w || !out) return fail(PE_ERR_INVALID_ARGUMENT, "cfg, w and out must be non-NULL");
+  *out = nullptr;
+  pe_status st = check_cfg(cfg);
+  if (st != PE_OK) return st;
+  if (!w->embed || !w->fc || !w->final_norm || !w->lm_head || (cfg->n_layers > 0 && !w->layers))
+    return fail(PE_ERR_INVALID_ARGUMENT, "a required weight pointer is NULL");
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const pe_layer_weights &L = w->layers[l];
+    if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.mlp_norm || !L.w_gate || !L.w_up ||
+        !L.w_down)
+      return fail(PE_ERR_INVALID_ARGUMENT, "layer %d has a NULL weight pointer", l);
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  pe_model *m = new pe_model();
+  m->cfg = *cfg;
+  m->ktile = cfg->dtype == PE_BF16 ? 32 : 16;
+  m->esz = cfg->dtype == PE_BF16 ? 2 : 4;
+  m->embed = w->embed;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) { destroy(m); return hip_fail(e, "hipGetDevice"); }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) { destroy(m); return hip_fail(e, "hipDeviceGetAttribute"); }
+  m->num_cus = cus > 0 ? cus : 256;
+  m->wpc = env_int("PE_GEMM_WAVES_PER_CU", 16);
+  m->min_tiles = env_int("PE_GEMM_MIN_TILES", 8);
+  m->lm_wpc = env_int("PE_LM_WAVES_PER_CU", 16);
+  m->attn_blocks_per_cu = env_int("PE_ATTN_BLOCKS_PER_CU", 1);
+  if (m->wpc < 1) m->wpc = 1;
+  if (m->min_tiles < 1) m->min_tiles = 1;
+  if (m->lm_wpc < 1) m->lm_wpc = 1;
+  if (m->attn_blocks_per_cu < 1) m->attn_blocks_per_cu = 1;
+
+  const int H = cfg->hidden, hd = cfg->head_dim, nq = cfg->n_q_heads, nkv = cfg->n_kv_heads;
+  const int I = cfg->intermediate;
+  {
+    const void *srcs[1] = {w->fc};
+    const int rows[1] = {H};
+    if ((st = tile_matrix(m, m->fc, srcs, rows, 1, H, 3 * H, MAP_IDENTITY, s)) != PE_OK) {
+      destroy(m); return st;
+    }
+  }
+  {
+    const void *srcs[1] = {w->lm_head};
+    const int rows[1] = {cfg->vocab};
+    if ((st = tile_matrix(m, m->lm, srcs, rows, 1, cfg->vocab, H, MAP_IDENTITY, s)) != PE_OK) {
+      destroy(m); return st;
+    }
+  }
+  m->layers.resize(cfg->n_layers);
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const pe_layer_weights &L = w->layers[l];
+    LayerT &T = m->layers[l];
+    const void *qkv_src[3] = {L.wq, L.wk, L.wv};
+    const int qkv_rows[3] = {nq * hd, nkv * hd, nkv * hd};
+    const void *o_src[1] = {L.wo};
+    const int o_rows[1] = {H};
+    const void *gu_src[2] = {L.w_gate, L.w_up};
+    const int gu_rows[2] = {I, I};
+    const void *d_src[1] = {L.w_down};
+    const int d_rows[1] = {H};
+    if ((st = tile_matrix(m, T.qkv, qkv_src, qkv_rows, 3, (nq + 2 * nkv) * hd, H, MAP_QKV, s)) ||
+        (st = tile_matrix(m, T.o, o_src, o_rows, 1, H, nq * hd, MAP_IDENTITY, s)) ||
+        (st = tile_matrix(m, T.gateup, gu_src, gu_rows, 2, 2 * I, H, MAP_GATEUP, s)) ||
+        (st = tile_matrix(m, T.down, d_src, d_rows, 1, H, I, MAP_IDENTITY, s)) ||
+        (st = gain_copy(m, L.attn_norm, T.attn_norm, s)) ||
+        (st = gain_copy(m, L.mlp_norm, T.mlp_norm, s))) {
+      destroy(m);
+      return st;
+    }
+  }
+  if ((st = gain_copy(m, w->final_norm, m->final_norm, s)) != PE_OK) { destroy(m); return st; }
+  {
+    std::vector<double> f(hd / 2);
+    for (int i = 0; i < hd / 2; ++i) f[i] = pow((double)cfg->rope_theta, -2.0 * i / hd);
+    e = hipMalloc(&m->inv_freq, f.size() * sizeof(double));
+    if (e != hipSuccess) { destroy(m); return hip_fail(e, "hipMalloc(inv_freq)"); }
+    m->allocs.push_back(m->inv_freq);
+    e = hipMemcpyAsync(m->inv_freq, f.data(), f.size() * sizeof(double), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) { destroy(m); return hip_fail(e, "hipMemcpyAsync(inv_freq)"); }
+  }
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) { destroy(m); return hip_fail(e, "hipStreamSynchronize after weight tiling"); }
+  *out = m;
+  return PE_OK;
+}
+
+pe_status pe_model_destroy(pe_model *m) {
+  if (!m) return fail(PE_ERR_INVALID_ARGUMENT, "model is NULL");
+  destroy(m);
+  return PE_OK;
+}
+
+pe_status pe_draft_workspace_size(const pe_model *m, int32_t B, int32_t K, int64_t ctx_stride,
+                                  size_t *bytes) {
+  if (!m || !bytes) return fail(PE_ERR_INVALID_ARGUMENT, "model and bytes must be non-NULL");
+  if (B < 1 || K < 1 || K > PE_K_MAX || B * K > PE_DECODE_ROWS_MAX || B + 1 > PE_DECODE_ROWS_MAX)
+    return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d outside 1<=K<=%d, B*K<=%d, B+1<=%d", B, K, PE_K_MAX,
+                PE_DECODE_ROWS_MAX, PE_DECODE_ROWS_MAX);
+  if (ctx_stride < 0) return fail(PE_ERR_INVALID_ARGUMENT, "ctx_stride must be >= 0");
+  *bytes = layout(m, B, K, ctx_stride).total;
+  return PE_OK;
+}
+
+pe_status pe_workspace_init(void *workspace, size_t ws_bytes, void *stream) {
+  if (!workspace) return fail(PE_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  hipError_t e = launch_zero(workspace, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "workspace zero launch");
+  return PE_OK;
+}
+
+pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K, const void *hidden3,
+                           const int32_t *token_ids, const void *mask_emb, const void *h_shared,
+                           const int32_t *ctx_lens, int64_t ctx_stride, const void *const *k_cache,
+                           const void *const *v_cache, int32_t *draft_out, float *logits_out,
+                           void *workspace, size_t ws_bytes, void *stream) {
+  if (!m) return fail(PE_ERR_INVALID_ARGUMENT, "model is NULL");
+  const pe_config &c = m->cfg;
+  if (N < 0 || N > c.n_layers)
+    return fail(PE_ERR_INVALID_ARGUMENT, "N=%d outside [0, n_layers=%d]", N, c.n_layers);
+  if (B < 1 || K < 1 || K > PE_K_MAX || B * K > PE_DECODE_ROWS_MAX || B + 1 > PE_DECODE_ROWS_MAX)
+    return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d outside 1<=K<=%d, B*K<=%d, B+1<=%d", B, K, PE_K_MAX,
+                PE_DECODE_ROWS_MAX, PE_DECODE_ROWS_MAX);
+  if (!hidden3 || !token_ids || !mask_emb || !h_shared || !draft_out)
+    return fail(PE_ERR_INVALID_ARGUMENT, "hidden3, token_ids, mask_emb, h_shared and draft_out "
+                                         "must be non-NULL");
+  if (ctx_stride < 0) return fail(PE_ERR_INVALID_ARGUMENT, "ctx_stride must be >= 0");
+  if (N > 0) {
+    if (!ctx_lens || !k_cache || !v_cache)
+      return fail(PE_ERR_INVALID_ARGUMENT, "ctx_lens, k_cache and v_cache must be non-NULL when N > 0");
+    for (int l = 0; l < N; ++l) {
+      if (!k_cache[l] || !v_cache[l])
+        return fail(PE_ERR_INVALID_ARGUMENT, "cache pointer of layer %d is NULL", l);
+      if (misaligned(k_cache[l]) || misaligned(v_cache[l]))
+        return fail(PE_ERR_INVALID_ARGUMENT, "cache pointer of layer %d is not 16-byte aligned", l);
+    }
+  }
+  if (misaligned(hidden3) || misaligned(mask_emb) || misaligned(h_shared) ||
+      (logits_out && misaligned(logits_out)) || misaligned(workspace))
+    return fail(PE_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  if (!workspace) return fail(PE_ERR_WORKSPACE, "workspace is NULL");
+  const WsLayout W = layout(m, B, K, ctx_stride);
+  if (ws_bytes < W.total)
+    return fail(PE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char *ws = reinterpret_cast<char *>(workspace);
+  float *xres = reinterpret_cast<float *>(ws + W.xres);
+  void *xg = ws + W.xg;
+  float *ssq = reinterpret_cast<float *>(ws + W.ssq);
+  const int M = B * K;
+  const int nf = (M + 15) / 16;
+  const int H = c.hidden, hd = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const int G = nq / nkv;
+
+  GemmParams base{};
+  base.part = reinterpret_cast<floatx4 *>(ws + W.gpart);
+  base.ctr = reinterpret_cast<int *>(ws + W.gctr);
+  base.H = H;
+  base.Kb = K;
+  base.B = B;
+  base.eps = c.rms_eps;
+  base.inv_width = 1.0f / (float)H;
+
+  auto run = [&](const Tiled &t, int epi, int nfr, GemmParams p, bool lm) -> pe_status {
+    const GemmPlan pl = plan_gemm(m, t, lm);
+    p.wt = t.ptr; p.NT = t.NT; p.KT = t.KT; p.N = t.N; p.K = t.K;
+    p.T = pl.T; p.U = pl.U;
+    hipError_t e = launch_gemm(c.dtype, nfr, epi, p, pl.wpb, s);
+    if (e != hipSuccess) return hip_fail(e, "GEMM launch");
+    return PE_OK;
+  };
+
+  pe_status st;
+  // Input fusion: fc over the B hidden rows plus h_shared, then embeddings.
+  {
+    GemmParams p = base;
+    p.act = hidden3; p.act_ld = 3L * H; p.act_rows = B; p.act_extra = h_shared;
+    p.M = B + 1;
+    p.xres = xres; p.xg = xg; p.ssq_out = ssq;
+    p.gnext = N > 0 ? m->layers[0].attn_norm : m->final_norm;
+    p.embed = m->embed; p.tok = token_ids; p.mask_emb = mask_emb; p.V = c.vocab;
+    if ((st = run(m->fc, EPI_FC, (B + 1 + 15) / 16, p, false)) != PE_OK) return st;
+  }
+  for (int l = 0; l < N; ++l) {
+    const LayerT &L = m->layers[l];
+    {
+      GemmParams p = base;
+      p.act = xg; p.act_ld = H; p.act_rows = M; p.M = M;
+      p.ssq = ssq; p.ssq_strips = H / 16;
+      p.q = ws + W.q; p.kb = ws + W.kb; p.vb = ws + W.vb;
+      p.ctx_lens = ctx_lens; p.inv_freq = m->inv_freq;
+      p.nq = nq; p.nkv = nkv; p.hd = hd; p.RP = W.RP;
+      p.C = ctx_stride;
+      if ((st = run(L.qkv, EPI_QKV, nf, p, false)) != PE_OK) return st;
+    }
+    {
+      AttnParams a{};
+      a.q = ws + W.q; a.kb = ws + W.kb; a.vb = ws + W.vb;
+      a.kc = k_cache[l]; a.vc = v_cache[l];
+      a.ctx_lens = ctx_lens; a.C = ctx_stride;
+      a.B = B; a.Kb = K; a.nq = nq; a.nkv = nkv; a.hd = hd; a.G = G; a.R = K * G; a.RP = W.RP;
+      a.L = W.ap.L; a.S = W.ap.S;
+      a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+      a.out = ws + W.attn_out;
+      a.part = reinterpret_cast<float *>(ws + W.apart);
+      a.ctr = reinterpret_cast<int *>(ws + W.actr);
+      hipError_t e = launch_attention(c.dtype, a, s);
+      if (e != hipSuccess) return hip_fail(e, "attention launch");
+    }
+    {
+      GemmParams p = base;
+      p.act = ws + W.attn_out; p.act_ld = (long)nq * hd; p.act_rows = M; p.M = M;
+      p.xres = xres; p.xg = xg; p.ssq_out = ssq; p.gnext = L.mlp_norm;
+      if ((st = run(L.o, EPI_RESID, nf, p, false)) != PE_OK) return st;
+    }
+    {
+      GemmParams p = base;
+      p.act = xg; p.act_ld = H; p.act_rows = M; p.M = M;
+      p.ssq = ssq; p.ssq_strips = H / 16;
+      p.hout = ws + W.mlp_h; p.I = c.intermediate;
+      if ((st = run(L.gateup, EPI_SWIGLU, nf, p, false)) != PE_OK) return st;
+    }
+    {
+      GemmParams p = base;
+      p.act = ws + W.mlp_h; p.act_ld = c.intermediate; p.act_rows = M; p.M = M;
+      p.xres = xres; p.xg = xg; p.ssq_out = ssq;
+      p.gnext = (l + 1 < N) ? m->layers[l + 1].attn_norm : m->final_norm;
+      if ((st = run(L.down, EPI_RESID, nf, p, false)) != PE_OK) return st;
+    }
+  }
+  // LM head with fused argmax.
+  {
+    GemmParams p = base;
+    p.act = xg; p.act_ld = H; p.act_rows = M; p.M = M;
+    p.ssq = ssq; p.ssq_strips = H / 16;
+    p.logits = logits_out;
+    p.blk_best = reinterpret_cast<unsigned long long *>(ws + W.blk);
+    p.done_ctr = reinterpret_cast<int *>(ws + W.done);
+    p.draft_out = draft_out;
+    p.V = c.vocab;
+    const bool prof = m->prof && m->nrec < (int)m->ev0.size();
+    if (prof) (void)hipEventRecord(m->ev0[m->nrec], s);
+    if ((st = run(m->lm, EPI_ARGMAX, nf, p, true)) != PE_OK) return st;
+    if (prof) {
+      (void)hipEventRecord(m->ev1[m->nrec], s);
+      ++m->nrec;
+    }
+  }
+  return PE_OK;
+}
+
+pe_status pe_accept(int32_t B, int32_t K, const int32_t *draft, const int32_t *target,
+                    int32_t *accept_len, int32_t *out_tokens, void *stream) {
+  if (B < 0) return fail(PE_ERR_INVALID_ARGUMENT, "B=%d must be >= 0", B);
+  if (K < 1 || K > PE_K_MAX) return fail(PE_ERR_INVALID_ARGUMENT, "K=%d outside [1, %d]", K, PE_K_MAX);
+  if (B == 0) return PE_OK;
+  if (!draft || !target || !accept_len)
+    return fail(PE_ERR_INVALID_ARGUMENT, "draft, target and accept_len must be non-NULL");
+  hipError_t e = launch_accept(B, K, draft, target, accept_len, out_tokens,
+                               reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "accept launch");
+  return PE_OK;
+}
+
+pe_status pe_profile_enable(pe_model *m, int32_t enable) {
+  if (!m) return fail(PE_ERR_INVALID_ARGUMENT, "model is NULL");
+  if (enable && m->ev0.empty()) {
+    const int n = 4096;
+    m->ev0.resize(n);
+    m->ev1.resize(n);
+    for (int i = 0; i < n; ++i) {
+      hipError_t e = hipEventCreate(&m->ev0[i]);
+      if (e == hipSuccess) e = hipEventCreate(&m->ev1[i]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+  }
+  m->prof = enable != 0;
+  m->nrec = 0;
+  return PE_OK;
+}
+
+pe_status pe_profile_read(pe_model *m, int32_t *count, double *mean_ms) {
+  if (!m || !count || !mean_ms) return fail(PE_ERR_INVALID_ARGUMENT, "NULL argument");
+  *count = m->nrec;
+  *mean_ms = 0.0;
+  if (m->nrec == 0) return PE_OK;
+  hipError_t e = hipEventSynchronize(m->ev1[m->nrec - 1]);
+  if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  double sum = 0.0;
+  for (int i = 0; i < m->nrec; ++i) {
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, m->ev0[i], m->ev1[i]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    sum += ms;
+  }
+  *mean_ms = sum / m->nrec;
+  m->nrec = 0;
+  return PE_OK;
+}
+
+}  // extern "C"

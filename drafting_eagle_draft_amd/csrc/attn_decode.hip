@@ -1,0 +1,297 @@
+// attn_decode.hip -- block-causal GQA attention of the K-row draft block.
+//
+// Query row k of sequence b (at RoPE position C_b + k) attends to the cached
+// context rows [0, C_b) and to the block's own rows 0..k ("Speeding LLM
+// inference with P-EAGLE in vLLM Speculators", section "Flex-attention mask",
+// restricted to one rollout: depth-0 base context up to the anchor plus the
+// rollout's own chain).  With grouped-query attention all G = nq/nkv query
+// heads of a kv head read the same keys, so one workgroup serves the
+// R = K*G query rows of a (sequence, kv head) pair from a single pass over
+// the keys: every 64-key tile is staged once in LDS and consumed by matrix
+// cores as two dense products per 16-query wave, S^T = K Q^T and
+// O^T += V^T P^T.  The key sequence (cache followed by the block) is split
+// over workgroups (split-KV); each split keeps an fp32 online softmax and
+// the last split to finish combines all splits' partials in split order.
+//
+// Fragment mappings (see pe_device.hpp): for S^T the contraction over head
+// dims uses 16-byte runs of a key row; for O^T the contraction over keys
+// uses the layout S^T leaves in registers -- lane group g holds keys
+// 4g..4g+3 of each 16-key block -- so P never leaves registers:
+//   bf16: slots 0..3 = keys 32c+4g+i, slots 4..7 = keys 32c+16+4g+i;
+//   fp32: slot j of 16-key block kb = key 16kb+4g+j.
+#include "pe_internal.hpp"
+
+namespace pe {
+
+namespace {
+
+template <typename T, int HD>
+struct AttnShape {
+  static constexpr int E = Frag<T>::E;
+  static constexpr int KTILE = Frag<T>::KTILE;
+  static constexpr int NC = HD / KTILE;   // q fragments per query row
+  static constexpr int ND = HD / 16;      // 16-dim output blocks
+  static constexpr int KS = HD + E;       // Ks row stride (elements), 16-byte aligned
+  static constexpr int VS = 64 + 4;       // Vt row stride (elements)
+  static constexpr int CPR = HD / E;      // 16-byte chunks per key row
+  static constexpr int CHUNKS = 64 * CPR; // chunks per 64-key tile
+  static constexpr int NTHR = 256;        // staging threads (minimum block size)
+  static constexpr int MAXC = CHUNKS / NTHR;
+};
+
+__device__ __forceinline__ u32x4 lds16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ uint2 lds8(const void *p) { return *reinterpret_cast<const uint2 *>(p); }
+
+template <typename T>
+__device__ __forceinline__ void store_out4(T *dst, const float v[4]);
+template <>
+__device__ __forceinline__ void store_out4<float>(float *dst, const float v[4]) {
+  *reinterpret_cast<floatx4 *>(dst) = floatx4{v[0], v[1], v[2], v[3]};
+}
+template <>
+__device__ __forceinline__ void store_out4<bf16_t>(bf16_t *dst, const float v[4]) {
+  uint2 w;
+  w.x = pack_bf16x2(v[0], v[1]);
+  w.y = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<uint2 *>(dst) = w;
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {
+  using S = AttnShape<T, HD>;
+  constexpr int E = S::E, KTILE = S::KTILE, NC = S::NC, ND = S::ND, KS = S::KS, VS = S::VS;
+  constexpr int CPR = S::CPR, CHUNKS = S::CHUNKS, MAXC = S::MAXC;
+  __shared__ __attribute__((aligned(16))) T Ks[64 * KS];
+  __shared__ __attribute__((aligned(16))) T Vt[HD * VS];
+  __shared__ int s_last;
+
+  // blockIdx.y = kv head * QP + query partition (64 query rows each).
+  const int QP = (p.RP + 63) / 64;
+  const int split = blockIdx.x, gk = blockIdx.y / QP, qp = blockIdx.y - gk * QP, b = blockIdx.z;
+  const int ctx = min(max(p.ctx_lens[b], 0), (int)p.C);  // out-of-range lengths are clamped
+  const int total = ctx + p.Kb;
+  const int Sb = (total + p.L - 1) / p.L;
+  if (split >= Sb) return;
+  const int j0 = split * p.L;
+  const int j1 = min(j0 + p.L, total);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int rq = 64 * qp + 16 * w + c16;    // this lane's query row in the group
+  const bool computes = 64 * qp + 16 * w < p.RP;
+  const int kp_q = rq / p.G;                // its block position
+
+  const long bg = (long)b * p.nkv + gk;
+  u32x4 qf[NC];
+  {
+    const T *qrow = reinterpret_cast<const T *>(p.q) + (bg * p.RP + rq) * HD;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      qf[c] = (computes && rq < p.R) ? ldg16(qrow + c * KTILE + g * E) : u32x4{0u, 0u, 0u, 0u};
+  }
+  const T *kc = reinterpret_cast<const T *>(p.kc) + bg * p.C * HD;
+  const T *vc = reinterpret_cast<const T *>(p.vc) + bg * p.C * HD;
+  const T *kbk = reinterpret_cast<const T *>(p.kb) + bg * p.Kb * HD;
+  const T *vbk = reinterpret_cast<const T *>(p.vb) + bg * p.Kb * HD;
+
+  u32x4 kreg[MAXC], vreg[MAXC];
+  auto gload = [&](int jt) {
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int id = tid + i * S::NTHR;
+      const int key = id / CPR, cc = id - key * CPR;
+      const int jj = jt + key;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (id < CHUNKS && tid < S::NTHR && jj < j1) {
+        const T *ks = (jj < ctx) ? kc + (long)jj * HD : kbk + (long)(jj - ctx) * HD;
+        const T *vs = (jj < ctx) ? vc + (long)jj * HD : vbk + (long)(jj - ctx) * HD;
+        kv = ldg16(ks + cc * E);
+        vv = ldg16(vs + cc * E);
+      }
+      kreg[i] = kv;
+      vreg[i] = vv;
+    }
+  };
+  auto lstore = [&]() {
+    if (tid >= S::NTHR) return;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int id = tid + i * S::NTHR;
+      const int key = id / CPR, cc = id - key * CPR;
+      *reinterpret_cast<u32x4 *>(&Ks[key * KS + cc * E]) = kreg[i];
+      T vals[E];
+      __builtin_memcpy(vals, &vreg[i], 16);
+#pragma unroll
+      for (int e = 0; e < E; ++e) Vt[(cc * E + e) * VS + key] = vals[e];
+    }
+  };
+
+  floatx4 oacc[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) oacc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_lane = 0.f;
+
+  gload(j0);
+  for (int jt = j0; jt < j1; jt += 64) {
+    lstore();
+    __syncthreads();
+    if (jt + 64 < j1) gload(jt + 64);
+    if (computes) {
+      floatx4 sacc[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        sacc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const u32x4 a = lds16(&Ks[(kb * 16 + c16) * KS + c * KTILE + g * E]);
+          sacc[kb] = Mma<T>::run(a, qf[c], sacc[kb]);
+        }
+      }
+      float sv[4][4];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int jj = jt + kb * 16 + 4 * g + r;
+          const bool ok = jj < j1 && (jj < ctx || jj - ctx <= kp_q);
+          sv[kb][r] = ok ? sacc[kb][r] * p.scale_log2 : -INFINITY;
+          mt = fmaxf(mt, sv[kb][r]);
+        }
+      mt = fmaxf(mt, shfl_xor_f(mt, 16));
+      mt = fmaxf(mt, shfl_xor_f(mt, 32));
+      const float m_new = fmaxf(m_run, mt);
+      float alpha = 1.f, msub = 0.f;
+      if (m_new != -INFINITY) {
+        alpha = exp2f(m_run - m_new);
+        msub = m_new;
+      }
+      float pv[4][4];
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pv[kb][r] = exp2f(sv[kb][r] - msub);
+          ps += pv[kb][r];
+        }
+      l_lane = l_lane * alpha + ps;
+      m_run = m_new;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const u32x4 bf = {pack_bf16x2(pv[2 * c2][0], pv[2 * c2][1]),
+                            pack_bf16x2(pv[2 * c2][2], pv[2 * c2][3]),
+                            pack_bf16x2(pv[2 * c2 + 1][0], pv[2 * c2 + 1][1]),
+                            pack_bf16x2(pv[2 * c2 + 1][2], pv[2 * c2 + 1][3])};
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            const T *vrow = &Vt[(d * 16 + c16) * VS + 32 * c2 + 4 * g];
+            const uint2 lo = lds8(vrow), hi = lds8(vrow + 16);
+            const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+            oacc[d] = Mma<T>::run(a, bf, oacc[d]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const u32x4 bf = {__float_as_uint(pv[kb][0]), __float_as_uint(pv[kb][1]),
+                            __float_as_uint(pv[kb][2]), __float_as_uint(pv[kb][3])};
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            const u32x4 a = lds16(&Vt[(d * 16 + c16) * VS + 16 * kb + 4 * g]);
+            oacc[d] = Mma<T>::run(a, bf, oacc[d]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  float l_tot = l_lane;
+  l_tot += shfl_xor_f(l_tot, 16);
+  l_tot += shfl_xor_f(l_tot, 32);
+
+  const int hq = p.nq * HD;
+  auto write_out = [&](const floatx4 (&o)[ND], float inv_l) {
+    if (!computes || rq >= p.R) return;
+    const int kp = rq / p.G, hl = rq - kp * p.G;
+    T *dst = reinterpret_cast<T *>(p.out) + (long)(b * p.Kb + kp) * hq + (gk * p.G + hl) * HD;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const float v[4] = {o[d][0] * inv_l, o[d][1] * inv_l, o[d][2] * inv_l, o[d][3] * inv_l};
+      store_out4<T>(dst + d * 16 + 4 * g, v);
+    }
+  };
+
+  if (Sb == 1) {
+    write_out(oacc, 1.0f / l_tot);
+    return;
+  }
+
+  // Partials of one split: 64 query rows x HD outputs, then 64 maxima and 64 sums.
+  const long stride = 64L * HD + 128;
+  const long bgq = bg * QP + qp;
+  const int rl = rq - 64 * qp;  // row within the partition
+  float *base = p.part + bgq * p.S * stride;
+  {
+    float *pp = base + (long)split * stride;
+    if (computes) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d) reinterpret_cast<floatx4 *>(pp)[(w * ND + d) * 64 + lane] = oacc[d];
+      if (g == 0) {
+        pp[64L * HD + rl] = m_run;
+        pp[64L * HD + 64 + rl] = l_tot;
+      }
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(p.ctr + bgq, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (old == Sb - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (computes) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < Sb; ++sp) M = fmaxf(M, base[sp * stride + 64L * HD + rl]);
+    floatx4 o[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) o[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+    for (int sp = 0; sp < Sb; ++sp) {
+      const float *pp = base + sp * stride;
+      const float sc = exp2f(pp[64L * HD + rl] - M);
+      l += sc * pp[64L * HD + 64 + rl];
+#pragma unroll
+      for (int d = 0; d < ND; ++d) o[d] += sc * reinterpret_cast<const floatx4 *>(pp)[(w * ND + d) * 64 + lane];
+    }
+    write_out(o, 1.0f / l);
+  }
+  if (tid == 0) __hip_atomic_store(p.ctr + bgq, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T, int HD>
+hipError_t launch_typed(const AttnParams &p, hipStream_t s) {
+  const int QP = (p.RP + 63) / 64;
+  hipLaunchKernelGGL((k_attn_decode<T, HD>), dim3(p.S, p.nkv * QP, p.B), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(int dtype, const AttnParams &p, hipStream_t s) {
+  if (dtype == 1) {
+    if (p.hd == 64) return launch_typed<bf16_t, 64>(p, s);
+    if (p.hd == 128) return launch_typed<bf16_t, 128>(p, s);
+  } else {
+    if (p.hd == 64) return launch_typed<float, 64>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pe

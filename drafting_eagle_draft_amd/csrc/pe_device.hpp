@@ -1,0 +1,131 @@
+// pe_device.hpp -- device-side building blocks shared by the gfx950 kernels.
+//
+// Fragments.  Every matrix-core operand in this library is a 16-byte value
+// per lane ("fragment"): 8 bf16 or 4 fp32.  A 16x16 output tile is produced
+// from one fragment pair:
+//   bf16: one v_mfma_f32_16x16x32_bf16; lane l supplies row (l % 16) and
+//         k-slots 0..7 of lane group g = l / 16;
+//   fp32: four v_mfma_f32_16x16x4_f32; op j takes slot j of every lane, so
+//         lane group g, slot j stands for k = 4g + j.
+// Because A and B use the same (lane group, slot) -> k assignment, any fixed
+// mapping of the contraction index onto (g, slot) gives the same sum; the
+// kernels choose the mapping that makes their loads contiguous.
+// The 16x16 fp32 result sits in 4 registers per lane: lane l holds column
+// (l % 16) and rows 4*(l/16) + r for r = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pe {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef uint16_t bf16_t;  // raw bf16 storage
+
+// Elements of T per 16-byte fragment and per 64-lane tile row (k extent).
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> { static constexpr int E = 8; static constexpr int KTILE = 32; };
+template <> struct Frag<float>  { static constexpr int E = 4; static constexpr int KTILE = 16; };
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(((unsigned)h) << 16);
+}
+
+// Round to nearest even (inputs are finite in this library).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  unsigned u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  return (unsigned)f32_to_bf16(lo) | ((unsigned)f32_to_bf16(hi) << 16);
+}
+
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16_t> {
+  static __device__ __forceinline__ floatx4 run(u32x4 a, u32x4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  static __device__ __forceinline__ floatx4 run(u32x4 a, u32x4 b, floatx4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+    return c;
+  }
+};
+
+__device__ __forceinline__ u32x4 ldg16(const void *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ void stg16(void *p, u32x4 v) {
+  *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+// Order-preserving map of a float onto uint32 (larger float -> larger code).
+__device__ __forceinline__ unsigned ordered_bits(float v) {
+  unsigned u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float unordered_bits(unsigned o) {
+  unsigned u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+
+// Argmax key: the larger value wins, then the lower index.
+__device__ __forceinline__ unsigned long long argmax_key(float v, unsigned idx) {
+  return ((unsigned long long)ordered_bits(v) << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
+}
+
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int mask) {
+  unsigned lo = (unsigned)v, hi = (unsigned)(v >> 32);
+  lo = __shfl_xor(lo, mask, 64);
+  hi = __shfl_xor(hi, mask, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Release this wave's global stores at device scope, then count arrival at
+// *ctr; returns the counter value before the increment (same in all lanes).
+__device__ __forceinline__ int arrive(int *ctr) {
+  __threadfence();
+  int old = 0;
+  if (__lane_id() == 0)
+    old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0, 64);
+  return old;
+}
+
+// Acquire side: make other waves' released stores visible to this wave.
+__device__ __forceinline__ void acquire() { __threadfence(); }
+
+__device__ __forceinline__ void reset_counter(int *ctr) {
+  if (__lane_id() == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace pe

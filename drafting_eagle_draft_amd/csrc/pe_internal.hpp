@@ -1,0 +1,119 @@
+// pe_internal.hpp -- launch interfaces between the C ABI layer and the
+// gfx950 kernels (host side).  Kernel files implement these launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pe_device.hpp"
+
+namespace pe {
+
+// Epilogues of the stream-K weight-streaming GEMM.
+enum Epi : int {
+  EPI_FC = 0,      // x = embedding/mask row + fc(h); expands to B*K rows
+  EPI_QKV = 1,     // RoPE on q,k; scatter q,k,v into the attention layouts
+  EPI_RESID = 2,   // x += y (O and down projections)
+  EPI_SWIGLU = 3,  // h = silu(gate) * up
+  EPI_ARGMAX = 4,  // LM head: optional logits, fused argmax
+};
+
+// Row orders of the tiled weight copies (applied when the tiles are built).
+enum RowMap : int {
+  MAP_IDENTITY = 0,
+  MAP_QKV = 1,     // q|k|v heads; q and k rows paired (i, i+hd/2) inside each lane
+  MAP_GATEUP = 2,  // per 16-row strip: 8 gate rows and the matching 8 up rows
+};
+
+constexpr int kMaxRows = 64;  // decode activation rows (B*K and B+1)
+
+struct GemmParams {
+  // Weights, tiled: fragment (nt, kt, lane) at wt[(nt*KT + kt)*64 + lane].
+  const u32x4 *wt;
+  int NT, KT;
+  int N;            // output rows of the (row-mapped) weight
+  int K;            // contraction length (multiple of the fragment width)
+  // Activations, row-major dtype rows: rows [0, act_rows) from act, row
+  // act_rows from act_extra when non-null; other rows read as zero.
+  const void *act;
+  long act_ld;
+  int act_rows;
+  const void *act_extra;
+  int M;            // valid activation rows (output columns)
+  // Stream-K: U waves split T = NT*KT tiles evenly in strip-major order.
+  long T;
+  int U;
+  floatx4 *part;    // [2*U][NF][64] partial strip results
+  int *ctr;         // [NT] arrival counters, zero between launches
+  // Optional RMSNorm scale of activation rows from a producer's partial
+  // sums of squares: rstd[m] = 1/sqrt(sum_s ssq[s*kMaxRows + m] * inv_width + eps).
+  const float *ssq;
+  int ssq_strips;
+  float inv_width;
+  float eps;
+  // ---- epilogue operands ----
+  float *xres;          // fp32 residual [rows][H] (FC, RESID)
+  void *xg;             // dtype copy of x * gnext for the next GEMM (FC, RESID)
+  const float *gnext;   // fp32 [H]
+  float *ssq_out;       // [NT][kMaxRows] strip sums of squares of x (FC, RESID)
+  int H;
+  // FC
+  int Kb;               // block length K (also QKV)
+  int B;                // sequences
+  const void *embed;    // [V][H]
+  const int *tok;       // [B]
+  const void *mask_emb; // [H]
+  // QKV
+  void *q, *kb, *vb;
+  const int *ctx_lens;  // clamped to [0, C] on use
+  long C;               // cache position stride
+  const double *inv_freq;
+  int nq, nkv, hd, RP;
+  // SWIGLU
+  void *hout;
+  int I;
+  // ARGMAX
+  float *logits;                  // [M][V] or null
+  unsigned long long *blk_best;   // [gridDim.x][kMaxRows]
+  int *done_ctr;                  // one counter
+  int *draft_out;                 // [M]
+  int V;
+};
+
+hipError_t launch_gemm(int dtype, int nf, int epi, const GemmParams &p, int waves_per_block,
+                       hipStream_t s);
+
+struct RepackParams {
+  const void *src[3];  // source matrices, each [rows_i][K] row-major
+  int src_rows[3];
+  int N, K, NT, KT;
+  int map;             // RowMap
+  int hd, nq, nkv, I;  // for MAP_QKV / MAP_GATEUP
+  u32x4 *dst;
+};
+
+hipError_t launch_repack(int dtype, const RepackParams &p, hipStream_t s);
+hipError_t launch_gain_to_f32(int dtype, const void *src, float *dst, int n, hipStream_t s);
+
+struct AttnParams {
+  const void *q;        // [B][nkv][RP][hd]
+  const void *kb, *vb;  // [B][nkv][Kb][hd]
+  const void *kc, *vc;  // [B][nkv][C][hd]
+  const int *ctx_lens;  // [B]
+  long C;               // ctx_stride
+  int B, Kb, nq, nkv, hd, G, R, RP;
+  int L;                // keys per split (multiple of 64)
+  int S;                // max splits per (b, kv head)
+  float scale_log2;     // log2(e)/sqrt(hd)
+  void *out;            // [B*Kb][nq*hd] dtype
+  float *part;          // [B][nkv][QP][S][64*hd + 128], QP = ceil(RP/64)
+  int *ctr;             // [B*nkv*QP]
+};
+
+hipError_t launch_attention(int dtype, const AttnParams &p, hipStream_t s);
+
+hipError_t launch_accept(int B, int K, const int *draft, const int *target, int *accept_len,
+                         int *out_tokens, hipStream_t s);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+
+}  // namespace pe

@@ -1,0 +1,124 @@
+"""Device-side helpers around the C ABI for tests, the smoke check and the
+benchmark.  PyTorch is used only to hold device memory and to supply the
+HIP stream; all drafter arithmetic runs in libpeagle.so.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as pe
+
+
+def _dtype(cfg) -> torch.dtype:
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def to_device(a, cfg, device) -> torch.Tensor:
+    """float32 host array holding dtype-exact values -> device tensor of the dtype."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    return t.to(_dtype(cfg)) if cfg.dtype == "bf16" else t
+
+
+def stream_handle() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+class Drafter:
+    """A pe_model built from host weights (dict from synth.drafter_weights)."""
+
+    def __init__(self, cfg, weights, device="cuda:0"):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        torch.cuda.set_device(self.device)
+        self.embed = to_device(weights["embed"], cfg, self.device)  # kept: read by reference
+        keep = []
+
+        def dev(a):
+            t = to_device(a, cfg, self.device)
+            keep.append(t)
+            return t.data_ptr()
+
+        layers = (pe.PeLayerWeights * max(1, cfg.n_layers))()
+        for l, lw in enumerate(weights["layers"]):
+            layers[l] = pe.PeLayerWeights(*[dev(lw[k]) for k in (
+                "attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")])
+        w = pe.PeWeights(self.embed.data_ptr(), dev(weights["fc"]), dev(weights["final_norm"]),
+                         dev(weights["lm_head"]), layers)
+        c = pe.PeConfig(cfg.hidden, cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
+                        cfg.intermediate, cfg.vocab, cfg.rope_theta, cfg.rms_eps,
+                        pe.PE_BF16 if cfg.dtype == "bf16" else pe.PE_F32)
+        self.handle = pe.pe_model_create(c, w, stream_handle())
+        del keep  # the model holds its own tiled copies of every weight but the embedding
+
+    def close(self):
+        if self.handle:
+            pe.pe_model_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace(self, B, K, ctx_stride):
+        n = pe.pe_draft_workspace_size(self.handle, B, K, ctx_stride)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+        pe.pe_workspace_init(ws.data_ptr(), ws.numel(), stream_handle())
+        return ws
+
+
+class DecodeBuffers:
+    """Device copies of one decode call's inputs plus its outputs."""
+
+    def __init__(self, drafter: Drafter, inp, N=None, want_logits=False):
+        cfg, dev = drafter.cfg, drafter.device
+        self.N = cfg.n_layers if N is None else N
+        self.K = int(inp["K"])
+        self.B = int(len(inp["token_ids"]))
+        self.ctx_stride = int(inp["ctx_stride"])
+        self.hidden3 = to_device(inp["hidden3"], cfg, dev)
+        self.token_ids = torch.from_numpy(np.asarray(inp["token_ids"], np.int32)).to(dev)
+        self.mask_emb = to_device(inp["mask_emb"], cfg, dev)
+        self.h_shared = to_device(inp["h_shared"], cfg, dev)
+        self.ctx_lens = torch.from_numpy(np.asarray(inp["ctx_lens"], np.int32)).to(dev)
+        self.k_cache = [to_device(k, cfg, dev) for k in inp["k_cache"][:self.N]]
+        self.v_cache = [to_device(v, cfg, dev) for v in inp["v_cache"][:self.N]]
+        self.draft = torch.full((self.B, self.K), -1, dtype=torch.int32, device=dev)
+        self.logits = (torch.empty((self.B, self.K, cfg.vocab), dtype=torch.float32, device=dev)
+                       if want_logits else None)
+        self.ws = drafter.workspace(self.B, self.K, self.ctx_stride)
+
+    def launch(self, drafter: Drafter, stream: int | None = None):
+        pe.pe_draft_forward(
+            drafter.handle, self.N, self.B, self.K, self.hidden3.data_ptr(),
+            self.token_ids.data_ptr(), self.mask_emb.data_ptr(), self.h_shared.data_ptr(),
+            self.ctx_lens.data_ptr(), self.ctx_stride,
+            [t.data_ptr() for t in self.k_cache], [t.data_ptr() for t in self.v_cache],
+            self.draft.data_ptr(), self.logits.data_ptr() if self.logits is not None else None,
+            self.ws.data_ptr(), self.ws.numel(), stream_handle() if stream is None else stream)
+
+
+def draft_forward(drafter: Drafter, inp, N=None, want_logits=False):
+    """Run one forward; returns (draft [B,K] int32, logits [B,K,V] float32 or None) on host."""
+    buf = DecodeBuffers(drafter, inp, N=N, want_logits=want_logits)
+    buf.launch(drafter)
+    torch.cuda.synchronize()
+    return (buf.draft.cpu().numpy(),
+            buf.logits.cpu().numpy() if buf.logits is not None else None)
+
+
+def accept(draft: np.ndarray, target: np.ndarray, device="cuda:0", with_tokens=True):
+    """Greedy acceptance on the GPU; returns (accept_len [B], out_tokens [B,K+1] or None)."""
+    draft = np.ascontiguousarray(draft, np.int32)
+    target = np.ascontiguousarray(target, np.int32)
+    B, K = draft.shape
+    d = torch.from_numpy(draft).to(device)
+    t = torch.from_numpy(target).to(device)
+    a = torch.full((max(B, 1),), -7, dtype=torch.int32, device=device)
+    o = torch.full((max(B, 1), K + 1), -7, dtype=torch.int32, device=device) if with_tokens else None
+    pe.pe_accept(B, K, d.data_ptr(), t.data_ptr(), a.data_ptr(),
+                 o.data_ptr() if o is not None else None, stream_handle())
+    torch.cuda.synchronize()
+    return a.cpu().numpy()[:B], (o.cpu().numpy()[:B] if o is not None else None)

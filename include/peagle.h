@@ -1,0 +1,174 @@
+/*
+ * peagle.h -- C ABI of the MI355X (gfx950) P-EAGLE parallel-drafter library.
+ *
+ * What the library computes (sources cited by page title and section):
+ *   - "P-EAGLE: A Technical Deep Dive into Parallel Speculative Decoding",
+ *     section "2. The P-EAGLE Parallel Drafter": one forward pass drafts K
+ *     tokens.  The first (next-token) position takes the new token's
+ *     embedding and the target's hidden state; positions 2..K take a shared
+ *     mask-token embedding and a shared hidden state h_shared.
+ *   - "P-EAGLE: Parallel-Drafting EAGLE with Scalable Training" (notes on
+ *     arXiv:2602.01469), section 2: the inputs are the concatenated target
+ *     hidden states of three layers; the block runs through N LLaMA-3 style
+ *     decoder layers with RoPE and an LM head.  Section 3.1: the attention
+ *     mask is precomputed once at the maximum length and sliced per sample.
+ *   - "Speeding LLM inference with P-EAGLE in vLLM Speculators", sections
+ *     "A learnable mask parameter" (mask_hidden is 3H wide) and
+ *     "Flex-attention mask" (who may attend to whom).
+ *   - "EAGLE-4" (lightseek.org), "EAGLE-4 overview": the verifier keeps the
+ *     longest agreeing prefix plus one bonus token.
+ *
+ * Conventions shared by every entry point:
+ *   - All pointers named *device* point to GPU memory owned by the caller;
+ *     *host* pointers point to CPU memory read during the call only.
+ *   - Matrices are row-major [out, in] (PyTorch nn.Linear layout): y = x W^T.
+ *   - "dtype" data (weights, hidden states, caches, mask embedding) is bf16
+ *     or fp32 as pe_config.dtype says; accumulation is always fp32.
+ *   - Validation happens before any launch: a non-OK status means nothing
+ *     was enqueued.  pe_last_error() returns a thread-local message.
+ *   - Work is asynchronous on the given hipStream_t (NULL = default stream);
+ *     the forward entry points never allocate, free or synchronise.
+ *   - Device pointers must be 16-byte aligned.
+ */
+#ifndef PEAGLE_H
+#define PEAGLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PE_OK = 0,
+  PE_ERR_INVALID_ARGUMENT = -1, /* a NULL required pointer, a bad size or shape */
+  PE_ERR_UNSUPPORTED = -2,      /* valid in principle, outside this build's limits */
+  PE_ERR_WORKSPACE = -3,        /* workspace NULL or smaller than the size query says */
+  PE_ERR_HIP = -4               /* a HIP runtime call or launch failed */
+} pe_status;
+
+typedef enum { PE_F32 = 0, PE_BF16 = 1 } pe_dtype;
+
+/* Build limits. */
+#define PE_K_MAX 16        /* draft block length K */
+#define PE_DECODE_ROWS_MAX 64 /* B*K rows per draft forward; also B+1 <= 64 */
+
+typedef struct {
+  int32_t hidden;        /* H, multiple of 16 */
+  int32_t n_layers;      /* decoder layers held by the model */
+  int32_t n_q_heads;     /* query heads */
+  int32_t n_kv_heads;    /* key/value heads; n_q_heads % n_kv_heads == 0 */
+  int32_t head_dim;      /* 64 or 128 */
+  int32_t intermediate;  /* SwiGLU width I, multiple of 8 */
+  int32_t vocab;         /* V, multiple of 16 */
+  float rope_theta;      /* RoPE base (500000 for LLaMA-3 style drafters) */
+  float rms_eps;         /* RMSNorm epsilon (1e-5) */
+  int32_t dtype;         /* pe_dtype of weights and activations */
+} pe_config;
+
+/* Device pointers of one decoder layer, all in pe_config.dtype. */
+typedef struct {
+  const void *attn_norm; /* [H] RMSNorm gain before attention */
+  const void *wq;        /* [n_q_heads*head_dim, H] */
+  const void *wk;        /* [n_kv_heads*head_dim, H] */
+  const void *wv;        /* [n_kv_heads*head_dim, H] */
+  const void *wo;        /* [H, n_q_heads*head_dim] */
+  const void *mlp_norm;  /* [H] RMSNorm gain before the MLP */
+  const void *w_gate;    /* [I, H] */
+  const void *w_up;      /* [I, H] */
+  const void *w_down;    /* [H, I] */
+} pe_layer_weights;
+
+typedef struct {
+  const void *embed;       /* [V, H] token embedding; kept by reference, must outlive the model */
+  const void *fc;          /* [H, 3H] projection of the concatenated target hidden states */
+  const void *final_norm;  /* [H] RMSNorm gain before the LM head */
+  const void *lm_head;     /* [V, H], untied from embed */
+  const pe_layer_weights *layers; /* host array of n_layers entries */
+} pe_weights;
+
+typedef struct pe_model pe_model;
+typedef struct pe_mask pe_mask;
+
+/* Copy every weight except the embedding into the library's MFMA tile layout
+ * (device memory owned by the model), convert norm gains to fp32 and build
+ * the RoPE frequency table in fp64.  Synchronises the stream before
+ * returning; the caller may free its weight copies afterwards (not embed). */
+pe_status pe_model_create(const pe_config *cfg, const pe_weights *w, void *stream, pe_model **out);
+pe_status pe_model_destroy(pe_model *m);
+
+/* Workspace bytes needed by pe_draft_forward for B sequences, block K and
+ * context stride ctx_stride.  The same workspace serves any smaller call. */
+pe_status pe_draft_workspace_size(const pe_model *m, int32_t B, int32_t K, int64_t ctx_stride,
+                                  size_t *bytes);
+
+/* Zero a workspace (device, ws_bytes) on the stream.  Required once after
+ * allocating it: the kernels keep their completion counters in it and leave
+ * them at zero when they finish. */
+pe_status pe_workspace_init(void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * One parallel-drafting forward ("2. The P-EAGLE Parallel Drafter").
+ *
+ *   N           layers to run, 0..n_layers (0 = fusion, final norm, LM head)
+ *   B, K        sequences and block length; 1 <= K <= PE_K_MAX,
+ *               B*K <= PE_DECODE_ROWS_MAX, B + 1 <= PE_DECODE_ROWS_MAX
+ *   hidden3     device [B, 3H]  concatenated target hidden states (low|mid|high)
+ *   token_ids   device int32 [B] newly generated token of each sequence
+ *   mask_emb    device [H]       mask-token embedding (e.g. row mask_token_id of embed)
+ *   h_shared    device [3H]      shared hidden state (the learnable mask_hidden)
+ *   ctx_lens    device int32 [B] cached context length C_b, 0 <= C_b <= ctx_stride
+ *   ctx_stride  C_max, the cache's position stride
+ *   k_cache, v_cache
+ *               host arrays of N device pointers; entry l points at layer l's
+ *               cache [B, n_kv_heads, ctx_stride, head_dim] (keys already
+ *               rotated).  Block row k of sequence b sits at RoPE position
+ *               C_b + k and attends to cache rows [0, C_b) and block rows 0..k.
+ *               The cache is only read.
+ *   draft_out   device int32 [B, K]: argmax of each position's logits, the
+ *               lowest index among equal maxima
+ *   logits_out  device fp32 [B, K, V] or NULL
+ *   workspace   device, ws_bytes >= pe_draft_workspace_size(m, B, K, ctx_stride),
+ *               initialised once by pe_workspace_init; calls that share a
+ *               workspace must be ordered on one stream.
+ */
+pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K,
+                           const void *hidden3, const int32_t *token_ids,
+                           const void *mask_emb, const void *h_shared,
+                           const int32_t *ctx_lens, int64_t ctx_stride,
+                           const void *const *k_cache, const void *const *v_cache,
+                           int32_t *draft_out, float *logits_out,
+                           void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Greedy longest-prefix acceptance ("EAGLE-4", "EAGLE-4 overview";
+ * "Speeding LLM inference with P-EAGLE in vLLM Speculators", introduction).
+ *   draft       device int32 [B, K]
+ *   target      device int32 [B, K+1]  the verifier's greedy token at each block
+ *               position plus the one after the last
+ *   accept_len  device int32 [B]: largest a <= K with draft[b,i] == target[b,i] for i < a
+ *   out_tokens  device int32 [B, K+1] or NULL: target[b, 0..a] then -1
+ * 1 <= K <= PE_K_MAX, B >= 0 (B == 0 enqueues nothing).
+ */
+pe_status pe_accept(int32_t B, int32_t K, const int32_t *draft, const int32_t *target,
+                    int32_t *accept_len, int32_t *out_tokens, void *stream);
+
+/* Thread-local description of the last non-OK status of this thread. */
+const char *pe_last_error(void);
+
+/* Library build string (kernel set, arch). */
+const char *pe_version(void);
+
+/* Optional per-stage timing of pe_draft_forward: when enabled, the model
+ * records HIP events around its LM-head launch on the forward's stream.
+ * pe_profile_read synchronises on the last event and returns the number of
+ * recorded launches and their mean duration in milliseconds, then clears. */
+pe_status pe_profile_enable(pe_model *m, int32_t enable);
+pe_status pe_profile_read(pe_model *m, int32_t *count, double *mean_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PEAGLE_H */
