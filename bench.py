@@ -1,0 +1,208 @@
+"""Benchmark of the P-EAGLE parallel-drafter forward on one MI355X.
+
+A step is one pe_draft_forward (input fusion, N decoder layers, LM head with
+fused argmax) over the synthetic GPT-OSS-20B-shaped drafter workload
+(H 2880, 4 layers, 64 q / 8 kv heads, head_dim 64, SwiGLU 8192, vocab
+201088, K = 8, batch 2, 4096 cached positions, bf16), all inputs resident
+in HBM.  Prints one JSON line:
+
+  value      draft tokens/s = B*K / mean step time over the timed steps
+  roofline   the dominant kernel (LM head with fused argmax): algorithmic
+             bytes per launch / mean launch time from HIP events recorded
+             around it on the forward's stream during the timed steps
+  forward_roofline  the whole forward's algorithmic bytes / step time
+  cpu_baseline      the CPU oracle on the same workload (host cores)
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
+       [--no-cpu-baseline] [--graph] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+METRIC = "draft tokens/s per P-EAGLE forward (K=8, ctx 4K) + % of HBM roofline"
+COUNTERS = os.path.join(ROOT, "profiles", "lm_head_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "drafting_eagle_draft_amd", "csrc", "gemm_stream.hip")
+
+
+def algorithmic_bytes(cfg, ctx_lens, B, K):
+    """Bytes one forward must move at least once: every weight streamed once,
+    the cached keys/values of each sequence read once, plus inputs/outputs."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    H, I, V, hd = cfg.hidden, cfg.intermediate, cfg.vocab, cfg.head_dim
+    nq, nkv, N = cfg.n_q_heads, cfg.n_kv_heads, cfg.n_layers
+    layer_w = ((nq + 2 * nkv) * hd * H + H * nq * hd + 2 * I * H + H * I) * e
+    kv = 2 * int(np.sum(ctx_lens)) * nkv * hd * e
+    fc = H * 3 * H * e
+    lm = V * H * e
+    io = (B * 3 * H + B * H + H + 3 * H) * e + B * 8 + B * K * 4
+    return {"total": fc + N * layer_w + N * kv + lm + io, "lm_head": lm + B * K * H * e,
+            "layers": N * layer_w, "kv": N * kv, "fc": fc}
+
+
+def cpu_baseline(cfg, w, inp, reps=2):
+    """The oracle as it stands, on this host's cores: one untimed warm run,
+    then the median of ``reps`` full forwards of the same workload."""
+    from threadpoolctl import threadpool_info
+    from oracle import peagle_oracle as po
+    wr = dict(w, embed_rows=w["embed"][inp["token_ids"]])
+    args = (wr, cfg, inp["hidden3"], inp["token_ids"], inp["mask_emb"], inp["h_shared"],
+            inp["ctx_lens"], inp["k_cache"], inp["v_cache"], inp["K"])
+    po.draft_forward(*args)
+    times = []
+    for _ in range(reps):
+        t = time.perf_counter()
+        po.draft_forward(*args)
+        times.append(time.perf_counter() - t)
+    t = float(np.median(times))
+    B, K = len(inp["token_ids"]), inp["K"]
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": B * K / t, "unit": "draft tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the full workload: {reps} timed full forwards (median {t:.2f} s each, "
+                      f"all {B * K} rows, fp64 NumPy) after one warm run"}
+
+
+def traffic_from_counters(lm_launch_bytes):
+    """HBM bytes per LM-head launch from the committed rocprofv3 PMC summary,
+    or None when missing or taken on a different kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        c = json.load(f)
+    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if c.get("kernel_sha256") != src:
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gptoss20b_k8_ctx4k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="also time hipGraph replays")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (counter calibration)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: this path runs on a single MI355X and has no "
+              f"multi-GPU mode (asked for --gpus {a.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from drafting_eagle_draft_amd import binding as pe
+    from drafting_eagle_draft_amd import runner, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.config(a.workload)
+    t0 = time.time()
+    w = synth.drafter_weights(cfg)
+    inp = synth.decode_inputs(cfg)
+    print(f"[bench] inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    drafter = runner.Drafter(cfg, w, dev)
+    buf = runner.DecodeBuffers(drafter, inp, want_logits=False)
+    B, K = buf.B, buf.K
+
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(a.warmup):
+        buf.launch(drafter)
+    torch.cuda.synchronize()
+
+    pe.pe_profile_enable(drafter.handle, True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(a.steps):
+        buf.launch(drafter)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / a.steps
+    n_lm, lm_ms = pe.pe_profile_read(drafter.handle)
+    pe.pe_profile_enable(drafter.handle, False)
+
+    graph_ms = None
+    if a.graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            buf.launch(drafter)
+        torch.cuda.current_stream().wait_stream(s)
+        with torch.cuda.graph(g):
+            buf.launch(drafter)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(a.steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / a.steps
+
+    nbytes = algorithmic_bytes(cfg, inp["ctx_lens"], B, K)
+    lm_gbs = nbytes["lm_head"] / (lm_ms * 1e-3) / 1e9 if lm_ms > 0 else None
+    fwd_gbs = nbytes["total"] / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": B * K / (ms * 1e-3),
+        "unit": "draft tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) hidden states and cache)",
+        "config": {"workload": cfg.name, "batch": B, "K": K, "ctx": int(inp["ctx_lens"][0]),
+                   "layers": cfg.n_layers, "hidden": cfg.hidden, "heads": [cfg.n_q_heads, cfg.n_kv_heads],
+                   "head_dim": cfg.head_dim, "intermediate": cfg.intermediate, "vocab": cfg.vocab,
+                   "launch": "eager, one stream"},
+        "roofline": {"bound": "hbm", "kernel": "LM head GEMM + fused argmax",
+                     "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": (lm_gbs / HBM_PEAK_GBS) if lm_gbs else None,
+                     "traffic": traffic_from_counters(nbytes["lm_head"]),
+                     "algorithmic_bytes_per_launch": nbytes["lm_head"], "launches": n_lm,
+                     "mean_launch_ms": lm_ms},
+        "forward_roofline": {"bound": "hbm", "achieved": fwd_gbs, "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": fwd_gbs / HBM_PEAK_GBS,
+                             "algorithmic_bytes": nbytes["total"]},
+    }
+    if graph_ms is not None:
+        out["graph_ms_per_step"] = graph_ms
+        out["graph_value"] = B * K / (graph_ms * 1e-3)
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, w, inp)
+    else:
+        out["cpu_baseline"] = None
+    drafter.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

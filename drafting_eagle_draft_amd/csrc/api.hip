@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -54,12 +55,6 @@ struct LayerT {
   float *attn_norm = nullptr, *mlp_norm = nullptr;
 };
 
-struct GemmPlan {
-  long T;
-  int U;
-  int wpb;
-};
-
 }  // namespace
 
 struct pe_model {
@@ -67,9 +62,7 @@ struct pe_model {
   int ktile = 32;      // contraction elements per tile
   size_t esz = 2;      // bytes per dtype element
   int num_cus = 256;
-  int wpc = 16;        // GEMM waves per CU
-  int min_tiles = 8;   // minimum tiles per GEMM wave
-  int lm_wpc = 16;     // LM-head waves per CU
+  size_t lds_budget = 159 * 1024;  // dynamic LDS per GEMM workgroup
   int attn_blocks_per_cu = 1;
   Tiled fc, lm;
   std::vector<LayerT> layers;
@@ -85,16 +78,49 @@ struct pe_model {
 
 namespace {
 
-GemmPlan plan_gemm(const pe_model *m, const Tiled &t, bool lm) {
-  GemmPlan p;
-  p.T = (long)t.NT * t.KT;
-  const long cap = (long)m->num_cus * (lm ? m->lm_wpc : m->wpc);
-  long u = (p.T + m->min_tiles - 1) / m->min_tiles;
-  if (u > cap) u = cap;
-  if (u < 1) u = 1;
-  p.U = (int)u;
-  p.wpb = lm ? 8 : 4;
-  return p;
+// Work split of one GEMM: the activations of a k-chunk (Mv rows) must fit in
+// LDS next to the per-wave reduction tiles (8 waves per workgroup); prefer no
+// K split.
+struct GemmPlan {
+  GemmLaunch L;
+  int KS, kc, nkw, Mv, nf;
+};
+
+GemmPlan plan_gemm(const pe_model *m, const Tiled &t, int Mv, int nf) {
+  GemmPlan g{};
+  g.Mv = Mv;
+  g.nf = nf;
+  const int E = 16 / (int)m->esz;
+  // Tile slots per wave that stay in registers with the epilogues (no spills).
+  const int max_slots = nf == 1 ? 24 : nf == 2 ? 18 : nf == 3 ? 8 : 4;
+  bool found = false;
+  for (int KS = 1; KS <= 64 && !found; ++KS) {
+    const int kc = (t.KT + KS - 1) / KS;
+    if (KS > 1 && (KS - 1) * kc >= t.KT) continue;  // no empty chunk
+    for (int W : {8}) {
+      const int nkw = (kc + W - 1) / W;
+      if (nkw > max_slots) continue;
+      const size_t lds = ((size_t)Mv * (kc * m->ktile + E) * m->esz + 15) / 16 * 16 +
+                         (size_t)W * nf * 1024 + 256;
+      if (lds > m->lds_budget) continue;
+      g.KS = KS; g.kc = kc; g.nkw = nkw;
+      g.L.waves = W;
+      g.L.lds = lds;
+      found = true;
+      break;
+    }
+  }
+  if (!found) { g.KS = 0; return g; }
+  g.L.maxkw = g.nkw <= 2 ? 2 : g.nkw <= 4 ? 4 : g.nkw <= 8 ? 8 : g.nkw <= 12 ? 12
+            : g.nkw <= 18 ? 18 : 24;
+  // Workgroups resident per CU: LDS and 32 waves per CU.
+  int per_cu = (int)((160 * 1024) / g.L.lds);
+  if (per_cu > 32 / g.L.waves) per_cu = 32 / g.L.waves;
+  if (per_cu < 1) per_cu = 1;
+  long G = (long)m->num_cus * per_cu;
+  if (G > t.NT) G = t.NT;
+  g.L.grid = (int)G;
+  return g;
 }
 
 struct AttnPlan {
@@ -116,11 +142,11 @@ AttnPlan plan_attn(const pe_model *m, int B, int K, long C) {
   return a;
 }
 
+
 struct WsLayout {
-  size_t xres, xg, ssq, q, kb, vb, attn_out, mlp_h, gpart, gctr, apart, actr, blk, done, total;
+  size_t xres, xg, ssq, q, kb, vb, attn_out, mlp_h, gpart, apart, blk, total;
   int RP;
   AttnPlan ap;
-  GemmPlan lm;
 };
 
 WsLayout layout(const pe_model *m, int B, int K, long C) {
@@ -128,21 +154,23 @@ WsLayout layout(const pe_model *m, int B, int K, long C) {
   WsLayout w;
   const int G = c.n_q_heads / c.n_kv_heads;
   const int R = K * G;
+  const int M = B * K, nf = (M + 15) / 16, nf_fc = (B + 1 + 15) / 16;
   w.RP = (R + 15) / 16 * 16;
   w.ap = plan_attn(m, B, K, C);
-  w.lm = plan_gemm(m, m->lm, true);
-  // Largest GEMM plan (partials) and largest strip count (counters).
-  long umax = w.lm.U;
-  int ntmax = m->lm.NT;
-  auto upd = [&](const Tiled &t) {
-    GemmPlan g = plan_gemm(m, t, false);
-    if (g.U > umax) umax = g.U;
-    if (t.NT > ntmax) ntmax = t.NT;
+  size_t part = 0, blk = 0;
+  auto upd = [&](const Tiled &t, int Mv, int nfr, bool lm) {
+    const GemmPlan g = plan_gemm(m, t, Mv, nfr);
+    if (g.KS > 1) part = std::max(part, (size_t)g.KS * t.NT * nfr * 1024);
+    if (lm) {
+      const size_t nb = g.KS > 1 ? (size_t)(t.NT + 3) / 4 : (size_t)g.L.grid;
+      blk = std::max(blk, nb * kMaxRows * 8);
+    }
   };
-  upd(m->fc);
+  upd(m->fc, B + 1, nf_fc, false);
   for (const LayerT &L : m->layers) {
-    upd(L.qkv); upd(L.o); upd(L.gateup); upd(L.down);
+    upd(L.qkv, M, nf, false); upd(L.o, M, nf, false); upd(L.gateup, M, nf, false); upd(L.down, M, nf, false);
   }
+  upd(m->lm, M, nf, true);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
   const size_t H = c.hidden, esz = m->esz;
@@ -154,14 +182,10 @@ WsLayout layout(const pe_model *m, int B, int K, long C) {
   w.vb = take((size_t)B * c.n_kv_heads * K * c.head_dim * esz);
   w.attn_out = take((size_t)kMaxRows * c.n_q_heads * c.head_dim * esz);
   w.mlp_h = take((size_t)kMaxRows * c.intermediate * esz);
-  w.gpart = take((size_t)2 * umax * 4 * 64 * 16);
-  w.gctr = take((size_t)ntmax * 4);
+  w.gpart = take(std::max(part, (size_t)256));
   const size_t qparts = (size_t)(w.RP + 63) / 64;
   w.apart = take((size_t)B * c.n_kv_heads * qparts * w.ap.S * (64 * (size_t)c.head_dim + 128) * 4);
-  w.actr = take((size_t)B * c.n_kv_heads * qparts * 4);
-  const int lm_blocks = (w.lm.U + w.lm.wpb - 1) / w.lm.wpb;
-  w.blk = take((size_t)lm_blocks * kMaxRows * 8);
-  w.done = take(64);
+  w.blk = take(std::max(blk, (size_t)256));
   w.total = off;
   return w;
 }
@@ -240,7 +264,7 @@ extern "C" {
 const char *pe_last_error(void) { return g_err.c_str(); }
 
 const char *pe_version(void) {
-  return "peagle-gfx950 stream-K MFMA GEMM + MFMA split-KV decode attention";
+  return "peagle-gfx950: LDS-staged MFMA weight-streaming GEMM, MFMA split-KV decode attention";
 }
 
 pe_status pe_model_create(const pe_config *cfg, const pe_weights *w, void *stream, pe_model **out) {
@@ -269,14 +293,10 @@ pe_status pe_model_create(const pe_config *cfg, const pe_weights *w, void *strea
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) { destroy(m); return hip_fail(e, "hipDeviceGetAttribute"); }
   m->num_cus = cus > 0 ? cus : 256;
-  m->wpc = env_int("PE_GEMM_WAVES_PER_CU", 16);
-  m->min_tiles = env_int("PE_GEMM_MIN_TILES", 8);
-  m->lm_wpc = env_int("PE_LM_WAVES_PER_CU", 16);
   m->attn_blocks_per_cu = env_int("PE_ATTN_BLOCKS_PER_CU", 1);
-  if (m->wpc < 1) m->wpc = 1;
-  if (m->min_tiles < 1) m->min_tiles = 1;
-  if (m->lm_wpc < 1) m->lm_wpc = 1;
   if (m->attn_blocks_per_cu < 1) m->attn_blocks_per_cu = 1;
+  e = gemm_set_lds_limits();
+  if (e != hipSuccess) { destroy(m); return hip_fail(e, "hipFuncSetAttribute(LDS)"); }
 
   const int H = cfg->hidden, hd = cfg->head_dim, nq = cfg->n_q_heads, nkv = cfg->n_kv_heads;
   const int I = cfg->intermediate;
@@ -402,18 +422,21 @@ pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K, c
 
   GemmParams base{};
   base.part = reinterpret_cast<floatx4 *>(ws + W.gpart);
-  base.ctr = reinterpret_cast<int *>(ws + W.gctr);
   base.H = H;
   base.Kb = K;
   base.B = B;
   base.eps = c.rms_eps;
   base.inv_width = 1.0f / (float)H;
 
-  auto run = [&](const Tiled &t, int epi, int nfr, GemmParams p, bool lm) -> pe_status {
-    const GemmPlan pl = plan_gemm(m, t, lm);
+  int lm_blocks = 0;
+  auto run = [&](const Tiled &t, int epi, int nfr, GemmParams p) -> pe_status {
+    const int Mv = p.act_rows + (p.act_extra ? 1 : 0);
+    const GemmPlan pl = plan_gemm(m, t, Mv, nfr);
+    if (pl.KS == 0) return fail(PE_ERR_UNSUPPORTED, "no LDS plan for a %d x %d GEMM with %d rows", t.N, t.K, Mv);
     p.wt = t.ptr; p.NT = t.NT; p.KT = t.KT; p.N = t.N; p.K = t.K;
-    p.T = pl.T; p.U = pl.U;
-    hipError_t e = launch_gemm(c.dtype, nfr, epi, p, pl.wpb, s);
+    p.epi = epi; p.KS = pl.KS; p.kc = pl.kc; p.nkw = pl.nkw; p.Mv = Mv;
+    lm_blocks = pl.KS > 1 ? (t.NT + 3) / 4 : pl.L.grid;
+    hipError_t e = launch_gemm(c.dtype, nfr, p, pl.L, s);
     if (e != hipSuccess) return hip_fail(e, "GEMM launch");
     return PE_OK;
   };
@@ -427,7 +450,7 @@ pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K, c
     p.xres = xres; p.xg = xg; p.ssq_out = ssq;
     p.gnext = N > 0 ? m->layers[0].attn_norm : m->final_norm;
     p.embed = m->embed; p.tok = token_ids; p.mask_emb = mask_emb; p.V = c.vocab;
-    if ((st = run(m->fc, EPI_FC, (B + 1 + 15) / 16, p, false)) != PE_OK) return st;
+    if ((st = run(m->fc, EPI_FC, (B + 1 + 15) / 16, p)) != PE_OK) return st;
   }
   for (int l = 0; l < N; ++l) {
     const LayerT &L = m->layers[l];
@@ -439,7 +462,7 @@ pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K, c
       p.ctx_lens = ctx_lens; p.inv_freq = m->inv_freq;
       p.nq = nq; p.nkv = nkv; p.hd = hd; p.RP = W.RP;
       p.C = ctx_stride;
-      if ((st = run(L.qkv, EPI_QKV, nf, p, false)) != PE_OK) return st;
+      if ((st = run(L.qkv, EPI_QKV, nf, p)) != PE_OK) return st;
     }
     {
       AttnParams a{};
@@ -451,7 +474,6 @@ pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K, c
       a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
       a.out = ws + W.attn_out;
       a.part = reinterpret_cast<float *>(ws + W.apart);
-      a.ctr = reinterpret_cast<int *>(ws + W.actr);
       hipError_t e = launch_attention(c.dtype, a, s);
       if (e != hipSuccess) return hip_fail(e, "attention launch");
     }
@@ -459,21 +481,21 @@ pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K, c
       GemmParams p = base;
       p.act = ws + W.attn_out; p.act_ld = (long)nq * hd; p.act_rows = M; p.M = M;
       p.xres = xres; p.xg = xg; p.ssq_out = ssq; p.gnext = L.mlp_norm;
-      if ((st = run(L.o, EPI_RESID, nf, p, false)) != PE_OK) return st;
+      if ((st = run(L.o, EPI_RESID, nf, p)) != PE_OK) return st;
     }
     {
       GemmParams p = base;
       p.act = xg; p.act_ld = H; p.act_rows = M; p.M = M;
       p.ssq = ssq; p.ssq_strips = H / 16;
       p.hout = ws + W.mlp_h; p.I = c.intermediate;
-      if ((st = run(L.gateup, EPI_SWIGLU, nf, p, false)) != PE_OK) return st;
+      if ((st = run(L.gateup, EPI_SWIGLU, nf, p)) != PE_OK) return st;
     }
     {
       GemmParams p = base;
       p.act = ws + W.mlp_h; p.act_ld = c.intermediate; p.act_rows = M; p.M = M;
       p.xres = xres; p.xg = xg; p.ssq_out = ssq;
       p.gnext = (l + 1 < N) ? m->layers[l + 1].attn_norm : m->final_norm;
-      if ((st = run(L.down, EPI_RESID, nf, p, false)) != PE_OK) return st;
+      if ((st = run(L.down, EPI_RESID, nf, p)) != PE_OK) return st;
     }
   }
   // LM head with fused argmax.
@@ -483,16 +505,16 @@ pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K, c
     p.ssq = ssq; p.ssq_strips = H / 16;
     p.logits = logits_out;
     p.blk_best = reinterpret_cast<unsigned long long *>(ws + W.blk);
-    p.done_ctr = reinterpret_cast<int *>(ws + W.done);
-    p.draft_out = draft_out;
     p.V = c.vocab;
     const bool prof = m->prof && m->nrec < (int)m->ev0.size();
     if (prof) (void)hipEventRecord(m->ev0[m->nrec], s);
-    if ((st = run(m->lm, EPI_ARGMAX, nf, p, true)) != PE_OK) return st;
+    if ((st = run(m->lm, EPI_ARGMAX, nf, p)) != PE_OK) return st;
     if (prof) {
       (void)hipEventRecord(m->ev1[m->nrec], s);
       ++m->nrec;
     }
+    hipError_t e = launch_argmax_final(p.blk_best, lm_blocks, M, draft_out, s);
+    if (e != hipSuccess) return hip_fail(e, "argmax launch");
   }
   return PE_OK;
 }

@@ -5,13 +5,13 @@
 // inference with P-EAGLE in vLLM Speculators", section "Flex-attention mask",
 // restricted to one rollout: depth-0 base context up to the anchor plus the
 // rollout's own chain).  With grouped-query attention all G = nq/nkv query
-// heads of a kv head read the same keys, so one workgroup serves the
-// R = K*G query rows of a (sequence, kv head) pair from a single pass over
-// the keys: every 64-key tile is staged once in LDS and consumed by matrix
-// cores as two dense products per 16-query wave, S^T = K Q^T and
+// heads of a kv head read the same keys, so one workgroup serves up to 64
+// of the R = K*G query rows of a (sequence, kv head) pair from a single
+// pass over the keys: every 64-key tile is staged once in LDS and consumed
+// by matrix cores as two dense products per 16-query wave, S^T = K Q^T and
 // O^T += V^T P^T.  The key sequence (cache followed by the block) is split
 // over workgroups (split-KV); each split keeps an fp32 online softmax and
-// the last split to finish combines all splits' partials in split order.
+// writes its partial, and k_attn_combine merges the splits in split order.
 //
 // Fragment mappings (see pe_device.hpp): for S^T the contraction over head
 // dims uses 16-byte runs of a key row; for O^T the contraction over keys
@@ -63,7 +63,6 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {
   constexpr int CPR = S::CPR, CHUNKS = S::CHUNKS, MAXC = S::MAXC;
   __shared__ __attribute__((aligned(16))) T Ks[64 * KS];
   __shared__ __attribute__((aligned(16))) T Vt[HD * VS];
-  __shared__ int s_last;
 
   // blockIdx.y = kv head * QP + query partition (64 query rows each).
   const int QP = (p.RP + 63) / 64;
@@ -231,54 +230,69 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {
     return;
   }
 
-  // Partials of one split: 64 query rows x HD outputs, then 64 maxima and 64 sums.
+  // Partials of one split: 64 query rows x HD outputs, then 64 maxima and
+  // 64 sums; k_attn_combine merges them after this kernel.
   const long stride = 64L * HD + 128;
   const long bgq = bg * QP + qp;
   const int rl = rq - 64 * qp;  // row within the partition
-  float *base = p.part + bgq * p.S * stride;
-  {
-    float *pp = base + (long)split * stride;
-    if (computes) {
-#pragma unroll
-      for (int d = 0; d < ND; ++d) reinterpret_cast<floatx4 *>(pp)[(w * ND + d) * 64 + lane] = oacc[d];
-      if (g == 0) {
-        pp[64L * HD + rl] = m_run;
-        pp[64L * HD + 64 + rl] = l_tot;
-      }
-    }
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(p.ctr + bgq, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (old == Sb - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  float *pp = p.part + (bgq * p.S + split) * stride;
   if (computes) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < Sb; ++sp) M = fmaxf(M, base[sp * stride + 64L * HD + rl]);
-    floatx4 o[ND];
 #pragma unroll
-    for (int d = 0; d < ND; ++d) o[d] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
-    for (int sp = 0; sp < Sb; ++sp) {
-      const float *pp = base + sp * stride;
-      const float sc = exp2f(pp[64L * HD + rl] - M);
-      l += sc * pp[64L * HD + 64 + rl];
-#pragma unroll
-      for (int d = 0; d < ND; ++d) o[d] += sc * reinterpret_cast<const floatx4 *>(pp)[(w * ND + d) * 64 + lane];
+    for (int d = 0; d < ND; ++d) reinterpret_cast<floatx4 *>(pp)[(w * ND + d) * 64 + lane] = oacc[d];
+    if (g == 0) {
+      pp[64L * HD + rl] = m_run;
+      pp[64L * HD + 64 + rl] = l_tot;
     }
-    write_out(o, 1.0f / l);
   }
-  if (tid == 0) __hip_atomic_store(p.ctr + bgq, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge the split partials of each (sequence, kv head, query partition) in
+// split order: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void k_attn_combine(AttnParams p) {
+  constexpr int ND = HD / 16;
+  const int QP = (p.RP + 63) / 64;
+  const int bgq = blockIdx.x;
+  const int b = bgq / (p.nkv * QP), rem = bgq - b * (p.nkv * QP);
+  const int gk = rem / QP, qp = rem - gk * QP;
+  const int ctx = min(max(p.ctx_lens[b], 0), (int)p.C);
+  const int Sb = (ctx + p.Kb + p.L - 1) / p.L;
+  if (Sb <= 1) return;  // the split kernel wrote the output itself
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+  const int rq = 64 * qp + 16 * w + c16, rl = rq - 64 * qp;
+  if (rq >= p.R) return;
+  const long stride = 64L * HD + 128;
+  const float *base = p.part + (long)bgq * p.S * stride;
+  float M = -INFINITY;
+  for (int sp = 0; sp < Sb; ++sp) M = fmaxf(M, base[sp * stride + 64L * HD + rl]);
+  floatx4 o[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) o[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  for (int sp = 0; sp < Sb; ++sp) {
+    const float *pp = base + sp * stride;
+    const float sc = exp2f(pp[64L * HD + rl] - M);
+    l += sc * pp[64L * HD + 64 + rl];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) o[d] += sc * reinterpret_cast<const floatx4 *>(pp)[(w * ND + d) * 64 + lane];
+  }
+  const float inv_l = 1.0f / l;
+  const int kp = rq / p.G, hl = rq - kp * p.G;
+  T *dst = reinterpret_cast<T *>(p.out) + (long)(b * p.Kb + kp) * (p.nq * HD) + (gk * p.G + hl) * HD;
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    const float v[4] = {o[d][0] * inv_l, o[d][1] * inv_l, o[d][2] * inv_l, o[d][3] * inv_l};
+    store_out4<T>(dst + d * 16 + 4 * g, v);
+  }
 }
 
 template <typename T, int HD>
 hipError_t launch_typed(const AttnParams &p, hipStream_t s) {
   const int QP = (p.RP + 63) / 64;
   hipLaunchKernelGGL((k_attn_decode<T, HD>), dim3(p.S, p.nkv * QP, p.B), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.S <= 1) return e;
+  hipLaunchKernelGGL((k_attn_combine<T, HD>), dim3(p.B * p.nkv * QP), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

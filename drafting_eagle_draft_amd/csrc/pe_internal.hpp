@@ -40,11 +40,11 @@ struct GemmParams {
   int act_rows;
   const void *act_extra;
   int M;            // valid activation rows (output columns)
-  // Stream-K: U waves split T = NT*KT tiles evenly in strip-major order.
-  long T;
-  int U;
-  floatx4 *part;    // [2*U][NF][64] partial strip results
-  int *ctr;         // [NT] arrival counters, zero between launches
+  // Work split: KS k-chunks of kc tiles (blockIdx.y); each workgroup wave
+  // holds nkw tile slots per strip; Mv activation rows are staged in LDS.
+  int epi;          // Epi
+  int KS, kc, nkw, Mv;
+  floatx4 *part;    // [KS][NT][NF][64] partial strips when KS > 1
   // Optional RMSNorm scale of activation rows from a producer's partial
   // sums of squares: rstd[m] = 1/sqrt(sum_s ssq[s*kMaxRows + m] * inv_width + eps).
   const float *ssq;
@@ -74,14 +74,21 @@ struct GemmParams {
   int I;
   // ARGMAX
   float *logits;                  // [M][V] or null
-  unsigned long long *blk_best;   // [gridDim.x][kMaxRows]
-  int *done_ctr;                  // one counter
-  int *draft_out;                 // [M]
+  unsigned long long *blk_best;   // [workgroups][kMaxRows] best key per row
   int V;
 };
 
-hipError_t launch_gemm(int dtype, int nf, int epi, const GemmParams &p, int waves_per_block,
-                       hipStream_t s);
+struct GemmLaunch {
+  int grid;     // workgroups per k-chunk
+  int waves;    // waves per workgroup
+  size_t lds;   // dynamic LDS bytes
+  int maxkw;    // tile-slot bucket (2, 4, 8, 12, 18, 24) >= nkw
+};
+
+hipError_t launch_gemm(int dtype, int nf, const GemmParams &p, const GemmLaunch &L, hipStream_t s);
+hipError_t launch_argmax_final(const unsigned long long *blk_best, int nblk, int M, int *draft_out,
+                               hipStream_t s);
+hipError_t gemm_set_lds_limits();
 
 struct RepackParams {
   const void *src[3];  // source matrices, each [rows_i][K] row-major
@@ -107,7 +114,6 @@ struct AttnParams {
   float scale_log2;     // log2(e)/sqrt(hd)
   void *out;            // [B*Kb][nq*hd] dtype
   float *part;          // [B][nkv][QP][S][64*hd + 128], QP = ceil(RP/64)
-  int *ctr;             // [B*nkv*QP]
 };
 
 hipError_t launch_attention(int dtype, const AttnParams &p, hipStream_t s);
