@@ -63,7 +63,7 @@ struct pe_model {
   size_t esz = 2;      // bytes per dtype element
   int num_cus = 256;
   size_t lds_budget = 159 * 1024;  // dynamic LDS per GEMM workgroup
-  int attn_blocks_per_cu = 1;
+  int attn_blocks_per_cu = 2;
   Tiled fc, lm;
   std::vector<LayerT> layers;
   float *final_norm = nullptr;
@@ -78,9 +78,10 @@ struct pe_model {
 
 namespace {
 
-// Work split of one GEMM: the activations of a k-chunk (Mv rows) must fit in
-// LDS next to the per-wave reduction tiles (8 waves per workgroup); prefer no
-// K split.
+// Work split of one GEMM: 8-wave workgroups; each wave keeps nkw weight
+// tiles per strip in flight and the matching activation fragments in
+// registers, so nkw is capped by the register budget (more activation rows,
+// fewer slots).  Larger K is split over KS workgroup columns.
 struct GemmPlan {
   GemmLaunch L;
   int KS, kc, nkw, Mv, nf;
@@ -90,36 +91,31 @@ GemmPlan plan_gemm(const pe_model *m, const Tiled &t, int Mv, int nf) {
   GemmPlan g{};
   g.Mv = Mv;
   g.nf = nf;
-  const int E = 16 / (int)m->esz;
-  // Tile slots per wave that stay in registers with the epilogues (no spills).
-  const int max_slots = nf == 1 ? 24 : nf == 2 ? 18 : nf == 3 ? 8 : 4;
-  bool found = false;
-  for (int KS = 1; KS <= 64 && !found; ++KS) {
+  const int W = 8;
+  const int max_slots = nf == 1 ? 18 : nf == 2 ? 8 : nf == 3 ? 4 : 2;  // as the kernel's buckets
+  // One workgroup per CU (8 waves at up to 256 VGPRs).  Each K split adds
+  // a finalize kernel, priced like ~100 extra tiles per CU; choose the split
+  // with the smallest modelled makespan (strip rounds x tiles per chunk).
+  const int cus = m->num_cus;
+  long best = -1;
+  for (int KS = 1; KS <= 16 && KS <= t.KT; ++KS) {
     const int kc = (t.KT + KS - 1) / KS;
-    if (KS > 1 && (KS - 1) * kc >= t.KT) continue;  // no empty chunk
-    for (int W : {8}) {
-      const int nkw = (kc + W - 1) / W;
-      if (nkw > max_slots) continue;
-      const size_t lds = ((size_t)Mv * (kc * m->ktile + E) * m->esz + 15) / 16 * 16 +
-                         (size_t)W * nf * 1024 + 256;
-      if (lds > m->lds_budget) continue;
-      g.KS = KS; g.kc = kc; g.nkw = nkw;
-      g.L.waves = W;
-      g.L.lds = lds;
-      found = true;
-      break;
+    const int nkw = (kc + W - 1) / W;
+    if (nkw > max_slots) continue;
+    const int ks = (t.KT + kc - 1) / kc;  // no empty chunk
+    int G = cus / ks;
+    if (G < 1) G = 1;
+    if (G > t.NT) G = t.NT;
+    const long rounds = (t.NT + G - 1) / G;
+    const long cost = rounds * kc + (ks > 1 ? 100 : 0);
+    if (best < 0 || cost < best) {
+      best = cost;
+      g.KS = ks; g.kc = kc; g.nkw = nkw; g.L.grid = G;
     }
   }
-  if (!found) { g.KS = 0; return g; }
-  g.L.maxkw = g.nkw <= 2 ? 2 : g.nkw <= 4 ? 4 : g.nkw <= 8 ? 8 : g.nkw <= 12 ? 12
-            : g.nkw <= 18 ? 18 : 24;
-  // Workgroups resident per CU: LDS and 32 waves per CU.
-  int per_cu = (int)((160 * 1024) / g.L.lds);
-  if (per_cu > 32 / g.L.waves) per_cu = 32 / g.L.waves;
-  if (per_cu < 1) per_cu = 1;
-  long G = (long)m->num_cus * per_cu;
-  if (G > t.NT) G = t.NT;
-  g.L.grid = (int)G;
+  g.L.waves = W;
+  g.L.lds = (size_t)W * nf * 1024 + 256;
+  g.L.maxkw = g.nkw <= 2 ? 2 : g.nkw <= 4 ? 4 : g.nkw <= 8 ? 8 : g.nkw <= 12 ? 12 : 18;
   return g;
 }
 
@@ -127,12 +123,16 @@ struct AttnPlan {
   int L, S;
 };
 
+// Split-KV plan: about attn_blocks_per_cu workgroups per CU over all
+// (sequence, kv head, query partition) units, splits a multiple of 64 keys.
 AttnPlan plan_attn(const pe_model *m, int B, int K, long C) {
-  const int bg = B * m->cfg.n_kv_heads;
-  long target = ((long)m->num_cus * m->attn_blocks_per_cu + bg - 1) / bg;
+  const int G = m->cfg.n_q_heads / m->cfg.n_kv_heads;
+  const int qparts = ((K * G + 15) / 16 * 16 + 63) / 64;
+  const long units = (long)B * m->cfg.n_kv_heads * qparts;
+  long target = ((long)m->num_cus * m->attn_blocks_per_cu + units - 1) / units;
   if (target < 1) target = 1;
   const long keys = C + K;
-  long tiles = (keys + 63) / 64;
+  const long tiles = (keys + 63) / 64;
   long per = (tiles + target - 1) / target;
   if (per < 1) per = 1;
   AttnPlan a;
@@ -141,7 +141,6 @@ AttnPlan plan_attn(const pe_model *m, int B, int K, long C) {
   if (a.S < 1) a.S = 1;
   return a;
 }
-
 
 struct WsLayout {
   size_t xres, xg, ssq, q, kb, vb, attn_out, mlp_h, gpart, apart, blk, total;
@@ -197,6 +196,8 @@ pe_status tile_matrix(pe_model *m, Tiled &t, const void *const *srcs, const int 
   t.NT = (N + 15) / 16;
   t.KT = (K + m->ktile - 1) / m->ktile;
   const size_t bytes = (size_t)t.NT * t.KT * 1024;
+  if (bytes > 0x7FFFF000ull)
+    return fail(PE_ERR_UNSUPPORTED, "a %d x %d weight exceeds 2 GiB of tiles", N, K);
   hipError_t e = hipMalloc(&t.ptr, bytes);
   if (e != hipSuccess) return hip_fail(e, "hipMalloc(weight tiles)");
   m->allocs.push_back(t.ptr);
@@ -293,7 +294,7 @@ pe_status pe_model_create(const pe_config *cfg, const pe_weights *w, void *strea
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) { destroy(m); return hip_fail(e, "hipDeviceGetAttribute"); }
   m->num_cus = cus > 0 ? cus : 256;
-  m->attn_blocks_per_cu = env_int("PE_ATTN_BLOCKS_PER_CU", 1);
+  m->attn_blocks_per_cu = env_int("PE_ATTN_BLOCKS_PER_CU", 2);
   if (m->attn_blocks_per_cu < 1) m->attn_blocks_per_cu = 1;
   e = gemm_set_lds_limits();
   if (e != hipSuccess) { destroy(m); return hip_fail(e, "hipFuncSetAttribute(LDS)"); }
@@ -432,8 +433,8 @@ pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K, c
   auto run = [&](const Tiled &t, int epi, int nfr, GemmParams p) -> pe_status {
     const int Mv = p.act_rows + (p.act_extra ? 1 : 0);
     const GemmPlan pl = plan_gemm(m, t, Mv, nfr);
-    if (pl.KS == 0) return fail(PE_ERR_UNSUPPORTED, "no LDS plan for a %d x %d GEMM with %d rows", t.N, t.K, Mv);
-    p.wt = t.ptr; p.NT = t.NT; p.KT = t.KT; p.N = t.N; p.K = t.K;
+    p.wt = t.ptr; p.wbytes = (unsigned)((size_t)t.NT * t.KT * 1024); p.NT = t.NT; p.KT = t.KT;
+    p.N = t.N; p.K = t.K;
     p.epi = epi; p.KS = pl.KS; p.kc = pl.kc; p.nkw = pl.nkw; p.Mv = Mv;
     lm_blocks = pl.KS > 1 ? (t.NT + 3) / 4 : pl.L.grid;
     hipError_t e = launch_gemm(c.dtype, nfr, p, pl.L, s);

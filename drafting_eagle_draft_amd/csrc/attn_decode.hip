@@ -35,8 +35,9 @@ struct AttnShape {
   static constexpr int VS = 64 + 4;       // Vt row stride (elements)
   static constexpr int CPR = HD / E;      // 16-byte chunks per key row
   static constexpr int CHUNKS = 64 * CPR; // chunks per 64-key tile
-  static constexpr int NTHR = 256;        // staging threads (minimum block size)
+  static constexpr int NTHR = 256;        // threads per workgroup
   static constexpr int MAXC = CHUNKS / NTHR;
+  static constexpr int NBUF = MAXC <= 2 ? 4 : 2;  // 64-key tiles prefetched per round
 };
 
 __device__ __forceinline__ u32x4 lds16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
@@ -93,33 +94,36 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {
   const T *kbk = reinterpret_cast<const T *>(p.kb) + bg * p.Kb * HD;
   const T *vbk = reinterpret_cast<const T *>(p.vb) + bg * p.Kb * HD;
 
-  u32x4 kreg[MAXC], vreg[MAXC];
-  auto gload = [&](int jt) {
+  // Key tiles of this split are loaded NBUF at a time into registers, so a
+  // split's whole HBM traffic is in flight together; each tile then goes
+  // through LDS (K row-major, V transposed) to the matrix cores.
+  constexpr int NBUF = S::NBUF;
+  u32x4 kreg[NBUF][MAXC], vreg[NBUF][MAXC];
+  auto gload = [&](int jt, u32x4 (&kr)[MAXC], u32x4 (&vr)[MAXC]) {
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
       const int id = tid + i * S::NTHR;
       const int key = id / CPR, cc = id - key * CPR;
       const int jj = jt + key;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (id < CHUNKS && tid < S::NTHR && jj < j1) {
+      if (jj < j1) {
         const T *ks = (jj < ctx) ? kc + (long)jj * HD : kbk + (long)(jj - ctx) * HD;
         const T *vs = (jj < ctx) ? vc + (long)jj * HD : vbk + (long)(jj - ctx) * HD;
         kv = ldg16(ks + cc * E);
         vv = ldg16(vs + cc * E);
       }
-      kreg[i] = kv;
-      vreg[i] = vv;
+      kr[i] = kv;
+      vr[i] = vv;
     }
   };
-  auto lstore = [&]() {
-    if (tid >= S::NTHR) return;
+  auto lstore = [&](const u32x4 (&kr)[MAXC], const u32x4 (&vr)[MAXC]) {
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
       const int id = tid + i * S::NTHR;
       const int key = id / CPR, cc = id - key * CPR;
-      *reinterpret_cast<u32x4 *>(&Ks[key * KS + cc * E]) = kreg[i];
+      *reinterpret_cast<u32x4 *>(&Ks[key * KS + cc * E]) = kr[i];
       T vals[E];
-      __builtin_memcpy(vals, &vreg[i], 16);
+      __builtin_memcpy(vals, &vr[i], 16);
 #pragma unroll
       for (int e = 0; e < E; ++e) Vt[(cc * E + e) * VS + key] = vals[e];
     }
@@ -130,83 +134,89 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {
   for (int d = 0; d < ND; ++d) oacc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_lane = 0.f;
 
-  gload(j0);
-  for (int jt = j0; jt < j1; jt += 64) {
-    lstore();
-    __syncthreads();
-    if (jt + 64 < j1) gload(jt + 64);
-    if (computes) {
-      floatx4 sacc[4];
+  for (int jr = j0; jr < j1; jr += 64 * NBUF) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        sacc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int b2 = 0; b2 < NBUF; ++b2) gload(jr + 64 * b2, kreg[b2], vreg[b2]);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const u32x4 a = lds16(&Ks[(kb * 16 + c16) * KS + c * KTILE + g * E]);
-          sacc[kb] = Mma<T>::run(a, qf[c], sacc[kb]);
-        }
-      }
-      float sv[4][4];
-      float mt = -INFINITY;
+    for (int b2 = 0; b2 < NBUF; ++b2) {
+      const int jt = jr + 64 * b2;
+      if (jt < j1) {
+        lstore(kreg[b2], vreg[b2]);
+        __syncthreads();
+        if (computes) {
+          floatx4 sacc[4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+          for (int kb = 0; kb < 4; ++kb) {
+            sacc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int jj = jt + kb * 16 + 4 * g + r;
-          const bool ok = jj < j1 && (jj < ctx || jj - ctx <= kp_q);
-          sv[kb][r] = ok ? sacc[kb][r] * p.scale_log2 : -INFINITY;
-          mt = fmaxf(mt, sv[kb][r]);
-        }
-      mt = fmaxf(mt, shfl_xor_f(mt, 16));
-      mt = fmaxf(mt, shfl_xor_f(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      float alpha = 1.f, msub = 0.f;
-      if (m_new != -INFINITY) {
-        alpha = exp2f(m_run - m_new);
-        msub = m_new;
-      }
-      float pv[4][4];
-      float ps = 0.f;
+            for (int c = 0; c < NC; ++c) {
+              const u32x4 a = lds16(&Ks[(kb * 16 + c16) * KS + c * KTILE + g * E]);
+              sacc[kb] = Mma<T>::run(a, qf[c], sacc[kb]);
+            }
+          }
+          float sv[4][4];
+          float mt = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+          for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pv[kb][r] = exp2f(sv[kb][r] - msub);
-          ps += pv[kb][r];
-        }
-      l_lane = l_lane * alpha + ps;
-      m_run = m_new;
+            for (int r = 0; r < 4; ++r) {
+              const int jj = jt + kb * 16 + 4 * g + r;
+              const bool ok = jj < j1 && (jj < ctx || jj - ctx <= kp_q);
+              sv[kb][r] = ok ? sacc[kb][r] * p.scale_log2 : -INFINITY;
+              mt = fmaxf(mt, sv[kb][r]);
+            }
+          mt = fmaxf(mt, shfl_xor_f(mt, 16));
+          mt = fmaxf(mt, shfl_xor_f(mt, 32));
+          const float m_new = fmaxf(m_run, mt);
+          float alpha = 1.f, msub = 0.f;
+          if (m_new != -INFINITY) {
+            alpha = exp2f(m_run - m_new);
+            msub = m_new;
+          }
+          float pv[4][4];
+          float ps = 0.f;
 #pragma unroll
-      for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
-      if constexpr (sizeof(T) == 2) {
+          for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const u32x4 bf = {pack_bf16x2(pv[2 * c2][0], pv[2 * c2][1]),
-                            pack_bf16x2(pv[2 * c2][2], pv[2 * c2][3]),
-                            pack_bf16x2(pv[2 * c2 + 1][0], pv[2 * c2 + 1][1]),
-                            pack_bf16x2(pv[2 * c2 + 1][2], pv[2 * c2 + 1][3])};
+            for (int r = 0; r < 4; ++r) {
+              pv[kb][r] = exp2f(sv[kb][r] - msub);
+              ps += pv[kb][r];
+            }
+          l_lane = l_lane * alpha + ps;
+          m_run = m_new;
 #pragma unroll
-          for (int d = 0; d < ND; ++d) {
-            const T *vrow = &Vt[(d * 16 + c16) * VS + 32 * c2 + 4 * g];
-            const uint2 lo = lds8(vrow), hi = lds8(vrow + 16);
-            const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
-            oacc[d] = Mma<T>::run(a, bf, oacc[d]);
+          for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+          if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+              const u32x4 bf = {pack_bf16x2(pv[2 * c2][0], pv[2 * c2][1]),
+                                pack_bf16x2(pv[2 * c2][2], pv[2 * c2][3]),
+                                pack_bf16x2(pv[2 * c2 + 1][0], pv[2 * c2 + 1][1]),
+                                pack_bf16x2(pv[2 * c2 + 1][2], pv[2 * c2 + 1][3])};
+#pragma unroll
+              for (int d = 0; d < ND; ++d) {
+                const T *vrow = &Vt[(d * 16 + c16) * VS + 32 * c2 + 4 * g];
+                const uint2 lo = lds8(vrow), hi = lds8(vrow + 16);
+                const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+                oacc[d] = Mma<T>::run(a, bf, oacc[d]);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+              const u32x4 bf = {__float_as_uint(pv[kb][0]), __float_as_uint(pv[kb][1]),
+                                __float_as_uint(pv[kb][2]), __float_as_uint(pv[kb][3])};
+#pragma unroll
+              for (int d = 0; d < ND; ++d) {
+                const u32x4 a = lds16(&Vt[(d * 16 + c16) * VS + 16 * kb + 4 * g]);
+                oacc[d] = Mma<T>::run(a, bf, oacc[d]);
+              }
+            }
           }
         }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const u32x4 bf = {__float_as_uint(pv[kb][0]), __float_as_uint(pv[kb][1]),
-                            __float_as_uint(pv[kb][2]), __float_as_uint(pv[kb][3])};
-#pragma unroll
-          for (int d = 0; d < ND; ++d) {
-            const u32x4 a = lds16(&Vt[(d * 16 + c16) * VS + 16 * kb + 4 * g]);
-            oacc[d] = Mma<T>::run(a, bf, oacc[d]);
-          }
-        }
+        __syncthreads();
       }
     }
-    __syncthreads();
   }
 
   float l_tot = l_lane;
@@ -246,42 +256,71 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {
   }
 }
 
-// Merge the split partials of each (sequence, kv head, query partition) in
-// split order: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// Merge the split partials of each (sequence, kv head, query partition):
+// o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  One workgroup per 16
+// query rows; its 4 waves take splits w, w+4, ... with a running (online)
+// merge, then wave 0 merges the 4 wave results in wave order.
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p) {
   constexpr int ND = HD / 16;
+  __shared__ float sm[4][64], sl[4][64];
+  __shared__ floatx4 so[4][ND][64];
   const int QP = (p.RP + 63) / 64;
-  const int bgq = blockIdx.x;
+  const int bgq = blockIdx.x >> 2, qgrp = blockIdx.x & 3;
   const int b = bgq / (p.nkv * QP), rem = bgq - b * (p.nkv * QP);
   const int gk = rem / QP, qp = rem - gk * QP;
   const int ctx = min(max(p.ctx_lens[b], 0), (int)p.C);
   const int Sb = (ctx + p.Kb + p.L - 1) / p.L;
-  if (Sb <= 1) return;  // the split kernel wrote the output itself
+  if (Sb <= 1 || 64 * qp + 16 * qgrp >= p.RP) return;  // uniform: the split kernel wrote it
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
-  const int rq = 64 * qp + 16 * w + c16, rl = rq - 64 * qp;
-  if (rq >= p.R) return;
+  const int rl = 16 * qgrp + c16, rq = 64 * qp + rl;
   const long stride = 64L * HD + 128;
   const float *base = p.part + (long)bgq * p.S * stride;
-  float M = -INFINITY;
-  for (int sp = 0; sp < Sb; ++sp) M = fmaxf(M, base[sp * stride + 64L * HD + rl]);
+  float M = -INFINITY, l = 0.f;
   floatx4 o[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) o[d] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float l = 0.f;
-  for (int sp = 0; sp < Sb; ++sp) {
+#pragma unroll 4
+  for (int sp = w; sp < Sb; sp += 4) {
     const float *pp = base + sp * stride;
-    const float sc = exp2f(pp[64L * HD + rl] - M);
-    l += sc * pp[64L * HD + 64 + rl];
+    const float ms = pp[64L * HD + rl], ls = pp[64L * HD + 64 + rl];
+    floatx4 ov[ND];
 #pragma unroll
-    for (int d = 0; d < ND; ++d) o[d] += sc * reinterpret_cast<const floatx4 *>(pp)[(w * ND + d) * 64 + lane];
+    for (int d = 0; d < ND; ++d) ov[d] = reinterpret_cast<const floatx4 *>(pp)[(qgrp * ND + d) * 64 + lane];
+    // A split may hold no key this query can see (only block rows beyond its
+    // own position): its maximum is -inf and it contributes nothing.
+    const float Mn = fmaxf(M, ms);
+    const float a = M == -INFINITY ? 0.f : exp2f(M - Mn);
+    const float c = ms == -INFINITY ? 0.f : exp2f(ms - Mn);
+    l = l * a + ls * c;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) o[d] = o[d] * a + ov[d] * c;
+    M = Mn;
   }
-  const float inv_l = 1.0f / l;
+  sm[w][lane] = M;
+  sl[w][lane] = l;
+#pragma unroll
+  for (int d = 0; d < ND; ++d) so[w][d][lane] = o[d];
+  __syncthreads();
+  if (w != 0 || rq >= p.R) return;
+  float Mt = sm[0][lane];
+  for (int q = 1; q < 4; ++q) Mt = fmaxf(Mt, sm[q][lane]);
+  float lt = 0.f;
+  floatx4 ot[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) ot[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < 4; ++q) {
+    const float sc = sm[q][lane] == -INFINITY ? 0.f : exp2f(sm[q][lane] - Mt);
+    lt += sc * sl[q][lane];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) ot[d] += sc * so[q][d][lane];
+  }
+  const float inv_l = 1.0f / lt;
   const int kp = rq / p.G, hl = rq - kp * p.G;
   T *dst = reinterpret_cast<T *>(p.out) + (long)(b * p.Kb + kp) * (p.nq * HD) + (gk * p.G + hl) * HD;
 #pragma unroll
   for (int d = 0; d < ND; ++d) {
-    const float v[4] = {o[d][0] * inv_l, o[d][1] * inv_l, o[d][2] * inv_l, o[d][3] * inv_l};
+    const float v[4] = {ot[d][0] * inv_l, ot[d][1] * inv_l, ot[d][2] * inv_l, ot[d][3] * inv_l};
     store_out4<T>(dst + d * 16 + 4 * g, v);
   }
 }
@@ -292,7 +331,7 @@ hipError_t launch_typed(const AttnParams &p, hipStream_t s) {
   hipLaunchKernelGGL((k_attn_decode<T, HD>), dim3(p.S, p.nkv * QP, p.B), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S <= 1) return e;
-  hipLaunchKernelGGL((k_attn_combine<T, HD>), dim3(p.B * p.nkv * QP), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_attn_combine<T, HD>), dim3(p.B * p.nkv * QP * 4), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -7,12 +7,13 @@
 //     see pe_device.hpp), strip-major: tile (n-strip, k-tile).
 //   * A workgroup owns whole 16-row strips (persistent over strips
 //     blockIdx.x, +gridDim.x, ...) and one contiguous k-chunk (blockIdx.y).
-//     It stages the activations of its k-chunk once in LDS (valid rows only),
-//     so the only HBM stream is W and the activations never compete with it.
 //   * Within a strip, wave w of W (<= 8) takes the k-tiles w, w+W, ... of the
-//     chunk and keeps up to D strips of its tile loads in flight in
-//     registers; partial 16x(16*NF) tiles are summed through LDS in wave
-//     order (deterministic) by one wave per strip, which runs the epilogue.
+//     chunk.  Those k-tiles are the same for every strip, so the wave loads
+//     their activation fragments into registers once; the only HBM stream
+//     is W.  Tile loads for the next D strips stay in flight in registers,
+//     issued without branches (buffer loads past the end read zero).
+//   * Partial 16x(16*NF) tiles are summed through LDS in wave order
+//     (deterministic) by one wave per strip, which runs the epilogue.
 //   * Nothing crosses workgroups inside a kernel: there is no device-scope
 //     fence or counter.  When the activations do not fit in LDS the K range
 //     is split over KS workgroup columns that write fp32 partial strips, and
@@ -30,18 +31,29 @@ struct Ring {
 
 __device__ __forceinline__ u32x4 lds_ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
-// rstd of the 64 activation rows from the producer's per-strip sums of
-// squares, into rsh[64] (block-wide; ends with a barrier).
-__device__ void block_rstd(const GemmParams &p, float *rsh, float *scratch) {
-  const int tid = threadIdx.x, nparts = blockDim.x >> 6;
-  const int m = tid & 63, part = tid >> 6;
+// rstd of the first `rows` activation rows (16*NF) from the producer's
+// per-strip sums of squares, into rsh[rows] (block-wide; ends with a
+// barrier).  Thread t folds row t % rows over strips t / rows + k*nparts with
+// four independent loads per step, then one thread per row folds the
+// nparts partials.  scratch holds blockDim.x floats.
+__device__ void block_rstd(const GemmParams &p, int rows, float *rsh, float *scratch) {
+  const int tid = threadIdx.x, nparts = blockDim.x / rows;
+  const int m = tid % rows, part = tid / rows;
   float a = 0.f;
-  for (int t = part; t < p.ssq_strips; t += nparts) a += p.ssq[t * kMaxRows + m];
-  scratch[part * 64 + m] = a;
+  if (part < nparts) {
+    int t = part;
+    for (; t + 3 * nparts < p.ssq_strips; t += 4 * nparts) {
+      const float v0 = p.ssq[t * kMaxRows + m], v1 = p.ssq[(t + nparts) * kMaxRows + m];
+      const float v2 = p.ssq[(t + 2 * nparts) * kMaxRows + m], v3 = p.ssq[(t + 3 * nparts) * kMaxRows + m];
+      a += (v0 + v1) + (v2 + v3);
+    }
+    for (; t < p.ssq_strips; t += nparts) a += p.ssq[t * kMaxRows + m];
+  }
+  scratch[tid] = a;
   __syncthreads();
-  if (tid < 64) {
+  if (tid < rows) {
     float s = 0.f;
-    for (int q = 0; q < nparts; ++q) s += scratch[q * 64 + tid];
+    for (int q = 0; q < nparts; ++q) s += scratch[q * rows + tid];
     rsh[tid] = rsqrtf(s * p.inv_width + p.eps);
   }
   __syncthreads();
@@ -80,84 +92,79 @@ __global__ __launch_bounds__(512) void k_gemm_wg(GemmParams p) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c16 = lane & 15, g = lane >> 4;
   const int chunk = blockIdx.y;
   const int kt0 = chunk * p.kc;
-  const int kc = min(p.kc, p.KT - kt0);         // tiles in this chunk
-  const int kel0 = kt0 * KTILE;
-  const int kelc = min(kc * KTILE, p.K - kel0);  // valid elements in this chunk
-  const int ldsrow = kc * KTILE + E;             // padded LDS row (elements)
+  const int kc = min(p.kc, p.KT - kt0);  // tiles in this chunk
 
-  T *Bs = reinterpret_cast<T *>(smem);
-  const size_t bbytes = ((size_t)p.Mv * ldsrow * sizeof(T) + 15) & ~(size_t)15;
-  floatx4 *red = reinterpret_cast<floatx4 *>(smem + bbytes);     // [W][NF][64]
+  floatx4 *red = reinterpret_cast<floatx4 *>(smem);                  // [W][NF][64]
   float *rsh = reinterpret_cast<float *>(red + (size_t)W * NF * 64);  // [64]
-  float *scratch = reinterpret_cast<float *>(red);               // aliases red before the loop
+  float *scratch = reinterpret_cast<float *>(red);                    // aliases red before the loop
 
-  // Stage this chunk's activation rows (zero past K).
-  {
-    const int cpr = kc * KTILE / E;  // fragments per row
-    const int total = p.Mv * cpr;
-    for (int i = tid; i < total; i += blockDim.x) {
-      const int m = i / cpr, cc = i - m * cpr;
-      const int k = cc * E;
-      const T *src = act_row<T>(p, m);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (src && k < kelc) v = ldg16(src + kel0 + k);
-      *reinterpret_cast<u32x4 *>(Bs + (size_t)m * ldsrow + k) = v;
-    }
-  }
-  if (p.ssq) {
-    block_rstd(p, rsh, scratch);
-  } else {
-    __syncthreads();
-  }
-  float rs[NF];
+  // This wave's k-tiles: kt0 + w + j*W for the slots j that hold one.
+  bool jok[MAXKW];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) rs[f] = p.ssq ? rsh[16 * f + c16] : 1.f;
+  for (int j = 0; j < MAXKW; ++j) jok[j] = j < p.nkw && w + j * W < kc;
 
+  // Weight tiles through a buffer resource: offsets past num_records read as
+  // zero without touching memory, so empty slots and the strips after the
+  // last one need no branches in the load stream.
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4 *>(p.wt), 0, (int)p.wbytes, 0x00020000);
+  const unsigned kOOB = 0x7FFFFFF0u;
   const int G = gridDim.x;
   const int ns = (p.NT - (int)blockIdx.x + G - 1) / G;  // strips of this workgroup
-  const int nkw = p.nkw;                                 // tile slots per wave per strip
-  const long wbase = (long)kt0 + w;                      // first k-tile of this wave
+  unsigned joff[MAXKW];  // byte offset of tile j within a strip (kOOB when empty)
+#pragma unroll
+  for (int j = 0; j < MAXKW; ++j)
+    joff[j] = jok[j] ? ((unsigned)(kt0 + w + j * W) * 64u + (unsigned)lane) * 16u : kOOB;
+  const unsigned strip_bytes = (unsigned)p.KT * 1024u;
+  auto tile_off = [&](int i, int j) -> unsigned {
+    // Tile j of this workgroup's i-th strip, or kOOB past the last strip.
+    return (i < ns && jok[j]) ? (unsigned)((int)blockIdx.x + i * G) * strip_bytes + joff[j] : kOOB;
+  };
   unsigned long long best[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) best[f] = 0ull;
 
   u32x4 abuf[D][MAXKW];
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    if (d < ns) {
-      const long s = (long)blockIdx.x + (long)d * G;
+  for (int d = 0; d < D; ++d)
 #pragma unroll
-      for (int j = 0; j < MAXKW; ++j)
-        if (j < nkw && w + j * W < kc) abuf[d][j] = ldg16(p.wt + ((s * p.KT + wbase + j * W) << 6) + lane);
+    for (int j = 0; j < MAXKW; ++j)
+      abuf[d][j] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)tile_off(d, j), 0, 0);
+  // Their activation fragments are the same for every strip, so they stay in
+  // registers for the whole kernel (loaded after the weight prefetch above).
+  u32x4 breg[MAXKW][NF];
+#pragma unroll
+  for (int j = 0; j < MAXKW; ++j) {
+    const int k = (kt0 + w + j * W) * KTILE + g * E;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const T *row = act_row<T>(p, 16 * f + c16);
+      breg[j][f] = (jok[j] && row && k < p.K) ? ldg16(row + k) : u32x4{0u, 0u, 0u, 0u};
     }
   }
+  if (p.ssq) block_rstd(p, 16 * NF, rsh, scratch);
+  float rs[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) rs[f] = p.ssq ? rsh[16 * f + c16] : 1.f;
+  __syncthreads();  // scratch (aliasing red) is free again
+
 
   for (int i0 = 0; i0 < ns; i0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int i = i0 + d;
+      floatx4 acc[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < MAXKW; ++j) {
+        const u32x4 a = abuf[d][j];
+        abuf[d][j] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)tile_off(i + D, j), 0, 0);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) acc[f] = Mma<T>::run(a, breg[j][f], acc[f]);
+      }
       if (i < ns) {
-        const long s = (long)blockIdx.x + (long)i * G;
-        const long snext = s + (long)D * G;
-        const bool more = i + D < ns;
-        floatx4 acc[NF];
-#pragma unroll
-        for (int f = 0; f < NF; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < MAXKW; ++j) {
-          const int kl = w + j * W;
-          if (j < nkw && kl < kc) {
-            const u32x4 a = abuf[d][j];
-            if (more) abuf[d][j] = ldg16(p.wt + ((snext * p.KT + wbase + j * W) << 6) + lane);
-#pragma unroll
-            for (int f = 0; f < NF; ++f) {
-              const int row = 16 * f + c16;
-              const u32x4 b = row < p.Mv ? lds_ld16(Bs + (size_t)row * ldsrow + kl * KTILE + g * E)
-                                         : u32x4{0u, 0u, 0u, 0u};
-              acc[f] = Mma<T>::run(a, b, acc[f]);
-            }
-          }
-        }
+        const int s = (int)blockIdx.x + i * G;
         // Sum the W partial tiles in wave order; wave i%W finishes the strip.
 #pragma unroll
         for (int f = 0; f < NF; ++f) red[(w * NF + f) * 64 + lane] = acc[f];
@@ -174,7 +181,7 @@ __global__ __launch_bounds__(512) void k_gemm_wg(GemmParams p) {
         __syncthreads();
         if (reducer) {
           if (p.KS == 1) {
-            finish_strip<T, NF>(p, (int)s, lane, res, rs, best);
+            finish_strip<T, NF>(p, s, lane, res, rs, best);
           } else {
 #pragma unroll
             for (int f = 0; f < NF; ++f)
@@ -193,10 +200,10 @@ __global__ __launch_bounds__(512) void k_gemm_wg(GemmParams p) {
 template <typename T, int NF>
 __global__ __launch_bounds__(256) void k_gemm_finalize(GemmParams p) {
   __shared__ float rsh[64];
-  __shared__ float scratch[4 * 64];
+  __shared__ float scratch[256];
   __shared__ unsigned long long sh[4 * 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c16 = lane & 15;
-  if (p.ssq) block_rstd(p, rsh, scratch);
+  if (p.ssq) block_rstd(p, 16 * NF, rsh, scratch);
   float rs[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) rs[f] = p.ssq ? rsh[16 * f + c16] : 1.f;
@@ -216,17 +223,29 @@ __global__ __launch_bounds__(256) void k_gemm_finalize(GemmParams p) {
   if (p.epi == EPI_ARGMAX) block_argmax_out<NF>(p, best, sh);
 }
 
-// Final argmax over the per-workgroup best keys: one workgroup.
-__global__ __launch_bounds__(256) void k_argmax_final(const unsigned long long *blk_best, int nblk,
-                                                      int M, int *draft_out) {
-  __shared__ unsigned long long sh[4 * 64];
+// Final argmax over the per-workgroup best keys: one 1024-thread workgroup;
+// thread t folds rows t%64 of workgroups t/64, t/64+16, ... (loads unrolled
+// so they are in flight together), then 16 partials per row are folded.
+__global__ __launch_bounds__(1024) void k_argmax_final(const unsigned long long *blk_best, int nblk,
+                                                       int M, int *draft_out) {
+  __shared__ unsigned long long sh[16 * 64];
   const int tid = threadIdx.x, m = tid & 63, part = tid >> 6;
   unsigned long long b = 0ull;
-  for (int q = part; q < nblk; q += 4) b = umax64(b, blk_best[(long)q * kMaxRows + m]);
+  int q = part;
+  for (; q + 48 < nblk; q += 64) {
+    const unsigned long long v0 = blk_best[(long)q * kMaxRows + m];
+    const unsigned long long v1 = blk_best[(long)(q + 16) * kMaxRows + m];
+    const unsigned long long v2 = blk_best[(long)(q + 32) * kMaxRows + m];
+    const unsigned long long v3 = blk_best[(long)(q + 48) * kMaxRows + m];
+    b = umax64(b, umax64(umax64(v0, v1), umax64(v2, v3)));
+  }
+  for (; q < nblk; q += 16) b = umax64(b, blk_best[(long)q * kMaxRows + m]);
   sh[part * 64 + m] = b;
   __syncthreads();
   if (tid < 64) {
-    unsigned long long r = umax64(umax64(sh[tid], sh[64 + tid]), umax64(sh[128 + tid], sh[192 + tid]));
+    unsigned long long r = 0ull;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) r = umax64(r, sh[k * 64 + tid]);
     if (tid < M) draft_out[tid] = (int)(0xFFFFFFFFu - (unsigned)(r & 0xFFFFFFFFull));
   }
 }
@@ -237,15 +256,20 @@ hipError_t launch_main(const GemmParams &p, const GemmLaunch &L, hipStream_t s) 
   return hipGetLastError();
 }
 
+// Slot buckets that fit in registers next to the epilogues (no spills):
+// NF=1: <= 18, NF=2: <= 8, NF=3: <= 4, NF=4: 2.
+template <int NF>
+constexpr int max_slots() { return NF == 1 ? 18 : NF == 2 ? 8 : NF == 3 ? 4 : 2; }
+
 template <typename T, int NF>
 hipError_t launch_kw(const GemmParams &p, const GemmLaunch &L, hipStream_t s) {
+  if (L.maxkw > max_slots<NF>()) return hipErrorInvalidValue;
   switch (L.maxkw) {
     case 2: return launch_main<T, NF, 2>(p, L, s);
-    case 4: return launch_main<T, NF, 4>(p, L, s);
-    case 8: return launch_main<T, NF, 8>(p, L, s);
-    case 12: return launch_main<T, NF, 12>(p, L, s);
-    case 18: return launch_main<T, NF, 18>(p, L, s);
-    case 24: return launch_main<T, NF, 24>(p, L, s);
+    case 4: if constexpr (max_slots<NF>() >= 4) return launch_main<T, NF, 4>(p, L, s); break;
+    case 8: if constexpr (max_slots<NF>() >= 8) return launch_main<T, NF, 8>(p, L, s); break;
+    case 12: if constexpr (max_slots<NF>() >= 12) return launch_main<T, NF, 12>(p, L, s); break;
+    case 18: if constexpr (max_slots<NF>() >= 18) return launch_main<T, NF, 18>(p, L, s); break;
   }
   return hipErrorInvalidValue;
 }
@@ -279,27 +303,10 @@ hipError_t launch_gemm(int dtype, int nf, const GemmParams &p, const GemmLaunch 
 
 hipError_t launch_argmax_final(const unsigned long long *blk_best, int nblk, int M, int *draft_out,
                                hipStream_t s) {
-  hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(256), 0, s, blk_best, nblk, M, draft_out);
+  hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(1024), 0, s, blk_best, nblk, M, draft_out);
   return hipGetLastError();
 }
 
-hipError_t gemm_set_lds_limits() {
-  // Allow the main kernels the full 160 KB LDS of a gfx950 workgroup.
-  const int bytes = 160 * 1024;
-#define PE_SET(T, NF, KW)                                                                        \
-  {                                                                                              \
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_wg<T, NF, KW>),    \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);       \
-    if (e != hipSuccess) return e;                                                               \
-  }
-#define PE_SET_NF(T, NF) \
-  PE_SET(T, NF, 2) PE_SET(T, NF, 4) PE_SET(T, NF, 8) PE_SET(T, NF, 12) PE_SET(T, NF, 18) \
-  PE_SET(T, NF, 24)
-  PE_SET_NF(bf16_t, 1) PE_SET_NF(bf16_t, 2) PE_SET_NF(bf16_t, 3) PE_SET_NF(bf16_t, 4)
-  PE_SET_NF(float, 1) PE_SET_NF(float, 2) PE_SET_NF(float, 3) PE_SET_NF(float, 4)
-#undef PE_SET_NF
-#undef PE_SET
-  return hipSuccess;
-}
+hipError_t gemm_set_lds_limits() { return hipSuccess; }
 
 }  // namespace pe

@@ -30,6 +30,7 @@ constexpr int kMaxRows = 64;  // decode activation rows (B*K and B+1)
 struct GemmParams {
   // Weights, tiled: fragment (nt, kt, lane) at wt[(nt*KT + kt)*64 + lane].
   const u32x4 *wt;
+  unsigned wbytes;  // NT*KT*1024, below 2^31
   int NT, KT;
   int N;            // output rows of the (row-mapped) weight
   int K;            // contraction length (multiple of the fragment width)
@@ -41,7 +42,7 @@ struct GemmParams {
   const void *act_extra;
   int M;            // valid activation rows (output columns)
   // Work split: KS k-chunks of kc tiles (blockIdx.y); each workgroup wave
-  // holds nkw tile slots per strip; Mv activation rows are staged in LDS.
+  // holds nkw tile slots per strip; Mv = valid activation rows.
   int epi;          // Epi
   int KS, kc, nkw, Mv;
   floatx4 *part;    // [KS][NT][NF][64] partial strips when KS > 1
@@ -82,7 +83,7 @@ struct GemmLaunch {
   int grid;     // workgroups per k-chunk
   int waves;    // waves per workgroup
   size_t lds;   // dynamic LDS bytes
-  int maxkw;    // tile-slot bucket (2, 4, 8, 12, 18, 24) >= nkw
+  int maxkw;    // tile-slot bucket (2, 4, 8, 12, 18) >= nkw
 };
 
 hipError_t launch_gemm(int dtype, int nf, const GemmParams &p, const GemmLaunch &L, hipStream_t s);
