@@ -33,7 +33,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 METRIC = "draft tokens/s per P-EAGLE forward (K=8, ctx 4K) + % of HBM roofline"
 COUNTERS = os.path.join(ROOT, "profiles", "lm_head_counters.json")
-KERNEL_SRC = os.path.join(ROOT, "drafting_eagle_draft_amd", "csrc", "gemm_stream.hip")
+# Sources of the LM-head kernel; counters taken on other sources are stale.
+KERNEL_SRCS = [os.path.join(ROOT, "drafting_eagle_draft_amd", "csrc", f) for f in
+               ("gemm_wg.hip", "pe_epilogue.hpp", "pe_device.hpp", "pe_internal.hpp")]
+
+
+def kernel_sha256():
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def algorithmic_bytes(cfg, ctx_lens, B, K):
@@ -80,8 +89,7 @@ def traffic_from_counters(lm_launch_bytes):
         return None
     with open(COUNTERS) as f:
         c = json.load(f)
-    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if c.get("kernel_sha256") != src:
+    if c.get("kernel_sha256") != kernel_sha256():
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -96,7 +104,12 @@ def main():
     ap.add_argument("--graph", action="store_true", help="also time hipGraph replays")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--print-kernel-sha", action="store_true",
+                    help="print the LM-head kernel source hash and exit")
     a = ap.parse_args()
+    if a.print_kernel_sha:
+        print(kernel_sha256())
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this path runs on a single MI355X and has no "
               f"multi-GPU mode (asked for --gpus {a.gpus})", file=sys.stderr)

@@ -85,7 +85,7 @@ __device__ void block_argmax_out(const GemmParams &p, const unsigned long long (
 }
 
 template <typename T, int NF, int MAXKW>
-__global__ __launch_bounds__(512) void k_gemm_wg(GemmParams p) {
+__device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
   constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE, D = Ring<MAXKW>::D;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int W = blockDim.x >> 6;
@@ -195,6 +195,18 @@ __global__ __launch_bounds__(512) void k_gemm_wg(GemmParams p) {
     block_argmax_out<NF>(p, best, reinterpret_cast<unsigned long long *>(red));
 }
 
+template <typename T, int NF, int MAXKW>
+__global__ __launch_bounds__(512) void k_gemm_wg(GemmParams p) {
+  gemm_wg_body<T, NF, MAXKW>(p);
+}
+
+// The LM head: the same weight-streaming body with the fused argmax (its
+// own symbol, so profiles report it apart from the layer projections).
+template <typename T, int NF, int MAXKW>
+__global__ __launch_bounds__(512) void k_lm_head_argmax(GemmParams p) {
+  gemm_wg_body<T, NF, MAXKW>(p);
+}
+
 // KS > 1: one wave per strip sums the chunk partials in chunk order and runs
 // the epilogue.
 template <typename T, int NF>
@@ -252,7 +264,10 @@ __global__ __launch_bounds__(1024) void k_argmax_final(const unsigned long long 
 
 template <typename T, int NF, int MAXKW>
 hipError_t launch_main(const GemmParams &p, const GemmLaunch &L, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm_wg<T, NF, MAXKW>), dim3(L.grid, p.KS), dim3(L.waves * 64), L.lds, s, p);
+  if (p.epi == EPI_ARGMAX)
+    hipLaunchKernelGGL((k_lm_head_argmax<T, NF, MAXKW>), dim3(L.grid, p.KS), dim3(L.waves * 64), L.lds, s, p);
+  else
+    hipLaunchKernelGGL((k_gemm_wg<T, NF, MAXKW>), dim3(L.grid, p.KS), dim3(L.waves * 64), L.lds, s, p);
   return hipGetLastError();
 }
 
