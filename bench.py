@@ -12,9 +12,14 @@ in HBM.  Prints one JSON line:
              around it on the forward's stream during the timed steps
   forward_roofline  the whole forward's algorithmic bytes / step time
   cpu_baseline      the CPU oracle on the same workload (host cores)
+  train_forward     the training-shape forward (one drafter layer over a COD
+                    layout of 8192 positions, K = 8, about 34K kept rows,
+                    bf16 logits at every row): rows/s and its matrix-core
+                    roofline (LM-head kernel and whole forward, TFLOP/s)
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
        [--no-cpu-baseline] [--graph] [--copy-calibration]
+       [--no-train | --train-only] [--train-steps S]
 """
 from __future__ import annotations
 
@@ -82,6 +87,86 @@ def cpu_baseline(cfg, w, inp, reps=2):
                       f"all {B * K} rows, fp64 NumPy) after one warm run"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def train_flops(cfg, n, rows, K):
+    """Algorithmic flops of one training-shape forward over kept rows ``rows``:
+    2 x weights per row for every projection of every kept row (fc once per
+    position plus once for the shared hidden state), and 4 x hd x n_q per
+    allowed query/key pair, each row seeing p + 1 keys."""
+    H, I, V, hd = cfg.hidden, cfg.intermediate, cfg.vocab, cfg.head_dim
+    nq, nkv, N = cfg.n_q_heads, cfg.n_kv_heads, cfg.n_layers
+    L = len(rows)
+    layer = (nq + 2 * nkv) * hd * H + H * nq * hd + 2 * I * H + H * I
+    fc = 2.0 * (n + 1) * 3 * H * H
+    gemm = 2.0 * L * (N * layer + V * H) + fc
+    pairs = float(np.sum(np.asarray(rows) // K + 1))
+    attn = N * 4.0 * hd * nq * pairs
+    return {"total": gemm + attn, "gemm": gemm, "attention": attn, "lm_head": 2.0 * L * V * H,
+            "pairs": pairs}
+
+
+def train_leg(steps, warmup):
+    """Training-shape forward (one GPT-OSS-20B-shaped drafter layer over a
+    COD layout of n = 8192, K = 8, r = 0.8; mask built once for n_max =
+    20480; bf16 logits at every kept row)."""
+    import torch
+    from drafting_eagle_draft_amd import binding as pe
+    from drafting_eagle_draft_amd import runner, synth
+    cfg = synth.config("train_gptoss20b_n8192_k8")
+    n, K = cfg.seq_len, cfg.K
+    t0 = time.time()
+    w = synth.drafter_weights(cfg)
+    inp = synth.train_inputs(cfg)
+    U = synth.cod_uniforms(cfg, n, K)
+    rows = pe.pe_cod_rows(n, K, cfg.cod_rate, cfg.cod_floor, U.reshape(-1))
+    print(f"[bench] training inputs in {time.time() - t0:.1f}s, L = {len(rows)}", file=sys.stderr,
+          flush=True)
+    d = runner.Drafter(cfg, w)
+    del w
+    mask = runner.TrainMask(cfg.n_max, K)
+    buf = runner.TrainBuffers(d, mask, inp, rows)
+    for _ in range(warmup):
+        buf.launch(d, mask)
+    torch.cuda.synchronize()
+    pe.pe_profile_enable(d.handle, True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        buf.launch(d, mask)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    n_lm, lm_ms = pe.pe_profile_read(d.handle)
+    pe.pe_profile_enable(d.handle, False)
+    L = len(rows)
+    f = train_flops(cfg, n, rows, K)
+    achieved = f["total"] / (ms * 1e-3) / 1e12
+    lm_tf = f["lm_head"] / (lm_ms * 1e-3) / 1e12 if lm_ms > 0 else None
+    del buf
+    mask.close()
+    d.close()
+    torch.cuda.empty_cache()
+    return {
+        "metric": "kept rows/s per training-shape forward (n 8192, K 8, COD r 0.8)",
+        "value": L / (ms * 1e-3), "unit": "rows/s", "ms_per_step": ms, "steps": steps,
+        "warmup": warmup, "dtype": cfg.dtype,
+        "config": {"workload": cfg.name, "n": n, "K": K, "L": L, "n_max": cfg.n_max,
+                   "layers": cfg.n_layers, "logits": "bf16 [L, V]"},
+        "roofline": {"bound": "mfma", "kernel": "LM head GEMM + argmax keys",
+                     "achieved": lm_tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": (lm_tf / MFMA_BF16_PEAK_TFLOPS) if lm_tf else None, "traffic": None,
+                     "algorithmic_flops_per_launch": f["lm_head"], "launches": n_lm,
+                     "mean_launch_ms": lm_ms},
+        "forward_roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                             "algorithmic_flops": f["total"], "gemm_flops": f["gemm"],
+                             "attention_flops": f["attention"], "allowed_pairs": f["pairs"]},
+    }
+
+
 def traffic_from_counters(lm_launch_bytes):
     """HBM bytes per LM-head launch from the committed rocprofv3 PMC summary,
     or None when missing or taken on a different kernel source."""
@@ -104,6 +189,11 @@ def main():
     ap.add_argument("--graph", action="store_true", help="also time hipGraph replays")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip the training-shape forward leg")
+    ap.add_argument("--train-only", action="store_true",
+                    help="run only the training-shape forward leg (its own JSON line)")
+    ap.add_argument("--train-steps", type=int, default=5)
     ap.add_argument("--print-kernel-sha", action="store_true",
                     help="print the LM-head kernel source hash and exit")
     a = ap.parse_args()
@@ -119,6 +209,9 @@ def main():
     from drafting_eagle_draft_amd import binding as pe
     from drafting_eagle_draft_amd import runner, synth
 
+    if a.train_only:
+        print(json.dumps(train_leg(a.train_steps, 2)), flush=True)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = synth.config(a.workload)
@@ -214,6 +307,11 @@ def main():
     else:
         out["cpu_baseline"] = None
     drafter.close()
+    del buf
+    torch.cuda.empty_cache()
+    if not a.no_train:
+        print("[bench] training-shape forward", file=sys.stderr, flush=True)
+        out["train_forward"] = train_leg(a.train_steps, 2)
     print(json.dumps(out), flush=True)
 
 

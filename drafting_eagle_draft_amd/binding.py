@@ -27,7 +27,8 @@ PE_DECODE_ROWS_MAX = 64
 EXPORTS = (
     "pe_model_create", "pe_model_destroy", "pe_draft_workspace_size", "pe_workspace_init",
     "pe_draft_forward", "pe_accept", "pe_last_error", "pe_version", "pe_profile_enable",
-    "pe_profile_read",
+    "pe_profile_read", "pe_mask_create", "pe_mask_destroy", "pe_mask_materialize",
+    "pe_train_workspace_size", "pe_train_forward", "pe_cod_rows", "pe_partition",
 )
 
 
@@ -81,6 +82,13 @@ def load(path: str = LIB_PATH):
         "pe_accept": [i32, i32, vp, vp, vp, vp, vp],
         "pe_profile_enable": [vp, i32],
         "pe_profile_read": [vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)],
+        "pe_mask_create": [i32, i32, vp, ctypes.POINTER(vp)],
+        "pe_mask_destroy": [vp],
+        "pe_mask_materialize": [vp, i32, vp, i32, vp, vp],
+        "pe_train_workspace_size": [vp, i32, i32, i32, ctypes.POINTER(sz)],
+        "pe_train_forward": [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp],
+        "pe_cod_rows": [i32, i32, ctypes.c_double, ctypes.c_double, vp, vp, ctypes.POINTER(i32)],
+        "pe_partition": [i32, i32, i32, vp, i32, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -165,3 +173,53 @@ def pe_profile_read(model: int):
     ms = ctypes.c_double()
     _check("pe_profile_read", load().pe_profile_read(model, ctypes.byref(n), ctypes.byref(ms)))
     return n.value, ms.value
+
+
+def pe_mask_create(n_max: int, K: int, stream: int = 0) -> int:
+    out = ctypes.c_void_p()
+    _check("pe_mask_create", load().pe_mask_create(n_max, K, stream, ctypes.byref(out)))
+    return out.value
+
+
+def pe_mask_destroy(mask: int) -> None:
+    _check("pe_mask_destroy", load().pe_mask_destroy(mask))
+
+
+def pe_mask_materialize(mask: int, n: int, rows: int, L: int, out: int, stream: int = 0) -> None:
+    _check("pe_mask_materialize", load().pe_mask_materialize(mask, n, rows, L, out, stream))
+
+
+def pe_train_workspace_size(model: int, n: int, K: int, L: int) -> int:
+    b = ctypes.c_size_t()
+    _check("pe_train_workspace_size", load().pe_train_workspace_size(model, n, K, L, ctypes.byref(b)))
+    return b.value
+
+
+def pe_train_forward(model: int, mask: int, N: int, n: int, K: int, hidden3: int, token_ids: int,
+                     mask_emb: int, h_shared: int, rows: int, L: int, logits_out: int | None,
+                     argmax_out: int | None, workspace: int, ws_bytes: int, stream: int = 0) -> None:
+    _check("pe_train_forward", load().pe_train_forward(
+        model, mask, N, n, K, hidden3, token_ids, mask_emb, h_shared, rows, L, logits_out,
+        argmax_out, workspace, ws_bytes, stream))
+
+
+def pe_cod_rows(n: int, K: int, r: float, floor_rate: float, U):
+    """Host COD sampling: U float64 array [n*K] -> int32 array of kept grid indices."""
+    import numpy as np
+    U = np.ascontiguousarray(U, dtype=np.float64)
+    if U.size != n * K:
+        raise ValueError(f"U has {U.size} entries, n*K = {n * K}")
+    rows = np.empty(max(1, n * K), dtype=np.int32)
+    L = ctypes.c_int32()
+    _check("pe_cod_rows", load().pe_cod_rows(n, K, r, floor_rate, U.ctypes.data, rows.ctypes.data,
+                                             ctypes.byref(L)))
+    return rows[:L.value].copy()
+
+
+def pe_partition(n: int, K: int, S: int, rows):
+    """Host partition of kept rows into S chunks -> int32 chunk index per row."""
+    import numpy as np
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    out = np.empty(max(1, rows.size), dtype=np.int32)
+    _check("pe_partition", load().pe_partition(n, K, S, rows.ctypes.data, rows.size, out.ctypes.data))
+    return out[:rows.size].copy()

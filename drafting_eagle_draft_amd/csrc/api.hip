@@ -29,6 +29,14 @@ pe_status fail(pe_status st, const char *fmt, ...) {
   return st;
 }
 
+}  // namespace
+
+namespace pe {
+pe_status set_error(pe_status st, const char *msg) { return fail(st, "%s", msg); }
+}  // namespace pe
+
+namespace {
+
 pe_status hip_fail(hipError_t e, const char *what) {
   return fail(PE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -74,6 +82,11 @@ struct pe_model {
   mutable bool prof = false;
   mutable std::vector<hipEvent_t> ev0, ev1;
   mutable int nrec = 0;
+};
+
+struct pe_mask {
+  int n_max = 0, K = 0;
+  int2 *table = nullptr;  // [n_max*K] (anchor, depth) of every grid cell
 };
 
 namespace {
@@ -255,6 +268,58 @@ pe_status check_cfg(const pe_config *c) {
     return fail(PE_ERR_UNSUPPORTED, "query heads per kv head must be <= 16");
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f))
     return fail(PE_ERR_INVALID_ARGUMENT, "rope_theta must be > 0 and rms_eps >= 0");
+  return PE_OK;
+}
+
+// Workspace of the training-shape forward.
+struct TrainLayout {
+  size_t anc, dep, inv, yfc, xres, u, q, kall, vall, k0, v0, attn, h, keys, total;
+  int col_groups;
+};
+
+TrainLayout train_layout(const pe_model *m, long n, int K, long L) {
+  const pe_config &c = m->cfg;
+  TrainLayout t{};
+  const size_t H = c.hidden, esz = m->esz, hd = c.head_dim;
+  // LM-head column groups: enough workgroups to fill the chip several
+  // times over, each group walking its share of the 128-column blocks.
+  const long row_blocks = (L + 127) / 128;
+  const int col_blocks = (m->lm.NT + 7) / 8;
+  long cg = (4L * m->num_cus + row_blocks - 1) / row_blocks;
+  if (cg < 1) cg = 1;
+  if (cg > col_blocks) cg = col_blocks;
+  t.col_groups = (int)cg;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + std::max(bytes, (size_t)1), 256); return o; };
+  t.anc = take((size_t)L * 4);
+  t.dep = take((size_t)L * 4);
+  t.inv = take((size_t)n * K * 4);
+  t.yfc = take((size_t)(n + 1) * H * 4);
+  t.xres = take((size_t)L * H * 4);
+  t.u = take((size_t)L * H * esz);
+  const bool layers = c.n_layers > 0;
+  t.q = take(layers ? (size_t)L * c.n_q_heads * hd * esz : 0);
+  t.kall = take(layers ? (size_t)L * c.n_kv_heads * hd * esz : 0);
+  t.vall = take(layers ? (size_t)L * c.n_kv_heads * hd * esz : 0);
+  t.k0 = take(layers ? (size_t)n * c.n_kv_heads * hd * esz : 0);
+  t.v0 = take(layers ? (size_t)n * c.n_kv_heads * hd * esz : 0);
+  t.attn = take(layers ? (size_t)L * c.n_q_heads * hd * esz : 0);
+  t.h = take(layers ? (size_t)L * c.intermediate * esz : 0);
+  t.keys = take((size_t)L * t.col_groups * 8);
+  t.total = off;
+  return t;
+}
+
+constexpr long kTrainRowsMax = 1L << 22;  // 128-row blocks stay well within the grid's y limit
+
+pe_status check_train_shape(const pe_model *m, const pe_mask *mask, int32_t n, int32_t K, int32_t L) {
+  if (!m || !mask) return fail(PE_ERR_INVALID_ARGUMENT, "model and mask must be non-NULL");
+  if (K != mask->K) return fail(PE_ERR_INVALID_ARGUMENT, "K=%d differs from the mask's K=%d", K, mask->K);
+  if (n < 1 || n > mask->n_max)
+    return fail(PE_ERR_INVALID_ARGUMENT, "n=%d outside [1, n_max=%d]", n, mask->n_max);
+  if (L < 1 || (long)L > (long)n * K || L > kTrainRowsMax)
+    return fail(PE_ERR_INVALID_ARGUMENT, "L=%d outside [1, min(n*K=%ld, %ld)]", L, (long)n * K,
+                kTrainRowsMax);
   return PE_OK;
 }
 
@@ -530,6 +595,168 @@ pe_status pe_accept(int32_t B, int32_t K, const int32_t *draft, const int32_t *t
   hipError_t e = launch_accept(B, K, draft, target, accept_len, out_tokens,
                                reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "accept launch");
+  return PE_OK;
+}
+
+pe_status pe_mask_create(int32_t n_max, int32_t K, void *stream, pe_mask **out) {
+  if (!out) return fail(PE_ERR_INVALID_ARGUMENT, "out must be non-NULL");
+  *out = nullptr;
+  if (K < 1 || K > PE_K_MAX) return fail(PE_ERR_INVALID_ARGUMENT, "K=%d outside [1, %d]", K, PE_K_MAX);
+  if (n_max < 1 || (long)n_max * K > kTrainRowsMax)
+    return fail(PE_ERR_INVALID_ARGUMENT, "n_max=%d: need 1 <= n_max and n_max*K <= %ld", n_max,
+                kTrainRowsMax);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  pe_mask *mk = new pe_mask();
+  mk->n_max = n_max;
+  mk->K = K;
+  hipError_t e = hipMalloc(&mk->table, (size_t)n_max * K * sizeof(int2));
+  if (e != hipSuccess) { delete mk; return hip_fail(e, "hipMalloc(mask table)"); }
+  e = launch_mask_table(n_max, K, mk->table, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    (void)hipFree(mk->table);
+    delete mk;
+    return hip_fail(e, "mask table build");
+  }
+  *out = mk;
+  return PE_OK;
+}
+
+pe_status pe_mask_destroy(pe_mask *mk) {
+  if (!mk) return fail(PE_ERR_INVALID_ARGUMENT, "mask is NULL");
+  (void)hipFree(mk->table);
+  delete mk;
+  return PE_OK;
+}
+
+pe_status pe_mask_materialize(const pe_mask *mk, int32_t n, const int32_t *rows, int32_t L, uint8_t *out,
+                              void *stream) {
+  if (!mk || !rows || !out) return fail(PE_ERR_INVALID_ARGUMENT, "mask, rows and out must be non-NULL");
+  if (n < 1 || n > mk->n_max) return fail(PE_ERR_INVALID_ARGUMENT, "n=%d outside [1, %d]", n, mk->n_max);
+  if (L < 1 || L > 65536 || (long)L > (long)n * mk->K)
+    return fail(PE_ERR_INVALID_ARGUMENT, "L=%d outside [1, min(n*K, 65536)]", L);
+  hipError_t e = launch_mask_materialize(mk->table, n * mk->K, rows, L, out,
+                                         reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mask materialize launch");
+  return PE_OK;
+}
+
+pe_status pe_train_workspace_size(const pe_model *m, int32_t n, int32_t K, int32_t L, size_t *bytes) {
+  if (!m || !bytes) return fail(PE_ERR_INVALID_ARGUMENT, "model and bytes must be non-NULL");
+  if (K < 1 || K > PE_K_MAX) return fail(PE_ERR_INVALID_ARGUMENT, "K=%d outside [1, %d]", K, PE_K_MAX);
+  if (n < 1 || L < 1 || (long)L > (long)n * K || L > kTrainRowsMax)
+    return fail(PE_ERR_INVALID_ARGUMENT, "need n >= 1 and 1 <= L <= min(n*K, %ld)", kTrainRowsMax);
+  *bytes = train_layout(m, n, K, L).total;
+  return PE_OK;
+}
+
+pe_status pe_train_forward(const pe_model *m, const pe_mask *mask, int32_t N, int32_t n, int32_t K,
+                           const void *hidden3, const int32_t *token_ids, const void *mask_emb,
+                           const void *h_shared, const int32_t *rows, int32_t L, void *logits_out,
+                           int32_t *argmax_out, void *workspace, size_t ws_bytes, void *stream) {
+  pe_status st = check_train_shape(m, mask, n, K, L);
+  if (st != PE_OK) return st;
+  const pe_config &c = m->cfg;
+  if (N < 0 || N > c.n_layers)
+    return fail(PE_ERR_INVALID_ARGUMENT, "N=%d outside [0, n_layers=%d]", N, c.n_layers);
+  if (!hidden3 || !token_ids || !mask_emb || !h_shared || !rows)
+    return fail(PE_ERR_INVALID_ARGUMENT, "hidden3, token_ids, mask_emb, h_shared and rows must be non-NULL");
+  if (misaligned(hidden3) || misaligned(mask_emb) || misaligned(h_shared) ||
+      (logits_out && misaligned(logits_out)) || misaligned(workspace))
+    return fail(PE_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  if (!workspace) return fail(PE_ERR_WORKSPACE, "workspace is NULL");
+  const TrainLayout W = train_layout(m, n, K, L);
+  if (ws_bytes < W.total)
+    return fail(PE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char *ws = reinterpret_cast<char *>(workspace);
+  int *anc = reinterpret_cast<int *>(ws + W.anc);
+  int *dep = reinterpret_cast<int *>(ws + W.dep);
+  int *inv = reinterpret_cast<int *>(ws + W.inv);
+  float *yfc = reinterpret_cast<float *>(ws + W.yfc);
+  float *xres = reinterpret_cast<float *>(ws + W.xres);
+  void *u = ws + W.u;
+  const int H = c.hidden, hd = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const int dt = c.dtype;
+
+  auto gemm = [&](const Tiled &t, int epi, BigGemmParams p, int col_groups) -> pe_status {
+    p.wt = t.ptr; p.NT = t.NT; p.KT = t.KT; p.N = t.N; p.K = t.K;
+    hipError_t e = launch_gemm_big(dt, epi, p, col_groups, s);
+    return e == hipSuccess ? PE_OK : hip_fail(e, "GEMM launch");
+  };
+  hipError_t e = launch_gather_rows(mask->table, n * K, rows, L, anc, dep, inv, s);
+  if (e != hipSuccess) return hip_fail(e, "row gather launch");
+  // Input fusion: fc over the n hidden rows and h_shared, then E[x_p] or mask_emb.
+  {
+    BigGemmParams p{};
+    p.A = hidden3; p.lda = 3L * H; p.M = n + 1; p.A_last = h_shared;
+    p.C = yfc; p.ldc = H;
+    if ((st = gemm(m->fc, BEPI_STORE, p, 0)) != PE_OK) return st;
+    e = launch_train_fuse(dt, yfc, m->embed, token_ids, mask_emb, anc, dep, L, n, H, c.vocab, xres, s);
+    if (e != hipSuccess) return hip_fail(e, "fusion launch");
+  }
+  for (int l = 0; l < N; ++l) {
+    const LayerT &Lw = m->layers[l];
+    if ((e = launch_rmsnorm_rows(dt, xres, Lw.attn_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
+      return hip_fail(e, "RMSNorm launch");
+    {
+      BigGemmParams p{};
+      p.A = u; p.lda = H; p.M = L;
+      p.q = ws + W.q; p.kall = ws + W.kall; p.vall = ws + W.vall; p.k0 = ws + W.k0; p.v0 = ws + W.v0;
+      p.anc = anc; p.dep = dep; p.inv_freq = m->inv_freq;
+      p.n = n; p.nq = nq; p.nkv = nkv; p.hd = hd;
+      if ((st = gemm(Lw.qkv, BEPI_QKV, p, 0)) != PE_OK) return st;
+    }
+    {
+      TrainAttnParams a{};
+      a.q = ws + W.q; a.k0 = ws + W.k0; a.v0 = ws + W.v0; a.kall = ws + W.kall; a.vall = ws + W.vall;
+      a.anc = anc; a.dep = dep; a.inv = inv;
+      a.L = L; a.n = n; a.K = K; a.nq = nq; a.nkv = nkv; a.hd = hd; a.G = nq / nkv;
+      a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+      a.out = ws + W.attn;
+      if ((e = launch_attn_train(dt, a, s)) != hipSuccess) return hip_fail(e, "attention launch");
+    }
+    {
+      BigGemmParams p{};
+      p.A = ws + W.attn; p.lda = (long)nq * hd; p.M = L;
+      p.C = xres; p.ldc = H;
+      if ((st = gemm(Lw.o, BEPI_ACCUM, p, 0)) != PE_OK) return st;
+    }
+    if ((e = launch_rmsnorm_rows(dt, xres, Lw.mlp_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
+      return hip_fail(e, "RMSNorm launch");
+    {
+      BigGemmParams p{};
+      p.A = u; p.lda = H; p.M = L;
+      p.h = ws + W.h; p.I = c.intermediate;
+      if ((st = gemm(Lw.gateup, BEPI_SWIGLU, p, 0)) != PE_OK) return st;
+    }
+    {
+      BigGemmParams p{};
+      p.A = ws + W.h; p.lda = c.intermediate; p.M = L;
+      p.C = xres; p.ldc = H;
+      if ((st = gemm(Lw.down, BEPI_ACCUM, p, 0)) != PE_OK) return st;
+    }
+  }
+  if ((e = launch_rmsnorm_rows(dt, xres, m->final_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
+    return hip_fail(e, "RMSNorm launch");
+  {
+    BigGemmParams p{};
+    p.A = u; p.lda = H; p.M = L;
+    p.logits = logits_out; p.ldc = c.vocab;
+    p.keys = reinterpret_cast<unsigned long long *>(ws + W.keys);
+    const bool prof = m->prof && m->nrec < (int)m->ev0.size();
+    if (prof) (void)hipEventRecord(m->ev0[m->nrec], s);
+    if ((st = gemm(m->lm, BEPI_LMHEAD, p, W.col_groups)) != PE_OK) return st;
+    if (prof) {
+      (void)hipEventRecord(m->ev1[m->nrec], s);
+      ++m->nrec;
+    }
+    if (argmax_out) {
+      e = launch_argmax_rows(p.keys, W.col_groups, L, argmax_out, s);
+      if (e != hipSuccess) return hip_fail(e, "argmax launch");
+    }
+  }
   return PE_OK;
 }
 

@@ -123,4 +123,66 @@ hipError_t launch_accept(int B, int K, const int *draft, const int *target, int 
                          int *out_tokens, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 
+// ---- training-shape forward (many rows) ----
+
+// C = A W^T over M activation rows with W in the tile layout above.
+enum BigEpi : int {
+  BEPI_STORE = 0,   // C fp32 [M][ldc] = result
+  BEPI_LMHEAD = 1,  // logits (dtype [M][ldc], optional) + best argmax key per
+                    // row and column group, keys[M][col_groups]
+  BEPI_ACCUM = 2,   // C += result (residual update)
+  BEPI_SWIGLU = 3,  // MAP_GATEUP rows: h[M][I] = silu(gate) * up
+  BEPI_QKV = 4,     // MAP_QKV rows: RoPE at position anc+dep, scatter q/k/v
+};
+
+struct BigGemmParams {
+  const u32x4 *wt;
+  int NT, KT, N, K;
+  const void *A;        // dtype [M][lda]
+  long lda;
+  int M;
+  const void *A_last;   // when non-null, row M-1 is read from here instead
+  float *C;
+  long ldc;
+  void *logits;
+  unsigned long long *keys;
+  // SWIGLU
+  void *h;
+  int I;
+  // QKV: q [M][nq][hd], kall/vall [M][nkv][hd], depth-0 rows also to
+  // k0/v0 [n][nkv][hd] at their position.
+  void *q, *kall, *vall, *k0, *v0;
+  const int *anc, *dep;
+  const double *inv_freq;
+  int n, nq, nkv, hd;
+};
+
+hipError_t launch_gemm_big(int dtype, int epi, const BigGemmParams &p, int col_groups, hipStream_t s);
+hipError_t launch_argmax_rows(const unsigned long long *keys, int ngroups, int M, int *out,
+                              hipStream_t s);
+
+hipError_t launch_mask_table(int n_max, int K, int2 *table, hipStream_t s);
+hipError_t launch_gather_rows(const int2 *table, int nK, const int *rows, int L, int *anc, int *dep,
+                              int *inv, hipStream_t s);
+hipError_t launch_mask_materialize(const int2 *table, int nK, const int *rows, int L, unsigned char *out,
+                                   hipStream_t s);
+hipError_t launch_train_fuse(int dtype, const float *Y, const void *embed, const int *tok,
+                             const void *mask_emb, const int *anc, const int *dep, int L, int n, int H,
+                             int V, float *x, hipStream_t s);
+hipError_t launch_rmsnorm_rows(int dtype, const float *x, const float *gain, int rows, int H, float eps,
+                               void *u, hipStream_t s);
+
+struct TrainAttnParams {
+  const void *q;            // [L][nq][hd] rotated queries
+  const void *k0, *v0;      // [n][nkv][hd] depth-0 keys/values by position
+  const void *kall, *vall;  // [L][nkv][hd] keys/values of every kept row
+  const int *anc, *dep;     // [L]
+  const int *inv;           // [n*K] grid index -> kept row or -1
+  int L, n, K, nq, nkv, hd, G;
+  float scale_log2;
+  void *out;                // [L][nq*hd] dtype
+};
+
+hipError_t launch_attn_train(int dtype, const TrainAttnParams &p, hipStream_t s);
+
 }  // namespace pe

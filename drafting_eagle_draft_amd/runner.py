@@ -122,3 +122,79 @@ def accept(draft: np.ndarray, target: np.ndarray, device="cuda:0", with_tokens=T
                  o.data_ptr() if o is not None else None, stream_handle())
     torch.cuda.synchronize()
     return a.cpu().numpy()[:B], (o.cpu().numpy()[:B] if o is not None else None)
+
+
+class TrainMask:
+    """The amortized mask handle, built once for sequences of up to n_max positions."""
+
+    def __init__(self, n_max: int, K: int):
+        self.n_max, self.K = n_max, K
+        self.handle = pe.pe_mask_create(n_max, K, stream_handle())
+
+    def close(self):
+        if self.handle:
+            pe.pe_mask_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def materialize(self, n: int, rows, device="cuda:0") -> np.ndarray:
+        """Dense boolean mask [L, L] of kept rows ``rows`` (tiny sizes only)."""
+        r = torch.from_numpy(np.ascontiguousarray(rows, np.int32)).to(device)
+        L = r.numel()
+        out = torch.full((L, L), 7, dtype=torch.uint8, device=device)
+        pe.pe_mask_materialize(self.handle, n, r.data_ptr(), L, out.data_ptr(), stream_handle())
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def materialize_device(self, n: int, rows_dev: torch.Tensor) -> torch.Tensor:
+        L = rows_dev.numel()
+        out = torch.empty((L, L), dtype=torch.uint8, device=rows_dev.device)
+        pe.pe_mask_materialize(self.handle, n, rows_dev.data_ptr(), L, out.data_ptr(), stream_handle())
+        return out
+
+
+class TrainBuffers:
+    """Device copies of one training-shape call's inputs plus its outputs."""
+
+    def __init__(self, drafter: Drafter, mask: TrainMask, inp, rows, N=None, want_logits=True,
+                 want_argmax=True):
+        cfg, dev = drafter.cfg, drafter.device
+        self.N = cfg.n_layers if N is None else N
+        self.n = int(len(inp["token_ids"]))
+        self.K = mask.K
+        self.hidden3 = to_device(inp["hidden3"], cfg, dev)
+        self.token_ids = torch.from_numpy(np.asarray(inp["token_ids"], np.int32)).to(dev)
+        self.mask_emb = to_device(inp["mask_emb"], cfg, dev)
+        self.h_shared = to_device(inp["h_shared"], cfg, dev)
+        self.rows = torch.from_numpy(np.ascontiguousarray(rows, np.int32)).to(dev)
+        self.L = int(self.rows.numel())
+        self.logits = (torch.empty((self.L, cfg.vocab), dtype=_dtype(cfg), device=dev)
+                       if want_logits else None)
+        self.argmax = (torch.full((self.L,), -1, dtype=torch.int32, device=dev)
+                       if want_argmax else None)
+        nbytes = pe.pe_train_workspace_size(drafter.handle, self.n, self.K, self.L)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        pe.pe_workspace_init(self.ws.data_ptr(), self.ws.numel(), stream_handle())
+
+    def launch(self, drafter: Drafter, mask: TrainMask, stream: int | None = None):
+        pe.pe_train_forward(
+            drafter.handle, mask.handle, self.N, self.n, self.K, self.hidden3.data_ptr(),
+            self.token_ids.data_ptr(), self.mask_emb.data_ptr(), self.h_shared.data_ptr(),
+            self.rows.data_ptr(), self.L,
+            self.logits.data_ptr() if self.logits is not None else None,
+            self.argmax.data_ptr() if self.argmax is not None else None,
+            self.ws.data_ptr(), self.ws.numel(), stream_handle() if stream is None else stream)
+
+
+def train_forward(drafter: Drafter, mask: TrainMask, inp, rows, N=None, want_logits=True):
+    """Run one training-shape forward; returns (argmax [L] int32, logits [L,V] float32 or None) on host."""
+    buf = TrainBuffers(drafter, mask, inp, rows, N=N, want_logits=want_logits)
+    buf.launch(drafter, mask)
+    torch.cuda.synchronize()
+    return (buf.argmax.cpu().numpy(),
+            buf.logits.float().cpu().numpy() if buf.logits is not None else None)

@@ -103,9 +103,9 @@ pe_status pe_model_destroy(pe_model *m);
 pe_status pe_draft_workspace_size(const pe_model *m, int32_t B, int32_t K, int64_t ctx_stride,
                                   size_t *bytes);
 
-/* Zero a workspace (device, ws_bytes) on the stream.  Required once after
- * allocating it: the kernels keep their completion counters in it and leave
- * them at zero when they finish. */
+/* Zero a workspace (device, ws_bytes) on the stream with a fill kernel (no
+ * memset node, so it may sit in a captured graph).  Every kernel writes what
+ * it later reads, so this only makes a fresh workspace's contents defined. */
 pe_status pe_workspace_init(void *workspace, size_t ws_bytes, void *stream);
 
 /*
@@ -153,6 +153,80 @@ pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K,
  */
 pe_status pe_accept(int32_t B, int32_t K, const int32_t *draft, const int32_t *target,
                     int32_t *accept_len, int32_t *out_tokens, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Training-shape forward ("P-EAGLE: A Technical Deep Dive into Parallel
+ * Speculative Decoding", section "Memory and Training Complexity";
+ * "P-EAGLE: Parallel-Drafting EAGLE with Scalable Training", sections 3,
+ * 3.1 and 3.2; visibility rules from "Speeding LLM inference with P-EAGLE
+ * in vLLM Speculators", section "Flex-attention mask").
+ *
+ * A sequence of n positions is expanded to the n x K grid of cells (p, d):
+ * position p, depth d, anchor a = p - d, grid index r = p*K + d
+ * (position-major).  COD sampling keeps a subset of cells; the kept grid
+ * indices ("rows") are strictly ascending, contain every depth-0 cell, and
+ * are chain-closed (a kept (p, d >= 1) has (p-1, d-1) kept).  Cell (p, d)
+ * takes E[x_p] + fc(h_p) at depth 0 and mask_emb + fc(h_shared) deeper, sits
+ * at RoPE position p, and attends to the depth-0 cells at positions <= a and
+ * to the kept cells of its own rollout (a + j, j), 1 <= j <= d.
+ * ---------------------------------------------------------------------- */
+
+/* Amortized mask: built once for the longest sequence n_max, it holds for
+ * every cell of the n_max x K grid the anchor and depth that define its mask
+ * row.  A sample of n positions uses the top-left n*K cells (a slice, no
+ * rebuilding), then gathers its kept cells. */
+pe_status pe_mask_create(int32_t n_max, int32_t K, void *stream, pe_mask **out);
+pe_status pe_mask_destroy(pe_mask *m);
+
+/* Test and debugging aid: materialise the mask of kept rows `rows` (device
+ * int32 [L]) of an n-position sample from the sliced table, as bytes
+ * out[i*L + j] = 1 if kept row i may attend to kept row j (device uint8
+ * [L, L]).  L <= 65536. */
+pe_status pe_mask_materialize(const pe_mask *m, int32_t n, const int32_t *rows, int32_t L,
+                              uint8_t *out, void *stream);
+
+/* Workspace bytes of pe_train_forward for n positions, block K and L kept rows. */
+pe_status pe_train_workspace_size(const pe_model *m, int32_t n, int32_t K, int32_t L, size_t *bytes);
+
+/*
+ * Forward of the first N layers over the L kept rows of one sequence.
+ *   hidden3    device [n, 3H]   target hidden states of every position
+ *   token_ids  device int32 [n] token at every position (out-of-range ids clamped)
+ *   mask_emb   device [H], h_shared device [3H]
+ *   rows       device int32 [L], kept grid indices as above (violations give
+ *              unspecified values but every access stays in bounds)
+ *   logits_out device [L, V] in the model dtype, or NULL
+ *   argmax_out device int32 [L] (lowest index among equal maxima), or NULL
+ * Requires n <= n_max and K equal to the mask's K.  Row i of the outputs
+ * belongs to rows[i].
+ */
+pe_status pe_train_forward(const pe_model *m, const pe_mask *mask, int32_t N, int32_t n, int32_t K,
+                           const void *hidden3, const int32_t *token_ids, const void *mask_emb,
+                           const void *h_shared, const int32_t *rows, int32_t L, void *logits_out,
+                           int32_t *argmax_out, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * COD sampling on the host ("Speeding LLM inference with P-EAGLE in vLLM
+ * Speculators", section "COD sampling"; paper notes, section 3): depth 0
+ * keeps every position; a cell (p, d >= 1) with p >= d is kept when its
+ * parent (p-1, d-1) is kept and U[p*K + d] < r_d, where
+ * r_d = max(r^d, floor) / max(r^(d-1), floor), so depth d keeps a fraction
+ * max(r^d, floor) of positions.  U: host double [n*K] uniforms in [0, 1).
+ * rows_out: host int32 with room for n*K entries; *L_out receives the count.
+ */
+pe_status pe_cod_rows(int32_t n, int32_t K, double r, double floor_rate, const double *U,
+                      int32_t *rows_out, int32_t *L_out);
+
+/*
+ * Sequence partition on the host (paper notes, section 3.2): S equal-width
+ * position segments [floor(s n / S), floor((s+1) n / S)); depth-0 and
+ * depth-1 cells go to the segment of their position, a deeper cell to the
+ * chunk of its parent (p-1, d-1).  Chunk s is completed by every depth-0
+ * cell before the end of segment s.  rows: host int32 [L] (kept rows as for
+ * pe_train_forward); chunk_out: host int32 [L].
+ */
+pe_status pe_partition(int32_t n, int32_t K, int32_t S, const int32_t *rows, int32_t L,
+                       int32_t *chunk_out);
 
 /* Thread-local description of the last non-OK status of this thread. */
 const char *pe_last_error(void);

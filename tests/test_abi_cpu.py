@@ -90,3 +90,21 @@ def test_forward_and_workspace_reject_null_model():
         pe.pe_draft_workspace_size(None, 1, 4, 0)
     with pytest.raises(pe.PeagleError):
         pe.pe_workspace_init(None, 16, 0)
+
+
+def test_mask_create_rejects_bad_sizes():
+    for n_max, K in [(0, 8), (16, 0), (16, 17), (1 << 22, 8)]:
+        with pytest.raises(pe.PeagleError) as ei:
+            pe.pe_mask_create(n_max, K, 0)
+        assert ei.value.status == pe.PE_ERR_INVALID_ARGUMENT
+
+
+def test_train_entry_points_reject_null_handles():
+    with pytest.raises(pe.PeagleError):
+        pe.pe_train_forward(None, None, 0, 8, 8, 16, 16, 16, 16, 16, 8, None, None, 16, 1 << 20, 0)
+    with pytest.raises(pe.PeagleError):
+        pe.pe_mask_materialize(None, 8, 16, 8, 16, 0)
+    with pytest.raises(pe.PeagleError):
+        pe.pe_train_workspace_size(None, 8, 8, 8)
+    with pytest.raises(pe.PeagleError):
+        pe.pe_mask_destroy(None)

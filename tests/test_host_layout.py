@@ -1,0 +1,61 @@
+"""Host-side training layout of the library (COD sampling and the sequence
+partition) against the oracle, on the CPU: same uniforms in, identical
+kept rows and chunk indices out ("Speeding LLM inference with P-EAGLE in
+vLLM Speculators", section "COD sampling"; paper notes, section 3.2)."""
+import os
+
+import numpy as np
+import pytest
+
+from drafting_eagle_draft_amd import binding as pe
+from drafting_eagle_draft_amd import synth
+from oracle import peagle_oracle as po
+
+pytestmark = pytest.mark.skipif(not os.path.exists(pe.LIB_PATH),
+                                reason="libpeagle.so not built (run __graft_entry__.build())")
+
+
+@pytest.mark.parametrize("n,K,r,floor", [(1, 1, 0.8, 0.2), (5, 8, 0.8, 0.2), (64, 8, 0.8, 0.2),
+                                         (300, 6, 0.7, 0.2), (257, 16, 0.8, 0.2), (97, 5, 0.5, 0.3),
+                                         (40, 4, 1.0, 0.0)])
+def test_cod_rows_match_oracle(n, K, r, floor):
+    cfg = synth.config("tiny_f32")
+    U = synth.cod_uniforms(cfg, n, K, tag=f"host{n}_{K}")
+    rows = pe.pe_cod_rows(n, K, r, floor, U.reshape(-1))
+    want = po.cod_rows(po.cod_keep(n, K, U, r=r, floor=floor))
+    np.testing.assert_array_equal(rows, want)
+
+
+def test_cod_rows_at_training_size():
+    cfg = synth.config("train_gptoss20b_n8192_k8")
+    n, K = 8192, 8
+    U = synth.cod_uniforms(cfg, n, K)
+    rows = pe.pe_cod_rows(n, K, 0.8, 0.2, U.reshape(-1))
+    want = po.cod_rows(po.cod_keep(n, K, U))
+    np.testing.assert_array_equal(rows, want)
+
+
+@pytest.mark.parametrize("n,K,S", [(50, 8, 2), (50, 8, 3), (64, 4, 4), (97, 6, 7), (7, 8, 7), (9, 3, 1)])
+def test_partition_matches_oracle(n, K, S):
+    cfg = synth.config("tiny_f32")
+    U = synth.cod_uniforms(cfg, n, K, tag=f"part{n}")
+    rows = po.cod_rows(po.cod_keep(n, K, U))
+    chunk = pe.pe_partition(n, K, S, rows)
+    want, _, _ = po.partition(n, K, S, rows)
+    np.testing.assert_array_equal(chunk, want)
+
+
+def test_partition_rejects_unclosed_and_unsorted_rows():
+    with pytest.raises(pe.PeagleError):
+        pe.pe_partition(10, 4, 2, np.array([0, 4, 10], dtype=np.int32))   # (2,2) without (1,1)
+    with pytest.raises(pe.PeagleError):
+        pe.pe_partition(10, 4, 2, np.array([4, 0], dtype=np.int32))
+    with pytest.raises(pe.PeagleError):
+        pe.pe_partition(10, 4, 11, np.array([0], dtype=np.int32))
+
+
+def test_cod_rows_rejects_bad_arguments():
+    with pytest.raises(pe.PeagleError):
+        pe.pe_cod_rows(4, 17, 0.8, 0.2, np.zeros(68))
+    with pytest.raises(pe.PeagleError):
+        pe.pe_cod_rows(4, 4, 0.0, 0.2, np.zeros(16))

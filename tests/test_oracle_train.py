@@ -133,3 +133,25 @@ def test_partition_invariant_and_completion(S):
         for j in np.where(m[i])[0]:
             pk, dk = divmod(int(rows[j]), K)
             assert where[(pk, dk)] == c or (dk == 0 and pk in comp)
+
+
+def test_key_closure_reproduces_sampled_rows():
+    """One layer of the sampled rows depends only on their key closure: the
+    oracle over that subset equals the oracle over the whole layout."""
+    from tests.layout_util import key_closure
+    from tests.toy import toy_problem, toy_cfg
+    cfg, w, _ = toy_problem(toy_cfg(n_layers=1, K=5))
+    n, K = 30, 5
+    rng = np.random.default_rng(4)
+    rows = po.cod_rows(po.cod_keep(n, K, rng.random((n, K)), r=0.8))
+    hidden3 = rng.standard_normal((n, 3 * cfg.hidden)).astype(np.float32)
+    tok = rng.integers(0, cfg.vocab, n)
+    wr = dict(w, embed_rows=w["embed"][tok])
+    mask_emb = rng.standard_normal(cfg.hidden).astype(np.float32) * 0.1
+    h_shared = rng.standard_normal(3 * cfg.hidden).astype(np.float32)
+    sample = np.array([3, 17, len(rows) // 2, len(rows) - 1])
+    full = po.train_forward(wr, cfg, hidden3, tok, mask_emb, h_shared, rows, K)
+    sub, lm = key_closure(rows, K, sample)
+    assert len(sub) < len(rows)
+    part = po.train_forward(wr, cfg, hidden3, tok, mask_emb, h_shared, sub, K, lm_rows=lm)
+    np.testing.assert_allclose(part, full[sample], rtol=0, atol=1e-12)
