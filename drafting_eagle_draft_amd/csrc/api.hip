@@ -274,21 +274,12 @@ pe_status check_cfg(const pe_config *c) {
 // Workspace of the training-shape forward.
 struct TrainLayout {
   size_t anc, dep, inv, yfc, xres, u, q, kall, vall, k0, v0, attn, h, keys, total;
-  int col_groups;
 };
 
 TrainLayout train_layout(const pe_model *m, long n, int K, long L) {
   const pe_config &c = m->cfg;
   TrainLayout t{};
   const size_t H = c.hidden, esz = m->esz, hd = c.head_dim;
-  // LM-head column groups: enough workgroups to fill the chip several
-  // times over, each group walking its share of the 128-column blocks.
-  const long row_blocks = (L + 127) / 128;
-  const int col_blocks = (m->lm.NT + 7) / 8;
-  long cg = (4L * m->num_cus + row_blocks - 1) / row_blocks;
-  if (cg < 1) cg = 1;
-  if (cg > col_blocks) cg = col_blocks;
-  t.col_groups = (int)cg;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + std::max(bytes, (size_t)1), 256); return o; };
   t.anc = take((size_t)L * 4);
@@ -305,7 +296,7 @@ TrainLayout train_layout(const pe_model *m, long n, int K, long L) {
   t.v0 = take(layers ? (size_t)n * c.n_kv_heads * hd * esz : 0);
   t.attn = take(layers ? (size_t)L * c.n_q_heads * hd * esz : 0);
   t.h = take(layers ? (size_t)L * c.intermediate * esz : 0);
-  t.keys = take((size_t)L * t.col_groups * 8);
+  t.keys = take((size_t)L * 8);
   t.total = off;
   return t;
 }
@@ -680,19 +671,21 @@ pe_status pe_train_forward(const pe_model *m, const pe_mask *mask, int32_t N, in
   const int H = c.hidden, hd = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
   const int dt = c.dtype;
 
-  auto gemm = [&](const Tiled &t, int epi, BigGemmParams p, int col_groups) -> pe_status {
+  auto gemm = [&](const Tiled &t, int epi, TileGemmParams p) -> pe_status {
     p.wt = t.ptr; p.NT = t.NT; p.KT = t.KT; p.N = t.N; p.K = t.K;
-    hipError_t e = launch_gemm_big(dt, epi, p, col_groups, s);
+    hipError_t e = launch_gemm_tile(dt, epi, p, m->num_cus, s);
     return e == hipSuccess ? PE_OK : hip_fail(e, "GEMM launch");
   };
   hipError_t e = launch_gather_rows(mask->table, n * K, rows, L, anc, dep, inv, s);
   if (e != hipSuccess) return hip_fail(e, "row gather launch");
   // Input fusion: fc over the n hidden rows and h_shared, then E[x_p] or mask_emb.
   {
-    BigGemmParams p{};
-    p.A = hidden3; p.lda = 3L * H; p.M = n + 1; p.A_last = h_shared;
+    TileGemmParams p{};
+    p.A = hidden3; p.lda = 3L * H; p.M = n;
     p.C = yfc; p.ldc = H;
-    if ((st = gemm(m->fc, BEPI_STORE, p, 0)) != PE_OK) return st;
+    if ((st = gemm(m->fc, BEPI_STORE, p)) != PE_OK) return st;
+    e = launch_matvec_tiled(dt, m->fc.ptr, m->fc.NT, m->fc.KT, H, h_shared, 3 * H, yfc + (size_t)n * H, s);
+    if (e != hipSuccess) return hip_fail(e, "shared-state projection launch");
     e = launch_train_fuse(dt, yfc, m->embed, token_ids, mask_emb, anc, dep, L, n, H, c.vocab, xres, s);
     if (e != hipSuccess) return hip_fail(e, "fusion launch");
   }
@@ -701,12 +694,12 @@ pe_status pe_train_forward(const pe_model *m, const pe_mask *mask, int32_t N, in
     if ((e = launch_rmsnorm_rows(dt, xres, Lw.attn_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
       return hip_fail(e, "RMSNorm launch");
     {
-      BigGemmParams p{};
+      TileGemmParams p{};
       p.A = u; p.lda = H; p.M = L;
       p.q = ws + W.q; p.kall = ws + W.kall; p.vall = ws + W.vall; p.k0 = ws + W.k0; p.v0 = ws + W.v0;
       p.anc = anc; p.dep = dep; p.inv_freq = m->inv_freq;
       p.n = n; p.nq = nq; p.nkv = nkv; p.hd = hd;
-      if ((st = gemm(Lw.qkv, BEPI_QKV, p, 0)) != PE_OK) return st;
+      if ((st = gemm(Lw.qkv, BEPI_QKV, p)) != PE_OK) return st;
     }
     {
       TrainAttnParams a{};
@@ -718,42 +711,43 @@ pe_status pe_train_forward(const pe_model *m, const pe_mask *mask, int32_t N, in
       if ((e = launch_attn_train(dt, a, s)) != hipSuccess) return hip_fail(e, "attention launch");
     }
     {
-      BigGemmParams p{};
+      TileGemmParams p{};
       p.A = ws + W.attn; p.lda = (long)nq * hd; p.M = L;
       p.C = xres; p.ldc = H;
-      if ((st = gemm(Lw.o, BEPI_ACCUM, p, 0)) != PE_OK) return st;
+      if ((st = gemm(Lw.o, BEPI_ACCUM, p)) != PE_OK) return st;
     }
     if ((e = launch_rmsnorm_rows(dt, xres, Lw.mlp_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
       return hip_fail(e, "RMSNorm launch");
     {
-      BigGemmParams p{};
+      TileGemmParams p{};
       p.A = u; p.lda = H; p.M = L;
       p.h = ws + W.h; p.I = c.intermediate;
-      if ((st = gemm(Lw.gateup, BEPI_SWIGLU, p, 0)) != PE_OK) return st;
+      if ((st = gemm(Lw.gateup, BEPI_SWIGLU, p)) != PE_OK) return st;
     }
     {
-      BigGemmParams p{};
+      TileGemmParams p{};
       p.A = ws + W.h; p.lda = c.intermediate; p.M = L;
       p.C = xres; p.ldc = H;
-      if ((st = gemm(Lw.down, BEPI_ACCUM, p, 0)) != PE_OK) return st;
+      if ((st = gemm(Lw.down, BEPI_ACCUM, p)) != PE_OK) return st;
     }
   }
   if ((e = launch_rmsnorm_rows(dt, xres, m->final_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
     return hip_fail(e, "RMSNorm launch");
   {
-    BigGemmParams p{};
+    TileGemmParams p{};
     p.A = u; p.lda = H; p.M = L;
     p.logits = logits_out; p.ldc = c.vocab;
     p.keys = reinterpret_cast<unsigned long long *>(ws + W.keys);
+    if ((e = launch_zero(p.keys, (size_t)L * 8, s)) != hipSuccess) return hip_fail(e, "key reset launch");
     const bool prof = m->prof && m->nrec < (int)m->ev0.size();
     if (prof) (void)hipEventRecord(m->ev0[m->nrec], s);
-    if ((st = gemm(m->lm, BEPI_LMHEAD, p, W.col_groups)) != PE_OK) return st;
+    if ((st = gemm(m->lm, BEPI_LMHEAD, p)) != PE_OK) return st;
     if (prof) {
       (void)hipEventRecord(m->ev1[m->nrec], s);
       ++m->nrec;
     }
     if (argmax_out) {
-      e = launch_argmax_rows(p.keys, W.col_groups, L, argmax_out, s);
+      e = launch_argmax_rows(p.keys, L, argmax_out, s);
       if (e != hipSuccess) return hip_fail(e, "argmax launch");
     }
   }

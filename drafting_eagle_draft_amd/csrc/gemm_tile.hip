@@ -1,0 +1,239 @@
+// gemm_tile.hip -- many-row GEMM of the training-shape forward:
+// C = A W^T over M activation rows (A dtype [M][lda] row-major, W in the
+// 1 KB fragment-tile layout of the weight copies), with the decoder-layer
+// step that follows each projection fused into the epilogue ("P-EAGLE:
+// Parallel-Drafting EAGLE with Scalable Training", section 2; input fusion
+// from "P-EAGLE: A Technical Deep Dive into Parallel Speculative Decoding",
+// section "2. The P-EAGLE Parallel Drafter").
+//
+// Design (gfx950):
+//  * 256 x 256 output tiles (16 row groups x 16 weight strips), one
+//    workgroup of four waves per CU, each wave a 128 x 128 quarter held in
+//    256 fp32 accumulators (8 x 8 MFMA 16x16 tiles);
+//  * operands move HBM/L2 -> LDS by buffer loads that write LDS directly
+//    (no staging registers), 32 fragments (32 KB) per k step, four LDS
+//    stages, issued three steps ahead of use; each wave then reads its 16
+//    fragments of the step and runs 64 MFMAs as they arrive;
+//  * buffer resources are rebased per tile with the rows/strips that
+//    remain, so reads past the last row, strip or k tile return zero
+//    without branches;
+//  * persistent grid of one workgroup per CU walking tiles in bands of four
+//    row blocks, with the tile index spread so that the 32 CUs of one XCD
+//    work on one 4 x 8 patch of tiles at a time (shared L2 panels).
+#include "pe_epilogue.hpp"
+
+namespace pe {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <typename T> __device__ __forceinline__ void store2(T *dst, float a, float b);
+template <> __device__ __forceinline__ void store2<float>(float *dst, float a, float b) {
+  *reinterpret_cast<float2 *>(dst) = make_float2(a, b);
+}
+template <> __device__ __forceinline__ void store2<bf16_t>(bf16_t *dst, float a, float b) {
+  *reinterpret_cast<unsigned *>(dst) = pack_bf16x2(a, b);
+}
+
+// Gate/up tile rows of strip s: lane group g holds gate rows 8s+2g, 8s+2g+1
+// in r = 0, 1 and the matching up rows in r = 2, 3.
+template <typename T>
+__device__ __forceinline__ void epi_tile_swiglu(const TileGemmParams &p, int m, int s, int g, floatx4 v) {
+  T *dst = reinterpret_cast<T *>(p.h) + (long)m * p.I + 8 * s + 2 * g;
+  store2<T>(dst, silu_f(v[0]) * v[2], silu_f(v[1]) * v[3]);
+}
+
+// q|k|v tile rows n..n+3 of row m.  For q and k heads, r = 2t + hi holds
+// dimension 8j + 2g + t (hi = 0) or that dimension + hd/2 (hi = 1), the two
+// halves that one rotation pairs; v heads keep their order.  Row m sits at
+// RoPE position anchor + depth; depth-0 rows also go to k0/v0 by position.
+template <typename T>
+__device__ __forceinline__ void epi_tile_qkv(const TileGemmParams &p, int m, int n, floatx4 v) {
+  const int hd = p.hd, half = hd >> 1;
+  const int hh = n / hd, within = n - hh * hd;
+  const int d = p.dep[m], pos = p.anc[m] + d;
+  const bool depth0 = d == 0 && pos >= 0 && pos < p.n;
+  if (hh < p.nq + p.nkv) {
+    const int dim = 8 * (within >> 4) + (within & 15) / 2;
+    float lo[2], hi[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float c, sn;
+      rope_cs(pos, p.inv_freq[dim + t], c, sn);
+      lo[t] = v[2 * t] * c - v[2 * t + 1] * sn;
+      hi[t] = v[2 * t + 1] * c + v[2 * t] * sn;
+    }
+    T *dst;
+    T *dst0 = nullptr;
+    if (hh < p.nq) {
+      dst = reinterpret_cast<T *>(p.q) + ((long)m * p.nq + hh) * hd;
+    } else {
+      const int gk = hh - p.nq;
+      dst = reinterpret_cast<T *>(p.kall) + ((long)m * p.nkv + gk) * hd;
+      if (depth0) dst0 = reinterpret_cast<T *>(p.k0) + ((long)pos * p.nkv + gk) * hd;
+    }
+    store2<T>(dst + dim, lo[0], lo[1]);
+    store2<T>(dst + dim + half, hi[0], hi[1]);
+    if (dst0) {
+      store2<T>(dst0 + dim, lo[0], lo[1]);
+      store2<T>(dst0 + dim + half, hi[0], hi[1]);
+    }
+  } else {
+    const int gk = hh - p.nq - p.nkv;
+    const float vals[4] = {v[0], v[1], v[2], v[3]};
+    store4<T>(reinterpret_cast<T *>(p.vall) + ((long)m * p.nkv + gk) * hd + within, vals);
+    if (depth0) store4<T>(reinterpret_cast<T *>(p.v0) + ((long)pos * p.nkv + gk) * hd + within, vals);
+  }
+}
+
+constexpr unsigned kRecordsCap = 0x7FFFF000u;  // buffer extent limit per tile
+constexpr int kOobOffset = 0x7FFFFFF0;         // beyond every extent: reads zero
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, size_t bytes) {
+  const unsigned n = bytes < (size_t)kRecordsCap ? (unsigned)bytes : kRecordsCap;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, 0x00020000);
+}
+
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_tile(TileGemmParams p) {
+  constexpr int KTILE = Frag<T>::KTILE, E = Frag<T>::E;
+  constexpr int NSTAGE = 4;
+  // Stage layout: fragments 0..15 are weight strips s0..s0+15, 16..31 are
+  // row groups of 16 activation rows; each fragment is 64 lanes x 16 bytes.
+  __shared__ u32x4 smem[NSTAGE][32][64];
+  const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
+  const int wm = w >> 1, wn = w & 1;
+  const int RB = (p.M + 255) >> 8, CB = (p.NT + 15) >> 4;
+  const int tiles = RB * CB;
+  const int G = gridDim.x, b = blockIdx.x;
+  const int slot = (G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
+  const size_t lda_b = (size_t)p.lda * sizeof(T);
+  const bool wave_w = w < 2;  // waves 0, 1 fetch weight strips; 2, 3 row groups
+  // Byte offset of this lane's 16 bytes within fragment 0 of this wave at k
+  // tile 0; fragment q and k tile kt add the wave-uniform qstride*q +
+  // kstep*kt.  Waves 0/1 fetch weight strips 0-7/8-15, waves 2/3 row groups.
+  const int lanebase = wave_w ? lane * 16 : c16 * (int)lda_b + g * E * (int)sizeof(T);
+  const int qstride = wave_w ? p.KT * 1024 : 16 * (int)lda_b;
+  const int fbase = (w & 1) * 8 * qstride;
+  const int kstep = wave_w ? 1024 : KTILE * (int)sizeof(T);
+  lds_void *dst0 = (lds_void *)&smem[0][(w >> 1) * 16 + (w & 1) * 8][0];
+  constexpr int stage_bytes = 32 * 64 * 16;
+
+  for (int t = slot; t < tiles; t += G) {
+    const int band = t / (4 * CB), rem = t - band * 4 * CB;
+    const int rows_in = min(4, RB - band * 4);
+    const int cb = rem / rows_in, rb = band * 4 + rem % rows_in;
+    const int m0 = rb * 256, s0 = cb * 16;
+    const __amdgpu_buffer_rsrc_t rs =
+        wave_w ? make_rsrc(reinterpret_cast<const char *>(p.wt) + (size_t)s0 * p.KT * 1024,
+                           (size_t)(p.NT - s0) * p.KT * 1024)
+               : make_rsrc(reinterpret_cast<const char *>(p.A) + (size_t)m0 * lda_b,
+                           (size_t)(p.M - m0) * lda_b);
+    auto issue = [&](int kt) {
+      lds_void *dst = (lds_void *)((char *)dst0 + (kt & (NSTAGE - 1)) * stage_bytes);
+      const bool live = kt < p.KT;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void *)((char *)dst + q * 1024), 16,
+            live ? lanebase + (fbase + q * qstride + kt * kstep) : kOobOffset, 0, 0, 0);
+    };
+
+    floatx4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // Three stages in flight ahead of the one being multiplied.  Step kt
+    // waits for its own stage (two younger stages may still be loading),
+    // refills the buffer of stage kt-1 (read into registers before this
+    // barrier) with stage kt+3, then reads its fragments and multiplies;
+    // the matrix cores start as soon as the first fragments arrive.
+    issue(0);
+    issue(1);
+    issue(2);
+    for (int kt = 0; kt < p.KT; ++kt) {
+      asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+      issue(kt + 3);
+      const int st = kt & (NSTAGE - 1);
+      u32x4 wf[8], af[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wf[i] = smem[st][wn * 8 + i][lane];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) af[j] = smem[st][16 + wm * 8 + j][lane];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = Mma<T>::run(wf[i], af[j], acc[i][j]);
+    }
+    // Drain the look-ahead loads (they target stages the next tile reuses).
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+    // acc[i][j][r] = C[m = m0 + (wm*8 + j)*16 + c16][n = (s0 + wn*8 + i)*16 + 4g + r]
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int m = m0 + (wm * 8 + j) * 16 + c16;
+      unsigned long long key = 0ull;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int s = s0 + wn * 8 + i;
+        const int n = s * 16 + 4 * g;
+        if (m < p.M && s < p.NT) {
+          if constexpr (EPI == BEPI_STORE) {
+            *reinterpret_cast<floatx4 *>(p.C + (long)m * p.ldc + n) = acc[i][j];
+          } else if constexpr (EPI == BEPI_ACCUM) {
+            floatx4 *dst = reinterpret_cast<floatx4 *>(p.C + (long)m * p.ldc + n);
+            *dst = *dst + acc[i][j];
+          } else if constexpr (EPI == BEPI_LMHEAD) {
+            if (p.logits) {
+              const float v4[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+              store4<T>(reinterpret_cast<T *>(p.logits) + (long)m * p.ldc + n, v4);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) key = umax64(key, argmax_key(acc[i][j][r], (unsigned)(n + r)));
+          } else if constexpr (EPI == BEPI_SWIGLU) {
+            epi_tile_swiglu<T>(p, m, s, g, acc[i][j]);
+          } else {
+            epi_tile_qkv<T>(p, m, n, acc[i][j]);
+          }
+        }
+      }
+      if constexpr (EPI == BEPI_LMHEAD) {
+        key = umax64(key, shfl_xor_u64(key, 16));
+        key = umax64(key, shfl_xor_u64(key, 32));
+        if (g == 0 && m < p.M) atomicMax(p.keys + m, key);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_tile(int dtype, int epi, const TileGemmParams &p, int num_cus, hipStream_t s) {
+  if (p.M < 1 || p.NT < 1 || p.KT < 1) return hipSuccess;
+  const long tiles = (long)((p.M + 255) / 256) * ((p.NT + 15) / 16);
+  const dim3 grid((unsigned)(tiles < num_cus ? tiles : num_cus));
+#define PE_TILE_CASE(T, E) \
+  case E: hipLaunchKernelGGL((k_gemm_tile<T, E>), grid, dim3(256), 0, s, p); break;
+  if (dtype == 1) {
+    switch (epi) {
+      PE_TILE_CASE(bf16_t, 0) PE_TILE_CASE(bf16_t, 1) PE_TILE_CASE(bf16_t, 2) PE_TILE_CASE(bf16_t, 3)
+      PE_TILE_CASE(bf16_t, 4)
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (epi) {
+      PE_TILE_CASE(float, 0) PE_TILE_CASE(float, 1) PE_TILE_CASE(float, 2) PE_TILE_CASE(float, 3)
+      PE_TILE_CASE(float, 4)
+      default: return hipErrorInvalidValue;
+    }
+  }
+#undef PE_TILE_CASE
+  return hipGetLastError();
+}
+
+}  // namespace pe

@@ -128,24 +128,22 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 // C = A W^T over M activation rows with W in the tile layout above.
 enum BigEpi : int {
   BEPI_STORE = 0,   // C fp32 [M][ldc] = result
-  BEPI_LMHEAD = 1,  // logits (dtype [M][ldc], optional) + best argmax key per
-                    // row and column group, keys[M][col_groups]
+  BEPI_LMHEAD = 1,  // logits (dtype [M][ldc], optional) + best argmax key per row
   BEPI_ACCUM = 2,   // C += result (residual update)
   BEPI_SWIGLU = 3,  // MAP_GATEUP rows: h[M][I] = silu(gate) * up
   BEPI_QKV = 4,     // MAP_QKV rows: RoPE at position anc+dep, scatter q/k/v
 };
 
-struct BigGemmParams {
+struct TileGemmParams {
   const u32x4 *wt;
   int NT, KT, N, K;
-  const void *A;        // dtype [M][lda]
+  const void *A;        // dtype [M][lda], lda >= K
   long lda;
   int M;
-  const void *A_last;   // when non-null, row M-1 is read from here instead
   float *C;
   long ldc;
   void *logits;
-  unsigned long long *keys;
+  unsigned long long *keys;  // [M], zeroed before the launch; atomically maxed
   // SWIGLU
   void *h;
   int I;
@@ -157,9 +155,11 @@ struct BigGemmParams {
   int n, nq, nkv, hd;
 };
 
-hipError_t launch_gemm_big(int dtype, int epi, const BigGemmParams &p, int col_groups, hipStream_t s);
-hipError_t launch_argmax_rows(const unsigned long long *keys, int ngroups, int M, int *out,
-                              hipStream_t s);
+hipError_t launch_gemm_tile(int dtype, int epi, const TileGemmParams &p, int num_cus, hipStream_t s);
+hipError_t launch_argmax_rows(const unsigned long long *keys, int M, int *out, hipStream_t s);
+// y[N] (fp32) = W x for one dtype vector x[K], W in the fragment-tile layout.
+hipError_t launch_matvec_tiled(int dtype, const u32x4 *wt, int NT, int KT, int N, const void *x, int K,
+                               float *y, hipStream_t s);
 
 hipError_t launch_mask_table(int n_max, int K, int2 *table, hipStream_t s);
 hipError_t launch_gather_rows(const int2 *table, int nK, const int *rows, int L, int *anc, int *dep,

@@ -9,7 +9,7 @@
 // Kept cells ("rows") are processed in ascending grid order.  Cell (p, d)
 // attends to depth-0 cells at positions <= a and to the kept cells (a+j, j),
 // 1 <= j <= d, of its own rollout.
-#include "pe_epilogue.hpp"
+#include "pe_internal.hpp"
 
 namespace pe {
 
@@ -61,193 +61,38 @@ __global__ void k_mask_materialize(const int2 *table, int nK, const int *rows, i
   out[idx] = allowed(a.x, a.y, b.x, b.y) ? 1 : 0;
 }
 
-// ---------------------------------------------------------------------------
-// Large-M GEMM: C[M][N'] = A[M][K] W'^T with W' in the 1 KB tile layout.
-// Block tile 128 rows x 128 columns (8 strips), four waves in a 2x2 grid,
-// each 64 x 64 (4 x 4 MFMA tiles); A fragments and W tiles double-buffered
-// in LDS.  EPI 0 writes fp32 C.  EPI 1 (LM head) loops over column blocks
-// blockIdx.x, +gridDim.x, ..., optionally writes dtype logits and keeps the
-// best argmax key per row, written per column group to keys[M][gridDim.x].
-// EPI 2 adds the result into fp32 C (residual update).
-// ---------------------------------------------------------------------------
-// Two adjacent values to dtype memory in one store.
-template <typename T> __device__ __forceinline__ void store2(T *dst, float a, float b);
-template <> __device__ __forceinline__ void store2<float>(float *dst, float a, float b) {
-  *reinterpret_cast<float2 *>(dst) = make_float2(a, b);
-}
-template <> __device__ __forceinline__ void store2<bf16_t>(bf16_t *dst, float a, float b) {
-  *reinterpret_cast<unsigned *>(dst) = pack_bf16x2(a, b);
-}
-
-// Gate/up tile rows of strip s: lane group g holds gate rows 8s+2g, 8s+2g+1
-// in r = 0, 1 and the matching up rows in r = 2, 3.
-template <typename T>
-__device__ __forceinline__ void epi_big_swiglu(const BigGemmParams &p, int m, int s, int g, floatx4 v) {
-  T *dst = reinterpret_cast<T *>(p.h) + (long)m * p.I + 8 * s + 2 * g;
-  store2<T>(dst, silu_f(v[0]) * v[2], silu_f(v[1]) * v[3]);
-}
-
-// q|k|v tile rows n..n+3 of row m.  For q and k heads, r = 2t + hi holds
-// dimension 8j + 2g + t (hi = 0) or that dimension + hd/2 (hi = 1), the two
-// halves that one rotation pairs; v heads keep their order.
-template <typename T>
-__device__ __forceinline__ void epi_big_qkv(const BigGemmParams &p, int m, int n, floatx4 v) {
-  const int hd = p.hd, half = hd >> 1;
-  const int hh = n / hd, within = n - hh * hd;
-  const int d = p.dep[m], pos = p.anc[m] + d;
-  const bool depth0 = d == 0 && pos >= 0 && pos < p.n;
-  if (hh < p.nq + p.nkv) {
-    const int dim = 8 * (within >> 4) + (within & 15) / 2;
-    float lo[2], hi[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float c, sn;
-      rope_cs(pos, p.inv_freq[dim + t], c, sn);
-      lo[t] = v[2 * t] * c - v[2 * t + 1] * sn;
-      hi[t] = v[2 * t + 1] * c + v[2 * t] * sn;
-    }
-    T *dst;
-    T *dst0 = nullptr;
-    if (hh < p.nq) {
-      dst = reinterpret_cast<T *>(p.q) + ((long)m * p.nq + hh) * hd;
-    } else {
-      const int gk = hh - p.nq;
-      dst = reinterpret_cast<T *>(p.kall) + ((long)m * p.nkv + gk) * hd;
-      if (depth0) dst0 = reinterpret_cast<T *>(p.k0) + ((long)pos * p.nkv + gk) * hd;
-    }
-    store2<T>(dst + dim, lo[0], lo[1]);
-    store2<T>(dst + dim + half, hi[0], hi[1]);
-    if (dst0) {
-      store2<T>(dst0 + dim, lo[0], lo[1]);
-      store2<T>(dst0 + dim + half, hi[0], hi[1]);
-    }
-  } else {
-    const int gk = hh - p.nq - p.nkv;
-    const float vals[4] = {v[0], v[1], v[2], v[3]};
-    store4<T>(reinterpret_cast<T *>(p.vall) + ((long)m * p.nkv + gk) * hd + within, vals);
-    if (depth0) store4<T>(reinterpret_cast<T *>(p.v0) + ((long)pos * p.nkv + gk) * hd + within, vals);
-  }
-}
-
-template <typename T, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_big(BigGemmParams p) {
-  constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE;
-  __shared__ u32x4 Ws[2][8][64];
-  __shared__ u32x4 As[2][8][64];
-  __shared__ unsigned long long kbest[2][128];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c16 = lane & 15, g = lane >> 4;
-  const int wn = w & 1, wm = w >> 1;
-  const int m0 = blockIdx.y * 128;
-  const T *A = reinterpret_cast<const T *>(p.A);
-  // This thread's two staging slots: fragment groups tid/64 and tid/64 + 4.
-  const int sg0 = tid >> 6, sg1 = sg0 + 4;
-  const int arow0 = m0 + sg0 * 16 + c16, arow1 = m0 + sg1 * 16 + c16;
-  const int akoff = g * E;
-  const T *A_last = reinterpret_cast<const T *>(p.A_last);
-  auto arow_ptr = [&](int r) -> const T * {
-    return (A_last && r == p.M - 1) ? A_last : A + (long)r * p.lda;
-  };
-
-  unsigned long long best[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) best[j] = 0ull;
-
-  for (int nb = blockIdx.x; nb * 8 < p.NT; nb += gridDim.x) {
-    const int s0 = nb * 8;
-    floatx4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    auto load = [&](int kt, u32x4 &w0, u32x4 &w1, u32x4 &a0, u32x4 &a1) {
-      w0 = (s0 + sg0 < p.NT) ? p.wt[((long)(s0 + sg0) * p.KT + kt) * 64 + lane] : u32x4{0u, 0u, 0u, 0u};
-      w1 = (s0 + sg1 < p.NT) ? p.wt[((long)(s0 + sg1) * p.KT + kt) * 64 + lane] : u32x4{0u, 0u, 0u, 0u};
-      const int k = kt * KTILE + akoff;
-      a0 = (arow0 < p.M && k < p.K) ? ldg16(arow_ptr(arow0) + k) : u32x4{0u, 0u, 0u, 0u};
-      a1 = (arow1 < p.M && k < p.K) ? ldg16(arow_ptr(arow1) + k) : u32x4{0u, 0u, 0u, 0u};
-    };
-    u32x4 w0, w1, a0, a1;
-    load(0, w0, w1, a0, a1);
-    Ws[0][sg0][lane] = w0; Ws[0][sg1][lane] = w1;
-    As[0][sg0][lane] = a0; As[0][sg1][lane] = a1;
-    __syncthreads();
-    for (int kt = 0; kt < p.KT; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < p.KT) load(kt + 1, w0, w1, a0, a1);
-      u32x4 wf[4], af[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wf[i] = Ws[cur][wn * 4 + i][lane];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) af[j] = As[cur][wm * 4 + j][lane];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::run(wf[i], af[j], acc[i][j]);
-      if (kt + 1 < p.KT) {
-        Ws[cur ^ 1][sg0][lane] = w0; Ws[cur ^ 1][sg1][lane] = w1;
-        As[cur ^ 1][sg0][lane] = a0; As[cur ^ 1][sg1][lane] = a1;
-      }
-      __syncthreads();
-    }
-    // acc[i][j][r] = C[m = m0 + (wm*4 + j)*16 + c16][n = (s0 + wn*4 + i)*16 + 4g + r]
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + (wm * 4 + j) * 16 + c16;
-      unsigned long long key = 0ull;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = s0 + wn * 4 + i;
-        const int n = s * 16 + 4 * g;
-        if (m < p.M && s < p.NT) {
-          if constexpr (EPI == 0) {
-            *reinterpret_cast<floatx4 *>(p.C + (long)m * p.ldc + n) = acc[i][j];
-          } else if constexpr (EPI == 2) {
-            floatx4 *dst = reinterpret_cast<floatx4 *>(p.C + (long)m * p.ldc + n);
-            *dst = *dst + acc[i][j];
-          } else if constexpr (EPI == 1) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (n + r < p.N) {
-                if (p.logits) reinterpret_cast<T *>(p.logits)[(long)m * p.ldc + n + r] = from_f32<T>(acc[i][j][r]);
-                key = umax64(key, argmax_key(acc[i][j][r], (unsigned)(n + r)));
-              }
-            }
-          } else if constexpr (EPI == 3) {
-            epi_big_swiglu<T>(p, m, s, g, acc[i][j]);
-          } else {
-            epi_big_qkv<T>(p, m, n, acc[i][j]);
-          }
-        }
-      }
-      if constexpr (EPI == 1) {
-        key = umax64(key, shfl_xor_u64(key, 16));
-        key = umax64(key, shfl_xor_u64(key, 32));
-        best[j] = umax64(best[j], key);
-      }
-    }
-  }
-  if constexpr (EPI == 1) {
-    // Combine the two column-halves (wn) of each row group, then write one
-    // key per row for this column group.
-    if (g == 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) kbest[wn][(wm * 4 + j) * 16 + c16] = best[j];
-    }
-    __syncthreads();
-    if (tid < 128) {
-      const int m = m0 + tid;
-      if (m < p.M) p.keys[(long)m * gridDim.x + blockIdx.x] = umax64(kbest[0][tid], kbest[1][tid]);
-    }
-  }
-}
-
-__global__ void k_argmax_rows(const unsigned long long *keys, int ngroups, int M, int *out) {
+__global__ void k_argmax_rows(const unsigned long long *keys, int M, int *out) {
   const int m = blockIdx.x * blockDim.x + threadIdx.x;
   if (m >= M) return;
-  unsigned long long b = 0ull;
-  for (int q = 0; q < ngroups; ++q) b = umax64(b, keys[(long)m * ngroups + q]);
-  out[m] = (int)(0xFFFFFFFFu - (unsigned)(b & 0xFFFFFFFFull));
+  out[m] = (int)(0xFFFFFFFFu - (unsigned)(keys[m] & 0xFFFFFFFFull));
+}
+
+// y = W x for one vector: one wave per 16-row weight strip; lane (c16, g)
+// holds row c16 and k-slots g*E.. of each fragment, partial sums are folded
+// over the four lane groups.
+template <typename T>
+__global__ __launch_bounds__(256) void k_matvec_tiled(const u32x4 *wt, int NT, int KT, int N, const T *x,
+                                                      int K, float *y) {
+  constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c16 = lane & 15, g = lane >> 4;
+  const int s = blockIdx.x * 4 + w;
+  if (s >= NT) return;
+  float acc = 0.f;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int k = kt * KTILE + g * E;
+    if (k >= K) continue;
+    const u32x4 wv = wt[((long)s * KT + kt) * 64 + lane];
+    const u32x4 xv = ldg16(x + k);
+    T ww[E], xx[E];
+    __builtin_memcpy(ww, &wv, 16);
+    __builtin_memcpy(xx, &xv, 16);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc += to_f32<T>(ww[e]) * to_f32<T>(xx[e]);
+  }
+  acc += shfl_xor_f(acc, 16);
+  acc += shfl_xor_f(acc, 32);
+  const int n = s * 16 + c16;
+  if (g == 0 && n < N) y[n] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -513,30 +358,20 @@ hipError_t launch_mask_materialize(const int2 *table, int nK, const int *rows, i
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_big(int dtype, int epi, const BigGemmParams &p, int col_groups, hipStream_t s) {
-  const dim3 grid(epi == 1 ? (unsigned)col_groups : (unsigned)((p.NT + 7) / 8), (unsigned)((p.M + 127) / 128));
-#define PE_BIG_CASE(T, E) \
-  case E: hipLaunchKernelGGL((k_gemm_big<T, E>), grid, dim3(256), 0, s, p); break;
-  if (dtype == 1) {
-    switch (epi) {
-      PE_BIG_CASE(bf16_t, 0) PE_BIG_CASE(bf16_t, 1) PE_BIG_CASE(bf16_t, 2) PE_BIG_CASE(bf16_t, 3)
-      PE_BIG_CASE(bf16_t, 4)
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (epi) {
-      PE_BIG_CASE(float, 0) PE_BIG_CASE(float, 1) PE_BIG_CASE(float, 2) PE_BIG_CASE(float, 3)
-      PE_BIG_CASE(float, 4)
-      default: return hipErrorInvalidValue;
-    }
-  }
-#undef PE_BIG_CASE
+hipError_t launch_argmax_rows(const unsigned long long *keys, int M, int *out, hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax_rows, dim3(blocks_for(M, 256)), dim3(256), 0, s, keys, M, out);
   return hipGetLastError();
 }
 
-hipError_t launch_argmax_rows(const unsigned long long *keys, int ngroups, int M, int *out,
-                              hipStream_t s) {
-  hipLaunchKernelGGL(k_argmax_rows, dim3(blocks_for(M, 256)), dim3(256), 0, s, keys, ngroups, M, out);
+hipError_t launch_matvec_tiled(int dtype, const u32x4 *wt, int NT, int KT, int N, const void *x, int K,
+                               float *y, hipStream_t s) {
+  const dim3 grid((unsigned)((NT + 3) / 4));
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_matvec_tiled<bf16_t>, grid, dim3(256), 0, s, wt, NT, KT, N,
+                       reinterpret_cast<const bf16_t *>(x), K, y);
+  else
+    hipLaunchKernelGGL(k_matvec_tiled<float>, grid, dim3(256), 0, s, wt, NT, KT, N,
+                       reinterpret_cast<const float *>(x), K, y);
   return hipGetLastError();
 }
 
