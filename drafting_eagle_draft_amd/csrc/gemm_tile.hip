@@ -8,12 +8,16 @@
 //
 // Design (gfx950):
 //  * 256 x 256 output tiles (16 row groups x 16 weight strips), one
-//    workgroup of four waves per CU, each wave a 128 x 128 quarter held in
-//    256 fp32 accumulators (8 x 8 MFMA 16x16 tiles);
+//    workgroup of eight waves per CU (two per SIMD, so one wave's LDS and
+//    barrier waits are covered by the other's matrix work), each wave a
+//    128 x 64 block held in 128 fp32 accumulators (4 x 8 MFMA 16x16 tiles);
 //  * operands move HBM/L2 -> LDS by buffer loads that write LDS directly
 //    (no staging registers), 32 fragments (32 KB) per k step, four LDS
-//    stages, issued three steps ahead of use; each wave then reads its 16
-//    fragments of the step and runs 64 MFMAs as they arrive;
+//    stages, issued three steps ahead of use; each wave then reads its 12
+//    fragments of the step and runs 32 MFMAs as they arrive;
+//  * the LM head stages its logits block through LDS and writes whole
+//    rows, and folds the argmax keys of the tile's four column quarters in
+//    LDS before one atomic maximum per row;
 //  * buffer resources are rebased per tile with the rows/strips that
 //    remain, so reads past the last row, strip or k tile return zero
 //    without branches;
@@ -90,36 +94,55 @@ __device__ __forceinline__ void epi_tile_qkv(const TileGemmParams &p, int m, int
 constexpr unsigned kRecordsCap = 0x7FFFF000u;  // buffer extent limit per tile
 constexpr int kOobOffset = 0x7FFFFFF0;         // beyond every extent: reads zero
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, size_t bytes) {
+// Buffer descriptor (base, extent, raw 32-bit dwords) in scalar registers.
+__device__ __forceinline__ u32x4 make_rsrc(const void *base, size_t bytes) {
   const unsigned n = bytes < (size_t)kRecordsCap ? (unsigned)bytes : kRecordsCap;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, 0x00020000);
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  return u32x4{(unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a),
+               (unsigned)__builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xFFFFu)),
+               (unsigned)__builtin_amdgcn_readfirstlane((int)n), 0x00020000u};
+}
+
+// 16 bytes per lane from rsrc + voffset into LDS at lds + 16 * lane.  Issued
+// as inline assembly so that the compiler neither counts it nor guards later
+// LDS reads with a wait for it: callers wait with explicit vmcnt counts.
+__device__ __forceinline__ void load_to_lds(const u32x4 &rsrc, unsigned lds, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
 }
 
 template <typename T, int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_tile(TileGemmParams p) {
   constexpr int KTILE = Frag<T>::KTILE, E = Frag<T>::E;
   constexpr int NSTAGE = 4;
   // Stage layout: fragments 0..15 are weight strips s0..s0+15, 16..31 are
   // row groups of 16 activation rows; each fragment is 64 lanes x 16 bytes.
+  // After the k loop the same memory stages the LM head's logits tile.
   __shared__ u32x4 smem[NSTAGE][32][64];
+  __shared__ unsigned long long kbuf[4][256];
   const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
-  const int wm = w >> 1, wn = w & 1;
+  // Wave (wm, wn): activation rows wm*128 .. +128 (8 row groups) and weight
+  // strips wn*4 .. +4 of the tile: 4 x 8 MFMA tiles, 128 accumulators.
+  const int wm = w >> 2, wn = w & 3;
   const int RB = (p.M + 255) >> 8, CB = (p.NT + 15) >> 4;
   const int tiles = RB * CB;
   const int G = gridDim.x, b = blockIdx.x;
   const int slot = (G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
   const size_t lda_b = (size_t)p.lda * sizeof(T);
-  const bool wave_w = w < 2;  // waves 0, 1 fetch weight strips; 2, 3 row groups
-  // Byte offset of this lane's 16 bytes within fragment 0 of this wave at k
-  // tile 0; fragment q and k tile kt add the wave-uniform qstride*q +
-  // kstep*kt.  Waves 0/1 fetch weight strips 0-7/8-15, waves 2/3 row groups.
+  const bool wave_w = w < 4;  // waves 0-3 fetch weight strips, 4-7 row groups, 4 each
+  // Byte offset of this lane's 16 bytes within the wave's first fragment at
+  // k tile 0; fragment q and k tile kt add the wave-uniform
+  // fbase + qstride*q + kstep*kt.
   const int lanebase = wave_w ? lane * 16 : c16 * (int)lda_b + g * E * (int)sizeof(T);
   const int qstride = wave_w ? p.KT * 1024 : 16 * (int)lda_b;
-  const int fbase = (w & 1) * 8 * qstride;
+  const int fbase = (w & 3) * 4 * qstride;
   const int kstep = wave_w ? 1024 : KTILE * (int)sizeof(T);
-  lds_void *dst0 = (lds_void *)&smem[0][(w >> 1) * 16 + (w & 1) * 8][0];
+  const unsigned lds0 = (unsigned)__builtin_amdgcn_readfirstlane(
+      (int)(unsigned)(size_t)(lds_void *)&smem[0][(w >> 2) * 16 + (w & 3) * 4][0]);
   constexpr int stage_bytes = 32 * 64 * 16;
 
   for (int t = slot; t < tiles; t += G) {
@@ -127,85 +150,132 @@ void k_gemm_tile(TileGemmParams p) {
     const int rows_in = min(4, RB - band * 4);
     const int cb = rem / rows_in, rb = band * 4 + rem % rows_in;
     const int m0 = rb * 256, s0 = cb * 16;
-    const __amdgpu_buffer_rsrc_t rs =
+    const u32x4 rs =
         wave_w ? make_rsrc(reinterpret_cast<const char *>(p.wt) + (size_t)s0 * p.KT * 1024,
                            (size_t)(p.NT - s0) * p.KT * 1024)
                : make_rsrc(reinterpret_cast<const char *>(p.A) + (size_t)m0 * lda_b,
                            (size_t)(p.M - m0) * lda_b);
     auto issue = [&](int kt) {
-      lds_void *dst = (lds_void *)((char *)dst0 + (kt & (NSTAGE - 1)) * stage_bytes);
+      const unsigned dst = lds0 + (unsigned)((kt & (NSTAGE - 1)) * stage_bytes);
       const bool live = kt < p.KT;
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_void *)((char *)dst + q * 1024), 16,
-            live ? lanebase + (fbase + q * qstride + kt * kstep) : kOobOffset, 0, 0, 0);
+      for (int q = 0; q < 4; ++q)
+        load_to_lds(rs, dst + q * 1024, live ? lanebase + (fbase + q * qstride + kt * kstep) : kOobOffset);
     };
 
-    floatx4 acc[8][8];
+    floatx4 acc[4][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     // Three stages in flight ahead of the one being multiplied.  Step kt
     // waits for its own stage (two younger stages may still be loading),
     // refills the buffer of stage kt-1 (read into registers before this
-    // barrier) with stage kt+3, then reads its fragments and multiplies;
-    // the matrix cores start as soon as the first fragments arrive.
+    // barrier) with stage kt+3, then reads its 12 fragments and multiplies;
+    // the second wave on each SIMD covers this wave's waits.
     issue(0);
     issue(1);
     issue(2);
     for (int kt = 0; kt < p.KT; ++kt) {
-      asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
       issue(kt + 3);
       const int st = kt & (NSTAGE - 1);
-      u32x4 wf[8], af[8];
+      u32x4 wf[4], af[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) wf[i] = smem[st][wn * 8 + i][lane];
+      for (int i = 0; i < 4; ++i) wf[i] = smem[st][wn * 4 + i][lane];
 #pragma unroll
       for (int j = 0; j < 8; ++j) af[j] = smem[st][16 + wm * 8 + j][lane];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = Mma<T>::run(wf[i], af[j], acc[i][j]);
     }
     // Drain the look-ahead loads (they target stages the next tile reuses).
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // acc[i][j][r] = C[m = m0 + (wm*8 + j)*16 + c16][n = (s0 + wn*8 + i)*16 + 4g + r]
+    // acc[i][j][r] = C[m = m0 + (wm*8 + j)*16 + c16][n = (s0 + wn*4 + i)*16 + 4g + r]
+    if constexpr (EPI == BEPI_LMHEAD) {
+      // Argmax keys of the wave's 128 rows over its 64 columns.
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int m = m0 + (wm * 8 + j) * 16 + c16;
-      unsigned long long key = 0ull;
+      for (int j = 0; j < 8; ++j) {
+        const int m = m0 + (wm * 8 + j) * 16 + c16;
+        unsigned long long key = 0ull;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int s = s0 + wn * 8 + i;
-        const int n = s * 16 + 4 * g;
-        if (m < p.M && s < p.NT) {
-          if constexpr (EPI == BEPI_STORE) {
-            *reinterpret_cast<floatx4 *>(p.C + (long)m * p.ldc + n) = acc[i][j];
-          } else if constexpr (EPI == BEPI_ACCUM) {
-            floatx4 *dst = reinterpret_cast<floatx4 *>(p.C + (long)m * p.ldc + n);
-            *dst = *dst + acc[i][j];
-          } else if constexpr (EPI == BEPI_LMHEAD) {
-            if (p.logits) {
-              const float v4[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-              store4<T>(reinterpret_cast<T *>(p.logits) + (long)m * p.ldc + n, v4);
-            }
+        for (int i = 0; i < 4; ++i) {
+          const int s = s0 + wn * 4 + i;
+          const int n = s * 16 + 4 * g;
+          if (m < p.M && s < p.NT) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) key = umax64(key, argmax_key(acc[i][j][r], (unsigned)(n + r)));
-          } else if constexpr (EPI == BEPI_SWIGLU) {
-            epi_tile_swiglu<T>(p, m, s, g, acc[i][j]);
-          } else {
-            epi_tile_qkv<T>(p, m, n, acc[i][j]);
+          }
+        }
+        key = umax64(key, shfl_xor_u64(key, 16));
+        key = umax64(key, shfl_xor_u64(key, 32));
+        if (g == 0) kbuf[wn][(wm * 8 + j) * 16 + c16] = key;
+      }
+      if (p.logits) {
+        // Each wave stages RCH of its 128 rows at a time as dtype rows in its
+        // own LDS region (row pitch 64 elements + 16 bytes), then writes
+        // whole 16-byte chunks of each row.
+        constexpr int PITCH = 64 * (int)sizeof(T) + 16;
+        constexpr int RCH = sizeof(T) == 2 ? 64 : 32;
+        constexpr int CH = 64 * (int)sizeof(T) / 16;  // 16-byte chunks per row
+        constexpr int ROWS_PER = 64 / CH;             // rows per store instruction
+        char *stage = reinterpret_cast<char *>(&smem[0][0][0]) + w * (RCH * PITCH);
+        const int col0 = (s0 + wn * 4) * 16;
+        const int nbytes = min(64, p.N - col0) * (int)sizeof(T);
+        const int lr = lane / CH, lc = lane % CH;
+#pragma unroll
+        for (int ph = 0; ph < 128 / RCH; ++ph) {
+#pragma unroll
+          for (int jj = 0; jj < RCH / 16; ++jj) {
+            const int j = ph * (RCH / 16) + jj;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float v4[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+              store4<T>(reinterpret_cast<T *>(stage + (jj * 16 + c16) * PITCH + (i * 16 + 4 * g) * sizeof(T)), v4);
+            }
+          }
+#pragma unroll
+          for (int r0 = 0; r0 < RCH; r0 += ROWS_PER) {
+            const int row = r0 + lr;
+            const int m = m0 + wm * 128 + ph * RCH + row;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * PITCH + lc * 16);
+            if (m < p.M && lc * 16 < nbytes)
+              stg16(reinterpret_cast<char *>(p.logits) + ((size_t)m * p.ldc + col0) * sizeof(T) + lc * 16, v);
           }
         }
       }
-      if constexpr (EPI == BEPI_LMHEAD) {
-        key = umax64(key, shfl_xor_u64(key, 16));
-        key = umax64(key, shfl_xor_u64(key, 32));
-        if (g == 0 && m < p.M) atomicMax(p.keys + m, key);
+      __syncthreads();
+      if (tid < 256) {
+        const int m = m0 + tid;
+        const unsigned long long k4 =
+            umax64(umax64(kbuf[0][tid], kbuf[1][tid]), umax64(kbuf[2][tid], kbuf[3][tid]));
+        if (m < p.M) atomicMax(p.keys + m, k4);
+      }
+      __syncthreads();  // staging and key buffers are reused by the next tile
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int m = m0 + (wm * 8 + j) * 16 + c16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = s0 + wn * 4 + i;
+          const int n = s * 16 + 4 * g;
+          if (m < p.M && s < p.NT) {
+            if constexpr (EPI == BEPI_STORE) {
+              *reinterpret_cast<floatx4 *>(p.C + (long)m * p.ldc + n) = acc[i][j];
+            } else if constexpr (EPI == BEPI_ACCUM) {
+              floatx4 *dst = reinterpret_cast<floatx4 *>(p.C + (long)m * p.ldc + n);
+              *dst = *dst + acc[i][j];
+            } else if constexpr (EPI == BEPI_SWIGLU) {
+              epi_tile_swiglu<T>(p, m, s, g, acc[i][j]);
+            } else {
+              epi_tile_qkv<T>(p, m, n, acc[i][j]);
+            }
+          }
+        }
       }
     }
   }
@@ -218,7 +288,7 @@ hipError_t launch_gemm_tile(int dtype, int epi, const TileGemmParams &p, int num
   const long tiles = (long)((p.M + 255) / 256) * ((p.NT + 15) / 16);
   const dim3 grid((unsigned)(tiles < num_cus ? tiles : num_cus));
 #define PE_TILE_CASE(T, E) \
-  case E: hipLaunchKernelGGL((k_gemm_tile<T, E>), grid, dim3(256), 0, s, p); break;
+  case E: hipLaunchKernelGGL((k_gemm_tile<T, E>), grid, dim3(512), 0, s, p); break;
   if (dtype == 1) {
     switch (epi) {
       PE_TILE_CASE(bf16_t, 0) PE_TILE_CASE(bf16_t, 1) PE_TILE_CASE(bf16_t, 2) PE_TILE_CASE(bf16_t, 3)
