@@ -154,38 +154,44 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {
               sacc[kb] = Mma<T>::run(a, qf[c], sacc[kb]);
             }
           }
-          float sv[4][4];
+          // Keys beyond the split's end or block rows after the query's
+          // own position are masked; cache-only tiles need no test.
+          if (jt + 63 >= j1 || jt + 63 >= ctx) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int jj = jt + kb * 16 + 4 * g + r;
+                if (!(jj < j1 && (jj < ctx || jj - ctx <= kp_q))) sacc[kb][r] = -INFINITY;
+              }
+          }
           float mt = -INFINITY;
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int jj = jt + kb * 16 + 4 * g + r;
-              const bool ok = jj < j1 && (jj < ctx || jj - ctx <= kp_q);
-              sv[kb][r] = ok ? sacc[kb][r] * p.scale_log2 : -INFINITY;
-              mt = fmaxf(mt, sv[kb][r]);
-            }
+            for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sacc[kb][r]);
           mt = fmaxf(mt, shfl_xor_f(mt, 16));
           mt = fmaxf(mt, shfl_xor_f(mt, 32));
-          const float m_new = fmaxf(m_run, mt);
-          float alpha = 1.f, msub = 0.f;
-          if (m_new != -INFINITY) {
-            alpha = exp2f(m_run - m_new);
-            msub = m_new;
-          }
+          // Running maximum in the exp2 domain (the scale is positive, so
+          // scaling commutes with the maximum); weights 2^(s*scale - m).
+          const float m_new = fmaxf(m_run, mt * p.scale_log2);
+          const float msub = m_new == -INFINITY ? 0.f : m_new;
+          const float alpha = fast_exp2(m_run - msub);
           float pv[4][4];
           float ps = 0.f;
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              pv[kb][r] = exp2f(sv[kb][r] - msub);
+              pv[kb][r] = fast_exp2(fmaf(sacc[kb][r], p.scale_log2, -msub));
               ps += pv[kb][r];
             }
           l_lane = l_lane * alpha + ps;
           m_run = m_new;
+          if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-          for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+            for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+          }
           if constexpr (sizeof(T) == 2) {
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
@@ -290,8 +296,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p) {
     // A split may hold no key this query can see (only block rows beyond its
     // own position): its maximum is -inf and it contributes nothing.
     const float Mn = fmaxf(M, ms);
-    const float a = M == -INFINITY ? 0.f : exp2f(M - Mn);
-    const float c = ms == -INFINITY ? 0.f : exp2f(ms - Mn);
+    const float a = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+    const float c = ms == -INFINITY ? 0.f : fast_exp2(ms - Mn);
     l = l * a + ls * c;
 #pragma unroll
     for (int d = 0; d < ND; ++d) o[d] = o[d] * a + ov[d] * c;
@@ -310,7 +316,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p) {
 #pragma unroll
   for (int d = 0; d < ND; ++d) ot[d] = floatx4{0.f, 0.f, 0.f, 0.f};
   for (int q = 0; q < 4; ++q) {
-    const float sc = sm[q][lane] == -INFINITY ? 0.f : exp2f(sm[q][lane] - Mt);
+    const float sc = sm[q][lane] == -INFINITY ? 0.f : fast_exp2(sm[q][lane] - Mt);
     lt += sc * sl[q][lane];
 #pragma unroll
     for (int d = 0; d < ND; ++d) ot[d] += sc * so[q][d][lane];

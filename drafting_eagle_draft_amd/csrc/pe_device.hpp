@@ -33,11 +33,11 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(((unsigned)h) << 16);
 }
 
-// Round to nearest even (inputs are finite in this library).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Round to nearest even: gfx950 converts in hardware (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  unsigned u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v);
@@ -49,8 +49,13 @@ template <> __device__ __forceinline__ float from_f32<float>(float v) { return v
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
 
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  return (unsigned)f32_to_bf16(lo) | ((unsigned)f32_to_bf16(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(unsigned, v);
 }
+
+// 2^x on the transcendental unit (no range fix-ups; results below the
+// normal range flush to zero, which softmax weights tolerate).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename T> struct Mma;
 

@@ -11,6 +11,7 @@
 // 1 <= j <= d, of its own rollout.
 #include "pe_internal.hpp"
 
+
 namespace pe {
 
 namespace {
@@ -136,8 +137,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const float *x, const floa
 }
 
 // ---------------------------------------------------------------------------
-// Training attention.  A workgroup serves 64 query rows = (64/G kept rows) x
-// (G query heads of one kv head).  Part 1 streams the depth-0 keys of
+// Training attention.  A workgroup of NW waves serves 16·NW query rows =
+// (16·NW/G kept rows) x (G query heads of one kv head); all its waves share
+// each staged key/value tile.  Part 1 streams the depth-0 keys of
 // positions 0..max anchor through LDS exactly as the decode kernel does
 // (matrix cores, fp32 online softmax, mask position <= own anchor).  Part 2
 // adds each row's own rollout cells (at most K-1 keys) on the vector units.
@@ -145,14 +147,15 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const float *x, const floa
 __device__ __forceinline__ u32x4 lds16t(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ uint2 lds8t(const void *p) { return *reinterpret_cast<const uint2 *>(p); }
 
-template <typename T, int HD>
-__global__ __launch_bounds__(256) void k_attn_train(TrainAttnParams p) {
+template <typename T, int HD, int NW>
+__global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
   constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE, NC = HD / KTILE, ND = HD / 16;
-  constexpr int KS = HD + E, VS = 64 + 4, CPR = HD / E, MAXC = 64 * CPR / 256;
+  constexpr int NT = 64 * NW;  // threads
+  constexpr int KS = HD + E, VS = 64 + 4, CPR = HD / E, MAXC = (64 * CPR + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) T Ks[64 * KS];
   __shared__ __attribute__((aligned(16))) T Vt[HD * VS];
-  __shared__ int s_amax[4];
-  const int G = p.G, QT = 64 / G;
+  __shared__ int s_amax[NW];
+  const int G = p.G, QT = 16 * NW / G;
   const int gk = blockIdx.y;
   // Later rows see longer prefixes: start them first.
   const int i0 = ((int)gridDim.x - 1 - (int)blockIdx.x) * QT;
@@ -163,12 +166,18 @@ __global__ __launch_bounds__(256) void k_attn_train(TrainAttnParams p) {
   const int a_q = valid ? p.anc[row] : -1;
   const int d_q = valid ? p.dep[row] : 0;
 
-  // Largest anchor of the tile.
-  int am = a_q;
-  for (int o = 32; o > 0; o >>= 1) am = max(am, __shfl_xor(am, o, 64));
+  // Largest anchor of the workgroup; this wave's own smallest and largest.
+  int am = a_q, an = valid ? a_q : 0x7FFFFFFF;
+  for (int o = 32; o > 0; o >>= 1) {
+    am = max(am, __shfl_xor(am, o, 64));
+    an = min(an, __shfl_xor(an, o, 64));
+  }
+  const int wave_amax = am, wave_amin = an;
   if (lane == 0) s_amax[w] = am;
   __syncthreads();
-  const int amax = max(max(s_amax[0], s_amax[1]), max(s_amax[2], s_amax[3]));
+  int amax = s_amax[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) amax = max(amax, s_amax[i]);
   const int nkeys = min(amax + 1, p.n);
 
   u32x4 qf[NC];
@@ -190,18 +199,20 @@ __global__ __launch_bounds__(256) void k_attn_train(TrainAttnParams p) {
   auto gload = [&](int jt) {
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
-      const int id = tid + i * 256;
+      const int id = tid + i * NT;
       const int key = id / CPR, cc = id - key * CPR;
       const int jj = jt + key;
-      kreg[i] = jj < nkeys ? ldg16(k0 + (long)jj * kvs + cc * E) : u32x4{0u, 0u, 0u, 0u};
-      vreg[i] = jj < nkeys ? ldg16(v0 + (long)jj * kvs + cc * E) : u32x4{0u, 0u, 0u, 0u};
+      const bool ok = id < 64 * CPR && jj < nkeys;
+      kreg[i] = ok ? ldg16(k0 + (long)jj * kvs + cc * E) : u32x4{0u, 0u, 0u, 0u};
+      vreg[i] = ok ? ldg16(v0 + (long)jj * kvs + cc * E) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   if (nkeys > 0) gload(0);
   for (int jt = 0; jt < nkeys; jt += 64) {
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
-      const int id = tid + i * 256;
+      const int id = tid + i * NT;
+      if (id >= 64 * CPR) break;
       const int key = id / CPR, cc = id - key * CPR;
       *reinterpret_cast<u32x4 *>(&Ks[key * KS + cc * E]) = kreg[i];
       T vals[E];
@@ -211,6 +222,8 @@ __global__ __launch_bounds__(256) void k_attn_train(TrainAttnParams p) {
     }
     __syncthreads();
     if (jt + 64 < nkeys) gload(jt + 64);
+    // A wave whose rows all sit before this tile has nothing to add.
+    if (jt <= wave_amax) {
     floatx4 sacc[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -219,34 +232,44 @@ __global__ __launch_bounds__(256) void k_attn_train(TrainAttnParams p) {
       for (int c = 0; c < NC; ++c)
         sacc[kb] = Mma<T>::run(lds16t(&Ks[(kb * 16 + c16) * KS + c * KTILE + g * E]), qf[c], sacc[kb]);
     }
-    float sv[4][4];
+    // Keys after a row's own anchor (or past the prefix) are masked; tiles
+    // below every anchor of the wave need no test.
+    if (jt + 63 > wave_amin || jt + 63 >= nkeys) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int jj = jt + kb * 16 + 4 * g + r;
+          if (!(jj < nkeys && jj <= a_q)) sacc[kb][r] = -INFINITY;
+        }
+    }
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int jj = jt + kb * 16 + 4 * g + r;
-        const bool ok = jj < nkeys && jj <= a_q;
-        sv[kb][r] = ok ? sacc[kb][r] * p.scale_log2 : -INFINITY;
-        mt = fmaxf(mt, sv[kb][r]);
-      }
+      for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sacc[kb][r]);
     mt = fmaxf(mt, shfl_xor_f(mt, 16));
     mt = fmaxf(mt, shfl_xor_f(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+    // Running maximum in the exp2 domain (positive scale commutes with the
+    // maximum); weights 2^(s*scale - m).
+    const float m_new = fmaxf(m_run, mt * p.scale_log2);
+    const float msub = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - msub);
     float pv[4][4];
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pv[kb][r] = sv[kb][r] == -INFINITY ? 0.f : exp2f(sv[kb][r] - m_new);
+        pv[kb][r] = fast_exp2(fmaf(sacc[kb][r], p.scale_log2, -msub));
         ps += pv[kb][r];
       }
     l_lane = l_lane * alpha + ps;
     m_run = m_new;
+    if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-    for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+      for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+    }
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
@@ -269,6 +292,7 @@ __global__ __launch_bounds__(256) void k_attn_train(TrainAttnParams p) {
         for (int d = 0; d < ND; ++d)
           oacc[d] = Mma<T>::run(lds16t(&Vt[(d * 16 + c16) * VS + 16 * kb + 4 * g]), bf, oacc[d]);
       }
+    }
     }
     __syncthreads();
   }
@@ -303,8 +327,8 @@ __global__ __launch_bounds__(256) void k_attn_train(TrainAttnParams p) {
     if (ci < 0) continue;
     const float s = part * p.scale_log2;
     const float m_new = fmaxf(m_run, s);
-    const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
-    const float pc = exp2f(s - m_new);
+    const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
+    const float pc = fast_exp2(s - m_new);
     l_lane = l_lane * alpha + (g == 0 ? pc : 0.f);
     m_run = m_new;
     const T *vr = vall + (long)ci * kvs;
@@ -402,14 +426,19 @@ hipError_t launch_rmsnorm_rows(int dtype, const float *x, const float *gain, int
 }
 
 hipError_t launch_attn_train(int dtype, const TrainAttnParams &p, hipStream_t s) {
-  const int QT = 64 / p.G;
-  const dim3 grid((unsigned)((p.L + QT - 1) / QT), (unsigned)p.nkv);
+  // NW waves share each staged key/value tile (16·NW query rows per
+  // workgroup): 16 where the wave fits in 128 registers, else 8.
+  auto go = [&](auto kern, int nw) {
+    const int QT = 16 * nw / p.G;
+    const dim3 grid((unsigned)((p.L + QT - 1) / QT), (unsigned)p.nkv);
+    hipLaunchKernelGGL(kern, grid, dim3(64 * nw), 0, s, p);
+  };
   if (dtype == 1) {
-    if (p.hd == 64) hipLaunchKernelGGL((k_attn_train<bf16_t, 64>), grid, dim3(256), 0, s, p);
-    else if (p.hd == 128) hipLaunchKernelGGL((k_attn_train<bf16_t, 128>), grid, dim3(256), 0, s, p);
+    if (p.hd == 64) go(k_attn_train<bf16_t, 64, 16>, 16);
+    else if (p.hd == 128) go(k_attn_train<bf16_t, 128, 8>, 8);
     else return hipErrorInvalidValue;
   } else {
-    if (p.hd == 64) hipLaunchKernelGGL((k_attn_train<float, 64>), grid, dim3(256), 0, s, p);
+    if (p.hd == 64) go(k_attn_train<float, 64, 8>, 8);
     else return hipErrorInvalidValue;
   }
   return hipGetLastError();
