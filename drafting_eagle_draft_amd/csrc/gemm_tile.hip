@@ -120,9 +120,15 @@ void k_gemm_tile(TileGemmParams p) {
   constexpr int NSTAGE = 4;
   // Stage layout: fragments 0..15 are weight strips s0..s0+15, 16..31 are
   // row groups of 16 activation rows; each fragment is 64 lanes x 16 bytes.
-  // After the k loop the same memory stages the LM head's logits tile.
   __shared__ u32x4 smem[NSTAGE][32][64];
-  __shared__ unsigned long long kbuf[4][256];
+  // LM head: per-wave staging of RCH logits rows (row pitch 64 elements +
+  // 16 bytes) and the per-quarter argmax keys of the tile's 256 rows.  Kept
+  // apart from the stages so the next tile's loads run during the epilogue.
+  // (bf16 only: fp32 logits are written from registers.)
+  constexpr int PITCH = 64 * (int)sizeof(T) + 16;
+  constexpr int RCH = 16;
+  __shared__ __attribute__((aligned(16))) char lstage[EPI == BEPI_LMHEAD && sizeof(T) == 2 ? 8 * RCH * PITCH : 16];
+  __shared__ unsigned long long kbuf[EPI == BEPI_LMHEAD ? 4 : 1][256];
   const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
   // Wave (wm, wn): activation rows wm*128 .. +128 (8 row groups) and weight
@@ -145,41 +151,54 @@ void k_gemm_tile(TileGemmParams p) {
       (int)(unsigned)(size_t)(lds_void *)&smem[0][(w >> 2) * 16 + (w & 3) * 4][0]);
   constexpr int stage_bytes = 32 * 64 * 16;
 
-  for (int t = slot; t < tiles; t += G) {
+  // Tile t -> (first activation row, first weight strip); bands of four row
+  // blocks, columns inside a band.
+  auto tile_origin = [&](int t, int &m0, int &s0) {
     const int band = t / (4 * CB), rem = t - band * 4 * CB;
     const int rows_in = min(4, RB - band * 4);
     const int cb = rem / rows_in, rb = band * 4 + rem % rows_in;
-    const int m0 = rb * 256, s0 = cb * 16;
-    const u32x4 rs =
-        wave_w ? make_rsrc(reinterpret_cast<const char *>(p.wt) + (size_t)s0 * p.KT * 1024,
-                           (size_t)(p.NT - s0) * p.KT * 1024)
-               : make_rsrc(reinterpret_cast<const char *>(p.A) + (size_t)m0 * lda_b,
-                           (size_t)(p.M - m0) * lda_b);
-    auto issue = [&](int kt) {
-      const unsigned dst = lds0 + (unsigned)((kt & (NSTAGE - 1)) * stage_bytes);
-      const bool live = kt < p.KT;
+    m0 = rb * 256;
+    s0 = cb * 16;
+  };
+  auto tile_rsrc = [&](int m0, int s0) {
+    return wave_w ? make_rsrc(reinterpret_cast<const char *>(p.wt) + (size_t)s0 * p.KT * 1024,
+                              (size_t)(p.NT - s0) * p.KT * 1024)
+                  : make_rsrc(reinterpret_cast<const char *>(p.A) + (size_t)m0 * lda_b,
+                              (size_t)(p.M - m0) * lda_b);
+  };
+  auto issue = [&](const u32x4 &rs, int kt) {
+    const unsigned dst = lds0 + (unsigned)((kt & (NSTAGE - 1)) * stage_bytes);
+    const bool live = kt < p.KT;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        load_to_lds(rs, dst + q * 1024, live ? lanebase + (fbase + q * qstride + kt * kstep) : kOobOffset);
-    };
+    for (int q = 0; q < 4; ++q)
+      load_to_lds(rs, dst + q * 1024, live ? lanebase + (fbase + q * qstride + kt * kstep) : kOobOffset);
+  };
 
+  int t = slot, m0 = 0, s0 = 0;
+  u32x4 rs = {0u, 0u, 0u, 0u};
+  if (t < tiles) {
+    tile_origin(t, m0, s0);
+    rs = tile_rsrc(m0, s0);
+    issue(rs, 0);
+    issue(rs, 1);
+    issue(rs, 2);
+  }
+  while (t < tiles) {
     floatx4 acc[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // Three stages in flight ahead of the one being multiplied.  Step kt
-    // waits for its own stage (two younger stages may still be loading),
-    // refills the buffer of stage kt-1 (read into registers before this
-    // barrier) with stage kt+3, then reads its 12 fragments and multiplies;
-    // the second wave on each SIMD covers this wave's waits.
-    issue(0);
-    issue(1);
-    issue(2);
+    // Three stages in flight ahead of the one being multiplied (the first
+    // three were issued before this tile started).  Step kt waits for its
+    // own stage (two younger stages may still be loading), refills the
+    // buffer of stage kt-1 (read into registers before this barrier) with
+    // stage kt+3, then reads its 12 fragments and multiplies; the second
+    // wave on each SIMD covers this wave's waits.
     for (int kt = 0; kt < p.KT; ++kt) {
       asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-      issue(kt + 3);
+      issue(rs, kt + 3);
       const int st = kt & (NSTAGE - 1);
       u32x4 wf[4], af[8];
 #pragma unroll
@@ -191,9 +210,21 @@ void k_gemm_tile(TileGemmParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = Mma<T>::run(wf[i], af[j], acc[i][j]);
     }
-    // Drain the look-ahead loads (they target stages the next tile reuses).
+    // Drain the look-ahead loads (they target stages the next tile reuses),
+    // then start the next tile's first three stages so that they load while
+    // this tile's epilogue runs.
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-
+    const int tm0 = m0, ts0 = s0;
+    t += G;
+    if (t < tiles) {
+      tile_origin(t, m0, s0);
+      rs = tile_rsrc(m0, s0);
+      issue(rs, 0);
+      issue(rs, 1);
+      issue(rs, 2);
+    }
+    {
+    const int m0 = tm0, s0 = ts0;
     // acc[i][j][r] = C[m = m0 + (wm*8 + j)*16 + c16][n = (s0 + wn*4 + i)*16 + 4g + r]
     if constexpr (EPI == BEPI_LMHEAD) {
       // Argmax keys of the wave's 128 rows over its 64 columns.
@@ -214,15 +245,25 @@ void k_gemm_tile(TileGemmParams p) {
         key = umax64(key, shfl_xor_u64(key, 32));
         if (g == 0) kbuf[wn][(wm * 8 + j) * 16 + c16] = key;
       }
-      if (p.logits) {
+      if (p.logits && sizeof(T) == 4) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int m = m0 + (wm * 8 + j) * 16 + c16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int s = s0 + wn * 4 + i;
+            if (m < p.M && s < p.NT) {
+              const float v4[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+              store4<T>(reinterpret_cast<T *>(p.logits) + (size_t)m * p.ldc + s * 16 + 4 * g, v4);
+            }
+          }
+        }
+      } else if (p.logits) {
         // Each wave stages RCH of its 128 rows at a time as dtype rows in its
-        // own LDS region (row pitch 64 elements + 16 bytes), then writes
-        // whole 16-byte chunks of each row.
-        constexpr int PITCH = 64 * (int)sizeof(T) + 16;
-        constexpr int RCH = sizeof(T) == 2 ? 64 : 32;
+        // own LDS region, then writes whole 16-byte chunks of each row.
         constexpr int CH = 64 * (int)sizeof(T) / 16;  // 16-byte chunks per row
         constexpr int ROWS_PER = 64 / CH;             // rows per store instruction
-        char *stage = reinterpret_cast<char *>(&smem[0][0][0]) + w * (RCH * PITCH);
+        char *stage = lstage + w * (RCH * PITCH);
         const int col0 = (s0 + wn * 4) * 16;
         const int nbytes = min(64, p.N - col0) * (int)sizeof(T);
         const int lr = lane / CH, lc = lane % CH;
@@ -277,6 +318,7 @@ void k_gemm_tile(TileGemmParams p) {
           }
         }
       }
+    }
     }
   }
 }
