@@ -287,15 +287,16 @@ TrainLayout train_layout(const pe_model *m, long n, int K, long L) {
   t.inv = take((size_t)n * K * 4);
   t.yfc = take((size_t)(n + 1) * H * 4);
   t.xres = take((size_t)L * H * 4);
-  t.u = take((size_t)L * H * esz);
+  const size_t Lp = (size_t)(L + 15) / 16 * 16;  // tiled activations hold whole 16-row groups
+  t.u = take(Lp * H * esz);
   const bool layers = c.n_layers > 0;
   t.q = take(layers ? (size_t)L * c.n_q_heads * hd * esz : 0);
   t.kall = take(layers ? (size_t)L * c.n_kv_heads * hd * esz : 0);
   t.vall = take(layers ? (size_t)L * c.n_kv_heads * hd * esz : 0);
   t.k0 = take(layers ? (size_t)n * c.n_kv_heads * hd * esz : 0);
   t.v0 = take(layers ? (size_t)n * c.n_kv_heads * hd * esz : 0);
-  t.attn = take(layers ? (size_t)L * c.n_q_heads * hd * esz : 0);
-  t.h = take(layers ? (size_t)L * c.intermediate * esz : 0);
+  t.attn = take(layers ? Lp * c.n_q_heads * hd * esz : 0);
+  t.h = take(layers ? Lp * c.intermediate * esz : 0);
   t.keys = take((size_t)L * 8);
   t.total = off;
   return t;
@@ -305,6 +306,9 @@ constexpr long kTrainRowsMax = 1L << 22;  // 128-row blocks stay well within the
 
 pe_status check_train_shape(const pe_model *m, const pe_mask *mask, int32_t n, int32_t K, int32_t L) {
   if (!m || !mask) return fail(PE_ERR_INVALID_ARGUMENT, "model and mask must be non-NULL");
+  if (m->cfg.hidden % m->ktile || m->cfg.intermediate % m->ktile)
+    return fail(PE_ERR_UNSUPPORTED, "the training forward needs hidden and intermediate multiples of %d",
+                m->ktile);
   if (K != mask->K) return fail(PE_ERR_INVALID_ARGUMENT, "K=%d differs from the mask's K=%d", K, mask->K);
   if (n < 1 || n > mask->n_max)
     return fail(PE_ERR_INVALID_ARGUMENT, "n=%d outside [1, n_max=%d]", n, mask->n_max);
@@ -691,11 +695,11 @@ pe_status pe_train_forward(const pe_model *m, const pe_mask *mask, int32_t N, in
   }
   for (int l = 0; l < N; ++l) {
     const LayerT &Lw = m->layers[l];
-    if ((e = launch_rmsnorm_rows(dt, xres, Lw.attn_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
+    if ((e = launch_rmsnorm_tiled(dt, xres, Lw.attn_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
       return hip_fail(e, "RMSNorm launch");
     {
       TileGemmParams p{};
-      p.A = u; p.lda = H; p.M = L;
+      p.A = u; p.lda = H; p.M = L; p.a_tiled = 1;
       p.q = ws + W.q; p.kall = ws + W.kall; p.vall = ws + W.vall; p.k0 = ws + W.k0; p.v0 = ws + W.v0;
       p.anc = anc; p.dep = dep; p.inv_freq = m->inv_freq;
       p.n = n; p.nq = nq; p.nkv = nkv; p.hd = hd;
@@ -712,30 +716,30 @@ pe_status pe_train_forward(const pe_model *m, const pe_mask *mask, int32_t N, in
     }
     {
       TileGemmParams p{};
-      p.A = ws + W.attn; p.lda = (long)nq * hd; p.M = L;
+      p.A = ws + W.attn; p.lda = (long)nq * hd; p.M = L; p.a_tiled = 1;
       p.C = xres; p.ldc = H;
       if ((st = gemm(Lw.o, BEPI_ACCUM, p)) != PE_OK) return st;
     }
-    if ((e = launch_rmsnorm_rows(dt, xres, Lw.mlp_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
+    if ((e = launch_rmsnorm_tiled(dt, xres, Lw.mlp_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
       return hip_fail(e, "RMSNorm launch");
     {
       TileGemmParams p{};
-      p.A = u; p.lda = H; p.M = L;
+      p.A = u; p.lda = H; p.M = L; p.a_tiled = 1;
       p.h = ws + W.h; p.I = c.intermediate;
       if ((st = gemm(Lw.gateup, BEPI_SWIGLU, p)) != PE_OK) return st;
     }
     {
       TileGemmParams p{};
-      p.A = ws + W.h; p.lda = c.intermediate; p.M = L;
+      p.A = ws + W.h; p.lda = c.intermediate; p.M = L; p.a_tiled = 1;
       p.C = xres; p.ldc = H;
       if ((st = gemm(Lw.down, BEPI_ACCUM, p)) != PE_OK) return st;
     }
   }
-  if ((e = launch_rmsnorm_rows(dt, xres, m->final_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
+  if ((e = launch_rmsnorm_tiled(dt, xres, m->final_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
     return hip_fail(e, "RMSNorm launch");
   {
     TileGemmParams p{};
-    p.A = u; p.lda = H; p.M = L;
+    p.A = u; p.lda = H; p.M = L; p.a_tiled = 1;
     p.logits = logits_out; p.ldc = c.vocab;
     p.keys = reinterpret_cast<unsigned long long *>(ws + W.keys);
     if ((e = launch_zero(p.keys, (size_t)L * 8, s)) != hipSuccess) return hip_fail(e, "key reset launch");

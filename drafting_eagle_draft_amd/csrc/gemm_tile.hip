@@ -41,10 +41,11 @@ template <> __device__ __forceinline__ void store2<bf16_t>(bf16_t *dst, float a,
 }
 
 // Gate/up tile rows of strip s: lane group g holds gate rows 8s+2g, 8s+2g+1
-// in r = 0, 1 and the matching up rows in r = 2, 3.
+// in r = 0, 1 and the matching up rows in r = 2, 3.  h is written in the
+// fragment-tile layout that the down projection reads.
 template <typename T>
 __device__ __forceinline__ void epi_tile_swiglu(const TileGemmParams &p, int m, int s, int g, floatx4 v) {
-  T *dst = reinterpret_cast<T *>(p.h) + (long)m * p.I + 8 * s + 2 * g;
+  T *dst = reinterpret_cast<T *>(p.h) + frag_off<T>(m, 8 * s + 2 * g, p.I / Frag<T>::KTILE);
   store2<T>(dst, silu_f(v[0]) * v[2], silu_f(v[1]) * v[3]);
 }
 
@@ -143,10 +144,13 @@ void k_gemm_tile(TileGemmParams p) {
   // Byte offset of this lane's 16 bytes within the wave's first fragment at
   // k tile 0; fragment q and k tile kt add the wave-uniform
   // fbase + qstride*q + kstep*kt.
-  const int lanebase = wave_w ? lane * 16 : c16 * (int)lda_b + g * E * (int)sizeof(T);
-  const int qstride = wave_w ? p.KT * 1024 : 16 * (int)lda_b;
+  // Weights and tiled activations: 1 KB fragments, k tiles 1 KB apart,
+  // groups KT KB apart.  Row-major activations: 16 rows of lda elements.
+  const bool frag = wave_w || p.a_tiled;
+  const int lanebase = frag ? lane * 16 : c16 * (int)lda_b + g * E * (int)sizeof(T);
+  const int qstride = frag ? p.KT * 1024 : 16 * (int)lda_b;
   const int fbase = (w & 3) * 4 * qstride;
-  const int kstep = wave_w ? 1024 : KTILE * (int)sizeof(T);
+  const int kstep = frag ? 1024 : KTILE * (int)sizeof(T);
   const unsigned lds0 = (unsigned)__builtin_amdgcn_readfirstlane(
       (int)(unsigned)(size_t)(lds_void *)&smem[0][(w >> 2) * 16 + (w & 3) * 4][0]);
   constexpr int stage_bytes = 32 * 64 * 16;
@@ -160,11 +164,15 @@ void k_gemm_tile(TileGemmParams p) {
     m0 = rb * 256;
     s0 = cb * 16;
   };
+  const int MG = (p.M + 15) >> 4;  // 16-row groups of a tiled A
   auto tile_rsrc = [&](int m0, int s0) {
-    return wave_w ? make_rsrc(reinterpret_cast<const char *>(p.wt) + (size_t)s0 * p.KT * 1024,
-                              (size_t)(p.NT - s0) * p.KT * 1024)
-                  : make_rsrc(reinterpret_cast<const char *>(p.A) + (size_t)m0 * lda_b,
-                              (size_t)(p.M - m0) * lda_b);
+    if (wave_w)
+      return make_rsrc(reinterpret_cast<const char *>(p.wt) + (size_t)s0 * p.KT * 1024,
+                       (size_t)(p.NT - s0) * p.KT * 1024);
+    if (p.a_tiled)
+      return make_rsrc(reinterpret_cast<const char *>(p.A) + (size_t)(m0 >> 4) * p.KT * 1024,
+                       (size_t)(MG - (m0 >> 4)) * p.KT * 1024);
+    return make_rsrc(reinterpret_cast<const char *>(p.A) + (size_t)m0 * lda_b, (size_t)(p.M - m0) * lda_b);
   };
   auto issue = [&](const u32x4 &rs, int kt) {
     const unsigned dst = lds0 + (unsigned)((kt & (NSTAGE - 1)) * stage_bytes);

@@ -76,6 +76,15 @@ template <> struct Mma<float> {
   }
 };
 
+// Element offset of (row m, column k) in the fragment-tile layout of a
+// matrix with KT k tiles per row group: 16-row groups, each a run of KT
+// 1 KB fragments; lane (m % 16, (k % KTILE) / E) holds E consecutive k.
+template <typename T>
+__device__ __forceinline__ long frag_off(int m, int k, int KT) {
+  constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE;
+  return ((long)((m >> 4) * KT + k / KTILE) * 64 + ((k % KTILE) / E) * 16 + (m & 15)) * E + (k % E);
+}
+
 __device__ __forceinline__ u32x4 ldg16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }

@@ -137,14 +137,15 @@ enum BigEpi : int {
 struct TileGemmParams {
   const u32x4 *wt;
   int NT, KT, N, K;
-  const void *A;        // dtype [M][lda], lda >= K
+  const void *A;        // dtype [M][lda] row-major (lda >= K), or fragment tiles
   long lda;
   int M;
+  int a_tiled;          // A in the fragment-tile layout: [ceil(M/16)][KT] 1 KB fragments
   float *C;
   long ldc;
   void *logits;
   unsigned long long *keys;  // [M], zeroed before the launch; atomically maxed
-  // SWIGLU
+  // SWIGLU: h in the fragment-tile layout of an [M][I] matrix
   void *h;
   int I;
   // QKV: q [M][nq][hd], kall/vall [M][nkv][hd], depth-0 rows also to
@@ -169,8 +170,10 @@ hipError_t launch_mask_materialize(const int2 *table, int nK, const int *rows, i
 hipError_t launch_train_fuse(int dtype, const float *Y, const void *embed, const int *tok,
                              const void *mask_emb, const int *anc, const int *dep, int L, int n, int H,
                              int V, float *x, hipStream_t s);
-hipError_t launch_rmsnorm_rows(int dtype, const float *x, const float *gain, int rows, int H, float eps,
-                               void *u, hipStream_t s);
+// u = RMSNorm(x) * gain for M rows, written in the fragment-tile layout
+// (H a multiple of the k tile).
+hipError_t launch_rmsnorm_tiled(int dtype, const float *x, const float *gain, int M, int H, float eps,
+                                void *u, hipStream_t s);
 
 struct TrainAttnParams {
   const void *q;            // [L][nq][hd] rotated queries
@@ -180,7 +183,7 @@ struct TrainAttnParams {
   const int *inv;           // [n*K] grid index -> kept row or -1
   int L, n, K, nq, nkv, hd, G;
   float scale_log2;
-  void *out;                // [L][nq*hd] dtype
+  void *out;                // [L][nq*hd] dtype, fragment-tile layout
 };
 
 hipError_t launch_attn_train(int dtype, const TrainAttnParams &p, hipStream_t s);

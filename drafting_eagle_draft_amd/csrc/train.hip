@@ -118,22 +118,40 @@ __global__ void k_train_fuse(const float *Y, const T *embed, const int *tok, con
   x[idx] = v;
 }
 
-// u[i] = x[i] / sqrt(mean(x[i]^2) + eps) * g, one 256-thread block per row.
+// u = x / sqrt(mean(x^2) + eps) * g for one 16-row group per block, written
+// as whole 1 KB fragments of the tile layout the GEMMs read.  Rows past M are
+// written as zeros.
 template <typename T>
-__global__ __launch_bounds__(256) void k_rmsnorm_rows(const float *x, const float *gain, int H,
-                                                      float eps, T *u) {
-  __shared__ float red[4];
-  const long row = blockIdx.x;
-  const float *xr = x + row * H;
-  float s = 0.f;
-  for (int c = threadIdx.x; c < H; c += 256) s += xr[c] * xr[c];
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+__global__ __launch_bounds__(256) void k_rmsnorm_tiled(const float *x, const float *gain, int M, int H,
+                                                       float eps, T *u) {
+  constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE;
+  __shared__ float rstd[16];
+  const int grp = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int r = w * 4; r < w * 4 + 4; ++r) {
+    const int row = grp * 16 + r;
+    float s = 0.f;
+    if (row < M) {
+      const float *xr = x + (long)row * H;
+      for (int c = lane; c < H; c += 64) s += xr[c] * xr[c];
+    }
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (lane == 0) rstd[r] = rsqrtf(s / (float)H + eps);
+  }
   __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-  const float rstd = rsqrtf(tot / (float)H + eps);
-  T *ur = u + row * H;
-  for (int c = threadIdx.x; c < H; c += 256) ur[c] = from_f32<T>(xr[c] * rstd * gain[c]);
+  const int KT = H / KTILE;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int row = grp * 16 + c16;
+  const float rs = rstd[c16];
+  for (int kt = w; kt < KT; kt += 4) {
+    const int k = kt * KTILE + g * E;
+    T vals[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      vals[e] = from_f32<T>(row < M ? x[(long)row * H + k + e] * rs * gain[k + e] : 0.f);
+    u32x4 v;
+    __builtin_memcpy(&v, vals, 16);
+    stg16(u + ((long)(grp * KT + kt) * 64 + lane) * E, v);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -144,6 +162,14 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const float *x, const floa
 // (matrix cores, fp32 online softmax, mask position <= own anchor).  Part 2
 // adds each row's own rollout cells (at most K-1 keys) on the vector units.
 // ---------------------------------------------------------------------------
+template <typename T> __device__ __forceinline__ void store_vals4(T *dst, const float v[4]);
+template <> __device__ __forceinline__ void store_vals4<float>(float *dst, const float v[4]) {
+  *reinterpret_cast<floatx4 *>(dst) = floatx4{v[0], v[1], v[2], v[3]};
+}
+template <> __device__ __forceinline__ void store_vals4<bf16_t>(bf16_t *dst, const float v[4]) {
+  *reinterpret_cast<uint2 *>(dst) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
 __device__ __forceinline__ u32x4 lds16t(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ uint2 lds8t(const void *p) { return *reinterpret_cast<const uint2 *>(p); }
 
@@ -348,11 +374,15 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
   l_tot += shfl_xor_f(l_tot, 32);
   if (!valid) return;
   const float inv_l = 1.0f / l_tot;
-  T *dst = reinterpret_cast<T *>(p.out) + (long)row * p.nq * HD + (gk * G + hl) * HD;
+  // Output row in the fragment-tile layout of the [L][nq*hd] O-projection
+  // input: the lane's 4 dimensions are contiguous there.
+  const int KTo = p.nq * HD / KTILE;
+  T *out = reinterpret_cast<T *>(p.out);
 #pragma unroll
-  for (int d = 0; d < ND; ++d)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dst[d * 16 + 4 * g + r] = from_f32<T>(oacc[d][r] * inv_l);
+  for (int d = 0; d < ND; ++d) {
+    const float v[4] = {oacc[d][0] * inv_l, oacc[d][1] * inv_l, oacc[d][2] * inv_l, oacc[d][3] * inv_l};
+    store_vals4<T>(out + frag_off<T>(row, (gk * G + hl) * HD + d * 16 + 4 * g, KTo), v);
+  }
 }
 
 unsigned blocks_for(long n, int threads) { return (unsigned)((n + threads - 1) / threads); }
@@ -414,13 +444,14 @@ hipError_t launch_train_fuse(int dtype, const float *Y, const void *embed, const
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm_rows(int dtype, const float *x, const float *gain, int rows, int H, float eps,
-                               void *u, hipStream_t s) {
+hipError_t launch_rmsnorm_tiled(int dtype, const float *x, const float *gain, int M, int H, float eps,
+                                void *u, hipStream_t s) {
+  const dim3 grid((unsigned)((M + 15) / 16));
   if (dtype == 1)
-    hipLaunchKernelGGL(k_rmsnorm_rows<bf16_t>, dim3(rows), dim3(256), 0, s, x, gain, H, eps,
+    hipLaunchKernelGGL(k_rmsnorm_tiled<bf16_t>, grid, dim3(256), 0, s, x, gain, M, H, eps,
                        reinterpret_cast<bf16_t *>(u));
   else
-    hipLaunchKernelGGL(k_rmsnorm_rows<float>, dim3(rows), dim3(256), 0, s, x, gain, H, eps,
+    hipLaunchKernelGGL(k_rmsnorm_tiled<float>, grid, dim3(256), 0, s, x, gain, M, H, eps,
                        reinterpret_cast<float *>(u));
   return hipGetLastError();
 }

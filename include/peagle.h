@@ -197,8 +197,9 @@ pe_status pe_train_workspace_size(const pe_model *m, int32_t n, int32_t K, int32
  *              unspecified values but every access stays in bounds)
  *   logits_out device [L, V] in the model dtype, or NULL
  *   argmax_out device int32 [L] (lowest index among equal maxima), or NULL
- * Requires n <= n_max and K equal to the mask's K.  Row i of the outputs
- * belongs to rows[i].
+ * Requires n <= n_max, K equal to the mask's K, and hidden and intermediate
+ * multiples of 32 (bf16) or 16 (fp32); PE_ERR_UNSUPPORTED otherwise.  Row i
+ * of the outputs belongs to rows[i].
  */
 pe_status pe_train_forward(const pe_model *m, const pe_mask *mask, int32_t N, int32_t n, int32_t K,
                            const void *hidden3, const int32_t *token_ids, const void *mask_emb,
