@@ -120,34 +120,59 @@ __global__ void k_train_fuse(const float *Y, const T *embed, const int *tok, con
 
 // u = x / sqrt(mean(x^2) + eps) * g for one 16-row group per block, written
 // as whole 1 KB fragments of the tile layout the GEMMs read.  Rows past M are
-// written as zeros.
+// written as zeros.  H is a multiple of the k tile (so of 4).
 template <typename T>
 __global__ __launch_bounds__(256) void k_rmsnorm_tiled(const float *x, const float *gain, int M, int H,
                                                        float eps, T *u) {
   constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE;
   __shared__ float rstd[16];
   const int grp = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int r = w * 4; r < w * 4 + 4; ++r) {
-    const int row = grp * 16 + r;
-    float s = 0.f;
-    if (row < M) {
-      const float *xr = x + (long)row * H;
-      for (int c = lane; c < H; c += 64) s += xr[c] * xr[c];
+  // Sums of squares: wave w takes rows 4w..4w+3 together (four independent
+  // 16-byte loads per step).
+  {
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    const float *xr[4];
+    bool ok[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = grp * 16 + w * 4 + r;
+      ok[r] = row < M;
+      xr[r] = x + (long)(ok[r] ? row : 0) * H;
     }
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-    if (lane == 0) rstd[r] = rsqrtf(s / (float)H + eps);
+    for (int c = lane * 4; c < H; c += 256) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (!ok[r]) continue;
+        const floatx4 v = *reinterpret_cast<const floatx4 *>(xr[r] + c);
+        s[r] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float t = s[r];
+      for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+      if (lane == 0) rstd[w * 4 + r] = rsqrtf(t / (float)H + eps);
+    }
   }
   __syncthreads();
   const int KT = H / KTILE;
   const int c16 = lane & 15, g = lane >> 4;
   const int row = grp * 16 + c16;
   const float rs = rstd[c16];
+  const float *xrow = x + (long)(row < M ? row : 0) * H;
   for (int kt = w; kt < KT; kt += 4) {
     const int k = kt * KTILE + g * E;
+    float xv[E], gv[E];
+#pragma unroll
+    for (int q = 0; q < E / 4; ++q) {
+      const floatx4 a = *reinterpret_cast<const floatx4 *>(xrow + k + 4 * q);
+      const floatx4 b = *reinterpret_cast<const floatx4 *>(gain + k + 4 * q);
+      xv[4 * q] = a.x; xv[4 * q + 1] = a.y; xv[4 * q + 2] = a.z; xv[4 * q + 3] = a.w;
+      gv[4 * q] = b.x; gv[4 * q + 1] = b.y; gv[4 * q + 2] = b.z; gv[4 * q + 3] = b.w;
+    }
     T vals[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      vals[e] = from_f32<T>(row < M ? x[(long)row * H + k + e] * rs * gain[k + e] : 0.f);
+    for (int e = 0; e < E; ++e) vals[e] = from_f32<T>(row < M ? xv[e] * rs * gv[e] : 0.f);
     u32x4 v;
     __builtin_memcpy(&v, vals, 16);
     stg16(u + ((long)(grp * KT + kt) * 64 + lane) * E, v);
