@@ -260,6 +260,113 @@ def _rotate_once(a, pos, theta, half):
 
 
 # ---------------------------------------------------------------------------
+# Depth-0 rows appended to the drafter's cache, and the autoregressive EAGLE-3
+# baseline built from them.
+#   [RH] "Flex-attention mask": depth-0 positions carry real tokens and real
+#   hidden states and attend causally to each other (the base context).
+#   [TD] "Technical Architecture: From Sequential to Parallel": EAGLE needs K
+#   sequential forward passes for K draft tokens.  [PN] section 2: each step
+#   depends on the previous step's token and hidden state.  [E4] "EAGLE-4":
+#   the drafter feeds its normalized output back as the next step's input.
+# ---------------------------------------------------------------------------
+
+
+def draft_extend(w, cfg, inputs, input_kind, embed_rows, ctx_lens, k_cache, v_cache, N=None):
+    """Forward of T real (depth-0) rows per sequence, whose keys and values
+    then extend the drafter's cache.
+
+    inputs: [B, T, 3H] target hidden states (input_kind "target": the row's
+    layer-0 input is E[token] + fc(h)) or [B, T, H] drafter output states
+    (input_kind "drafter": E[token] + z, the fed-back state taking the place
+    of the projected target state).  embed_rows: [B, T, H] = E[token].
+    Row t of sequence b sits at position ctx_lens[b] + t and attends to cache
+    rows [0, ctx_lens[b]) and to rows 0..t of the block.
+
+    Returns (logits [B, T, V], z [B, T, H] the final-norm output,
+    k_new, v_new: per layer [B, n_kv, T, hd], keys rotated) -- k_new/v_new are
+    what a cache append writes at positions ctx_lens[b] .. ctx_lens[b] + T - 1.
+    """
+    N = cfg.n_layers if N is None else N
+    inputs = np.asarray(inputs, dtype=F64)
+    B, T = inputs.shape[0], inputs.shape[1]
+    nq, nkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    G = nq // nkv
+    scale = 1.0 / math.sqrt(hd)
+    if input_kind == "target":
+        x = np.asarray(embed_rows, F64) + linear(inputs.reshape(B * T, -1), w["fc"]).reshape(B, T, -1)
+    elif input_kind == "drafter":
+        x = np.asarray(embed_rows, F64) + inputs
+    else:
+        raise ValueError(input_kind)
+    pos = np.asarray(ctx_lens, dtype=F64)[:, None] + np.arange(T)[None, :]
+    k_new, v_new = [], []
+    for l in range(N):
+        lw = w["layers"][l]
+        q, k, v = _layer_qkv(x, lw, cfg)
+        q = rope(q, pos[:, :, None], cfg.rope_theta)
+        k = rope(k, pos[:, :, None], cfg.rope_theta)
+        k_new.append(np.transpose(k, (0, 2, 1, 3)).copy())
+        v_new.append(np.transpose(v, (0, 2, 1, 3)).copy())
+        attn = np.empty((B, T, nq, hd), dtype=F64)
+        for b in range(B):
+            C = int(ctx_lens[b])
+            for g in range(nkv):
+                ck = np.asarray(k_cache[l][b, g, :C], dtype=F64)
+                cv = np.asarray(v_cache[l][b, g, :C], dtype=F64)
+                for t in range(T):
+                    keys = np.concatenate([ck, k[b, :t + 1, g]], axis=0)
+                    vals = np.concatenate([cv, v[b, :t + 1, g]], axis=0)
+                    attn[b, t, g * G:(g + 1) * G] = attend(q[b, t, g * G:(g + 1) * G], keys, vals, scale)
+        x = _layer_finish(x, attn.reshape(B, T, nq * hd), lw, cfg)
+    z = rmsnorm(x, w["final_norm"], cfg.rms_eps)
+    return linear(z.reshape(B * T, -1), w["lm_head"]).reshape(B, T, -1), z, k_new, v_new
+
+
+def eagle3_chain(w, cfg, hidden3, token_ids, ctx_lens, k_cache, v_cache, K, embed_lookup, N=None):
+    """K autoregressive EAGLE-3 drafter steps per sequence (the sequential
+    baseline P-EAGLE replaces).
+
+    Step 0 takes the new token and the target's hidden state (3H, through
+    fc) at position ctx_lens[b]; step j > 0 takes step j-1's draft token and
+    its final-norm output state z at position ctx_lens[b] + j.  Each step's
+    keys and values join the cache before the next step.  embed_lookup(ids)
+    returns the embedding rows of int ids.  The caller's caches are not
+    modified.  Returns (drafts [B, K] int32, logits [B, K, V]).
+    """
+    N = cfg.n_layers if N is None else N
+    B = len(token_ids)
+    ctx = np.asarray(ctx_lens, dtype=np.int64)
+    kc, vc = [], []
+    for l in range(N):
+        shp = np.asarray(k_cache[l]).shape
+        cap = max(shp[2], int(ctx.max()) + K)
+        a = np.zeros(shp[:2] + (cap, shp[3]), dtype=F64)
+        c = np.zeros_like(a)
+        a[:, :, :shp[2]] = k_cache[l]
+        c[:, :, :shp[2]] = v_cache[l]
+        kc.append(a)
+        vc.append(c)
+    drafts = np.zeros((B, K), dtype=np.int32)
+    logits = None
+    tok = np.asarray(token_ids, dtype=np.int64)
+    inputs, kind = np.asarray(hidden3, F64)[:, None, :], "target"
+    for j in range(K):
+        lg, z, kn, vn = draft_extend(w, cfg, inputs, kind, np.asarray(embed_lookup(tok), F64)[:, None, :],
+                                     ctx + j, kc, vc, N)
+        for l in range(N):
+            for b in range(B):
+                kc[l][b, :, ctx[b] + j] = kn[l][b, :, 0]
+                vc[l][b, :, ctx[b] + j] = vn[l][b, :, 0]
+        if logits is None:
+            logits = np.zeros((B, K, lg.shape[-1]), dtype=F64)
+        logits[:, j] = lg[:, 0]
+        drafts[:, j] = argmax_lowest(lg[:, 0])
+        tok = drafts[:, j].astype(np.int64)
+        inputs, kind = z, "drafter"
+    return drafts, logits
+
+
+# ---------------------------------------------------------------------------
 # Greedy acceptance ([RH] introduction: the verifier accepts the correct
 # prefix; [E4] "EAGLE-4 overview": longest agreeing path plus one bonus token).
 # ---------------------------------------------------------------------------
