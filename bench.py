@@ -167,6 +167,34 @@ def train_leg(steps, warmup):
     }
 
 
+def chain_leg(drafter, inp, K, steps, parallel_ms):
+    """The sequential drafter the parallel one replaces, on the same kernels:
+    K one-row cache extensions per sequence (each step's token and normalized
+    output feed the next), timed like the parallel forward on the same
+    workload."""
+    import torch
+    from drafting_eagle_draft_amd import runner
+
+    ch = runner.Eagle3Chain(drafter, inp, K)
+    for _ in range(3):
+        ch.launch(drafter)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        ch.launch(drafter)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    B = ch.B
+    del ch
+    torch.cuda.empty_cache()
+    return {"steps": steps, "ms_per_chain": ms, "ms_per_draft_step": ms / K,
+            "value": B * K / (ms * 1e-3), "unit": "draft tokens/s",
+            "parallel_speedup": ms / parallel_ms,
+            "launch": "eager, one stream, K sequential pe_draft_extend calls"}
+
+
 def traffic_from_counters(lm_launch_bytes):
     """HBM bytes per LM-head launch from the committed rocprofv3 PMC summary,
     or None when missing or taken on a different kernel source."""
@@ -194,6 +222,9 @@ def main():
     ap.add_argument("--train-only", action="store_true",
                     help="run only the training-shape forward leg (its own JSON line)")
     ap.add_argument("--train-steps", type=int, default=5)
+    ap.add_argument("--no-chain", action="store_true",
+                    help="skip the autoregressive EAGLE-3 chain leg")
+    ap.add_argument("--chain-steps", type=int, default=20)
     ap.add_argument("--print-kernel-sha", action="store_true",
                     help="print the LM-head kernel source hash and exit")
     a = ap.parse_args()
@@ -301,6 +332,9 @@ def main():
     if graph_ms is not None:
         out["graph_ms_per_step"] = graph_ms
         out["graph_value"] = B * K / (graph_ms * 1e-3)
+    if not a.no_chain:
+        print("[bench] autoregressive EAGLE-3 chain", file=sys.stderr, flush=True)
+        out["eagle3_chain"] = chain_leg(drafter, inp, K, a.chain_steps, ms)
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, w, inp)

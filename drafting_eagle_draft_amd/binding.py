@@ -23,12 +23,15 @@ PE_F32 = 0
 PE_BF16 = 1
 PE_K_MAX = 16
 PE_DECODE_ROWS_MAX = 64
+PE_INPUT_TARGET = 0
+PE_INPUT_DRAFTER = 1
 
 EXPORTS = (
     "pe_model_create", "pe_model_destroy", "pe_draft_workspace_size", "pe_workspace_init",
     "pe_draft_forward", "pe_accept", "pe_last_error", "pe_version", "pe_profile_enable",
     "pe_profile_read", "pe_mask_create", "pe_mask_destroy", "pe_mask_materialize",
     "pe_train_workspace_size", "pe_train_forward", "pe_cod_rows", "pe_partition",
+    "pe_draft_extend",
 )
 
 
@@ -89,6 +92,8 @@ def load(path: str = LIB_PATH):
         "pe_train_forward": [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp],
         "pe_cod_rows": [i32, i32, ctypes.c_double, ctypes.c_double, vp, vp, ctypes.POINTER(i32)],
         "pe_partition": [i32, i32, i32, vp, i32, vp],
+        "pe_draft_extend": [vp, i32, i32, i32, vp, i32, vp, vp, i32, i64, ctypes.POINTER(vp),
+                            ctypes.POINTER(vp), vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -156,6 +161,21 @@ def pe_draft_forward(model: int, N: int, B: int, K: int, hidden3: int, token_ids
         ctypes.cast(kc, ctypes.POINTER(ctypes.c_void_p)) if kc is not None else None,
         ctypes.cast(vc, ctypes.POINTER(ctypes.c_void_p)) if vc is not None else None,
         draft_out, logits_out, workspace, ws_bytes, stream))
+
+
+def pe_draft_extend(model: int, N: int, B: int, T: int, inputs: int, input_kind: int, token_ids: int,
+                    ctx_lens: int, pos_offset: int, ctx_stride: int, k_cache, v_cache,
+                    draft_out: int | None, logits_out: int | None, z_out: int | None,
+                    workspace: int, ws_bytes: int, stream: int = 0) -> None:
+    """k_cache / v_cache: sequences of N device pointers; the block's keys and
+    values are appended at positions ctx_lens[b] + pos_offset + t."""
+    kc = _ptr_array(list(k_cache)) if k_cache is not None else None
+    vc = _ptr_array(list(v_cache)) if v_cache is not None else None
+    _check("pe_draft_extend", load().pe_draft_extend(
+        model, N, B, T, inputs, input_kind, token_ids, ctx_lens, pos_offset, ctx_stride,
+        ctypes.cast(kc, ctypes.POINTER(ctypes.c_void_p)) if kc is not None else None,
+        ctypes.cast(vc, ctypes.POINTER(ctypes.c_void_p)) if vc is not None else None,
+        draft_out, logits_out, z_out, workspace, ws_bytes, stream))
 
 
 def pe_accept(B: int, K: int, draft: int, target: int, accept_len: int,

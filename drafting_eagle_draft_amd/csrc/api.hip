@@ -179,6 +179,7 @@ WsLayout layout(const pe_model *m, int B, int K, long C) {
     }
   };
   upd(m->fc, B + 1, nf_fc, false);
+  upd(m->fc, M, nf, false);  // cache extension: one fc row per block row
   for (const LayerT &L : m->layers) {
     upd(L.qkv, M, nf, false); upd(L.o, M, nf, false); upd(L.gateup, M, nf, false); upd(L.down, M, nf, false);
   }
@@ -315,6 +316,158 @@ pe_status check_train_shape(const pe_model *m, const pe_mask *mask, int32_t n, i
   if (L < 1 || (long)L > (long)n * K || L > kTrainRowsMax)
     return fail(PE_ERR_INVALID_ARGUMENT, "L=%d outside [1, min(n*K=%ld, %ld)]", L, (long)n * K,
                 kTrainRowsMax);
+  return PE_OK;
+}
+
+// The layered forward of a block of K rows per sequence: input fusion (the
+// parallel drafter's NTP + MTP rows, or cache-extension rows with their own
+// inputs), N decoder layers, final norm, LM head with argmax.
+enum DraftMode : int { DRAFT_PARALLEL = 0, EXTEND_TARGET = 1, EXTEND_DRAFTER = 2 };
+
+struct DraftCall {
+  int N, B, K, mode;
+  const void *in;            // [B,3H] (parallel), [B,K,3H] (extend, target), fp32 [B,K,H] (extend, drafter)
+  const int32_t *tok;        // [B] (parallel) or [B,K]
+  const void *mask_emb, *h_shared;
+  const int32_t *ctx_lens;
+  int64_t C;
+  int pos_off;
+  const void *const *kc, *const *vc;
+  void *const *kc_out, *const *vc_out;  // extend: caches to append to (or NULL)
+  int32_t *draft_out;
+  float *logits_out, *z_out;
+};
+
+pe_status enqueue_draft(const pe_model *m, const WsLayout &W, const DraftCall &d, char *ws, hipStream_t s) {
+  const pe_config &c = m->cfg;
+  const int N = d.N, B = d.B, K = d.K;
+  const int64_t ctx_stride = d.C;
+  float *xres = reinterpret_cast<float *>(ws + W.xres);
+  void *xg = ws + W.xg;
+  float *ssq = reinterpret_cast<float *>(ws + W.ssq);
+  const int M = B * K;
+  const int nf = (M + 15) / 16;
+  const int H = c.hidden, hd = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const int G = nq / nkv;
+
+  GemmParams base{};
+  base.part = reinterpret_cast<floatx4 *>(ws + W.gpart);
+  base.H = H;
+  base.Kb = K;
+  base.B = B;
+  base.eps = c.rms_eps;
+  base.inv_width = 1.0f / (float)H;
+
+  int lm_blocks = 0;
+  auto run = [&](const Tiled &t, int epi, int nfr, GemmParams p) -> pe_status {
+    const int Mv = p.act_rows + (p.act_extra ? 1 : 0);
+    const GemmPlan pl = plan_gemm(m, t, Mv, nfr);
+    p.wt = t.ptr; p.wbytes = (unsigned)((size_t)t.NT * t.KT * 1024); p.NT = t.NT; p.KT = t.KT;
+    p.N = t.N; p.K = t.K;
+    p.epi = epi; p.KS = pl.KS; p.kc = pl.kc; p.nkw = pl.nkw; p.Mv = Mv;
+    lm_blocks = pl.KS > 1 ? (t.NT + 3) / 4 : pl.L.grid;
+    hipError_t e = launch_gemm(c.dtype, nfr, p, pl.L, s);
+    if (e != hipSuccess) return hip_fail(e, "GEMM launch");
+    return PE_OK;
+  };
+
+  pe_status st;
+  const float *g0 = N > 0 ? m->layers[0].attn_norm : m->final_norm;
+  if (d.mode == DRAFT_PARALLEL) {
+    // Input fusion: fc over the B hidden rows plus h_shared, then embeddings.
+    GemmParams p = base;
+    p.act = d.in; p.act_ld = 3L * H; p.act_rows = B; p.act_extra = d.h_shared;
+    p.M = B + 1;
+    p.xres = xres; p.xg = xg; p.ssq_out = ssq;
+    p.gnext = g0;
+    p.embed = m->embed; p.tok = d.tok; p.mask_emb = d.mask_emb; p.V = c.vocab;
+    if ((st = run(m->fc, EPI_FC, (B + 1 + 15) / 16, p)) != PE_OK) return st;
+  } else if (d.mode == EXTEND_TARGET) {
+    // Every block row has its own token and target hidden state.
+    GemmParams p = base;
+    p.act = d.in; p.act_ld = 3L * H; p.act_rows = M;
+    p.M = M; p.fc_direct = 1;
+    p.xres = xres; p.xg = xg; p.ssq_out = ssq;
+    p.gnext = g0;
+    p.embed = m->embed; p.tok = d.tok; p.V = c.vocab;
+    if ((st = run(m->fc, EPI_FC, nf, p)) != PE_OK) return st;
+  } else {
+    // Rows fed back from the drafter: x = E[token] + z.
+    hipError_t e = launch_fuse_feedback(c.dtype, reinterpret_cast<const float *>(d.in), m->embed, d.tok, M, H,
+                                        c.vocab, g0, xres, xg, ssq, s);
+    if (e != hipSuccess) return hip_fail(e, "feedback fusion launch");
+  }
+  for (int l = 0; l < N; ++l) {
+    const LayerT &L = m->layers[l];
+    {
+      GemmParams p = base;
+      p.act = xg; p.act_ld = H; p.act_rows = M; p.M = M;
+      p.ssq = ssq; p.ssq_strips = H / 16;
+      p.q = ws + W.q; p.kb = ws + W.kb; p.vb = ws + W.vb;
+      p.ctx_lens = d.ctx_lens; p.inv_freq = m->inv_freq;
+      p.nq = nq; p.nkv = nkv; p.hd = hd; p.RP = W.RP;
+      p.C = ctx_stride; p.pos_off = d.pos_off;
+      if (d.kc_out) { p.kc_out = d.kc_out[l]; p.vc_out = d.vc_out[l]; }
+      if ((st = run(L.qkv, EPI_QKV, nf, p)) != PE_OK) return st;
+    }
+    {
+      AttnParams a{};
+      a.q = ws + W.q; a.kb = ws + W.kb; a.vb = ws + W.vb;
+      a.kc = d.kc[l]; a.vc = d.vc[l];
+      a.ctx_lens = d.ctx_lens; a.C = ctx_stride; a.ctx_off = d.pos_off;
+      a.B = B; a.Kb = K; a.nq = nq; a.nkv = nkv; a.hd = hd; a.G = G; a.R = K * G; a.RP = W.RP;
+      a.L = W.ap.L; a.S = W.ap.S;
+      a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+      a.out = ws + W.attn_out;
+      a.part = reinterpret_cast<float *>(ws + W.apart);
+      hipError_t e = launch_attention(c.dtype, a, s);
+      if (e != hipSuccess) return hip_fail(e, "attention launch");
+    }
+    {
+      GemmParams p = base;
+      p.act = ws + W.attn_out; p.act_ld = (long)nq * hd; p.act_rows = M; p.M = M;
+      p.xres = xres; p.xg = xg; p.ssq_out = ssq; p.gnext = L.mlp_norm;
+      if ((st = run(L.o, EPI_RESID, nf, p)) != PE_OK) return st;
+    }
+    {
+      GemmParams p = base;
+      p.act = xg; p.act_ld = H; p.act_rows = M; p.M = M;
+      p.ssq = ssq; p.ssq_strips = H / 16;
+      p.hout = ws + W.mlp_h; p.I = c.intermediate;
+      if ((st = run(L.gateup, EPI_SWIGLU, nf, p)) != PE_OK) return st;
+    }
+    {
+      GemmParams p = base;
+      p.act = ws + W.mlp_h; p.act_ld = c.intermediate; p.act_rows = M; p.M = M;
+      p.xres = xres; p.xg = xg; p.ssq_out = ssq;
+      p.gnext = (l + 1 < N) ? m->layers[l + 1].attn_norm : m->final_norm;
+      if ((st = run(L.down, EPI_RESID, nf, p)) != PE_OK) return st;
+    }
+  }
+  // LM head with fused argmax (skipped when neither tokens nor logits are wanted).
+  if (d.draft_out || d.logits_out) {
+    GemmParams p = base;
+    p.act = xg; p.act_ld = H; p.act_rows = M; p.M = M;
+    p.ssq = ssq; p.ssq_strips = H / 16;
+    p.logits = d.logits_out;
+    p.blk_best = reinterpret_cast<unsigned long long *>(ws + W.blk);
+    p.V = c.vocab;
+    const bool prof = m->prof && m->nrec < (int)m->ev0.size();
+    if (prof) (void)hipEventRecord(m->ev0[m->nrec], s);
+    if ((st = run(m->lm, EPI_ARGMAX, nf, p)) != PE_OK) return st;
+    if (prof) {
+      (void)hipEventRecord(m->ev1[m->nrec], s);
+      ++m->nrec;
+    }
+    if (d.draft_out) {
+      hipError_t e = launch_argmax_final(p.blk_best, lm_blocks, M, d.draft_out, s);
+      if (e != hipSuccess) return hip_fail(e, "argmax launch");
+    }
+  }
+  if (d.z_out) {
+    hipError_t e = launch_norm_rows(xres, m->final_norm, ssq, M, H, c.rms_eps, d.z_out, s);
+    if (e != hipSuccess) return hip_fail(e, "final norm launch");
+  }
   return PE_OK;
 }
 
@@ -471,113 +624,58 @@ pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K, c
   if (ws_bytes < W.total)
     return fail(PE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char *ws = reinterpret_cast<char *>(workspace);
-  float *xres = reinterpret_cast<float *>(ws + W.xres);
-  void *xg = ws + W.xg;
-  float *ssq = reinterpret_cast<float *>(ws + W.ssq);
-  const int M = B * K;
-  const int nf = (M + 15) / 16;
-  const int H = c.hidden, hd = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
-  const int G = nq / nkv;
+  DraftCall d{};
+  d.N = N; d.B = B; d.K = K; d.mode = DRAFT_PARALLEL;
+  d.in = hidden3; d.tok = token_ids; d.mask_emb = mask_emb; d.h_shared = h_shared;
+  d.ctx_lens = ctx_lens; d.C = ctx_stride; d.pos_off = 0;
+  d.kc = k_cache; d.vc = v_cache;
+  d.draft_out = draft_out; d.logits_out = logits_out;
+  return enqueue_draft(m, W, d, reinterpret_cast<char *>(workspace), reinterpret_cast<hipStream_t>(stream));
+}
 
-  GemmParams base{};
-  base.part = reinterpret_cast<floatx4 *>(ws + W.gpart);
-  base.H = H;
-  base.Kb = K;
-  base.B = B;
-  base.eps = c.rms_eps;
-  base.inv_width = 1.0f / (float)H;
-
-  int lm_blocks = 0;
-  auto run = [&](const Tiled &t, int epi, int nfr, GemmParams p) -> pe_status {
-    const int Mv = p.act_rows + (p.act_extra ? 1 : 0);
-    const GemmPlan pl = plan_gemm(m, t, Mv, nfr);
-    p.wt = t.ptr; p.wbytes = (unsigned)((size_t)t.NT * t.KT * 1024); p.NT = t.NT; p.KT = t.KT;
-    p.N = t.N; p.K = t.K;
-    p.epi = epi; p.KS = pl.KS; p.kc = pl.kc; p.nkw = pl.nkw; p.Mv = Mv;
-    lm_blocks = pl.KS > 1 ? (t.NT + 3) / 4 : pl.L.grid;
-    hipError_t e = launch_gemm(c.dtype, nfr, p, pl.L, s);
-    if (e != hipSuccess) return hip_fail(e, "GEMM launch");
-    return PE_OK;
-  };
-
-  pe_status st;
-  // Input fusion: fc over the B hidden rows plus h_shared, then embeddings.
-  {
-    GemmParams p = base;
-    p.act = hidden3; p.act_ld = 3L * H; p.act_rows = B; p.act_extra = h_shared;
-    p.M = B + 1;
-    p.xres = xres; p.xg = xg; p.ssq_out = ssq;
-    p.gnext = N > 0 ? m->layers[0].attn_norm : m->final_norm;
-    p.embed = m->embed; p.tok = token_ids; p.mask_emb = mask_emb; p.V = c.vocab;
-    if ((st = run(m->fc, EPI_FC, (B + 1 + 15) / 16, p)) != PE_OK) return st;
-  }
-  for (int l = 0; l < N; ++l) {
-    const LayerT &L = m->layers[l];
-    {
-      GemmParams p = base;
-      p.act = xg; p.act_ld = H; p.act_rows = M; p.M = M;
-      p.ssq = ssq; p.ssq_strips = H / 16;
-      p.q = ws + W.q; p.kb = ws + W.kb; p.vb = ws + W.vb;
-      p.ctx_lens = ctx_lens; p.inv_freq = m->inv_freq;
-      p.nq = nq; p.nkv = nkv; p.hd = hd; p.RP = W.RP;
-      p.C = ctx_stride;
-      if ((st = run(L.qkv, EPI_QKV, nf, p)) != PE_OK) return st;
-    }
-    {
-      AttnParams a{};
-      a.q = ws + W.q; a.kb = ws + W.kb; a.vb = ws + W.vb;
-      a.kc = k_cache[l]; a.vc = v_cache[l];
-      a.ctx_lens = ctx_lens; a.C = ctx_stride;
-      a.B = B; a.Kb = K; a.nq = nq; a.nkv = nkv; a.hd = hd; a.G = G; a.R = K * G; a.RP = W.RP;
-      a.L = W.ap.L; a.S = W.ap.S;
-      a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
-      a.out = ws + W.attn_out;
-      a.part = reinterpret_cast<float *>(ws + W.apart);
-      hipError_t e = launch_attention(c.dtype, a, s);
-      if (e != hipSuccess) return hip_fail(e, "attention launch");
-    }
-    {
-      GemmParams p = base;
-      p.act = ws + W.attn_out; p.act_ld = (long)nq * hd; p.act_rows = M; p.M = M;
-      p.xres = xres; p.xg = xg; p.ssq_out = ssq; p.gnext = L.mlp_norm;
-      if ((st = run(L.o, EPI_RESID, nf, p)) != PE_OK) return st;
-    }
-    {
-      GemmParams p = base;
-      p.act = xg; p.act_ld = H; p.act_rows = M; p.M = M;
-      p.ssq = ssq; p.ssq_strips = H / 16;
-      p.hout = ws + W.mlp_h; p.I = c.intermediate;
-      if ((st = run(L.gateup, EPI_SWIGLU, nf, p)) != PE_OK) return st;
-    }
-    {
-      GemmParams p = base;
-      p.act = ws + W.mlp_h; p.act_ld = c.intermediate; p.act_rows = M; p.M = M;
-      p.xres = xres; p.xg = xg; p.ssq_out = ssq;
-      p.gnext = (l + 1 < N) ? m->layers[l + 1].attn_norm : m->final_norm;
-      if ((st = run(L.down, EPI_RESID, nf, p)) != PE_OK) return st;
+pe_status pe_draft_extend(const pe_model *m, int32_t N, int32_t B, int32_t T, const void *inputs,
+                          int32_t input_kind, const int32_t *token_ids, const int32_t *ctx_lens,
+                          int32_t pos_offset, int64_t ctx_stride, void *const *k_cache, void *const *v_cache,
+                          int32_t *draft_out, float *logits_out, float *z_out, void *workspace, size_t ws_bytes,
+                          void *stream) {
+  if (!m) return fail(PE_ERR_INVALID_ARGUMENT, "model is NULL");
+  const pe_config &c = m->cfg;
+  if (N < 0 || N > c.n_layers)
+    return fail(PE_ERR_INVALID_ARGUMENT, "N=%d outside [0, n_layers=%d]", N, c.n_layers);
+  if (B < 1 || T < 1 || T > PE_K_MAX || B * T > PE_DECODE_ROWS_MAX)
+    return fail(PE_ERR_UNSUPPORTED, "B=%d T=%d outside 1<=T<=%d, B*T<=%d", B, T, PE_K_MAX, PE_DECODE_ROWS_MAX);
+  if (input_kind != PE_INPUT_TARGET && input_kind != PE_INPUT_DRAFTER)
+    return fail(PE_ERR_INVALID_ARGUMENT, "input_kind %d is neither PE_INPUT_TARGET nor PE_INPUT_DRAFTER",
+                input_kind);
+  if (!inputs || !token_ids) return fail(PE_ERR_INVALID_ARGUMENT, "inputs and token_ids must be non-NULL");
+  if (pos_offset < 0 || ctx_stride < 1)
+    return fail(PE_ERR_INVALID_ARGUMENT, "pos_offset must be >= 0 and ctx_stride >= 1");
+  if (N > 0) {
+    if (!ctx_lens || !k_cache || !v_cache)
+      return fail(PE_ERR_INVALID_ARGUMENT, "ctx_lens, k_cache and v_cache must be non-NULL when N > 0");
+    for (int l = 0; l < N; ++l) {
+      if (!k_cache[l] || !v_cache[l])
+        return fail(PE_ERR_INVALID_ARGUMENT, "cache pointer of layer %d is NULL", l);
+      if (misaligned(k_cache[l]) || misaligned(v_cache[l]))
+        return fail(PE_ERR_INVALID_ARGUMENT, "cache pointer of layer %d is not 16-byte aligned", l);
     }
   }
-  // LM head with fused argmax.
-  {
-    GemmParams p = base;
-    p.act = xg; p.act_ld = H; p.act_rows = M; p.M = M;
-    p.ssq = ssq; p.ssq_strips = H / 16;
-    p.logits = logits_out;
-    p.blk_best = reinterpret_cast<unsigned long long *>(ws + W.blk);
-    p.V = c.vocab;
-    const bool prof = m->prof && m->nrec < (int)m->ev0.size();
-    if (prof) (void)hipEventRecord(m->ev0[m->nrec], s);
-    if ((st = run(m->lm, EPI_ARGMAX, nf, p)) != PE_OK) return st;
-    if (prof) {
-      (void)hipEventRecord(m->ev1[m->nrec], s);
-      ++m->nrec;
-    }
-    hipError_t e = launch_argmax_final(p.blk_best, lm_blocks, M, draft_out, s);
-    if (e != hipSuccess) return hip_fail(e, "argmax launch");
-  }
-  return PE_OK;
+  if (misaligned(inputs) || (logits_out && misaligned(logits_out)) || (z_out && misaligned(z_out)) ||
+      misaligned(workspace))
+    return fail(PE_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  if (!workspace) return fail(PE_ERR_WORKSPACE, "workspace is NULL");
+  const WsLayout W = layout(m, B, T, ctx_stride);
+  if (ws_bytes < W.total)
+    return fail(PE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
+  DraftCall d{};
+  d.N = N; d.B = B; d.K = T; d.mode = input_kind == PE_INPUT_TARGET ? EXTEND_TARGET : EXTEND_DRAFTER;
+  d.in = inputs; d.tok = token_ids;
+  d.ctx_lens = ctx_lens; d.C = ctx_stride; d.pos_off = pos_offset;
+  d.kc = reinterpret_cast<const void *const *>(k_cache);
+  d.vc = reinterpret_cast<const void *const *>(v_cache);
+  d.kc_out = k_cache; d.vc_out = v_cache;
+  d.draft_out = draft_out; d.logits_out = logits_out; d.z_out = z_out;
+  return enqueue_draft(m, W, d, reinterpret_cast<char *>(workspace), reinterpret_cast<hipStream_t>(stream));
 }
 
 pe_status pe_accept(int32_t B, int32_t K, const int32_t *draft, const int32_t *target,

@@ -68,7 +68,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {
   // blockIdx.y = kv head * QP + query partition (64 query rows each).
   const int QP = (p.RP + 63) / 64;
   const int split = blockIdx.x, gk = blockIdx.y / QP, qp = blockIdx.y - gk * QP, b = blockIdx.z;
-  const int ctx = min(max(p.ctx_lens[b], 0), (int)p.C);  // out-of-range lengths are clamped
+  // out-of-range lengths are clamped
+  const int ctx = min(max(p.ctx_lens[b], 0) + p.ctx_off, (int)p.C);
   const int total = ctx + p.Kb;
   const int Sb = (total + p.L - 1) / p.L;
   if (split >= Sb) return;
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p) {
   const int bgq = blockIdx.x >> 2, qgrp = blockIdx.x & 3;
   const int b = bgq / (p.nkv * QP), rem = bgq - b * (p.nkv * QP);
   const int gk = rem / QP, qp = rem - gk * QP;
-  const int ctx = min(max(p.ctx_lens[b], 0), (int)p.C);
+  const int ctx = min(max(p.ctx_lens[b], 0) + p.ctx_off, (int)p.C);
   const int Sb = (ctx + p.Kb + p.L - 1) / p.L;
   if (Sb <= 1 || 64 * qp + 16 * qgrp >= p.RP) return;  // uniform: the split kernel wrote it
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;

@@ -73,6 +73,31 @@ __device__ void epi_fc(const GemmParams &p, int s, int lane, const floatx4 (&res
   float gn[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) gn[r] = p.gnext[n0 + r];
+  if (p.fc_direct) {
+    // Cache extension rows: activation row m is block row m, token tok[m].
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int m = 16 * f + c16;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (m < p.M) {
+        float e[4];
+        const int tok = min(max(p.tok[m], 0), p.V - 1);  // out-of-range ids are clamped
+        load4<T>(reinterpret_cast<const T *>(p.embed) + (long)tok * H + n0, e);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = e[r] + res[f][r];
+      }
+      const float sq = sum_groups(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]);
+      if (m < p.M) {
+        float xgv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xgv[r] = v[r] * gn[r];
+        store4<float>(p.xres + (long)m * H + n0, v);
+        store4<T>(reinterpret_cast<T *>(p.xg) + (long)m * H + n0, xgv);
+        if (g == 0) p.ssq_out[s * kMaxRows + m] = sq;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const int m = 16 * f + c16;
@@ -124,15 +149,20 @@ __device__ void epi_qkv(const GemmParams &p, int s, int lane, const floatx4 (&re
     const int m = 16 * f + c16;
     if (m >= p.M) continue;
     const int b = m / p.Kb, kp = m - b * p.Kb;
+    // Block row kp sits at position C_b + off + kp (C_b + off clamped to C);
+    // with a cache to extend, its rotated key and its value are also written
+    // at that position when it lies inside the cache.
+    const int pos = min(max(p.ctx_lens[b], 0) + p.pos_off, (int)p.C) + kp;
     if (hh < p.nq + p.nkv) {
-      const int pos = min(max(p.ctx_lens[b], 0), (int)p.C) + kp;
-      T *dst;
+      T *dst, *dst2 = nullptr;
       if (hh < p.nq) {
         const int gk = hh / G, hl = hh - gk * G;
         dst = reinterpret_cast<T *>(p.q) + ((long)(b * p.nkv + gk) * p.RP + kp * G + hl) * hd;
       } else {
         const int gk = hh - p.nq;
         dst = reinterpret_cast<T *>(p.kb) + ((long)(b * p.nkv + gk) * p.Kb + kp) * hd;
+        if (p.kc_out && pos < p.C)
+          dst2 = reinterpret_cast<T *>(p.kc_out) + ((long)(b * p.nkv + gk) * p.C + pos) * hd;
       }
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
@@ -140,14 +170,21 @@ __device__ void epi_qkv(const GemmParams &p, int s, int lane, const floatx4 (&re
         float c, sn;
         rope_cs(pos, p.inv_freq[i], c, sn);
         const float lo = res[f][2 * pp], hi = res[f][2 * pp + 1];
-        dst[i] = from_f32<T>(lo * c - hi * sn);
-        dst[i + half] = from_f32<T>(hi * c + lo * sn);
+        const T a = from_f32<T>(lo * c - hi * sn), bb = from_f32<T>(hi * c + lo * sn);
+        dst[i] = a;
+        dst[i + half] = bb;
+        if (dst2) {
+          dst2[i] = a;
+          dst2[i + half] = bb;
+        }
       }
     } else {
       const int gk = hh - p.nq - p.nkv;
       T *dst = reinterpret_cast<T *>(p.vb) + ((long)(b * p.nkv + gk) * p.Kb + kp) * hd + within;
       float v[4] = {res[f][0], res[f][1], res[f][2], res[f][3]};
       store4<T>(dst, v);
+      if (p.vc_out && pos < p.C)
+        store4<T>(reinterpret_cast<T *>(p.vc_out) + ((long)(b * p.nkv + gk) * p.C + pos) * hd + within, v);
     }
   }
 }

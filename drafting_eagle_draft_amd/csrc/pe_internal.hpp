@@ -62,12 +62,16 @@ struct GemmParams {
   int Kb;               // block length K (also QKV)
   int B;                // sequences
   const void *embed;    // [V][H]
-  const int *tok;       // [B]
+  const int *tok;       // [B], or [M] when fc_direct
   const void *mask_emb; // [H]
+  int fc_direct;        // every activation row m is block row m (cache extension rows)
   // QKV
   void *q, *kb, *vb;
   const int *ctx_lens;  // clamped to [0, C] on use
   long C;               // cache position stride
+  int pos_off;          // added to every context length (cache extension steps)
+  void *kc_out, *vc_out;  // when non-null: rotated k and v of the block rows appended to the
+                          // cache [B][nkv][C][hd] at their positions (< C)
   const double *inv_freq;
   int nq, nkv, hd, RP;
   // SWIGLU
@@ -109,6 +113,7 @@ struct AttnParams {
   const void *kc, *vc;  // [B][nkv][C][hd]
   const int *ctx_lens;  // [B]
   long C;               // ctx_stride
+  int ctx_off;          // added to every context length (cache extension steps)
   int B, Kb, nq, nkv, hd, G, R, RP;
   int L;                // keys per split (multiple of 64)
   int S;                // max splits per (b, kv head)
@@ -118,6 +123,16 @@ struct AttnParams {
 };
 
 hipError_t launch_attention(int dtype, const AttnParams &p, hipStream_t s);
+
+// Cache extension fed back from the drafter: x = E[tok] + z for M rows (z
+// fp32 [M][H]); writes x (fp32), x * gnext (dtype) and per-strip sums of
+// squares as the input-fusion epilogue does.
+hipError_t launch_fuse_feedback(int dtype, const float *z, const void *embed, const int *tok, int M, int H,
+                                int V, const float *gnext, float *xres, void *xg, float *ssq, hipStream_t s);
+// z[m] = RMSNorm(x[m]) * gain from x (fp32 [M][H]) and its per-strip sums of
+// squares ssq[H/16][kMaxRows].
+hipError_t launch_norm_rows(const float *x, const float *gain, const float *ssq, int M, int H, float eps,
+                            float *z, hipStream_t s);
 
 hipError_t launch_accept(int B, int K, const int *draft, const int *target, int *accept_len,
                          int *out_tokens, hipStream_t s);

@@ -100,6 +100,104 @@ class DecodeBuffers:
             self.ws.data_ptr(), self.ws.numel(), stream_handle() if stream is None else stream)
 
 
+def cache_with_room(cache, extra):
+    """Device copy of one layer's cache [B, nkv, C, hd] with `extra` more positions."""
+    B, nkv, C, hd = cache.shape
+    out = torch.zeros((B, nkv, C + extra, hd), dtype=cache.dtype, device=cache.device)
+    out[:, :, :C] = cache
+    return out
+
+
+class ExtendBuffers:
+    """One drafter-cache extension call (pe_draft_extend) on device buffers.
+
+    inputs: host array [B, T, 3H] (kind PE_INPUT_TARGET, dtype data) or
+    [B, T, H] fp32 (PE_INPUT_DRAFTER).  The caches (lists of device tensors
+    [B, nkv, C, hd]) are extended in place.
+    """
+
+    def __init__(self, drafter: Drafter, inputs, kind, token_ids, ctx_lens, k_cache, v_cache, N=None,
+                 pos_offset=0, want_draft=True, want_logits=True, want_z=True):
+        cfg, dev = drafter.cfg, drafter.device
+        self.N = cfg.n_layers if N is None else N
+        inputs = np.asarray(inputs)
+        self.B, self.T = inputs.shape[0], inputs.shape[1]
+        self.kind = kind
+        self.pos_offset = pos_offset
+        if kind == pe.PE_INPUT_TARGET:
+            self.inputs = to_device(inputs, cfg, dev)
+        else:
+            self.inputs = torch.from_numpy(np.ascontiguousarray(inputs, np.float32)).to(dev)
+        self.tok = torch.from_numpy(np.ascontiguousarray(token_ids, np.int32)).to(dev)
+        self.ctx_lens = torch.from_numpy(np.asarray(ctx_lens, np.int32)).to(dev)
+        self.k_cache, self.v_cache = list(k_cache)[:self.N], list(v_cache)[:self.N]
+        self.ctx_stride = int(self.k_cache[0].shape[2]) if self.N > 0 else 1
+        B, T = self.B, self.T
+        self.draft = torch.full((B, T), -1, dtype=torch.int32, device=dev) if want_draft else None
+        self.logits = (torch.empty((B, T, cfg.vocab), dtype=torch.float32, device=dev)
+                       if want_logits else None)
+        self.z = torch.empty((B, T, cfg.hidden), dtype=torch.float32, device=dev) if want_z else None
+        self.ws = drafter.workspace(B, T, self.ctx_stride)
+
+    def launch(self, drafter: Drafter, stream: int | None = None):
+        pe.pe_draft_extend(
+            drafter.handle, self.N, self.B, self.T, self.inputs.data_ptr(), self.kind, self.tok.data_ptr(),
+            self.ctx_lens.data_ptr(), self.pos_offset, self.ctx_stride,
+            [t.data_ptr() for t in self.k_cache], [t.data_ptr() for t in self.v_cache],
+            self.draft.data_ptr() if self.draft is not None else None,
+            self.logits.data_ptr() if self.logits is not None else None,
+            self.z.data_ptr() if self.z is not None else None,
+            self.ws.data_ptr(), self.ws.numel(), stream_handle() if stream is None else stream)
+
+
+class Eagle3Chain:
+    """The autoregressive EAGLE-3 drafter on the library's kernels: K
+    sequential one-row cache extensions per sequence.  Step 0 takes the new
+    token and the target hidden state; step j > 0 takes step j-1's draft
+    token and its final-norm output, at pos_offset j.  All steps are enqueued
+    on the device with no host synchronisation; caches get K spare positions."""
+
+    def __init__(self, drafter: Drafter, inp, K, N=None, want_logits=False):
+        cfg, dev = drafter.cfg, drafter.device
+        self.N = cfg.n_layers if N is None else N
+        self.K = K
+        self.B = B = int(len(inp["token_ids"]))
+        self.hidden3 = to_device(inp["hidden3"], cfg, dev)
+        self.tok0 = torch.from_numpy(np.asarray(inp["token_ids"], np.int32)).to(dev)
+        self.ctx_lens = torch.from_numpy(np.asarray(inp["ctx_lens"], np.int32)).to(dev)
+        C = int(inp["ctx_stride"])
+        self.k_cache = [cache_with_room(to_device(k, cfg, dev), K) for k in inp["k_cache"][:self.N]]
+        self.v_cache = [cache_with_room(to_device(v, cfg, dev), K) for v in inp["v_cache"][:self.N]]
+        self.ctx_stride = C + K
+        self.drafts = torch.full((K, B), -1, dtype=torch.int32, device=dev)
+        self.logits = (torch.empty((K, B, cfg.vocab), dtype=torch.float32, device=dev)
+                       if want_logits else None)
+        self.z = torch.empty((2, B, cfg.hidden), dtype=torch.float32, device=dev)
+        self.ws = drafter.workspace(B, 1, self.ctx_stride)
+
+    def launch(self, drafter: Drafter, stream: int | None = None):
+        s = stream_handle() if stream is None else stream
+        kc = [t.data_ptr() for t in self.k_cache]
+        vc = [t.data_ptr() for t in self.v_cache]
+        for j in range(self.K):
+            if j == 0:
+                inputs, kind, tok = self.hidden3.data_ptr(), pe.PE_INPUT_TARGET, self.tok0.data_ptr()
+            else:
+                inputs, kind = self.z[(j - 1) % 2].data_ptr(), pe.PE_INPUT_DRAFTER
+                tok = self.drafts[j - 1].data_ptr()
+            pe.pe_draft_extend(drafter.handle, self.N, self.B, 1, inputs, kind, tok, self.ctx_lens.data_ptr(), j,
+                               self.ctx_stride, kc, vc, self.drafts[j].data_ptr(),
+                               self.logits[j].data_ptr() if self.logits is not None else None,
+                               self.z[j % 2].data_ptr(), self.ws.data_ptr(), self.ws.numel(), s)
+
+    def result(self):
+        """(drafts [B, K], logits [B, K, V] or None) on host."""
+        torch.cuda.synchronize()
+        d = self.drafts.cpu().numpy().T.copy()
+        lg = self.logits.cpu().numpy().transpose(1, 0, 2).copy() if self.logits is not None else None
+        return d, lg
+
+
 def draft_forward(drafter: Drafter, inp, N=None, want_logits=False):
     """Run one forward; returns (draft [B,K] int32, logits [B,K,V] float32 or None) on host."""
     buf = DecodeBuffers(drafter, inp, N=N, want_logits=want_logits)

@@ -142,6 +142,52 @@ pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K,
                            void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Drafter-cache extension: T real rows per sequence ("Speeding LLM inference
+ * with P-EAGLE in vLLM Speculators", "Flex-attention mask": depth-0
+ * positions carry real tokens and real hidden states and attend causally to
+ * each other).  Two uses:
+ *   - after verification, the accepted tokens with their target hidden
+ *     states become drafter context (input_kind PE_INPUT_TARGET);
+ *   - the autoregressive EAGLE-3 drafter that P-EAGLE replaces ("P-EAGLE: A
+ *     Technical Deep Dive into Parallel Speculative Decoding", "Technical
+ *     Architecture: From Sequential to Parallel": K sequential passes for K
+ *     tokens): step 0 takes the new token and the target's hidden state,
+ *     step j > 0 takes step j-1's draft token and its final-norm output
+ *     (input_kind PE_INPUT_DRAFTER; "EAGLE-4", "EAGLE-4 overview": the
+ *     drafter feeds its normalized output back), with pos_offset = j.
+ *
+ *   N, B, T     layers (0..n_layers), sequences, rows per sequence;
+ *               1 <= T <= PE_K_MAX, B*T <= PE_DECODE_ROWS_MAX
+ *   inputs      device; PE_INPUT_TARGET: dtype [B, T, 3H] target hidden
+ *               states (row input E[token] + fc(h));
+ *               PE_INPUT_DRAFTER: fp32 [B, T, H] drafter states z (row
+ *               input E[token] + z)
+ *   token_ids   device int32 [B, T]
+ *   ctx_lens, pos_offset, ctx_stride
+ *               row t of sequence b sits at position P_b + t with
+ *               P_b = min(ctx_lens[b] + pos_offset, ctx_stride); it attends to
+ *               cache rows [0, P_b) and block rows 0..t
+ *   k_cache, v_cache
+ *               host arrays of N device pointers, layout as in
+ *               pe_draft_forward.  Read at [0, P_b) and WRITTEN at
+ *               [P_b, P_b + T): each row's rotated key and its value; rows at
+ *               positions >= ctx_stride are not written (the caller keeps
+ *               ctx_lens[b] + pos_offset + T <= ctx_stride)
+ *   draft_out   device int32 [B, T] argmax per row, or NULL
+ *   logits_out  device fp32 [B, T, V], or NULL (with draft_out NULL as well
+ *               the LM head is skipped)
+ *   z_out       device fp32 [B, T, H] final-norm output of each row, or NULL
+ *   workspace   as for pe_draft_forward with K = T
+ */
+#define PE_INPUT_TARGET 0
+#define PE_INPUT_DRAFTER 1
+pe_status pe_draft_extend(const pe_model *m, int32_t N, int32_t B, int32_t T, const void *inputs,
+                          int32_t input_kind, const int32_t *token_ids, const int32_t *ctx_lens,
+                          int32_t pos_offset, int64_t ctx_stride, void *const *k_cache, void *const *v_cache,
+                          int32_t *draft_out, float *logits_out, float *z_out, void *workspace, size_t ws_bytes,
+                          void *stream);
+
+/*
  * Greedy longest-prefix acceptance ("EAGLE-4", "EAGLE-4 overview";
  * "Speeding LLM inference with P-EAGLE in vLLM Speculators", introduction).
  *   draft       device int32 [B, K]

@@ -322,7 +322,8 @@ def draft_extend(w, cfg, inputs, input_kind, embed_rows, ctx_lens, k_cache, v_ca
     return linear(z.reshape(B * T, -1), w["lm_head"]).reshape(B, T, -1), z, k_new, v_new
 
 
-def eagle3_chain(w, cfg, hidden3, token_ids, ctx_lens, k_cache, v_cache, K, embed_lookup, N=None):
+def eagle3_chain(w, cfg, hidden3, token_ids, ctx_lens, k_cache, v_cache, K, embed_lookup, N=None,
+                 feed_tokens=None):
     """K autoregressive EAGLE-3 drafter steps per sequence (the sequential
     baseline P-EAGLE replaces).
 
@@ -332,6 +333,10 @@ def eagle3_chain(w, cfg, hidden3, token_ids, ctx_lens, k_cache, v_cache, K, embe
     keys and values join the cache before the next step.  embed_lookup(ids)
     returns the embedding rows of int ids.  The caller's caches are not
     modified.  Returns (drafts [B, K] int32, logits [B, K, V]).
+
+    feed_tokens: optional [B, K]; step j + 1 then takes feed_tokens[:, j]
+    instead of step j's own argmax (drafts still hold the argmaxes).  This
+    follows another chain whose near-tied argmax went the other way.
     """
     N = cfg.n_layers if N is None else N
     B = len(token_ids)
@@ -361,7 +366,7 @@ def eagle3_chain(w, cfg, hidden3, token_ids, ctx_lens, k_cache, v_cache, K, embe
             logits = np.zeros((B, K, lg.shape[-1]), dtype=F64)
         logits[:, j] = lg[:, 0]
         drafts[:, j] = argmax_lowest(lg[:, 0])
-        tok = drafts[:, j].astype(np.int64)
+        tok = (drafts[:, j] if feed_tokens is None else np.asarray(feed_tokens)[:, j]).astype(np.int64)
         inputs, kind = z, "drafter"
     return drafts, logits
 

@@ -73,8 +73,9 @@ def test_chain_of_one_step_equals_parallel_k1():
     np.testing.assert_array_equal(drafts, po.argmax_lowest(ref))
 
 
-def _brute_chain(w, cfg, hidden3, tok, C, kcache, vcache, K):
-    """Two or more EAGLE-3 steps for one sequence with explicit loops."""
+def _brute_chain(w, cfg, hidden3, tok, C, kcache, vcache, K, feed=None):
+    """Two or more EAGLE-3 steps for one sequence with explicit loops; step
+    j + 1 takes token feed[j] when feed is given, else step j's argmax."""
     H, nq, nkv, hd = cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
 
     def mv(W, v):
@@ -128,7 +129,7 @@ def _brute_chain(w, cfg, hidden3, tok, C, kcache, vcache, K):
         zf = norm(x, w["final_norm"])
         lg = mv(w["lm_head"], zf)
         out.append(lg)
-        d = int(np.argmax(lg))
+        d = int(np.argmax(lg)) if feed is None else int(feed[j])
         e = [float(t) for t in w["embed"][d]]
         x = [e[i] + zf[i] for i in range(H)]   # the next step's input: E[draft] + normalized output
     return np.array(out)
@@ -144,3 +145,24 @@ def test_chain_matches_brute_force_with_feedback():
                            [k[b] for k in inp["k_cache"]], [v[b] for v in inp["v_cache"]], K)
         np.testing.assert_allclose(lg[b], ref, rtol=0, atol=1e-9)
         np.testing.assert_array_equal(drafts[b], np.argmax(ref, axis=1))
+
+
+def test_chain_with_fed_tokens_matches_brute_force():
+    """feed_tokens replaces only the token of the next step: the state fed
+    back is still the step's own normalized output, and drafts stay argmaxes."""
+    cfg, w, inp = toy_problem(ctx_lens=[3, 6], tag="feed")
+    K = 3
+    feed = np.array([[7, 1, 0], [2, 9, 4]], dtype=np.int32) % cfg.vocab
+    drafts, lg = po.eagle3_chain(w, cfg, inp["hidden3"], inp["token_ids"], inp["ctx_lens"], inp["k_cache"],
+                                 inp["v_cache"], K, lambda ids: w["embed"][ids], feed_tokens=feed)
+    for b in range(2):
+        ref = _brute_chain(w, cfg, inp["hidden3"][b], int(inp["token_ids"][b]), int(inp["ctx_lens"][b]),
+                           [k[b] for k in inp["k_cache"]], [v[b] for v in inp["v_cache"]], K, feed=feed[b])
+        np.testing.assert_allclose(lg[b], ref, rtol=0, atol=1e-9)
+        np.testing.assert_array_equal(drafts[b], np.argmax(ref, axis=1))
+    # the fed tokens differ from the chain's own argmaxes, so steps 1.. differ
+    own, own_lg = po.eagle3_chain(w, cfg, inp["hidden3"], inp["token_ids"], inp["ctx_lens"], inp["k_cache"],
+                                  inp["v_cache"], K, lambda ids: w["embed"][ids])
+    assert not np.array_equal(own[:, :-1], feed[:, :-1])
+    np.testing.assert_allclose(lg[:, 0], own_lg[:, 0], rtol=0, atol=0)
+    assert np.max(np.abs(lg[:, 1:] - own_lg[:, 1:])) > 1e-6
