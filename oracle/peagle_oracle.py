@@ -551,8 +551,10 @@ def train_forward(w, cfg, hidden3, token_ids, mask_emb, h_shared, rows, K, N=Non
             x[i] = np.asarray(mask_emb, F64) + mtp
     # Keys each row may see: depth-0 rows of positions <= anchor, then the
     # row's own chain (depths 1..d at the same anchor).
+    # The depth-0 cells of positions up to the largest anchor must be present
+    # (a chunk of a sequence partition holds no depth-0 cells beyond it).
     index = {(int(P[i]), int(D[i])): i for i in range(L)}
-    depth0 = np.array([index[(p, 0)] for p in range(int(P.max()) + 1)]) if L else np.zeros(0, int)
+    depth0 = np.array([index[(p, 0)] for p in range(int((P - D).max()) + 1)]) if L else np.zeros(0, int)
     kv_out = []
     for l in range(N):
         lw = w["layers"][l]
@@ -581,3 +583,37 @@ def train_forward(w, cfg, hidden3, token_ids, mask_emb, h_shared, rows, K, N=Non
     if return_kv:
         return logits, kv_out
     return logits
+
+
+def chunk_cells(n, K, S, rows, s):
+    """Cells the forward of chunk s of a sequence partition runs on ([PN]
+    3.2): the depth-0 completion (every depth-0 cell of a position before
+    the end of segment s) joined with the chunk's own cells, ascending.
+    Returns (cells, own) with own the indices into ``rows`` of the chunk's
+    own cells, in the order they appear in ``cells``."""
+    rows = np.asarray(rows, dtype=np.int64)
+    chunk_of_row, _, completion = partition(n, K, S, rows)
+    own = np.nonzero(chunk_of_row == s)[0]
+    cells = np.union1d(np.asarray(completion[s], dtype=np.int64) * K, rows[own])
+    return cells, own
+
+
+def train_forward_partitioned(w, cfg, hidden3, token_ids, mask_emb, h_shared, rows, K, S, N=None):
+    """The training-shape forward run chunk by chunk ([PN] 3.2): each chunk
+    is a forward over its own cells plus its depth-0 completion, with no
+    state shared between chunks; the logits of each chunk's own cells are
+    placed at their rows.  Every cell belongs to exactly one chunk, so the
+    result has the shape of train_forward's."""
+    rows = np.asarray(rows, dtype=np.int64)
+    n = len(np.asarray(token_ids))
+    out = None
+    for s in range(S):
+        cells, own = chunk_cells(n, K, S, rows, s)
+        if len(own) == 0:
+            continue
+        lg = train_forward(w, cfg, hidden3, token_ids, mask_emb, h_shared, cells, K, N,
+                           lm_rows=np.searchsorted(cells, rows[own]))
+        if out is None:
+            out = np.zeros((len(rows), lg.shape[-1]), dtype=F64)
+        out[own] = lg
+    return out

@@ -5,8 +5,8 @@ import numpy as np
 def key_closure(rows, K, sample):
     """Kept rows that one layer of the sampled rows depends on: the sample,
     the depth-0 rows up to the largest sampled position (those up to the
-    largest anchor are keys; the oracle indexes depth-0 rows through the
-    last position) and each sampled row's chain.  Visibility depends only on (position, depth), so with one layer
+    largest anchor are keys) and each sampled row's chain.  Visibility
+    depends only on (position, depth), so with one layer
     the oracle over this chain-closed subset gives the sampled rows' exact
     results.  Returns (subset rows, indices of the sample in the subset)."""
     P, D = rows // K, rows % K

@@ -155,3 +155,66 @@ def test_key_closure_reproduces_sampled_rows():
     assert len(sub) < len(rows)
     part = po.train_forward(wr, cfg, hidden3, tok, mask_emb, h_shared, sub, K, lm_rows=lm)
     np.testing.assert_allclose(part, full[sample], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("S", [2, 3, 4, 7])
+def test_partitioned_forward_equals_whole_forward(S):
+    """Sequence partitioning ("P-EAGLE: Parallel-Drafting EAGLE with Scalable
+    Training", section 3.2): chunks that each recompute their depth-0
+    completion through every layer and share nothing give every cell the
+    logits of the unpartitioned forward (equal in exact arithmetic; two
+    layers, so the completion's own keys are recomputed too)."""
+    from tests.toy import toy_problem, toy_cfg
+    cfg, w, _ = toy_problem(toy_cfg(n_layers=2, K=5))
+    n, K = 23, 5
+    rng = np.random.default_rng(40 + S)
+    rows = po.cod_rows(po.cod_keep(n, K, rng.random((n, K)), r=0.8))
+    hidden3 = rng.standard_normal((n, 3 * cfg.hidden)).astype(np.float32)
+    tok = rng.integers(0, cfg.vocab, n)
+    wr = dict(w, embed_rows=w["embed"][tok])
+    mask_emb = rng.standard_normal(cfg.hidden).astype(np.float32) * 0.1
+    h_shared = rng.standard_normal(3 * cfg.hidden).astype(np.float32)
+    full = po.train_forward(wr, cfg, hidden3, tok, mask_emb, h_shared, rows, K)
+    part = po.train_forward_partitioned(wr, cfg, hidden3, tok, mask_emb, h_shared, rows, K, S)
+    np.testing.assert_allclose(part, full, rtol=0, atol=1e-10)
+    # Each chunk's cells: chain-closed, every depth-0 cell up to the largest
+    # anchor, own cells once over all chunks, and fewer cells than the whole.
+    seen = np.zeros(len(rows), dtype=int)
+    for s in range(S):
+        cells, own = po.chunk_cells(n, K, S, rows, s)
+        seen[own] += 1
+        cs = set(int(c) for c in cells)
+        amax = max(int(c) // K - int(c) % K for c in cells)
+        assert all(p * K in cs for p in range(amax + 1))
+        assert all((c - K - 1) in cs for c in cs if c % K >= 1)
+        if s < S - 1:
+            assert len(cells) < len(rows)
+    assert np.all(seen == 1)
+
+
+def test_partition_chunk_without_completion_differs():
+    """A chunk's segment run with no completion sees no earlier context.
+    Rotary attention depends on relative positions only, so running the
+    segment's depth-0 cells as a sequence of their own changes nothing but
+    the missing context, and their logits move: the completion is needed."""
+    from tests.toy import toy_problem, toy_cfg
+    cfg, w, _ = toy_problem(toy_cfg(n_layers=1, K=3))
+    n, K, S = 12, 3, 3
+    rows = np.array([p * K + d for p in range(n) for d in range(K) if p >= d], dtype=np.int64)
+    rng = np.random.default_rng(9)
+    hidden3 = rng.standard_normal((n, 3 * cfg.hidden)).astype(np.float32)
+    tok = rng.integers(0, cfg.vocab, n)
+    me, hs = np.zeros(cfg.hidden, np.float32), np.ones(3 * cfg.hidden, np.float32)
+    full = po.train_forward(dict(w, embed_rows=w["embed"][tok]), cfg, hidden3, tok, me, hs, rows, K)
+    _, bounds, _ = po.partition(n, K, S, rows)
+    b0, b1 = int(bounds[1]), int(bounds[2])
+    alone = po.train_forward(dict(w, embed_rows=w["embed"][tok[b0:b1]]), cfg, hidden3[b0:b1], tok[b0:b1],
+                             me, hs, np.arange(b1 - b0) * K, K)
+    ref = full[np.searchsorted(rows, np.arange(b0, b1) * K)]
+    # the first cell of the segment keeps its own key but loses all earlier ones
+    assert np.max(np.abs(alone - ref)) > 1e-3
+    # sanity of the relative-position claim: the whole sequence shifted by
+    # nothing reproduces itself through the same call pattern
+    again = po.train_forward(dict(w, embed_rows=w["embed"][tok[:b1]]), cfg, hidden3[:b1], tok[:b1], me, hs,
+                             np.arange(b1) * K, K)
+    np.testing.assert_allclose(again[b0:], ref, rtol=0, atol=1e-10)
