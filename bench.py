@@ -141,11 +141,27 @@ def train_leg(steps, warmup):
     ms = e0.elapsed_time(e1) / steps
     n_lm, lm_ms = pe.pe_profile_read(d.handle)
     pe.pe_profile_enable(d.handle, False)
+    del buf
+    # The same forward as S = 4 independent chunks, each recomputing its
+    # depth-0 completion (sequence partitioning); outputs identical.
+    S = 4
+    part = runner.PartitionedTrain(d, mask, inp, rows, S)
+    part.launch(d, mask)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        part.launch(d, mask)
+    e1.record()
+    torch.cuda.synchronize()
+    part_ms = e0.elapsed_time(e1) / steps
+    part_cells = part.cells_total
+    part_ws = part.ws.numel()
+    del part
     L = len(rows)
     f = train_flops(cfg, n, rows, K)
     achieved = f["total"] / (ms * 1e-3) / 1e12
     lm_tf = f["lm_head"] / (lm_ms * 1e-3) / 1e12 if lm_ms > 0 else None
-    del buf
+    whole_ws = pe.pe_train_workspace_size(d.handle, n, K, L)
     mask.close()
     d.close()
     torch.cuda.empty_cache()
@@ -164,6 +180,9 @@ def train_leg(steps, warmup):
                              "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                              "algorithmic_flops": f["total"], "gemm_flops": f["gemm"],
                              "attention_flops": f["attention"], "allowed_pairs": f["pairs"]},
+        "partitioned": {"S": S, "ms_per_step": part_ms, "cells_run": part_cells,
+                        "recompute_factor": part_cells / L, "value": L / (part_ms * 1e-3),
+                        "workspace_bytes": part_ws, "whole_workspace_bytes": whole_ws},
     }
 
 

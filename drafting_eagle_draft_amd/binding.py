@@ -31,7 +31,7 @@ EXPORTS = (
     "pe_draft_forward", "pe_accept", "pe_last_error", "pe_version", "pe_profile_enable",
     "pe_profile_read", "pe_mask_create", "pe_mask_destroy", "pe_mask_materialize",
     "pe_train_workspace_size", "pe_train_forward", "pe_cod_rows", "pe_partition",
-    "pe_draft_extend",
+    "pe_draft_extend", "pe_partition_chunk", "pe_train_forward_chunk",
 )
 
 
@@ -94,6 +94,10 @@ def load(path: str = LIB_PATH):
         "pe_partition": [i32, i32, i32, vp, i32, vp],
         "pe_draft_extend": [vp, i32, i32, i32, vp, i32, vp, vp, i32, i64, ctypes.POINTER(vp),
                             ctypes.POINTER(vp), vp, vp, vp, vp, sz, vp],
+        "pe_partition_chunk": [i32, i32, i32, i32, vp, i32, vp, vp, ctypes.POINTER(i32),
+                               ctypes.POINTER(i32), ctypes.POINTER(i32)],
+        "pe_train_forward_chunk": [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, vp,
+                                   vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -223,6 +227,15 @@ def pe_train_forward(model: int, mask: int, N: int, n: int, K: int, hidden3: int
         argmax_out, workspace, ws_bytes, stream))
 
 
+def pe_train_forward_chunk(model: int, mask: int, N: int, n: int, K: int, hidden3: int, token_ids: int,
+                           mask_emb: int, h_shared: int, cells: int, L: int, n_lead: int, out_rows: int | None,
+                           L_out: int, logits_out: int | None, argmax_out: int | None, workspace: int,
+                           ws_bytes: int, stream: int = 0) -> None:
+    _check("pe_train_forward_chunk", load().pe_train_forward_chunk(
+        model, mask, N, n, K, hidden3, token_ids, mask_emb, h_shared, cells, L, n_lead, out_rows, L_out,
+        logits_out, argmax_out, workspace, ws_bytes, stream))
+
+
 def pe_cod_rows(n: int, K: int, r: float, floor_rate: float, U):
     """Host COD sampling: U float64 array [n*K] -> int32 array of kept grid indices."""
     import numpy as np
@@ -243,3 +256,16 @@ def pe_partition(n: int, K: int, S: int, rows):
     out = np.empty(max(1, rows.size), dtype=np.int32)
     _check("pe_partition", load().pe_partition(n, K, S, rows.ctypes.data, rows.size, out.ctypes.data))
     return out[:rows.size].copy()
+
+
+def pe_partition_chunk(n: int, K: int, S: int, s: int, rows):
+    """Cells of chunk s -> (cells int32 [Lc], n_lead, out_rows int32 [Lc - n_lead], n_chunk)."""
+    import numpy as np
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    cells = np.empty(max(1, rows.size), dtype=np.int32)
+    out_rows = np.empty(max(1, rows.size), dtype=np.int32)
+    Lc, lead, nc = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check("pe_partition_chunk", load().pe_partition_chunk(
+        n, K, S, s, rows.ctypes.data, rows.size, cells.ctypes.data, out_rows.ctypes.data, ctypes.byref(Lc),
+        ctypes.byref(lead), ctypes.byref(nc)))
+    return cells[:Lc.value].copy(), lead.value, out_rows[:Lc.value - lead.value].copy(), nc.value

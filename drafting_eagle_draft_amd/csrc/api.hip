@@ -743,10 +743,19 @@ pe_status pe_train_workspace_size(const pe_model *m, int32_t n, int32_t K, int32
   return PE_OK;
 }
 
-pe_status pe_train_forward(const pe_model *m, const pe_mask *mask, int32_t N, int32_t n, int32_t K,
-                           const void *hidden3, const int32_t *token_ids, const void *mask_emb,
-                           const void *h_shared, const int32_t *rows, int32_t L, void *logits_out,
-                           int32_t *argmax_out, void *workspace, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The training-shape forward over L cells.  The first n_lead cells produce
+// no outputs; cell n_lead + i writes output row out_rows[i] (out_rows NULL:
+// cell i writes row i; targets outside [0, L_out) are dropped).  The LM head
+// starts at the 16-row group holding cell n_lead.
+pe_status enqueue_train(const pe_model *m, const pe_mask *mask, int32_t N, int32_t n, int32_t K,
+                        const void *hidden3, const int32_t *token_ids, const void *mask_emb,
+                        const void *h_shared, const int32_t *rows, int32_t L, int32_t n_lead,
+                        const int32_t *out_rows, int32_t L_out, void *logits_out, int32_t *argmax_out,
+                        void *workspace, size_t ws_bytes, void *stream) {
   pe_status st = check_train_shape(m, mask, n, K, L);
   if (st != PE_OK) return st;
   const pe_config &c = m->cfg;
@@ -835,12 +844,17 @@ pe_status pe_train_forward(const pe_model *m, const pe_mask *mask, int32_t N, in
   }
   if ((e = launch_rmsnorm_tiled(dt, xres, m->final_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
     return hip_fail(e, "RMSNorm launch");
-  {
+  if (n_lead < L && (logits_out || argmax_out)) {
+    // Rows before the 16-row group of cell n_lead are skipped; the group's
+    // earlier rows are computed but not written.
+    const int r0 = n_lead & ~15;
     TileGemmParams p{};
-    p.A = u; p.lda = H; p.M = L; p.a_tiled = 1;
+    p.A = reinterpret_cast<const char *>(u) + (size_t)(r0 >> 4) * m->lm.KT * 1024;
+    p.lda = H; p.M = L - r0; p.a_tiled = 1;
     p.logits = logits_out; p.ldc = c.vocab;
+    p.out_rows = out_rows; p.row_skip = n_lead - r0; p.out_M = L_out;
     p.keys = reinterpret_cast<unsigned long long *>(ws + W.keys);
-    if ((e = launch_zero(p.keys, (size_t)L * 8, s)) != hipSuccess) return hip_fail(e, "key reset launch");
+    if ((e = launch_zero(p.keys, (size_t)p.M * 8, s)) != hipSuccess) return hip_fail(e, "key reset launch");
     const bool prof = m->prof && m->nrec < (int)m->ev0.size();
     if (prof) (void)hipEventRecord(m->ev0[m->nrec], s);
     if ((st = gemm(m->lm, BEPI_LMHEAD, p)) != PE_OK) return st;
@@ -849,11 +863,37 @@ pe_status pe_train_forward(const pe_model *m, const pe_mask *mask, int32_t N, in
       ++m->nrec;
     }
     if (argmax_out) {
-      e = launch_argmax_rows(p.keys, L, argmax_out, s);
+      e = launch_argmax_rows(p.keys, p.M, argmax_out, out_rows, p.row_skip, L_out, s);
       if (e != hipSuccess) return hip_fail(e, "argmax launch");
     }
   }
   return PE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pe_status pe_train_forward(const pe_model *m, const pe_mask *mask, int32_t N, int32_t n, int32_t K,
+                           const void *hidden3, const int32_t *token_ids, const void *mask_emb,
+                           const void *h_shared, const int32_t *rows, int32_t L, void *logits_out,
+                           int32_t *argmax_out, void *workspace, size_t ws_bytes, void *stream) {
+  return enqueue_train(m, mask, N, n, K, hidden3, token_ids, mask_emb, h_shared, rows, L, 0, nullptr, L,
+                       logits_out, argmax_out, workspace, ws_bytes, stream);
+}
+
+pe_status pe_train_forward_chunk(const pe_model *m, const pe_mask *mask, int32_t N, int32_t n, int32_t K,
+                                 const void *hidden3, const int32_t *token_ids, const void *mask_emb,
+                                 const void *h_shared, const int32_t *cells, int32_t L, int32_t n_lead,
+                                 const int32_t *out_rows, int32_t L_out, void *logits_out, int32_t *argmax_out,
+                                 void *workspace, size_t ws_bytes, void *stream) {
+  if (n_lead < 0 || n_lead > L)
+    return fail(PE_ERR_INVALID_ARGUMENT, "n_lead=%d outside [0, L=%d]", n_lead, L);
+  if (L_out < 1) return fail(PE_ERR_INVALID_ARGUMENT, "L_out=%d must be >= 1", L_out);
+  if (n_lead < L && (logits_out || argmax_out) && !out_rows)
+    return fail(PE_ERR_INVALID_ARGUMENT, "out_rows must be non-NULL when cells past n_lead write outputs");
+  return enqueue_train(m, mask, N, n, K, hidden3, token_ids, mask_emb, h_shared, cells, L, n_lead, out_rows,
+                       L_out, logits_out, argmax_out, workspace, ws_bytes, stream);
 }
 
 pe_status pe_profile_enable(pe_model *m, int32_t enable) {

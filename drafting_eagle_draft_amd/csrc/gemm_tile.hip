@@ -235,6 +235,13 @@ void k_gemm_tile(TileGemmParams p) {
     const int m0 = tm0, s0 = ts0;
     // acc[i][j][r] = C[m = m0 + (wm*8 + j)*16 + c16][n = (s0 + wn*4 + i)*16 + 4g + r]
     if constexpr (EPI == BEPI_LMHEAD) {
+      // Output row of activation row m, or -1 when it is not written.
+      auto out_row = [&](int m) -> long {
+        if (m >= p.M) return -1;
+        if (!p.out_rows) return m;
+        const int r = m < p.row_skip ? -1 : p.out_rows[m - p.row_skip];
+        return r < p.out_M ? r : -1;
+      };
       // Argmax keys of the wave's 128 rows over its 64 columns.
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -256,13 +263,13 @@ void k_gemm_tile(TileGemmParams p) {
       if (p.logits && sizeof(T) == 4) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int m = m0 + (wm * 8 + j) * 16 + c16;
+          const long mo = out_row(m0 + (wm * 8 + j) * 16 + c16);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int s = s0 + wn * 4 + i;
-            if (m < p.M && s < p.NT) {
+            if (mo >= 0 && s < p.NT) {
               const float v4[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-              store4<T>(reinterpret_cast<T *>(p.logits) + (size_t)m * p.ldc + s * 16 + 4 * g, v4);
+              store4<T>(reinterpret_cast<T *>(p.logits) + (size_t)mo * p.ldc + s * 16 + 4 * g, v4);
             }
           }
         }
@@ -289,10 +296,10 @@ void k_gemm_tile(TileGemmParams p) {
 #pragma unroll
           for (int r0 = 0; r0 < RCH; r0 += ROWS_PER) {
             const int row = r0 + lr;
-            const int m = m0 + wm * 128 + ph * RCH + row;
+            const long mo = out_row(m0 + wm * 128 + ph * RCH + row);
             const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * PITCH + lc * 16);
-            if (m < p.M && lc * 16 < nbytes)
-              stg16(reinterpret_cast<char *>(p.logits) + ((size_t)m * p.ldc + col0) * sizeof(T) + lc * 16, v);
+            if (mo >= 0 && lc * 16 < nbytes)
+              stg16(reinterpret_cast<char *>(p.logits) + ((size_t)mo * p.ldc + col0) * sizeof(T) + lc * 16, v);
           }
         }
       }

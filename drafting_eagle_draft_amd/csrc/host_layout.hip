@@ -75,4 +75,42 @@ pe_status pe_partition(int32_t n, int32_t K, int32_t S, const int32_t *rows, int
   return PE_OK;
 }
 
+// The cells of chunk s (paper notes, section 3.2): the chunk's own cells
+// plus its depth-0 completion, the depth-0 cells of every position before
+// the end of segment s.  Every own cell of chunk s sits at a position at or
+// after b_s (a deeper cell's rollout starts in segment s), so in ascending
+// order the cells are the n_lead = b_s depth-0 cells of positions before the
+// segment, which belong to earlier chunks, then the own cells.
+pe_status pe_partition_chunk(int32_t n, int32_t K, int32_t S, int32_t s, const int32_t *rows, int32_t L,
+                             int32_t *cells_out, int32_t *out_rows, int32_t *L_chunk, int32_t *n_lead,
+                             int32_t *n_chunk) {
+  if (s < 0 || s >= S || !cells_out || !out_rows || !L_chunk || !n_lead || !n_chunk)
+    return pe::set_error(PE_ERR_INVALID_ARGUMENT, "pe_partition_chunk: bad s or NULL pointer");
+  std::vector<int32_t> chunk((size_t)(L > 0 ? L : 1));
+  pe_status st = pe_partition(n, K, S, rows, L, chunk.data());
+  if (st != PE_OK) return st;
+  const long b0 = (long)s * n / S, b1 = (long)(s + 1) * n / S;
+  int32_t c = 0;
+  for (int i = 0; i < L && rows[i] < b0 * K; ++i)
+    if (rows[i] % K == 0) cells_out[c++] = rows[i];
+  if (c != b0)
+    return pe::set_error(PE_ERR_INVALID_ARGUMENT, "pe_partition_chunk: rows lack a depth-0 cell before the segment");
+  const int32_t lead = c;
+  long pmax = b0 - 1, own_d0 = 0;
+  for (int i = 0; i < L; ++i) {
+    if (chunk[i] != s) continue;
+    cells_out[c] = rows[i];
+    out_rows[c - lead] = i;
+    ++c;
+    pmax = rows[i] / K > pmax ? rows[i] / K : pmax;
+    own_d0 += rows[i] % K == 0;
+  }
+  if (own_d0 != b1 - b0)
+    return pe::set_error(PE_ERR_INVALID_ARGUMENT, "pe_partition_chunk: rows lack a depth-0 cell of the segment");
+  *L_chunk = c;
+  *n_lead = lead;
+  *n_chunk = (int32_t)(pmax + 1);
+  return PE_OK;
+}
+
 }  // extern "C"

@@ -160,6 +160,11 @@ struct TileGemmParams {
   long ldc;
   void *logits;
   unsigned long long *keys;  // [M], zeroed before the launch; atomically maxed
+  // LM head output rows: row m goes to logits row out_rows[m - row_skip]
+  // (rows m < row_skip, and targets outside [0, out_M), are not written);
+  // without out_rows, row m goes to row m.
+  const int *out_rows;
+  int row_skip, out_M;
   // SWIGLU: h in the fragment-tile layout of an [M][I] matrix
   void *h;
   int I;
@@ -172,7 +177,9 @@ struct TileGemmParams {
 };
 
 hipError_t launch_gemm_tile(int dtype, int epi, const TileGemmParams &p, int num_cus, hipStream_t s);
-hipError_t launch_argmax_rows(const unsigned long long *keys, int M, int *out, hipStream_t s);
+// out[r(m)] = argmax of keys[m], r(m) as for the LM head's output rows (out_rows NULL: r(m) = m).
+hipError_t launch_argmax_rows(const unsigned long long *keys, int M, int *out, const int *out_rows,
+                              int row_skip, int out_M, hipStream_t s);
 // y[N] (fp32) = W x for one dtype vector x[K], W in the fragment-tile layout.
 hipError_t launch_matvec_tiled(int dtype, const u32x4 *wt, int NT, int KT, int N, const void *x, int K,
                                float *y, hipStream_t s);

@@ -62,10 +62,13 @@ __global__ void k_mask_materialize(const int2 *table, int nK, const int *rows, i
   out[idx] = allowed(a.x, a.y, b.x, b.y) ? 1 : 0;
 }
 
-__global__ void k_argmax_rows(const unsigned long long *keys, int M, int *out) {
+__global__ void k_argmax_rows(const unsigned long long *keys, int M, int *out, const int *out_rows, int row_skip,
+                              int out_M) {
   const int m = blockIdx.x * blockDim.x + threadIdx.x;
   if (m >= M) return;
-  out[m] = (int)(0xFFFFFFFFu - (unsigned)(keys[m] & 0xFFFFFFFFull));
+  const int r = out_rows ? (m < row_skip ? -1 : out_rows[m - row_skip]) : m;
+  if (r < 0 || r >= out_M) return;
+  out[r] = (int)(0xFFFFFFFFu - (unsigned)(keys[m] & 0xFFFFFFFFull));
 }
 
 // y = W x for one vector: one wave per 16-row weight strip; lane (c16, g)
@@ -491,8 +494,10 @@ hipError_t launch_mask_materialize(const int2 *table, int nK, const int *rows, i
   return hipGetLastError();
 }
 
-hipError_t launch_argmax_rows(const unsigned long long *keys, int M, int *out, hipStream_t s) {
-  hipLaunchKernelGGL(k_argmax_rows, dim3(blocks_for(M, 256)), dim3(256), 0, s, keys, M, out);
+hipError_t launch_argmax_rows(const unsigned long long *keys, int M, int *out, const int *out_rows,
+                              int row_skip, int out_M, hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax_rows, dim3(blocks_for(M, 256)), dim3(256), 0, s, keys, M, out, out_rows,
+                     row_skip, out_M);
   return hipGetLastError();
 }
 

@@ -296,3 +296,53 @@ def train_forward(drafter: Drafter, mask: TrainMask, inp, rows, N=None, want_log
     torch.cuda.synchronize()
     return (buf.argmax.cpu().numpy(),
             buf.logits.float().cpu().numpy() if buf.logits is not None else None)
+
+
+class PartitionedTrain:
+    """The training-shape forward as S independent chunk forwards (sequence
+    partition: each chunk runs its own cells plus its depth-0 completion and
+    writes its own rows of the whole sequence's outputs).  Chunk layouts
+    come from the library's host partition; one workspace serves the
+    largest chunk, and the chunks run one after another on one stream."""
+
+    def __init__(self, drafter: Drafter, mask: TrainMask, inp, rows, S, N=None, want_logits=True):
+        cfg, dev = drafter.cfg, drafter.device
+        self.N = cfg.n_layers if N is None else N
+        self.n = n = int(len(inp["token_ids"]))
+        self.K = K = mask.K
+        self.S = S
+        rows = np.ascontiguousarray(rows, np.int32)
+        self.L = int(rows.size)
+        self.hidden3 = to_device(inp["hidden3"], cfg, dev)
+        self.token_ids = torch.from_numpy(np.asarray(inp["token_ids"], np.int32)).to(dev)
+        self.mask_emb = to_device(inp["mask_emb"], cfg, dev)
+        self.h_shared = to_device(inp["h_shared"], cfg, dev)
+        self.chunks = []
+        ws_bytes = 256
+        for s in range(S):
+            cells, lead, out_rows, nc = pe.pe_partition_chunk(n, K, S, s, rows)
+            self.chunks.append((torch.from_numpy(cells).to(dev), lead,
+                                torch.from_numpy(out_rows).to(dev) if out_rows.size else None, nc))
+            ws_bytes = max(ws_bytes, pe.pe_train_workspace_size(drafter.handle, nc, K, int(cells.size)))
+        self.cells_total = sum(int(c[0].numel()) for c in self.chunks)
+        self.logits = (torch.empty((self.L, cfg.vocab), dtype=_dtype(cfg), device=dev)
+                       if want_logits else None)
+        self.argmax = torch.full((self.L,), -1, dtype=torch.int32, device=dev)
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        pe.pe_workspace_init(self.ws.data_ptr(), self.ws.numel(), stream_handle())
+
+    def launch(self, drafter: Drafter, mask: TrainMask, stream: int | None = None):
+        st = stream_handle() if stream is None else stream
+        for cells, lead, out_rows, nc in self.chunks:
+            pe.pe_train_forward_chunk(
+                drafter.handle, mask.handle, self.N, nc, self.K, self.hidden3.data_ptr(),
+                self.token_ids.data_ptr(), self.mask_emb.data_ptr(), self.h_shared.data_ptr(),
+                cells.data_ptr(), int(cells.numel()), lead,
+                out_rows.data_ptr() if out_rows is not None else None, self.L,
+                self.logits.data_ptr() if self.logits is not None else None, self.argmax.data_ptr(),
+                self.ws.data_ptr(), self.ws.numel(), st)
+
+    def result(self):
+        torch.cuda.synchronize()
+        return (self.argmax.cpu().numpy(),
+                self.logits.float().cpu().numpy() if self.logits is not None else None)

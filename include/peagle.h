@@ -275,6 +275,46 @@ pe_status pe_cod_rows(int32_t n, int32_t K, double r, double floor_rate, const d
 pe_status pe_partition(int32_t n, int32_t K, int32_t S, const int32_t *rows, int32_t L,
                        int32_t *chunk_out);
 
+/*
+ * Cells of chunk s of that partition, the unit of a chunked training
+ * forward (paper notes, section 3.2: each chunk is completed by the depth-0
+ * cells before the end of its segment, so chunks share no state).
+ *   rows       host int32 [L], kept cells of the whole sequence as for
+ *              pe_train_forward (every depth-0 cell present)
+ *   cells_out  host int32 with room for L entries: the chunk's cells,
+ *              ascending; the first *n_lead (the depth-0 cells of positions
+ *              before segment s) belong to earlier chunks
+ *   out_rows   host int32 with room for L entries: for cell *n_lead + i,
+ *              its index in rows
+ *   *L_chunk   number of cells; *n_chunk positions the chunk covers (its
+ *              largest position + 1): the chunk forward reads hidden3 and
+ *              token_ids rows [0, *n_chunk) only
+ * PE_ERR_INVALID_ARGUMENT as pe_partition, for s outside [0, S), or when a
+ * depth-0 cell of a position before the end of segment s is missing.
+ */
+pe_status pe_partition_chunk(int32_t n, int32_t K, int32_t S, int32_t s, const int32_t *rows, int32_t L,
+                             int32_t *cells_out, int32_t *out_rows, int32_t *L_chunk, int32_t *n_lead,
+                             int32_t *n_chunk);
+
+/*
+ * Training-shape forward of one chunk (paper notes, section 3.2), run with
+ * no state from other chunks: pe_train_forward over the chunk's L cells
+ * (device int32 [L], from pe_partition_chunk, n = its n_chunk), writing
+ * only the cells from n_lead on, each to row out_rows[i] (device int32
+ * [L - n_lead]) of the whole sequence's outputs logits_out [L_out, V] and
+ * argmax_out [L_out]; rows outside [0, L_out) are dropped.  Over all chunks
+ * of a partition this writes every row of pe_train_forward's outputs with
+ * the same values.  Workspace: pe_train_workspace_size(m, n, K, L).  cells
+ * must contain the depth-0 cell of every position up to their largest
+ * anchor and be chain-closed (violations give unspecified values but every
+ * access stays in bounds).
+ */
+pe_status pe_train_forward_chunk(const pe_model *m, const pe_mask *mask, int32_t N, int32_t n, int32_t K,
+                                 const void *hidden3, const int32_t *token_ids, const void *mask_emb,
+                                 const void *h_shared, const int32_t *cells, int32_t L, int32_t n_lead,
+                                 const int32_t *out_rows, int32_t L_out, void *logits_out, int32_t *argmax_out,
+                                 void *workspace, size_t ws_bytes, void *stream);
+
 /* Thread-local description of the last non-OK status of this thread. */
 const char *pe_last_error(void);
 

@@ -182,6 +182,70 @@ def test_train_repeat_is_identical_and_argmax_only():
     d.close()
 
 
+# ---------------------------------------------------------------- sequence partition
+
+
+def run_partitioned(cfg, w, inp, rows, K, S, n_max, N=None):
+    """Chunked forward (each chunk with its depth-0 completion) against the
+    whole forward on the GPU (identical: every row's arithmetic is the same)
+    and against the oracle's partitioned forward (parity rule)."""
+    d = runner.Drafter(cfg, w)
+    mask = runner.TrainMask(n_max, K)
+    whole_arg, whole_lg = runner.train_forward(d, mask, inp, rows, N=N)
+    part = runner.PartitionedTrain(d, mask, inp, rows, S, N=N)
+    part.launch(d, mask)
+    arg, lg = part.result()
+    cells = part.cells_total
+    del part
+    mask.close()
+    d.close()
+    np.testing.assert_array_equal(arg, whole_arg)
+    np.testing.assert_array_equal(lg, whole_lg)
+    wr = dict(w, embed_rows=w["embed"][inp["token_ids"]])
+    ref = po.train_forward_partitioned(wr, cfg, inp["hidden3"], inp["token_ids"], inp["mask_emb"],
+                                       inp["h_shared"], rows, K, S, N=N)
+    stats = compare(cfg, ref, arg, lg)
+    log(f"  {cfg.name} n={len(inp['token_ids'])} K={K} S={S} L={len(rows)} chunk cells={cells}: {stats}")
+
+
+@pytest.mark.parametrize("n,K,S", [(70, 8, 2), (70, 8, 7), (33, 4, 3), (5, 4, 5)])
+def test_train_partitioned_tiny_f32(n, K, S):
+    cfg = synth.config("tiny_f32")
+    w = synth.drafter_weights(cfg, gain_jitter=0.1)
+    inp = synth.train_inputs(cfg, n=n, tag=f"part{n}_{K}")
+    rows = cod_layout(cfg, n, K, r=0.8, tag=f"part{n}_{K}")
+    run_partitioned(cfg, w, inp, rows, K, S, n_max=n + 5)
+
+
+@pytest.mark.parametrize("S", [2, 4])
+def test_train_partitioned_bf16_small(S):
+    cfg = train_small(name="train_small_part", seed=3006)
+    w = synth.drafter_weights(cfg, gain_jitter=0.1)
+    inp = synth.train_inputs(cfg)
+    rows = cod_layout(cfg, cfg.seq_len, cfg.K)
+    run_partitioned(cfg, w, inp, rows, cfg.K, S, n_max=cfg.n_max)
+
+
+def test_train_chunk_rejects_bad_lead_and_missing_rows():
+    from drafting_eagle_draft_amd import binding as pe
+    cfg = synth.config("tiny_f32")
+    w = synth.drafter_weights(cfg)
+    d = runner.Drafter(cfg, w)
+    mask = runner.TrainMask(16, 4)
+    cells = torch.arange(0, 16, 4, dtype=torch.int32, device="cuda")
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+    out = torch.empty(4, dtype=torch.int32, device="cuda")
+    h = torch.zeros((4, 3 * cfg.hidden), dtype=torch.float32, device="cuda")
+    t = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for lead, rows_ptr in [(5, out.data_ptr()), (-1, out.data_ptr()), (1, None)]:
+        with pytest.raises(pe.PeagleError):
+            pe.pe_train_forward_chunk(d.handle, mask.handle, 1, 4, 4, h.data_ptr(), t.data_ptr(), h.data_ptr(),
+                                      h.data_ptr(), cells.data_ptr(), 4, lead, rows_ptr, 4, None,
+                                      out.data_ptr(), ws.data_ptr(), ws.numel(), 0)
+    mask.close()
+    d.close()
+
+
 # ---------------------------------------------------------------- training size
 
 
@@ -222,3 +286,30 @@ def test_train_full_size_sampled_rows():
     log(f"  oracle {time.time() - t1:.1f}s")
     stats = compare(cfg, ref, argmax, logits)
     log(f"  {cfg.name} L={L} sample={len(sample)} {stats}")
+
+
+@pytest.mark.timeout(400)
+def test_train_full_size_partitioned_equals_whole():
+    """The training size (n = 8192, K = 8, COD r = 0.8) in S = 4 chunks:
+    every row's logits and argmax equal the whole forward's."""
+    cfg = synth.config("train_gptoss20b_n8192_k8")
+    n, K = cfg.seq_len, cfg.K
+    w = synth.drafter_weights(cfg)
+    inp = synth.train_inputs(cfg)
+    rows = cod_layout(cfg, n, K)
+    d = runner.Drafter(cfg, w)
+    mask = runner.TrainMask(cfg.n_max, K)
+    whole = runner.TrainBuffers(d, mask, inp, rows)
+    whole.launch(d, mask)
+    part = runner.PartitionedTrain(d, mask, inp, rows, 4)
+    part.launch(d, mask)
+    torch.cuda.synchronize()
+    same_arg = bool(torch.equal(part.argmax, whole.argmax))
+    same_lg = bool(torch.equal(part.logits, whole.logits))
+    log(f"  {cfg.name} L={len(rows)} S=4 chunk cells={part.cells_total}: argmax equal {same_arg}, "
+        f"logits equal {same_lg}")
+    del part, whole
+    mask.close()
+    d.close()
+    torch.cuda.empty_cache()
+    assert same_arg and same_lg

@@ -59,3 +59,30 @@ def test_cod_rows_rejects_bad_arguments():
         pe.pe_cod_rows(4, 17, 0.8, 0.2, np.zeros(68))
     with pytest.raises(pe.PeagleError):
         pe.pe_cod_rows(4, 4, 0.0, 0.2, np.zeros(16))
+
+
+@pytest.mark.parametrize("n,K,S", [(50, 8, 2), (50, 8, 3), (64, 4, 4), (97, 6, 7), (7, 8, 7), (9, 3, 1)])
+def test_partition_chunk_matches_oracle(n, K, S):
+    cfg = synth.config("tiny_f32")
+    U = synth.cod_uniforms(cfg, n, K, tag=f"pchunk{n}")
+    rows = po.cod_rows(po.cod_keep(n, K, U))
+    owned = np.zeros(len(rows), dtype=int)
+    for s in range(S):
+        cells, lead, out_rows, nc = pe.pe_partition_chunk(n, K, S, s, rows)
+        want_cells, own = po.chunk_cells(n, K, S, rows, s)
+        np.testing.assert_array_equal(cells, want_cells)
+        np.testing.assert_array_equal(out_rows, own)
+        np.testing.assert_array_equal(cells[lead:], rows[own])
+        assert lead == (s * n) // S
+        assert nc == int(cells.max()) // K + 1 and nc <= n
+        owned[out_rows] += 1
+    assert np.all(owned == 1)
+
+
+def test_partition_chunk_rejects_missing_depth0_and_bad_s():
+    K = 4
+    rows = np.array([0, 4, 5, 12], dtype=np.int32)   # position 2 has no depth-0 cell
+    with pytest.raises(pe.PeagleError):
+        pe.pe_partition_chunk(4, K, 2, 1, rows)
+    with pytest.raises(pe.PeagleError):
+        pe.pe_partition_chunk(4, K, 2, 2, np.array([0, 4, 8, 12], dtype=np.int32))
