@@ -108,7 +108,7 @@ def train_flops(cfg, n, rows, K):
             "pairs": pairs}
 
 
-def train_leg(steps, warmup):
+def train_leg(steps, warmup, partition=True):
     """Training-shape forward (one GPT-OSS-20B-shaped drafter layer over a
     COD layout of n = 8192, K = 8, r = 0.8; mask built once for n_max =
     20480; bf16 logits at every kept row)."""
@@ -144,19 +144,19 @@ def train_leg(steps, warmup):
     del buf
     # The same forward as S = 4 independent chunks, each recomputing its
     # depth-0 completion (sequence partitioning); outputs identical.
-    S = 4
-    part = runner.PartitionedTrain(d, mask, inp, rows, S)
-    part.launch(d, mask)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(steps):
+    S, part_ms, part_cells, part_ws = 4, None, None, None
+    if partition:
+        part = runner.PartitionedTrain(d, mask, inp, rows, S)
         part.launch(d, mask)
-    e1.record()
-    torch.cuda.synchronize()
-    part_ms = e0.elapsed_time(e1) / steps
-    part_cells = part.cells_total
-    part_ws = part.ws.numel()
-    del part
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            part.launch(d, mask)
+        e1.record()
+        torch.cuda.synchronize()
+        part_ms = e0.elapsed_time(e1) / steps
+        part_cells, part_ws = part.cells_total, part.ws.numel()
+        del part
     L = len(rows)
     f = train_flops(cfg, n, rows, K)
     achieved = f["total"] / (ms * 1e-3) / 1e12
@@ -180,9 +180,10 @@ def train_leg(steps, warmup):
                              "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                              "algorithmic_flops": f["total"], "gemm_flops": f["gemm"],
                              "attention_flops": f["attention"], "allowed_pairs": f["pairs"]},
-        "partitioned": {"S": S, "ms_per_step": part_ms, "cells_run": part_cells,
-                        "recompute_factor": part_cells / L, "value": L / (part_ms * 1e-3),
-                        "workspace_bytes": part_ws, "whole_workspace_bytes": whole_ws},
+        "partitioned": ({"S": S, "ms_per_step": part_ms, "cells_run": part_cells,
+                         "recompute_factor": part_cells / L, "value": L / (part_ms * 1e-3),
+                         "workspace_bytes": part_ws, "whole_workspace_bytes": whole_ws}
+                        if partition else None),
     }
 
 
@@ -241,6 +242,8 @@ def main():
     ap.add_argument("--train-only", action="store_true",
                     help="run only the training-shape forward leg (its own JSON line)")
     ap.add_argument("--train-steps", type=int, default=5)
+    ap.add_argument("--no-partition", action="store_true",
+                    help="skip the 4-chunk form of the training-shape forward")
     ap.add_argument("--no-chain", action="store_true",
                     help="skip the autoregressive EAGLE-3 chain leg")
     ap.add_argument("--chain-steps", type=int, default=20)
@@ -260,7 +263,7 @@ def main():
     from drafting_eagle_draft_amd import runner, synth
 
     if a.train_only:
-        print(json.dumps(train_leg(a.train_steps, 2)), flush=True)
+        print(json.dumps(train_leg(a.train_steps, 2, not a.no_partition)), flush=True)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -364,7 +367,7 @@ def main():
     torch.cuda.empty_cache()
     if not a.no_train:
         print("[bench] training-shape forward", file=sys.stderr, flush=True)
-        out["train_forward"] = train_leg(a.train_steps, 2)
+        out["train_forward"] = train_leg(a.train_steps, 2, not a.no_partition)
     print(json.dumps(out), flush=True)
 
 

@@ -857,7 +857,7 @@ pe_status enqueue_train(const pe_model *m, const pe_mask *mask, int32_t N, int32
     if ((e = launch_zero(p.keys, (size_t)p.M * 8, s)) != hipSuccess) return hip_fail(e, "key reset launch");
     const bool prof = m->prof && m->nrec < (int)m->ev0.size();
     if (prof) (void)hipEventRecord(m->ev0[m->nrec], s);
-    if ((st = gemm(m->lm, BEPI_LMHEAD, p)) != PE_OK) return st;
+    if ((st = gemm(m->lm, out_rows ? BEPI_LMHEAD_MAP : BEPI_LMHEAD, p)) != PE_OK) return st;
     if (prof) {
       (void)hipEventRecord(m->ev1[m->nrec], s);
       ++m->nrec;

@@ -128,8 +128,9 @@ void k_gemm_tile(TileGemmParams p) {
   // (bf16 only: fp32 logits are written from registers.)
   constexpr int PITCH = 64 * (int)sizeof(T) + 16;
   constexpr int RCH = 16;
-  __shared__ __attribute__((aligned(16))) char lstage[EPI == BEPI_LMHEAD && sizeof(T) == 2 ? 8 * RCH * PITCH : 16];
-  __shared__ unsigned long long kbuf[EPI == BEPI_LMHEAD ? 4 : 1][256];
+  constexpr bool LMH = EPI == BEPI_LMHEAD || EPI == BEPI_LMHEAD_MAP;
+  __shared__ __attribute__((aligned(16))) char lstage[LMH && sizeof(T) == 2 ? 8 * RCH * PITCH : 16];
+  __shared__ unsigned long long kbuf[LMH ? 4 : 1][256];
   const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
   // Wave (wm, wn): activation rows wm*128 .. +128 (8 row groups) and weight
@@ -234,11 +235,12 @@ void k_gemm_tile(TileGemmParams p) {
     {
     const int m0 = tm0, s0 = ts0;
     // acc[i][j][r] = C[m = m0 + (wm*8 + j)*16 + c16][n = (s0 + wn*4 + i)*16 + 4g + r]
-    if constexpr (EPI == BEPI_LMHEAD) {
-      // Output row of activation row m, or -1 when it is not written.
+    if constexpr (LMH) {
+      // Output row of activation row m, or -1 when it is not written (the
+      // map is a variant of its own so the plain LM head keeps its code).
       auto out_row = [&](int m) -> long {
         if (m >= p.M) return -1;
-        if (!p.out_rows) return m;
+        if constexpr (EPI == BEPI_LMHEAD) return m;
         const int r = m < p.row_skip ? -1 : p.out_rows[m - p.row_skip];
         return r < p.out_M ? r : -1;
       };
@@ -349,13 +351,13 @@ hipError_t launch_gemm_tile(int dtype, int epi, const TileGemmParams &p, int num
   if (dtype == 1) {
     switch (epi) {
       PE_TILE_CASE(bf16_t, 0) PE_TILE_CASE(bf16_t, 1) PE_TILE_CASE(bf16_t, 2) PE_TILE_CASE(bf16_t, 3)
-      PE_TILE_CASE(bf16_t, 4)
+      PE_TILE_CASE(bf16_t, 4) PE_TILE_CASE(bf16_t, 5)
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (epi) {
       PE_TILE_CASE(float, 0) PE_TILE_CASE(float, 1) PE_TILE_CASE(float, 2) PE_TILE_CASE(float, 3)
-      PE_TILE_CASE(float, 4)
+      PE_TILE_CASE(float, 4) PE_TILE_CASE(float, 5)
       default: return hipErrorInvalidValue;
     }
   }

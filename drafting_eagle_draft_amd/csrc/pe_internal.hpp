@@ -147,6 +147,7 @@ enum BigEpi : int {
   BEPI_ACCUM = 2,   // C += result (residual update)
   BEPI_SWIGLU = 3,  // MAP_GATEUP rows: h[M][I] = silu(gate) * up
   BEPI_QKV = 4,     // MAP_QKV rows: RoPE at position anc+dep, scatter q/k/v
+  BEPI_LMHEAD_MAP = 5,  // BEPI_LMHEAD writing row m to out_rows[m - row_skip]
 };
 
 struct TileGemmParams {
