@@ -585,6 +585,178 @@ def train_forward(w, cfg, hidden3, token_ids, mask_emb, h_shared, rows, K, N=Non
     return logits
 
 
+# ---------------------------------------------------------------------------
+# Training loss and gradients over a COD layout ([TD] "Memory and Training
+# Complexity": training runs the K-depth layout in one forward and backward,
+# with gradients accumulated over the chunks of a sequence partition; [PN] 3
+# and 3.2).  Each cell (p, d) predicts the token after position p (reading:
+# anchor a = p - d, depth d drafts the token at a + d + 1); the loss is the
+# cross-entropy of the cell's logits against labels[p], summed over cells
+# with a label and multiplied by loss_scale.  The backward is written out
+# step by step (reverse order of the forward), not derived automatically.
+# ---------------------------------------------------------------------------
+
+
+def silu_grad(z):
+    """d silu / dz = s (1 + z (1 - s)), s = sigmoid(z)."""
+    z = np.asarray(z, dtype=F64)
+    sg = 1.0 / (1.0 + np.exp(-z))
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+def rmsnorm_backward(x, gain, eps, dy):
+    """Gradients of y = x r g, r = (mean(x^2) + eps)^(-1/2), over the last
+    axis: returns (dx, dgain summed over rows)."""
+    x = np.asarray(x, F64)
+    g = np.asarray(gain, F64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    gdy = dy * g
+    dx = r * gdy - x * r ** 3 * np.mean(gdy * x, axis=-1, keepdims=True)
+    return dx, np.sum(dy * x * r, axis=0)
+
+
+def train_loss_grads(w, cfg, hidden3, token_ids, mask_emb, h_shared, rows, K, labels,
+                     loss_scale=None, loss_rows=None, N=None):
+    """Loss and parameter gradients of the training-shape forward.
+
+    labels: int [n]; cell (p, d) is scored against labels[p] (negative: not
+    scored).  loss_rows: optional indices into ``rows`` of the cells whose
+    loss counts (a chunk scores only its own cells); default all.
+    loss_scale: multiplies the summed cross-entropy; default 1 / (number of
+    scored cells).  ``w["embed_rows"]`` holds E[token_ids[p]].
+
+    Returns (loss, grads) with grads keys fc, final_norm, lm_head, mask_emb,
+    h_shared, embed_rows ([n, H], the gradient of E[token_ids[p]] as used at
+    position p), and layers[l] with attn_norm, wq, wk, wv, wo, mlp_norm,
+    w_gate, w_up, w_down.
+    """
+    N = cfg.n_layers if N is None else N
+    rows = np.asarray(rows, dtype=np.int64)
+    L = len(rows)
+    P, D = rows // K, rows % K
+    n = len(np.asarray(token_ids))
+    H, nq, nkv, hd = cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    G = nq // nkv
+    scale = 1.0 / math.sqrt(hd)
+    eps = cfg.rms_eps
+    hid = np.asarray(hidden3, F64)
+    hs = np.asarray(h_shared, F64)
+    Wf = lambda a: np.asarray(a, F64)
+
+    # ---- forward, keeping what the backward needs
+    ntp = hid @ Wf(w["fc"]).T
+    mtp = Wf(w["fc"]) @ hs
+    deep = D > 0
+    x = np.where(deep[:, None], Wf(mask_emb)[None] + mtp[None], 0.0)
+    x[~deep] = Wf(w["embed_rows"])[P[~deep]] + ntp[P[~deep]]
+    index = {(int(P[i]), int(D[i])): i for i in range(L)}
+    depth0 = [index[(p, 0)] for p in range(int((P - D).max()) + 1)] if L else []
+    keys_of = [depth0[:int(P[i] - D[i]) + 1] + [index[(int(P[i] - D[i]) + j, j)] for j in range(1, int(D[i]) + 1)]
+               for i in range(L)]
+    saved = []
+    for l in range(N):
+        lw = w["layers"][l]
+        u1 = rmsnorm(x, lw["attn_norm"], eps)
+        q = rope((u1 @ Wf(lw["wq"]).T).reshape(L, nq, hd), P[:, None].astype(F64), cfg.rope_theta)
+        k = rope((u1 @ Wf(lw["wk"]).T).reshape(L, nkv, hd), P[:, None].astype(F64), cfg.rope_theta)
+        v = (u1 @ Wf(lw["wv"]).T).reshape(L, nkv, hd)
+        probs = []
+        a = np.zeros((L, nq, hd))
+        for i in range(L):
+            ki = keys_of[i]
+            pr = np.empty((nq, len(ki)))
+            for h in range(nq):
+                g = h // G
+                pr[h] = softmax(q[i, h] @ k[ki, g].T * scale)
+                a[i, h] = pr[h] @ v[ki, g]
+            probs.append(pr)
+        a = a.reshape(L, nq * hd)
+        xm = x + a @ Wf(lw["wo"]).T
+        u2 = rmsnorm(xm, lw["mlp_norm"], eps)
+        ga = u2 @ Wf(lw["w_gate"]).T
+        ub = u2 @ Wf(lw["w_up"]).T
+        hh = silu(ga) * ub
+        saved.append((x, u1, q, k, v, probs, a, xm, u2, ga, ub, hh))
+        x = xm + hh @ Wf(lw["w_down"]).T
+    z = rmsnorm(x, w["final_norm"], eps)
+    logits = z @ Wf(w["lm_head"]).T
+
+    # ---- loss: cross-entropy of each scored cell against labels[p]
+    lab = np.asarray(labels, dtype=np.int64)[P]
+    scored = lab >= 0
+    if loss_rows is not None:
+        keep = np.zeros(L, dtype=bool)
+        keep[np.asarray(loss_rows, dtype=np.int64)] = True
+        scored &= keep
+    if loss_scale is None:
+        loss_scale = 1.0 / max(int(scored.sum()), 1)
+    mx = logits.max(axis=1, keepdims=True)
+    lse = mx[:, 0] + np.log(np.sum(np.exp(logits - mx), axis=1))
+    idx = np.flatnonzero(scored)
+    loss = loss_scale * float(np.sum(lse[idx] - logits[idx, lab[idx]]))
+    dlogits = np.zeros_like(logits)
+    dlogits[idx] = np.exp(logits[idx] - lse[idx, None])
+    dlogits[idx, lab[idx]] -= 1.0
+    dlogits *= loss_scale
+
+    # ---- backward
+    grads = {"layers": [None] * N}
+    grads["lm_head"] = dlogits.T @ z
+    dz = dlogits @ Wf(w["lm_head"])
+    dx, grads["final_norm"] = rmsnorm_backward(x, w["final_norm"], eps, dz)
+    for l in reversed(range(N)):
+        lw = w["layers"][l]
+        x_in, u1, q, k, v, probs, a, xm, u2, ga, ub, hh = saved[l]
+        gl = {}
+        # MLP: x = xm + (silu(ga) * ub) @ w_down^T
+        gl["w_down"] = dx.T @ hh
+        dh = dx @ Wf(lw["w_down"])
+        dga = dh * ub * silu_grad(ga)
+        dub = dh * silu(ga)
+        gl["w_gate"] = dga.T @ u2
+        gl["w_up"] = dub.T @ u2
+        du2 = dga @ Wf(lw["w_gate"]) + dub @ Wf(lw["w_up"])
+        dxm_n, gl["mlp_norm"] = rmsnorm_backward(xm, lw["mlp_norm"], eps, du2)
+        dxm = dx + dxm_n
+        # O projection: xm = x_in + a @ wo^T
+        gl["wo"] = dxm.T @ a
+        da = (dxm @ Wf(lw["wo"])).reshape(L, nq, hd)
+        # attention, row by row over each row's visible keys
+        dq = np.zeros((L, nq, hd))
+        dk = np.zeros((L, nkv, hd))
+        dv = np.zeros((L, nkv, hd))
+        for i in range(L):
+            ki = keys_of[i]
+            for h in range(nq):
+                g = h // G
+                pr = probs[i][h]
+                dv[ki, g] += pr[:, None] * da[i, h][None, :]
+                dp = v[ki, g] @ da[i, h]
+                ds = pr * (dp - np.dot(pr, dp))
+                dq[i, h] = scale * (ds @ k[ki, g])
+                dk[ki, g] += scale * ds[:, None] * q[i, h][None, :]
+        # RoPE is a rotation: its transpose rotates by the opposite angle
+        dq = rope(dq, -P[:, None].astype(F64), cfg.rope_theta).reshape(L, nq * hd)
+        dk = rope(dk, -P[:, None].astype(F64), cfg.rope_theta).reshape(L, nkv * hd)
+        dv = dv.reshape(L, nkv * hd)
+        gl["wq"] = dq.T @ u1
+        gl["wk"] = dk.T @ u1
+        gl["wv"] = dv.T @ u1
+        du1 = dq @ Wf(lw["wq"]) + dk @ Wf(lw["wk"]) + dv @ Wf(lw["wv"])
+        dx_n, gl["attn_norm"] = rmsnorm_backward(x_in, lw["attn_norm"], eps, du1)
+        dx = dxm + dx_n
+        grads["layers"][l] = gl
+    # fusion: depth-0 cells E[x_p] + fc(h_p), deeper cells mask_emb + fc(h_shared)
+    d_shared = dx[deep].sum(axis=0)
+    grads["mask_emb"] = d_shared.copy()
+    grads["h_shared"] = d_shared @ Wf(w["fc"])
+    d_ntp = np.zeros((n, H))
+    d_ntp[P[~deep]] = dx[~deep]
+    grads["embed_rows"] = d_ntp.copy()
+    grads["fc"] = d_ntp.T @ hid + np.outer(d_shared, hs)
+    return loss, grads
+
+
 def chunk_cells(n, K, S, rows, s):
     """Cells the forward of chunk s of a sequence partition runs on ([PN]
     3.2): the depth-0 completion (every depth-0 cell of a position before
