@@ -187,6 +187,64 @@ def train_leg(steps, warmup, partition=True):
     }
 
 
+def step_flops(cfg, n, rows, K):
+    """Algorithmic flops of one training step (forward, loss, backward): the
+    forward's; twice the projections' GEMM flops for the backward (data and
+    weight gradients); and 2.5x the forward attention pairs' work for its
+    backward (dP, dS^T Q, dS K, P^T dO against the forward's Q K^T, P V)."""
+    f = train_flops(cfg, n, rows, K)
+    bwd = 2.0 * f["gemm"] + 2.5 * f["attention"]
+    return {"total": f["total"] + bwd, "forward": f["total"], "backward": bwd,
+            "lm_head_dgrad": f["lm_head"], "lm_head_wgrad": f["lm_head"]}
+
+
+def step_leg(steps):
+    """Training step (forward, cross-entropy against synthetic next-token
+    labels, backward to every weight) of one GPT-OSS-20B-shaped drafter layer
+    over the COD layout of n = 8192, K = 8, r = 0.8."""
+    import torch
+    from drafting_eagle_draft_amd import binding as pe
+    from drafting_eagle_draft_amd import runner, synth
+    cfg = synth.config("train_gptoss20b_n8192_k8")
+    n, K = cfg.seq_len, cfg.K
+    w = synth.drafter_weights(cfg)
+    inp = synth.train_inputs(cfg)
+    U = synth.cod_uniforms(cfg, n, K)
+    rows = pe.pe_cod_rows(n, K, cfg.cod_rate, cfg.cod_floor, U.reshape(-1))
+    rng = np.random.default_rng(5)
+    labels = rng.integers(0, cfg.vocab, n).astype(np.int32)
+    labels[-1] = -1
+    d = runner.Drafter(cfg, w, backward=True)
+    del w
+    mask = runner.TrainMask(cfg.n_max, K)
+    st = runner.TrainStep(d, mask, inp, rows, labels)
+    st.launch(d, mask)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        st.launch(d, mask)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    f = step_flops(cfg, n, rows, K)
+    L = len(rows)
+    ws = st.ws.numel()
+    del st
+    mask.close()
+    d.close()
+    torch.cuda.empty_cache()
+    achieved = f["total"] / (ms * 1e-3) / 1e12
+    return {"metric": "kept rows/s per training step (forward + loss + backward; n 8192, K 8, COD r 0.8)",
+            "value": L / (ms * 1e-3), "unit": "rows/s", "ms_per_step": ms, "steps": steps, "dtype": cfg.dtype,
+            "config": {"workload": cfg.name, "n": n, "K": K, "L": L, "layers": cfg.n_layers,
+                       "labels": "synthetic next tokens"},
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops": f["total"],
+                         "forward_flops": f["forward"], "backward_flops": f["backward"]},
+            "workspace_bytes": ws}
+
+
 def chain_leg(drafter, inp, K, steps, parallel_ms):
     """The sequential drafter the parallel one replaces, on the same kernels:
     K one-row cache extensions per sequence (each step's token and normalized
@@ -242,6 +300,8 @@ def main():
     ap.add_argument("--train-only", action="store_true",
                     help="run only the training-shape forward leg (its own JSON line)")
     ap.add_argument("--train-steps", type=int, default=5)
+    ap.add_argument("--no-step", action="store_true", help="skip the training-step leg")
+    ap.add_argument("--step-only", action="store_true", help="run only the training-step leg")
     ap.add_argument("--no-partition", action="store_true",
                     help="skip the 4-chunk form of the training-shape forward")
     ap.add_argument("--no-chain", action="store_true",
@@ -264,6 +324,9 @@ def main():
 
     if a.train_only:
         print(json.dumps(train_leg(a.train_steps, 2, not a.no_partition)), flush=True)
+        return
+    if a.step_only:
+        print(json.dumps(step_leg(a.train_steps)), flush=True)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -368,6 +431,9 @@ def main():
     if not a.no_train:
         print("[bench] training-shape forward", file=sys.stderr, flush=True)
         out["train_forward"] = train_leg(a.train_steps, 2, not a.no_partition)
+    if not a.no_step:
+        print("[bench] training step", file=sys.stderr, flush=True)
+        out["train_step"] = step_leg(a.train_steps)
     print(json.dumps(out), flush=True)
 
 

@@ -31,7 +31,8 @@ EXPORTS = (
     "pe_draft_forward", "pe_accept", "pe_last_error", "pe_version", "pe_profile_enable",
     "pe_profile_read", "pe_mask_create", "pe_mask_destroy", "pe_mask_materialize",
     "pe_train_workspace_size", "pe_train_forward", "pe_cod_rows", "pe_partition",
-    "pe_draft_extend", "pe_partition_chunk", "pe_train_forward_chunk",
+    "pe_draft_extend", "pe_partition_chunk", "pe_train_forward_chunk", "pe_model_prepare_backward",
+    "pe_train_step_workspace_size", "pe_train_step",
 )
 
 
@@ -53,6 +54,17 @@ class PeWeights(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("fc", ctypes.c_void_p),
                 ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
                 ("layers", ctypes.POINTER(PeLayerWeights))]
+
+
+class PeLayerGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")]
+
+
+class PeGrads(ctypes.Structure):
+    _fields_ = [("fc", ctypes.c_void_p), ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+                ("mask_emb", ctypes.c_void_p), ("h_shared", ctypes.c_void_p), ("embed_rows", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(PeLayerGrads))]
 
 
 class PeagleError(RuntimeError):
@@ -98,6 +110,10 @@ def load(path: str = LIB_PATH):
                                ctypes.POINTER(i32), ctypes.POINTER(i32)],
         "pe_train_forward_chunk": [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, vp,
                                    vp, sz, vp],
+        "pe_model_prepare_backward": [vp, ctypes.POINTER(PeWeights), vp],
+        "pe_train_step_workspace_size": [vp, i32, i32, i32, i32, ctypes.POINTER(sz)],
+        "pe_train_step": [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, i32, vp, ctypes.c_float, vp,
+                          ctypes.POINTER(PeGrads), vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -234,6 +250,24 @@ def pe_train_forward_chunk(model: int, mask: int, N: int, n: int, K: int, hidden
     _check("pe_train_forward_chunk", load().pe_train_forward_chunk(
         model, mask, N, n, K, hidden3, token_ids, mask_emb, h_shared, cells, L, n_lead, out_rows, L_out,
         logits_out, argmax_out, workspace, ws_bytes, stream))
+
+
+def pe_model_prepare_backward(model: int, weights: PeWeights, stream: int = 0) -> None:
+    _check("pe_model_prepare_backward", load().pe_model_prepare_backward(model, ctypes.byref(weights), stream))
+
+
+def pe_train_step_workspace_size(model: int, N: int, n: int, K: int, L: int) -> int:
+    out = ctypes.c_size_t()
+    _check("pe_train_step_workspace_size", load().pe_train_step_workspace_size(model, N, n, K, L, ctypes.byref(out)))
+    return out.value
+
+
+def pe_train_step(model: int, mask: int, N: int, n: int, K: int, hidden3: int, token_ids: int, mask_emb: int,
+                  h_shared: int, cells: int, L: int, n_lead: int, labels: int, loss_scale: float,
+                  loss_out: int | None, grads: PeGrads, workspace: int, ws_bytes: int, stream: int = 0) -> None:
+    _check("pe_train_step", load().pe_train_step(
+        model, mask, N, n, K, hidden3, token_ids, mask_emb, h_shared, cells, L, n_lead, labels, loss_scale,
+        loss_out, ctypes.byref(grads), workspace, ws_bytes, stream))
 
 
 def pe_cod_rows(n: int, K: int, r: float, floor_rate: float, U):

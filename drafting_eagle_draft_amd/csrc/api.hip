@@ -61,6 +61,8 @@ struct Tiled {
 struct LayerT {
   Tiled qkv, o, gateup, down;
   float *attn_norm = nullptr, *mlp_norm = nullptr;
+  // transposed tiles for the backward's data gradients (pe_model_prepare_backward)
+  Tiled qkvT, oT, guT, downT;
 };
 
 }  // namespace
@@ -73,6 +75,8 @@ struct pe_model {
   size_t lds_budget = 159 * 1024;  // dynamic LDS per GEMM workgroup
   int attn_blocks_per_cu = 2;
   Tiled fc, lm;
+  Tiled fcT, lmT;      // transposed tiles (backward)
+  bool has_bwd = false;
   std::vector<LayerT> layers;
   float *final_norm = nullptr;
   double *inv_freq = nullptr;
@@ -747,15 +751,24 @@ pe_status pe_train_workspace_size(const pe_model *m, int32_t n, int32_t K, int32
 
 namespace {
 
-// The training-shape forward over L cells.  The first n_lead cells produce
-// no outputs; cell n_lead + i writes output row out_rows[i] (out_rows NULL:
-// cell i writes row i; targets outside [0, L_out) are dropped).  The LM head
-// starts at the 16-row group holding cell n_lead.
-pe_status enqueue_train(const pe_model *m, const pe_mask *mask, int32_t N, int32_t n, int32_t K,
-                        const void *hidden3, const int32_t *token_ids, const void *mask_emb,
-                        const void *h_shared, const int32_t *rows, int32_t L, int32_t n_lead,
-                        const int32_t *out_rows, int32_t L_out, void *logits_out, int32_t *argmax_out,
-                        void *workspace, size_t ws_bytes, void *stream) {
+// Activations of one layer that the backward reads (per-layer buffers of a
+// training step; the plain forward reuses one set for every layer).
+struct StepLayer {
+  float *x = nullptr, *xm = nullptr, *lse = nullptr;  // residual in, after attention; softmax lse
+  void *u1 = nullptr, *q = nullptr, *kall = nullptr, *vall = nullptr, *k0 = nullptr, *v0 = nullptr;
+  void *attn = nullptr, *u2 = nullptr, *gu = nullptr, *h = nullptr;
+};
+struct StepSaves {
+  std::vector<StepLayer> layer;
+  float *xN = nullptr;   // residual after the last layer
+  void *z = nullptr;     // final-norm rows (fragment tiles)
+  void *logits = nullptr;  // [L][V] dtype
+};
+
+pe_status check_train_args(const pe_model *m, const pe_mask *mask, int32_t N, int32_t n, int32_t K,
+                           const void *hidden3, const int32_t *token_ids, const void *mask_emb,
+                           const void *h_shared, const int32_t *rows, int32_t L, const void *logits_out,
+                           const void *workspace) {
   pe_status st = check_train_shape(m, mask, n, K, L);
   if (st != PE_OK) return st;
   const pe_config &c = m->cfg;
@@ -767,12 +780,24 @@ pe_status enqueue_train(const pe_model *m, const pe_mask *mask, int32_t N, int32
       (logits_out && misaligned(logits_out)) || misaligned(workspace))
     return fail(PE_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
   if (!workspace) return fail(PE_ERR_WORKSPACE, "workspace is NULL");
-  const TrainLayout W = train_layout(m, n, K, L);
-  if (ws_bytes < W.total)
-    return fail(PE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
+  return PE_OK;
+}
 
+// The training-shape forward over L cells.  The first n_lead cells produce
+// no outputs; cell n_lead + i writes output row out_rows[i] (out_rows NULL:
+// cell i writes row i; targets outside [0, L_out) are dropped).  The LM head
+// starts at the 16-row group holding cell n_lead.  With sv, every layer
+// writes its own activation buffers (kept for the backward), the gate/up
+// pre-activations and softmax statistics are kept too, and the logits go to
+// sv->logits (rows from the 16-row group of n_lead on).
+pe_status enqueue_train(const pe_model *m, const pe_mask *mask, int32_t N, int32_t n, int32_t K,
+                        const void *hidden3, const int32_t *token_ids, const void *mask_emb,
+                        const void *h_shared, const int32_t *rows, int32_t L, int32_t n_lead,
+                        const int32_t *out_rows, int32_t L_out, void *logits_out, int32_t *argmax_out,
+                        const TrainLayout &W, char *ws, const StepSaves *sv, void *stream) {
+  pe_status st;
+  const pe_config &c = m->cfg;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char *ws = reinterpret_cast<char *>(workspace);
   int *anc = reinterpret_cast<int *>(ws + W.anc);
   int *dep = reinterpret_cast<int *>(ws + W.dep);
   int *inv = reinterpret_cast<int *>(ws + W.inv);
@@ -797,61 +822,84 @@ pe_status enqueue_train(const pe_model *m, const pe_mask *mask, int32_t N, int32
     if ((st = gemm(m->fc, BEPI_STORE, p)) != PE_OK) return st;
     e = launch_matvec_tiled(dt, m->fc.ptr, m->fc.NT, m->fc.KT, H, h_shared, 3 * H, yfc + (size_t)n * H, s);
     if (e != hipSuccess) return hip_fail(e, "shared-state projection launch");
-    e = launch_train_fuse(dt, yfc, m->embed, token_ids, mask_emb, anc, dep, L, n, H, c.vocab, xres, s);
+    e = launch_train_fuse(dt, yfc, m->embed, token_ids, mask_emb, anc, dep, L, n, H, c.vocab,
+                          sv ? sv->layer.empty() ? sv->xN : sv->layer[0].x : xres, s);
     if (e != hipSuccess) return hip_fail(e, "fusion launch");
   }
+  const size_t xbytes = (size_t)L * H * sizeof(float);
   for (int l = 0; l < N; ++l) {
     const LayerT &Lw = m->layers[l];
-    if ((e = launch_rmsnorm_tiled(dt, xres, Lw.attn_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
+    StepLayer B;
+    if (sv) {
+      B = sv->layer[l];
+    } else {
+      B.x = B.xm = xres; B.u1 = B.u2 = u;
+      B.q = ws + W.q; B.kall = ws + W.kall; B.vall = ws + W.vall; B.k0 = ws + W.k0; B.v0 = ws + W.v0;
+      B.attn = ws + W.attn; B.h = ws + W.h;
+    }
+    float *xnext = sv ? (l + 1 < N ? sv->layer[l + 1].x : sv->xN) : xres;
+    if ((e = launch_rmsnorm_tiled(dt, B.x, Lw.attn_norm, L, H, c.rms_eps, B.u1, s)) != hipSuccess)
       return hip_fail(e, "RMSNorm launch");
     {
       TileGemmParams p{};
-      p.A = u; p.lda = H; p.M = L; p.a_tiled = 1;
-      p.q = ws + W.q; p.kall = ws + W.kall; p.vall = ws + W.vall; p.k0 = ws + W.k0; p.v0 = ws + W.v0;
+      p.A = B.u1; p.lda = H; p.M = L; p.a_tiled = 1;
+      p.q = B.q; p.kall = B.kall; p.vall = B.vall; p.k0 = B.k0; p.v0 = B.v0;
       p.anc = anc; p.dep = dep; p.inv_freq = m->inv_freq;
       p.n = n; p.nq = nq; p.nkv = nkv; p.hd = hd;
       if ((st = gemm(Lw.qkv, BEPI_QKV, p)) != PE_OK) return st;
     }
     {
       TrainAttnParams a{};
-      a.q = ws + W.q; a.k0 = ws + W.k0; a.v0 = ws + W.v0; a.kall = ws + W.kall; a.vall = ws + W.vall;
+      a.q = B.q; a.k0 = B.k0; a.v0 = B.v0; a.kall = B.kall; a.vall = B.vall;
       a.anc = anc; a.dep = dep; a.inv = inv;
       a.L = L; a.n = n; a.K = K; a.nq = nq; a.nkv = nkv; a.hd = hd; a.G = nq / nkv;
       a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
-      a.out = ws + W.attn;
+      a.out = B.attn;
+      a.lse = B.lse;
       if ((e = launch_attn_train(dt, a, s)) != hipSuccess) return hip_fail(e, "attention launch");
     }
+    if (B.xm != B.x && (e = hipMemcpyAsync(B.xm, B.x, xbytes, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return hip_fail(e, "residual copy");
     {
       TileGemmParams p{};
-      p.A = ws + W.attn; p.lda = (long)nq * hd; p.M = L; p.a_tiled = 1;
-      p.C = xres; p.ldc = H;
+      p.A = B.attn; p.lda = (long)nq * hd; p.M = L; p.a_tiled = 1;
+      p.C = B.xm; p.ldc = H;
       if ((st = gemm(Lw.o, BEPI_ACCUM, p)) != PE_OK) return st;
     }
-    if ((e = launch_rmsnorm_tiled(dt, xres, Lw.mlp_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
+    if ((e = launch_rmsnorm_tiled(dt, B.xm, Lw.mlp_norm, L, H, c.rms_eps, B.u2, s)) != hipSuccess)
       return hip_fail(e, "RMSNorm launch");
     {
       TileGemmParams p{};
-      p.A = u; p.lda = H; p.M = L; p.a_tiled = 1;
-      p.h = ws + W.h; p.I = c.intermediate;
-      if ((st = gemm(Lw.gateup, BEPI_SWIGLU, p)) != PE_OK) return st;
+      p.A = B.u2; p.lda = H; p.M = L; p.a_tiled = 1;
+      p.h = B.h; p.I = c.intermediate; p.gu = B.gu;
+      if ((st = gemm(Lw.gateup, B.gu ? BEPI_SWIGLU_SAVE : BEPI_SWIGLU, p)) != PE_OK) return st;
     }
+    if (xnext != B.xm && (e = hipMemcpyAsync(xnext, B.xm, xbytes, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return hip_fail(e, "residual copy");
     {
       TileGemmParams p{};
-      p.A = ws + W.h; p.lda = c.intermediate; p.M = L; p.a_tiled = 1;
-      p.C = xres; p.ldc = H;
+      p.A = B.h; p.lda = c.intermediate; p.M = L; p.a_tiled = 1;
+      p.C = xnext; p.ldc = H;
       if ((st = gemm(Lw.down, BEPI_ACCUM, p)) != PE_OK) return st;
     }
   }
-  if ((e = launch_rmsnorm_tiled(dt, xres, m->final_norm, L, H, c.rms_eps, u, s)) != hipSuccess)
+  void *zrows = sv ? sv->z : u;
+  if ((e = launch_rmsnorm_tiled(dt, sv ? sv->xN : xres, m->final_norm, L, H, c.rms_eps, zrows, s)) != hipSuccess)
     return hip_fail(e, "RMSNorm launch");
+  if (sv) {
+    logits_out = sv->logits;
+    argmax_out = nullptr;
+    out_rows = nullptr;
+  }
   if (n_lead < L && (logits_out || argmax_out)) {
     // Rows before the 16-row group of cell n_lead are skipped; the group's
     // earlier rows are computed but not written.
     const int r0 = n_lead & ~15;
     TileGemmParams p{};
-    p.A = reinterpret_cast<const char *>(u) + (size_t)(r0 >> 4) * m->lm.KT * 1024;
+    p.A = reinterpret_cast<const char *>(zrows) + (size_t)(r0 >> 4) * m->lm.KT * 1024;
     p.lda = H; p.M = L - r0; p.a_tiled = 1;
-    p.logits = logits_out; p.ldc = c.vocab;
+    p.logits = sv ? reinterpret_cast<char *>(logits_out) + (size_t)r0 * c.vocab * m->esz : logits_out;
+    p.ldc = c.vocab;
     p.out_rows = out_rows; p.row_skip = n_lead - r0; p.out_M = L_out;
     p.keys = reinterpret_cast<unsigned long long *>(ws + W.keys);
     if ((e = launch_zero(p.keys, (size_t)p.M * 8, s)) != hipSuccess) return hip_fail(e, "key reset launch");
@@ -870,6 +918,232 @@ pe_status enqueue_train(const pe_model *m, const pe_mask *mask, int32_t N, int32
   return PE_OK;
 }
 
+// Workspace of a training step: the forward's row bookkeeping, every
+// layer's saved activations, the logits, and the backward's scratch.
+struct StepLayout {
+  TrainLayout tl{};
+  std::vector<StepLayer> off;  // byte offsets stored in the pointer fields
+  size_t xN = 0, z = 0, logits = 0, row_loss = 0;
+  size_t dx = 0, dx2 = 0, dxt = 0, gbuf = 0, dgu = 0, doutt = 0, D = 0, dq = 0, dk = 0, dv = 0, dqkv = 0;
+  size_t packA = 0, packB = 0, part = 0, dntp = 0, dshared = 0;
+  size_t total = 0;
+};
+
+size_t tiles_bytes(long rows, long k, int ktile) {
+  return (size_t)((rows + 15) / 16) * (size_t)((k + ktile - 1) / ktile) * 1024;
+}
+
+StepLayout step_layout(const pe_model *m, int N, long n, int K, long L) {
+  const pe_config &c = m->cfg;
+  StepLayout t{};
+  const size_t H = c.hidden, esz = m->esz, hd = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const size_t I = c.intermediate, V = c.vocab;
+  const size_t Lp = (size_t)(L + 15) / 16 * 16;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + std::max(bytes, (size_t)1), 256); return o; };
+  t.tl.anc = take((size_t)L * 4);
+  t.tl.dep = take((size_t)L * 4);
+  t.tl.inv = take((size_t)n * K * 4);
+  t.tl.yfc = take((size_t)(n + 1) * H * 4);
+  t.tl.keys = take((size_t)L * 8);
+  t.off.resize(N);
+  auto at = [](size_t o) { return reinterpret_cast<void *>(o); };
+  for (int l = 0; l < N; ++l) {
+    StepLayer &B = t.off[l];
+    B.x = reinterpret_cast<float *>(at(take(L * H * 4)));
+    B.xm = reinterpret_cast<float *>(at(take(L * H * 4)));
+    B.lse = reinterpret_cast<float *>(at(take(L * nq * 4)));
+    B.u1 = at(take(Lp * H * esz));
+    B.q = at(take(L * nq * hd * esz));
+    B.kall = at(take(L * nkv * hd * esz));
+    B.vall = at(take(L * nkv * hd * esz));
+    B.k0 = at(take(n * nkv * hd * esz));
+    B.v0 = at(take(n * nkv * hd * esz));
+    B.attn = at(take(Lp * nq * hd * esz));
+    B.u2 = at(take(Lp * H * esz));
+    B.gu = at(take(L * 2 * I * esz));
+    B.h = at(take(Lp * I * esz));
+  }
+  t.xN = take(L * H * 4);
+  t.z = take(Lp * H * esz);
+  t.logits = take(L * V * esz);
+  t.row_loss = take(L * 4);
+  const size_t wide = std::max(std::max(H, I), nq * hd);
+  t.dx = take(L * H * 4);
+  t.dx2 = take(L * H * 4);
+  t.dxt = take(L * H * esz);
+  t.gbuf = take(L * wide * 4);
+  t.dgu = take(L * 2 * I * esz);
+  t.doutt = take(L * nq * hd * esz);
+  t.D = take(L * nq * 4);
+  t.dq = take(L * nq * hd * 4);
+  t.dk = take(L * nkv * hd * 4);
+  t.dv = take(L * nkv * hd * 4);
+  t.dqkv = take(L * (nq + 2 * nkv) * hd * esz);
+  const int kt = m->ktile;
+  size_t a = tiles_bytes((long)V, L, kt);
+  a = std::max(a, tiles_bytes((long)(2 * I), L, kt));
+  a = std::max(a, tiles_bytes((long)((nq + 2 * nkv) * hd), L, kt));
+  a = std::max(a, tiles_bytes((long)H, std::max(L, n), kt));
+  t.packA = take(a);
+  size_t b = tiles_bytes((long)std::max(std::max(H, I), nq * hd), L, kt);
+  b = std::max(b, tiles_bytes((long)(3 * H), n, kt));
+  t.packB = take(b);
+  t.part = take((size_t)((L + 63) / 64) * H * 4);
+  t.dntp = take(n * H * esz);
+  t.dshared = take(H * 4);
+  t.total = off;
+  return t;
+}
+
+// Backward of the training step enqueued after the forward with saves:
+// cross-entropy -> LM head -> final norm -> layers in reverse -> input
+// fusion.  Data gradients: C = dY W with W's transposed tiles; weight
+// gradients: C += dY^T X with both operands packed transposed (k = rows).
+pe_status enqueue_backward(const pe_model *m, int32_t N, int32_t n, int32_t K, const void *hidden3,
+                           const void *h_shared, int32_t L, int32_t n_lead, const int32_t *labels,
+                           float loss_scale, float *loss_out, const pe_grads *gr, const StepLayout &SL,
+                           const StepSaves &sv, char *ws, hipStream_t s) {
+  const pe_config &c = m->cfg;
+  const int dt = c.dtype, H = c.hidden, I = c.intermediate, V = c.vocab;
+  const int hd = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads, kt = m->ktile;
+  const int QKV = (nq + 2 * nkv) * hd;
+  const int KTL = (L + kt - 1) / kt;
+  int *anc = reinterpret_cast<int *>(ws + SL.tl.anc);
+  int *dep = reinterpret_cast<int *>(ws + SL.tl.dep);
+  int *inv = reinterpret_cast<int *>(ws + SL.tl.inv);
+  auto F = [&](size_t o) { return reinterpret_cast<float *>(ws + o); };
+  float *dx = F(SL.dx), *dx2 = F(SL.dx2), *gbuf = F(SL.gbuf), *part = F(SL.part);
+  void *dxt = ws + SL.dxt, *packA = ws + SL.packA, *packB = ws + SL.packB;
+  const int nblk = (L + 63) / 64;
+  hipError_t e;
+  pe_status st;
+  auto chk = [&](hipError_t err, const char *what) { return err == hipSuccess ? PE_OK : hip_fail(err, what); };
+  auto gemm = [&](const void *A, int a_tiled, long lda, int M, const u32x4 *Bt, int NT, int KT, int Nn, int Kk,
+                  int epi, float *C, long ldc) -> pe_status {
+    TileGemmParams p{};
+    p.A = A; p.a_tiled = a_tiled; p.lda = lda; p.M = M;
+    p.wt = Bt; p.NT = NT; p.KT = KT; p.N = Nn; p.K = Kk;
+    p.C = C; p.ldc = ldc;
+    return chk(launch_gemm_tile(dt, epi, p, m->num_cus, s), "backward GEMM launch");
+  };
+  auto dgrad = [&](const void *dY, long ld, const Tiled &WT, float *out) {  // out [L][WT.N] = dY W
+    return gemm(dY, 0, ld, L, WT.ptr, WT.NT, WT.KT, WT.N, WT.K, BEPI_STORE, out, WT.N);
+  };
+  // grad[rows][cols] += A^T B over the L cells, with A [L][rows] (packed into
+  // packA) and B [L][cols] (packed into packB) already transposed.
+  auto wgrad = [&](int rows, int cols, int a_row0, float *grad, int Kk) {
+    const int KTk = (Kk + kt - 1) / kt;
+    const char *A = reinterpret_cast<const char *>(packA) + (size_t)(a_row0 / 16) * KTk * 1024;
+    return gemm(A, 1, 0, rows, reinterpret_cast<const u32x4 *>(packB), (cols + 15) / 16, KTk, cols, Kk, BEPI_ACCUM,
+                grad, cols);
+  };
+  auto packT = [&](int kind, const void *src, long ld, int R, int C, void *dst) {
+    return chk(launch_pack_t(dt, kind, src, ld, R, C, dst, (R + kt - 1) / kt, 0, s), "pack launch");
+  };
+
+  // ---- loss and LM head
+  if ((st = chk(launch_ce_rows(dt, sv.logits, L, V, anc, dep, labels, n, n_lead, loss_scale, F(SL.row_loss), s),
+                "cross-entropy launch")) != PE_OK) return st;
+  if (loss_out && (st = chk(launch_sum_acc(F(SL.row_loss), L, loss_out, s), "loss sum launch")) != PE_OK) return st;
+  if ((st = dgrad(sv.logits, V, m->lmT, gbuf)) != PE_OK) return st;                 // dz [L][H]
+  if (gr->lm_head) {
+    if ((st = packT(PACK_ROW, sv.logits, V, L, V, packA)) != PE_OK) return st;      // dlogits^T
+    if ((st = packT(PACK_TILED, sv.z, 0, L, H, packB)) != PE_OK) return st;          // z^T
+    if ((st = wgrad(V, H, 0, gr->lm_head, L)) != PE_OK) return st;
+  }
+  if ((st = chk(launch_rms_bwd(dt, sv.xN, m->final_norm, gbuf, nullptr, L, H, c.rms_eps, dx, dxt, part, s),
+                "RMSNorm backward launch")) != PE_OK) return st;
+  if (gr->final_norm && (st = chk(launch_colsum_acc(part, nblk, H, gr->final_norm, s), "gain sum")) != PE_OK)
+    return st;
+
+  for (int l = N - 1; l >= 0; --l) {
+    const LayerT &Lw = m->layers[l];
+    const StepLayer &B = sv.layer[l];
+    const pe_layer_grads *g = gr->layers ? &gr->layers[l] : nullptr;
+    // MLP: x_out = xm + (silu(gate) up) W_down^T; dx holds dL/dx_out.
+    if ((st = dgrad(dxt, H, Lw.downT, gbuf)) != PE_OK) return st;                    // dh [L][I]
+    if (g && g->w_down) {
+      if ((st = packT(PACK_ROW, dxt, H, L, H, packA)) != PE_OK) return st;
+      if ((st = packT(PACK_TILED, B.h, 0, L, I, packB)) != PE_OK) return st;
+      if ((st = wgrad(H, I, 0, g->w_down, L)) != PE_OK) return st;
+    }
+    if ((st = chk(launch_swiglu_bwd(dt, gbuf, B.gu, L, I, ws + SL.dgu, s), "SwiGLU backward launch")) != PE_OK)
+      return st;
+    if ((st = dgrad(ws + SL.dgu, 2L * I, Lw.guT, gbuf)) != PE_OK) return st;         // du2 [L][H]
+    if (g && (g->w_gate || g->w_up)) {
+      if ((st = packT(PACK_ROW, ws + SL.dgu, 2L * I, L, 2 * I, packA)) != PE_OK) return st;
+      if ((st = packT(PACK_TILED, B.u2, 0, L, H, packB)) != PE_OK) return st;
+      if (g->w_gate && (st = wgrad(I, H, 0, g->w_gate, L)) != PE_OK) return st;
+      if (g->w_up && (st = wgrad(I, H, I, g->w_up, L)) != PE_OK) return st;
+    }
+    // mlp norm: dxm = dx + RMSNorm'(xm) du2
+    if ((st = chk(launch_rms_bwd(dt, B.xm, Lw.mlp_norm, gbuf, dx, L, H, c.rms_eps, dx2, dxt, part, s),
+                  "RMSNorm backward launch")) != PE_OK) return st;
+    if (g && g->mlp_norm && (st = chk(launch_colsum_acc(part, nblk, H, g->mlp_norm, s), "gain sum")) != PE_OK)
+      return st;
+    // O projection: xm = x + attn W_o^T
+    if ((st = dgrad(dxt, H, Lw.oT, gbuf)) != PE_OK) return st;                       // d attn [L][nq hd]
+    if (g && g->wo) {
+      if ((st = packT(PACK_ROW, dxt, H, L, H, packA)) != PE_OK) return st;
+      if ((st = packT(PACK_TILED, B.attn, 0, L, nq * hd, packB)) != PE_OK) return st;
+      if ((st = wgrad(H, nq * hd, 0, g->wo, L)) != PE_OK) return st;
+    }
+    // attention
+    if ((st = chk(launch_attn_bwd_pre(dt, gbuf, B.attn, L, nq, hd, ws + SL.doutt, F(SL.D), s),
+                  "attention backward launch")) != PE_OK) return st;
+    {
+      AttnBwdParams a{};
+      a.q = B.q; a.k0 = B.k0; a.v0 = B.v0; a.kall = B.kall; a.vall = B.vall;
+      a.dout = ws + SL.doutt; a.lse = B.lse; a.D = F(SL.D);
+      a.anc = anc; a.dep = dep; a.inv = inv;
+      a.L = L; a.n = n; a.K = K; a.nq = nq; a.nkv = nkv; a.hd = hd; a.G = nq / nkv;
+      a.scale = (float)(1.0 / sqrt((double)hd));
+      a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+      a.dq = F(SL.dq); a.dk = F(SL.dk); a.dv = F(SL.dv);
+      if ((st = chk(launch_attn_bwd(dt, a, s), "attention backward launch")) != PE_OK) return st;
+    }
+    if ((st = chk(launch_rope_bwd(dt, F(SL.dq), F(SL.dk), F(SL.dv), anc, dep, m->inv_freq, L, nq, nkv, hd,
+                                  ws + SL.dqkv, s), "RoPE backward launch")) != PE_OK) return st;
+    if ((st = dgrad(ws + SL.dqkv, QKV, Lw.qkvT, gbuf)) != PE_OK) return st;          // du1 [L][H]
+    if (g && (g->wq || g->wk || g->wv)) {
+      if ((st = packT(PACK_ROW, ws + SL.dqkv, QKV, L, QKV, packA)) != PE_OK) return st;
+      if ((st = packT(PACK_TILED, B.u1, 0, L, H, packB)) != PE_OK) return st;
+      if (g->wq && (st = wgrad(nq * hd, H, 0, g->wq, L)) != PE_OK) return st;
+      if (g->wk && (st = wgrad(nkv * hd, H, nq * hd, g->wk, L)) != PE_OK) return st;
+      if (g->wv && (st = wgrad(nkv * hd, H, (nq + nkv) * hd, g->wv, L)) != PE_OK) return st;
+    }
+    // attn norm: dx = dxm + RMSNorm'(x) du1
+    if ((st = chk(launch_rms_bwd(dt, B.x, Lw.attn_norm, gbuf, dx2, L, H, c.rms_eps, dx, dxt, part, s),
+                  "RMSNorm backward launch")) != PE_OK) return st;
+    if (g && g->attn_norm && (st = chk(launch_colsum_acc(part, nblk, H, g->attn_norm, s), "gain sum")) != PE_OK)
+      return st;
+  }
+
+  // ---- input fusion: depth-0 cells E[x_p] + fc(h_p), deeper cells mask_emb + fc(h_shared)
+  void *dntp = ws + SL.dntp;
+  float *dsh = F(SL.dshared);
+  if ((st = chk(launch_zero(dntp, (size_t)n * H * m->esz, s), "zero launch")) != PE_OK) return st;
+  if ((st = chk(launch_zero(dsh, (size_t)H * 4, s), "zero launch")) != PE_OK) return st;
+  if ((st = chk(launch_fuse_bwd(dt, dx, anc, dep, L, n, H, dntp, gr->embed_rows, part, s), "fusion backward")) !=
+      PE_OK) return st;
+  if ((st = chk(launch_colsum_acc(part, nblk, H, dsh, s), "column sum")) != PE_OK) return st;
+  if (gr->mask_emb && (st = chk(launch_colsum_acc(part, nblk, H, gr->mask_emb, s), "column sum")) != PE_OK)
+    return st;
+  if (gr->h_shared &&
+      (st = chk(launch_matvec_acc(dt, m->fcT.ptr, m->fcT.NT, m->fcT.KT, 3 * H, dsh, H, gr->h_shared, s),
+                "shared-state gradient")) != PE_OK) return st;
+  if (gr->fc) {
+    if ((st = packT(PACK_ROW, dntp, H, n, H, packA)) != PE_OK) return st;
+    if ((st = packT(PACK_ROW, hidden3, 3L * H, n, 3 * H, packB)) != PE_OK) return st;
+    if ((st = wgrad(H, 3 * H, 0, gr->fc, n)) != PE_OK) return st;
+    if ((st = chk(launch_outer_acc(dt, dsh, h_shared, H, 3 * H, gr->fc, s), "outer product")) != PE_OK) return st;
+  }
+  (void)KTL;
+  (void)e;
+  return PE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -878,8 +1152,13 @@ pe_status pe_train_forward(const pe_model *m, const pe_mask *mask, int32_t N, in
                            const void *hidden3, const int32_t *token_ids, const void *mask_emb,
                            const void *h_shared, const int32_t *rows, int32_t L, void *logits_out,
                            int32_t *argmax_out, void *workspace, size_t ws_bytes, void *stream) {
+  pe_status st = check_train_args(m, mask, N, n, K, hidden3, token_ids, mask_emb, h_shared, rows, L, logits_out,
+                                  workspace);
+  if (st != PE_OK) return st;
+  const TrainLayout W = train_layout(m, n, K, L);
+  if (ws_bytes < W.total) return fail(PE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
   return enqueue_train(m, mask, N, n, K, hidden3, token_ids, mask_emb, h_shared, rows, L, 0, nullptr, L,
-                       logits_out, argmax_out, workspace, ws_bytes, stream);
+                       logits_out, argmax_out, W, reinterpret_cast<char *>(workspace), nullptr, stream);
 }
 
 pe_status pe_train_forward_chunk(const pe_model *m, const pe_mask *mask, int32_t N, int32_t n, int32_t K,
@@ -892,8 +1171,129 @@ pe_status pe_train_forward_chunk(const pe_model *m, const pe_mask *mask, int32_t
   if (L_out < 1) return fail(PE_ERR_INVALID_ARGUMENT, "L_out=%d must be >= 1", L_out);
   if (n_lead < L && (logits_out || argmax_out) && !out_rows)
     return fail(PE_ERR_INVALID_ARGUMENT, "out_rows must be non-NULL when cells past n_lead write outputs");
+  pe_status st = check_train_args(m, mask, N, n, K, hidden3, token_ids, mask_emb, h_shared, cells, L, logits_out,
+                                  workspace);
+  if (st != PE_OK) return st;
+  const TrainLayout W = train_layout(m, n, K, L);
+  if (ws_bytes < W.total) return fail(PE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
   return enqueue_train(m, mask, N, n, K, hidden3, token_ids, mask_emb, h_shared, cells, L, n_lead, out_rows,
-                       L_out, logits_out, argmax_out, workspace, ws_bytes, stream);
+                       L_out, logits_out, argmax_out, W, reinterpret_cast<char *>(workspace), nullptr, stream);
+}
+
+pe_status pe_model_prepare_backward(pe_model *m, const pe_weights *w, void *stream) {
+  if (!m || !w) return fail(PE_ERR_INVALID_ARGUMENT, "model and weights must be non-NULL");
+  const pe_config &c = m->cfg;
+  if (!w->fc || !w->lm_head || (c.n_layers > 0 && !w->layers))
+    return fail(PE_ERR_INVALID_ARGUMENT, "a required weight pointer is NULL");
+  if (c.hidden % m->ktile || c.intermediate % m->ktile)
+    return fail(PE_ERR_UNSUPPORTED, "the backward needs hidden and intermediate multiples of %d", m->ktile);
+  if (m->has_bwd) return PE_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int H = c.hidden, I = c.intermediate, hd = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const int kt = m->ktile;
+  // Tiles of the transpose of row-major sources stacked along the
+  // transpose's k axis (source i holds rows[i] rows of cols columns).
+  auto build = [&](Tiled &t, const void *const *src, const int *rows, int nsrc, int cols) -> pe_status {
+    int K = 0;
+    for (int i = 0; i < nsrc; ++i) K += rows[i];
+    t.N = cols; t.K = K; t.NT = (cols + 15) / 16; t.KT = (K + kt - 1) / kt;
+    const size_t bytes = (size_t)t.NT * t.KT * 1024;
+    if (bytes > 0x7FFFF000ull) return fail(PE_ERR_UNSUPPORTED, "transposed weight tiles exceed 2 GiB");
+    hipError_t e = hipMalloc(&t.ptr, bytes);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(transposed weight tiles)");
+    m->allocs.push_back(t.ptr);
+    int kt0 = 0;
+    for (int i = 0; i < nsrc; ++i) {
+      if (i + 1 < nsrc && rows[i] % kt) return fail(PE_ERR_UNSUPPORTED, "stacked weight rows not a multiple of %d", kt);
+      e = launch_pack_t(c.dtype, PACK_ROW, src[i], cols, rows[i], cols, t.ptr, t.KT, kt0, s);
+      if (e != hipSuccess) return hip_fail(e, "transposed tiling launch");
+      kt0 += rows[i] / kt;
+    }
+    return PE_OK;
+  };
+  pe_status st;
+  {
+    const void *src[1] = {w->lm_head};
+    const int rows[1] = {c.vocab};
+    if ((st = build(m->lmT, src, rows, 1, H)) != PE_OK) return st;
+  }
+  {
+    const void *src[1] = {w->fc};
+    const int rows[1] = {H};
+    if ((st = build(m->fcT, src, rows, 1, 3 * H)) != PE_OK) return st;
+  }
+  for (int l = 0; l < c.n_layers; ++l) {
+    const pe_layer_weights &Lw = w->layers[l];
+    if (!Lw.wq || !Lw.wk || !Lw.wv || !Lw.wo || !Lw.w_gate || !Lw.w_up || !Lw.w_down)
+      return fail(PE_ERR_INVALID_ARGUMENT, "layer %d has a NULL weight pointer", l);
+    LayerT &T = m->layers[l];
+    const void *qkv[3] = {Lw.wq, Lw.wk, Lw.wv};
+    const int qkv_rows[3] = {nq * hd, nkv * hd, nkv * hd};
+    const void *o[1] = {Lw.wo};
+    const int o_rows[1] = {H};
+    const void *gu[2] = {Lw.w_gate, Lw.w_up};
+    const int gu_rows[2] = {I, I};
+    const void *dn[1] = {Lw.w_down};
+    const int dn_rows[1] = {H};
+    if ((st = build(T.qkvT, qkv, qkv_rows, 3, H)) || (st = build(T.oT, o, o_rows, 1, nq * hd)) ||
+        (st = build(T.guT, gu, gu_rows, 2, H)) || (st = build(T.downT, dn, dn_rows, 1, I)))
+      return st;
+  }
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize after transposed tiling");
+  m->has_bwd = true;
+  return PE_OK;
+}
+
+pe_status pe_train_step_workspace_size(const pe_model *m, int32_t N, int32_t n, int32_t K, int32_t L,
+                                       size_t *bytes) {
+  if (!m || !bytes) return fail(PE_ERR_INVALID_ARGUMENT, "model and bytes must be non-NULL");
+  if (N < 0 || N > m->cfg.n_layers)
+    return fail(PE_ERR_INVALID_ARGUMENT, "N=%d outside [0, n_layers=%d]", N, m->cfg.n_layers);
+  if (n < 1 || K < 1 || L < 1 || (long)L > (long)n * K || L > kTrainRowsMax)
+    return fail(PE_ERR_INVALID_ARGUMENT, "need n >= 1 and 1 <= L <= min(n*K, %ld)", kTrainRowsMax);
+  *bytes = step_layout(m, N, n, K, L).total;
+  return PE_OK;
+}
+
+pe_status pe_train_step(const pe_model *m, const pe_mask *mask, int32_t N, int32_t n, int32_t K,
+                        const void *hidden3, const int32_t *token_ids, const void *mask_emb, const void *h_shared,
+                        const int32_t *cells, int32_t L, int32_t n_lead, const int32_t *labels, float loss_scale,
+                        float *loss_out, const pe_grads *grads, void *workspace, size_t ws_bytes, void *stream) {
+  pe_status st = check_train_args(m, mask, N, n, K, hidden3, token_ids, mask_emb, h_shared, cells, L, nullptr,
+                                  workspace);
+  if (st != PE_OK) return st;
+  const pe_config &c = m->cfg;
+  if (!m->has_bwd) return fail(PE_ERR_INVALID_ARGUMENT, "call pe_model_prepare_backward before pe_train_step");
+  if (!labels || !grads) return fail(PE_ERR_INVALID_ARGUMENT, "labels and grads must be non-NULL");
+  if (N > 0 && !grads->layers) return fail(PE_ERR_INVALID_ARGUMENT, "grads->layers must be non-NULL when N > 0");
+  if (n_lead < 0 || n_lead > L) return fail(PE_ERR_INVALID_ARGUMENT, "n_lead=%d outside [0, L=%d]", n_lead, L);
+  if (c.head_dim != 64 && !(c.dtype == PE_BF16 && c.head_dim == 128))
+    return fail(PE_ERR_UNSUPPORTED, "the attention backward supports head_dim 64 (and 128 for bf16)");
+  if (c.n_q_heads / c.n_kv_heads > 64) return fail(PE_ERR_UNSUPPORTED, "GQA groups above 64 heads");
+  if (c.hidden > 4096) return fail(PE_ERR_UNSUPPORTED, "hidden above 4096");
+  const StepLayout SL = step_layout(m, N, n, K, L);
+  if (ws_bytes < SL.total) return fail(PE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, SL.total);
+  char *ws = reinterpret_cast<char *>(workspace);
+  StepSaves sv;
+  sv.layer.resize(N);
+  auto P = [&](const void *off) -> void * { return ws + reinterpret_cast<size_t>(off); };
+  for (int l = 0; l < N; ++l) {
+    const StepLayer &O = SL.off[l];
+    StepLayer &B = sv.layer[l];
+    B.x = reinterpret_cast<float *>(P(O.x)); B.xm = reinterpret_cast<float *>(P(O.xm));
+    B.lse = reinterpret_cast<float *>(P(O.lse));
+    B.u1 = P(O.u1); B.q = P(O.q); B.kall = P(O.kall); B.vall = P(O.vall); B.k0 = P(O.k0); B.v0 = P(O.v0);
+    B.attn = P(O.attn); B.u2 = P(O.u2); B.gu = P(O.gu); B.h = P(O.h);
+  }
+  sv.xN = reinterpret_cast<float *>(ws + SL.xN);
+  sv.z = ws + SL.z;
+  sv.logits = ws + SL.logits;
+  if ((st = enqueue_train(m, mask, N, n, K, hidden3, token_ids, mask_emb, h_shared, cells, L, n_lead, nullptr, L,
+                          nullptr, nullptr, SL.tl, ws, &sv, stream)) != PE_OK)
+    return st;
+  return enqueue_backward(m, N, n, K, hidden3, h_shared, L, n_lead, labels, loss_scale, loss_out, grads, SL, sv, ws,
+                          reinterpret_cast<hipStream_t>(stream));
 }
 
 pe_status pe_profile_enable(pe_model *m, int32_t enable) {

@@ -43,10 +43,16 @@ template <> __device__ __forceinline__ void store2<bf16_t>(bf16_t *dst, float a,
 // Gate/up tile rows of strip s: lane group g holds gate rows 8s+2g, 8s+2g+1
 // in r = 0, 1 and the matching up rows in r = 2, 3.  h is written in the
 // fragment-tile layout that the down projection reads.
-template <typename T>
+template <typename T, bool SAVE>
 __device__ __forceinline__ void epi_tile_swiglu(const TileGemmParams &p, int m, int s, int g, floatx4 v) {
   T *dst = reinterpret_cast<T *>(p.h) + frag_off<T>(m, 8 * s + 2 * g, p.I / Frag<T>::KTILE);
   store2<T>(dst, silu_f(v[0]) * v[2], silu_f(v[1]) * v[3]);
+  if constexpr (SAVE) {
+    // Pre-activations for the backward: gate at column i, up at I + i.
+    T *gu = reinterpret_cast<T *>(p.gu) + (long)m * 2 * p.I + 8 * s + 2 * g;
+    store2<T>(gu, v[0], v[1]);
+    store2<T>(gu + p.I, v[2], v[3]);
+  }
 }
 
 // q|k|v tile rows n..n+3 of row m.  For q and k heads, r = 2t + hi holds
@@ -328,7 +334,9 @@ void k_gemm_tile(TileGemmParams p) {
               floatx4 *dst = reinterpret_cast<floatx4 *>(p.C + (long)m * p.ldc + n);
               *dst = *dst + acc[i][j];
             } else if constexpr (EPI == BEPI_SWIGLU) {
-              epi_tile_swiglu<T>(p, m, s, g, acc[i][j]);
+              epi_tile_swiglu<T, false>(p, m, s, g, acc[i][j]);
+            } else if constexpr (EPI == BEPI_SWIGLU_SAVE) {
+              epi_tile_swiglu<T, true>(p, m, s, g, acc[i][j]);
             } else {
               epi_tile_qkv<T>(p, m, n, acc[i][j]);
             }
@@ -351,13 +359,13 @@ hipError_t launch_gemm_tile(int dtype, int epi, const TileGemmParams &p, int num
   if (dtype == 1) {
     switch (epi) {
       PE_TILE_CASE(bf16_t, 0) PE_TILE_CASE(bf16_t, 1) PE_TILE_CASE(bf16_t, 2) PE_TILE_CASE(bf16_t, 3)
-      PE_TILE_CASE(bf16_t, 4) PE_TILE_CASE(bf16_t, 5)
+      PE_TILE_CASE(bf16_t, 4) PE_TILE_CASE(bf16_t, 5) PE_TILE_CASE(bf16_t, 6)
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (epi) {
       PE_TILE_CASE(float, 0) PE_TILE_CASE(float, 1) PE_TILE_CASE(float, 2) PE_TILE_CASE(float, 3)
-      PE_TILE_CASE(float, 4) PE_TILE_CASE(float, 5)
+      PE_TILE_CASE(float, 4) PE_TILE_CASE(float, 5) PE_TILE_CASE(float, 6)
       default: return hipErrorInvalidValue;
     }
   }

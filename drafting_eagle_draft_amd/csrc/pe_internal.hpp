@@ -148,6 +148,7 @@ enum BigEpi : int {
   BEPI_SWIGLU = 3,  // MAP_GATEUP rows: h[M][I] = silu(gate) * up
   BEPI_QKV = 4,     // MAP_QKV rows: RoPE at position anc+dep, scatter q/k/v
   BEPI_LMHEAD_MAP = 5,  // BEPI_LMHEAD writing row m to out_rows[m - row_skip]
+  BEPI_SWIGLU_SAVE = 6, // BEPI_SWIGLU that also keeps gate | up [M][2I] (dtype) for the backward
 };
 
 struct TileGemmParams {
@@ -169,6 +170,7 @@ struct TileGemmParams {
   // SWIGLU: h in the fragment-tile layout of an [M][I] matrix
   void *h;
   int I;
+  void *gu;  // SWIGLU_SAVE: gate | up pre-activations [M][2I], row-major dtype
   // QKV: q [M][nq][hd], kall/vall [M][nkv][hd], depth-0 rows also to
   // k0/v0 [n][nkv][hd] at their position.
   void *q, *kall, *vall, *k0, *v0;
@@ -207,8 +209,72 @@ struct TrainAttnParams {
   int L, n, K, nq, nkv, hd, G;
   float scale_log2;
   void *out;                // [L][nq*hd] dtype, fragment-tile layout
+  float *lse;               // optional [L][nq]: log2 of each softmax denominator in scaled-score units
 };
 
 hipError_t launch_attn_train(int dtype, const TrainAttnParams &p, hipStream_t s);
+
+// ---- training backward (train_bwd.hip) ----
+
+// Transposing copy into the fragment-tile layout: dst holds the tiles of the
+// [C][R] transpose of a source [R][C] (rows of dst = source columns, k =
+// source rows), k tiles kt0 .. kt0 + ceil(R/KTILE) - 1 of a destination with
+// KTd k tiles per 16-row group; zero past R and C.  Source kinds: row-major
+// dtype, row-major fp32 (rounded to the dtype), or fragment tiles of [R][C].
+enum PackSrc : int { PACK_ROW = 0, PACK_ROW_F32 = 1, PACK_TILED = 2 };
+hipError_t launch_pack_t(int dtype, int src_kind, const void *src, long ld, int R, int C, void *dst, int KTd,
+                         int kt0, hipStream_t s);
+
+// Cross-entropy rows: logits [L][V] dtype in place -> loss_scale * (softmax -
+// onehot(label)) for scored rows (i >= n_lead, label of position
+// anc[i] + dep[i] >= 0), zero for the others; row_loss[i] = loss_scale *
+// (logsumexp - logit[label]) or 0.
+hipError_t launch_ce_rows(int dtype, void *logits, int L, int V, const int *anc, const int *dep,
+                          const int *labels, int n, int n_lead, float loss_scale, float *row_loss, hipStream_t s);
+// *out += sum of x[0..n) in a fixed order.
+hipError_t launch_sum_acc(const float *x, long n, float *out, hipStream_t s);
+
+// RMSNorm backward over rows: dx = dres + r (g . dy) - x r^3 mean(g . dy . x)
+// (dres may be NULL); also dx in the dtype (row-major) and per-block column
+// partials of dy . x r into part [ceil(L/64)][H].
+hipError_t launch_rms_bwd(int dtype, const float *x, const float *gain, const float *dy, const float *dres,
+                          int L, int H, float eps, float *dx, void *dx_t, float *part, hipStream_t s);
+// out[j] += sum over blocks of part[b][j], in block order.
+hipError_t launch_colsum_acc(const float *part, int nblk, int H, float *out, hipStream_t s);
+
+// SwiGLU backward: dgu[m][i] = dh ub silu'(ga), dgu[m][I + i] = dh silu(ga).
+hipError_t launch_swiglu_bwd(int dtype, const float *dh, const void *gu, int L, int I, void *dgu, hipStream_t s);
+
+struct AttnBwdParams {
+  const void *q, *k0, *v0, *kall, *vall;  // as TrainAttnParams
+  const void *dout;                       // [L][nq][hd] dtype, gradient of the attention output
+  const float *lse, *D;                   // [L][nq]
+  const int *anc, *dep, *inv;
+  int L, n, K, nq, nkv, hd, G;
+  float scale_log2, scale;
+  float *dq;                              // [L][nq][hd] fp32
+  float *dk, *dv;                         // [L][nkv][hd] fp32 (every kept row)
+};
+// D[i][h] = sum_d dout . out (out in the fragment-tile layout of [L][nq*hd]);
+// dout fp32 [L][nq*hd] -> dout_t (dtype, row-major).
+hipError_t launch_attn_bwd_pre(int dtype, const float *dout, const void *out, int L, int nq, int hd,
+                               void *dout_t, float *D, hipStream_t s);
+hipError_t launch_attn_bwd(int dtype, const AttnBwdParams &p, hipStream_t s);
+
+// Rotate dq, dk back by -position and pack [dq | dk | dv] into [L][(nq + 2 nkv) hd] dtype.
+hipError_t launch_rope_bwd(int dtype, const float *dq, const float *dk, const float *dv, const int *anc,
+                           const int *dep, const double *inv_freq, int L, int nq, int nkv, int hd, void *out,
+                           hipStream_t s);
+
+// Input-fusion backward: d_ntp[p] (dtype [n][H]) = dx0 of the depth-0 row of
+// position p (zero when absent); embed_rows[p] += the same (fp32); per-block
+// column partials of the deeper rows' dx0 into part [ceil(L/64)][H].
+hipError_t launch_fuse_bwd(int dtype, const float *dx0, const int *anc, const int *dep, int L, int n, int H,
+                           void *d_ntp, float *embed_rows, float *part, hipStream_t s);
+// G[i][j] += a[i] * b[j] (b in the dtype).
+hipError_t launch_outer_acc(int dtype, const float *a, const void *b, int R, int C, float *G, hipStream_t s);
+// y[N] += W x with W in the fragment-tile layout and x fp32.
+hipError_t launch_matvec_acc(int dtype, const u32x4 *wt, int NT, int KT, int N, const float *x, int K, float *y,
+                             hipStream_t s);
 
 }  // namespace pe

@@ -453,6 +453,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
     float l_tot = l_lane[qb];
     l_tot += shfl_xor_f(l_tot, 16);
     l_tot += shfl_xor_f(l_tot, 32);
+    // Softmax statistics for the backward: weights are 2^(s * scale_log2 - lse).
+    if (p.lse && valid[qb] && g == 0) p.lse[(long)row[qb] * p.nq + gk * G + hl[qb]] = m_run[qb] + log2f(l_tot);
     if (valid[qb]) {
       const float inv_l = 1.0f / l_tot;
       // Output row in the fragment-tile layout of the [L][nq*hd]

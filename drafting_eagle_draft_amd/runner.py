@@ -27,7 +27,7 @@ def stream_handle() -> int:
 class Drafter:
     """A pe_model built from host weights (dict from synth.drafter_weights)."""
 
-    def __init__(self, cfg, weights, device="cuda:0"):
+    def __init__(self, cfg, weights, device="cuda:0", backward=False):
         self.cfg = cfg
         self.device = torch.device(device)
         torch.cuda.set_device(self.device)
@@ -49,6 +49,8 @@ class Drafter:
                         cfg.intermediate, cfg.vocab, cfg.rope_theta, cfg.rms_eps,
                         pe.PE_BF16 if cfg.dtype == "bf16" else pe.PE_F32)
         self.handle = pe.pe_model_create(c, w, stream_handle())
+        if backward:
+            pe.pe_model_prepare_backward(self.handle, w, stream_handle())
         del keep  # the model holds its own tiled copies of every weight but the embedding
 
     def close(self):
@@ -346,3 +348,74 @@ class PartitionedTrain:
         torch.cuda.synchronize()
         return (self.argmax.cpu().numpy(),
                 self.logits.float().cpu().numpy() if self.logits is not None else None)
+
+
+LAYER_GRADS = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
+
+
+class Grads:
+    """Zeroed fp32 gradient buffers on the device in the weights' layouts,
+    accumulated by pe_train_step calls."""
+
+    def __init__(self, cfg, n, N=None, device="cuda:0"):
+        N = cfg.n_layers if N is None else N
+        H, I, hd = cfg.hidden, cfg.intermediate, cfg.head_dim
+        nq, nkv, V = cfg.n_q_heads, cfg.n_kv_heads, cfg.vocab
+        z = lambda *shape: torch.zeros(shape, dtype=torch.float32, device=device)
+        self.t = {"fc": z(H, 3 * H), "final_norm": z(H), "lm_head": z(V, H), "mask_emb": z(H),
+                  "h_shared": z(3 * H), "embed_rows": z(n, H)}
+        shapes = {"attn_norm": (H,), "wq": (nq * hd, H), "wk": (nkv * hd, H), "wv": (nkv * hd, H),
+                  "wo": (H, nq * hd), "mlp_norm": (H,), "w_gate": (I, H), "w_up": (I, H), "w_down": (H, I)}
+        self.layers = [{k: z(*shapes[k]) for k in LAYER_GRADS} for _ in range(N)]
+        self._lg = (pe.PeLayerGrads * max(1, N))()
+        for l, g in enumerate(self.layers):
+            self._lg[l] = pe.PeLayerGrads(*[g[k].data_ptr() for k in LAYER_GRADS])
+        self.c = pe.PeGrads(*[self.t[k].data_ptr() for k in ("fc", "final_norm", "lm_head", "mask_emb",
+                                                               "h_shared", "embed_rows")], self._lg)
+
+    def numpy(self):
+        torch.cuda.synchronize()
+        out = {k: v.cpu().numpy() for k, v in self.t.items()}
+        out["layers"] = [{k: v.cpu().numpy() for k, v in g.items()} for g in self.layers]
+        return out
+
+
+class TrainStep:
+    """One pe_train_step call (forward, loss, backward) on device buffers.
+
+    cells: kept cells (whole sequence, or one chunk's cells with n_lead);
+    labels: host int [n] (label of position p; negative: not scored);
+    loss_scale defaults to 1 / (number of scored cells)."""
+
+    def __init__(self, drafter: Drafter, mask: TrainMask, inp, cells, labels, N=None, n_lead=0, n=None,
+                 loss_scale=None, grads: Grads | None = None):
+        cfg, dev = drafter.cfg, drafter.device
+        self.N = cfg.n_layers if N is None else N
+        self.n = int(len(inp["token_ids"])) if n is None else n
+        self.K = mask.K
+        self.hidden3 = to_device(inp["hidden3"], cfg, dev)
+        self.token_ids = torch.from_numpy(np.asarray(inp["token_ids"], np.int32)).to(dev)
+        self.mask_emb = to_device(inp["mask_emb"], cfg, dev)
+        self.h_shared = to_device(inp["h_shared"], cfg, dev)
+        cells = np.ascontiguousarray(cells, np.int32)
+        self.cells = torch.from_numpy(cells).to(dev)
+        self.L = int(cells.size)
+        self.n_lead = n_lead
+        labels = np.asarray(labels, np.int32)
+        self.labels = torch.from_numpy(labels).to(dev)
+        if loss_scale is None:
+            pos = cells[n_lead:] // self.K
+            loss_scale = 1.0 / max(1, int(np.sum(labels[pos] >= 0)))
+        self.loss_scale = float(loss_scale)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.grads = grads if grads is not None else Grads(cfg, int(len(inp["token_ids"])), self.N, dev)
+        nbytes = pe.pe_train_step_workspace_size(drafter.handle, self.N, self.n, self.K, self.L)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        pe.pe_workspace_init(self.ws.data_ptr(), self.ws.numel(), stream_handle())
+
+    def launch(self, drafter: Drafter, mask: TrainMask, stream: int | None = None):
+        pe.pe_train_step(drafter.handle, mask.handle, self.N, self.n, self.K, self.hidden3.data_ptr(),
+                         self.token_ids.data_ptr(), self.mask_emb.data_ptr(), self.h_shared.data_ptr(),
+                         self.cells.data_ptr(), self.L, self.n_lead, self.labels.data_ptr(), self.loss_scale,
+                         self.loss.data_ptr(), self.grads.c, self.ws.data_ptr(), self.ws.numel(),
+                         stream_handle() if stream is None else stream)

@@ -315,6 +315,63 @@ pe_status pe_train_forward_chunk(const pe_model *m, const pe_mask *mask, int32_t
                                  const int32_t *out_rows, int32_t L_out, void *logits_out, int32_t *argmax_out,
                                  void *workspace, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Training step: loss and gradients over a COD layout ("P-EAGLE: A
+ * Technical Deep Dive into Parallel Speculative Decoding", section "Memory
+ * and Training Complexity": the K-depth layout trains in one forward and
+ * backward pass, gradients accumulated over the chunks of a sequence
+ * partition; "P-EAGLE: Parallel-Drafting EAGLE with Scalable Training",
+ * sections 3 and 3.2; learnable mask embedding, hidden state and embedding
+ * table from "Speeding LLM inference with P-EAGLE in vLLM Speculators",
+ * sections "A learnable mask parameter" and "Learnable embedding").
+ *
+ * Cell (p, d) drafts the token after position p: its loss is the
+ * cross-entropy of its logits against labels[p] (negative: not scored).
+ * Gradients are fp32, in the weights' own [out, in] row-major layouts, and
+ * are ADDED to the caller's buffers, so calls over the chunks of a
+ * partition (each with the whole sequence's loss_scale) accumulate the
+ * whole sequence's gradients.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  float *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *w_gate, *w_up, *w_down;  /* NULL: not wanted */
+} pe_layer_grads;
+
+typedef struct {
+  float *fc;          /* [H, 3H] */
+  float *final_norm;  /* [H] */
+  float *lm_head;     /* [V, H] */
+  float *mask_emb;    /* [H] */
+  float *h_shared;    /* [3H] */
+  float *embed_rows;  /* [n, H]: gradient of the embedding row looked up at position p (depth-0 cells); the
+                         caller adds row p into its table's row token_ids[p] */
+  const pe_layer_grads *layers;  /* host array [N] */
+} pe_grads;
+
+/* Builds the transposed weight tiles the backward's data gradients read,
+ * from the same weights the model was created from (device, row-major).
+ * Allocates once (about the size of the model's own tiles); later calls
+ * return PE_OK at once. */
+pe_status pe_model_prepare_backward(pe_model *m, const pe_weights *w, void *stream);
+
+/* Workspace bytes of pe_train_step for N layers, n positions, block K and L cells. */
+pe_status pe_train_step_workspace_size(const pe_model *m, int32_t N, int32_t n, int32_t K, int32_t L,
+                                       size_t *bytes);
+
+/*
+ * Forward, loss and backward of the first N layers over L cells (device
+ * int32 [L], as for pe_train_forward or pe_train_forward_chunk; n positions).
+ * The first n_lead cells are not scored (a chunk's depth-0 completion from
+ * earlier segments).  labels: device int32 [n].  *loss_out (device fp32, or
+ * NULL) += loss_scale * the summed cross-entropy of the scored cells; every
+ * non-NULL gradient pointer in grads receives += its gradient.  Needs
+ * pe_model_prepare_backward, head_dim 64 (or 128 for bf16), at most 64 query
+ * heads per kv head and hidden <= 4096.
+ */
+pe_status pe_train_step(const pe_model *m, const pe_mask *mask, int32_t N, int32_t n, int32_t K,
+                        const void *hidden3, const int32_t *token_ids, const void *mask_emb, const void *h_shared,
+                        const int32_t *cells, int32_t L, int32_t n_lead, const int32_t *labels, float loss_scale,
+                        float *loss_out, const pe_grads *grads, void *workspace, size_t ws_bytes, void *stream);
+
 /* Thread-local description of the last non-OK status of this thread. */
 const char *pe_last_error(void);
 
