@@ -923,9 +923,10 @@ pe_status enqueue_train(const pe_model *m, const pe_mask *mask, int32_t N, int32
 struct StepLayout {
   TrainLayout tl{};
   std::vector<StepLayer> off;  // byte offsets stored in the pointer fields
-  size_t xN = 0, z = 0, logits = 0, row_loss = 0;
+  size_t xN = 0, z = 0, logits = 0, dlA = 0, row_loss = 0;
   size_t dx = 0, dx2 = 0, dxt = 0, gbuf = 0, dgu = 0, doutt = 0, D = 0, dq = 0, dk = 0, dv = 0, dqkv = 0;
-  size_t packA = 0, packB = 0, part = 0, dntp = 0, dshared = 0;
+  size_t packA = 0, packB = 0, part = 0, dntp = 0, dshared = 0, pk = 0, pv = 0, qt = 0;
+  int qsplit = 1;
   size_t total = 0;
 };
 
@@ -967,6 +968,7 @@ StepLayout step_layout(const pe_model *m, int N, long n, int K, long L) {
   t.xN = take(L * H * 4);
   t.z = take(Lp * H * esz);
   t.logits = take(L * V * esz);
+  t.dlA = take(tiles_bytes(L, (long)V, m->ktile));
   t.row_loss = take(L * 4);
   const size_t wide = std::max(std::max(H, I), nq * hd);
   t.dx = take(L * H * 4);
@@ -992,6 +994,12 @@ StepLayout step_layout(const pe_model *m, int N, long n, int K, long L) {
   t.part = take((size_t)((L + 63) / 64) * H * 4);
   t.dntp = take(n * H * esz);
   t.dshared = take(H * 4);
+  // Query shares per depth-0 key tile in the attention backward: about 256
+  // rows each, at most 16.
+  t.qsplit = (int)std::min<long>(16, std::max<long>(1, L / 256));
+  t.pk = take((size_t)t.qsplit * n * nkv * hd * 4);
+  t.pv = take((size_t)t.qsplit * n * nkv * hd * 4);
+  t.qt = take(attn_bwd_tile_bytes((int)L, (int)nkv, (int)(nq / nkv), (int)hd, c.dtype));
   t.total = off;
   return t;
 }
@@ -1042,13 +1050,14 @@ pe_status enqueue_backward(const pe_model *m, int32_t N, int32_t n, int32_t K, c
     return chk(launch_pack_t(dt, kind, src, ld, R, C, dst, (R + kt - 1) / kt, 0, s), "pack launch");
   };
 
-  // ---- loss and LM head
-  if ((st = chk(launch_ce_rows(dt, sv.logits, L, V, anc, dep, labels, n, n_lead, loss_scale, F(SL.row_loss), s),
-                "cross-entropy launch")) != PE_OK) return st;
+  // ---- loss and LM head: dlogits as tiles of [L][V] and of [V][L] (packA)
+  void *dlA = ws + SL.dlA;
+  if ((st = chk(launch_ce_tiles(dt, sv.logits, L, V, anc, dep, labels, n, n_lead, loss_scale, F(SL.row_loss), dlA,
+                                packA, s), "cross-entropy launch")) != PE_OK) return st;
   if (loss_out && (st = chk(launch_sum_acc(F(SL.row_loss), L, loss_out, s), "loss sum launch")) != PE_OK) return st;
-  if ((st = dgrad(sv.logits, V, m->lmT, gbuf)) != PE_OK) return st;                 // dz [L][H]
+  if ((st = gemm(dlA, 1, V, L, m->lmT.ptr, m->lmT.NT, m->lmT.KT, m->lmT.N, m->lmT.K, BEPI_STORE, gbuf, H)) != PE_OK)
+    return st;                                                                      // dz [L][H]
   if (gr->lm_head) {
-    if ((st = packT(PACK_ROW, sv.logits, V, L, V, packA)) != PE_OK) return st;      // dlogits^T
     if ((st = packT(PACK_TILED, sv.z, 0, L, H, packB)) != PE_OK) return st;          // z^T
     if ((st = wgrad(V, H, 0, gr->lm_head, L)) != PE_OK) return st;
   }
@@ -1101,6 +1110,12 @@ pe_status enqueue_backward(const pe_model *m, int32_t N, int32_t n, int32_t K, c
       a.scale = (float)(1.0 / sqrt((double)hd));
       a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
       a.dq = F(SL.dq); a.dk = F(SL.dk); a.dv = F(SL.dv);
+      a.qsplit = SL.qsplit; a.pk = F(SL.pk); a.pv = F(SL.pv);
+      {
+        const int G = nq / nkv, QC = 64 / G, Tq = (L + QC - 1) / QC, NC = hd / kt, NKC = dt == 1 ? 2 : 4;
+        a.qt = reinterpret_cast<u32x4 *>(ws + SL.qt);
+        a.qinfo = reinterpret_cast<float4 *>(ws + SL.qt + (size_t)nkv * Tq * (8 * NC + 2 * (hd / 16) * NKC) * 1024);
+      }
       if ((st = chk(launch_attn_bwd(dt, a, s), "attention backward launch")) != PE_OK) return st;
     }
     if ((st = chk(launch_rope_bwd(dt, F(SL.dq), F(SL.dk), F(SL.dv), anc, dep, m->inv_freq, L, nq, nkv, hd,

@@ -225,12 +225,14 @@ enum PackSrc : int { PACK_ROW = 0, PACK_ROW_F32 = 1, PACK_TILED = 2 };
 hipError_t launch_pack_t(int dtype, int src_kind, const void *src, long ld, int R, int C, void *dst, int KTd,
                          int kt0, hipStream_t s);
 
-// Cross-entropy rows: logits [L][V] dtype in place -> loss_scale * (softmax -
-// onehot(label)) for scored rows (i >= n_lead, label of position
-// anc[i] + dep[i] >= 0), zero for the others; row_loss[i] = loss_scale *
-// (logsumexp - logit[label]) or 0.
-hipError_t launch_ce_rows(int dtype, void *logits, int L, int V, const int *anc, const int *dep,
-                          const int *labels, int n, int n_lead, float loss_scale, float *row_loss, hipStream_t s);
+// Cross-entropy rows: for scored rows (i >= n_lead, label of position
+// anc[i] + dep[i] >= 0) dlogits = loss_scale * (softmax - onehot(label)),
+// zero for the others, written as fragment tiles of [L][V] (dlA) and of its
+// transpose [V][L] (dlT); row_loss[i] = loss_scale * (logsumexp -
+// logit[label]) or 0.
+hipError_t launch_ce_tiles(int dtype, const void *logits, int L, int V, const int *anc, const int *dep,
+                           const int *labels, int n, int n_lead, float loss_scale, float *row_loss, void *dlA,
+                           void *dlT, hipStream_t s);
 // *out += sum of x[0..n) in a fixed order.
 hipError_t launch_sum_acc(const float *x, long n, float *out, hipStream_t s);
 
@@ -254,7 +256,13 @@ struct AttnBwdParams {
   float scale_log2, scale;
   float *dq;                              // [L][nq][hd] fp32
   float *dk, *dv;                         // [L][nkv][hd] fp32 (every kept row)
+  int qsplit;                             // query-range splits per depth-0 key tile
+  float *pk, *pv;                         // [qsplit][n][nkv][hd] fp32 partial dK, dV of depth-0 keys
+  u32x4 *qt;                              // query tiles laid out as matrix-core fragments (scratch)
+  float4 *qinfo;                          // per tile and pair: lse, D, anchor (scratch, after qt)
 };
+// Bytes of the query-tile scratch (qt followed by qinfo).
+size_t attn_bwd_tile_bytes(int L, int nkv, int G, int hd, int dtype);
 // D[i][h] = sum_d dout . out (out in the fragment-tile layout of [L][nq*hd]);
 // dout fp32 [L][nq*hd] -> dout_t (dtype, row-major).
 hipError_t launch_attn_bwd_pre(int dtype, const float *dout, const void *out, int L, int nq, int hd,

@@ -11,6 +11,8 @@
 // the transposed operands produced by the packing kernel below.  This file
 // holds the steps between the GEMMs (cross-entropy, RMSNorm, SwiGLU, RoPE,
 // input-fusion backward), the packing kernel, and the attention backward.
+#include <algorithm>
+
 #include "pe_internal.hpp"
 
 namespace pe {
@@ -106,36 +108,117 @@ __global__ __launch_bounds__(256) void k_pack_t(const void *src, long ld, int R,
 }
 
 // ---------------------------------------------------------------------------
-// Cross-entropy rows (one workgroup per kept row).
+// Cross-entropy.
 // ---------------------------------------------------------------------------
+// Cross-entropy over a block of 32 kept rows, writing dlogits straight
+// into the two operand layouts of the LM head's backward GEMMs: fragment
+// tiles of [L][V] (A of dz = dlogits W) and of the transpose [V][L] (A of
+// dW = dlogits^T z).  Pass 1: per-row log-sum-exp, one wave per 4 rows at a
+// time with 16-byte loads (a per-lane maximum over each loaded group, then
+// one rescale).  Pass 2: 256-column blocks through LDS, each written as
+// whole 1 KB tiles of both layouts.  Needs V a multiple of 8.
 template <typename T>
-__global__ __launch_bounds__(256) void k_ce_rows(T *logits, int V, const int *anc, const int *dep,
-                                                 const int *labels, int n, int n_lead, float loss_scale,
-                                                 float *row_loss) {
-  __shared__ float red[4];
-  const int i = blockIdx.x, t = threadIdx.x;
-  T *row = logits + (long)i * V;
-  const int pos = anc[i] + dep[i];
-  const int lab = (i >= n_lead && pos >= 0 && pos < n) ? labels[pos] : -1;
-  if (lab < 0 || lab >= V) {
-    for (int v = t; v < V; v += 256) row[v] = T(0);
-    if (t == 0) row_loss[i] = 0.f;
-    return;
+__global__ __launch_bounds__(512) void k_ce_tiles(const T *logits, int L, int V, const int *anc, const int *dep,
+                                                  const int *labels, int n, int n_lead, float loss_scale,
+                                                  float *row_loss, u32x4 *dlA, u32x4 *dlT) {
+  constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE;
+  constexpr int CB = 256, PITCH = CB + 8;  // columns per block; padded row pitch (elements)
+  constexpr int NTH = 512;
+  __shared__ float s_lse[32];
+  __shared__ int s_lab[32];
+  __shared__ __attribute__((aligned(16))) T tile[32 * PITCH];
+  const int i0 = blockIdx.x * 32, t = threadIdx.x, w = t >> 6, lane = t & 63;
+  // pass 1: wave w takes rows w, w + 8, w + 16, w + 24
+  for (int rr = w; rr < 32; rr += 8) {
+    const int i = i0 + rr;
+    int lab = -1;
+    if (i < L) {
+      const int pos = anc[i] + dep[i];
+      if (i >= n_lead && pos >= 0 && pos < n) lab = labels[pos];
+      if (lab >= V) lab = -1;
+    }
+    float m = -INFINITY, ssum = 0.f;
+    if (lab >= 0) {
+      const T *row = logits + (long)i * V;
+      for (int v = lane * E; v < V; v += 64 * E) {
+        const u32x4 q = ldg16(row + v);
+        T x[E];
+        __builtin_memcpy(x, &q, 16);
+        float f[E], mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          f[e] = to_f32<T>(x[e]);
+          mx = fmaxf(mx, f[e]);
+        }
+        const float mn = fmaxf(m, mx);
+        float acc = m == -INFINITY ? 0.f : ssum * __expf(m - mn);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc += __expf(f[e] - mn);
+        ssum = acc;
+        m = mn;
+      }
+      for (int o = 32; o > 0; o >>= 1) {
+        const float mo = __shfl_xor(m, o, 64), so = __shfl_xor(ssum, o, 64);
+        const float mn = fmaxf(m, mo);
+        ssum = (m == -INFINITY ? 0.f : ssum * __expf(m - mn)) + (mo == -INFINITY ? 0.f : so * __expf(mo - mn));
+        m = mn;
+      }
+    }
+    if (lane == 0) {
+      const float lse = lab >= 0 ? m + __logf(ssum) : 0.f;
+      s_lse[rr] = lse;
+      s_lab[rr] = lab;
+      if (i < L) row_loss[i] = lab >= 0 ? loss_scale * (lse - to_f32<T>(logits[(long)i * V + lab])) : 0.f;
+    }
   }
-  float m = -INFINITY;
-  for (int v = t; v < V; v += 256) m = fmaxf(m, to_f32<T>(row[v]));
-  m = block_max_256(m, red);
-  float ssum = 0.f;
-  for (int v = t; v < V; v += 256) ssum += __expf(to_f32<T>(row[v]) - m);
-  ssum = block_sum_256(ssum, red);
-  const float lse = m + __logf(ssum);
-  const float lab_logit = to_f32<T>(row[lab]);
-  __syncthreads();  // every thread has read row[lab] before it is overwritten
-  for (int v = t; v < V; v += 256) {
-    const float pv = __expf(to_f32<T>(row[v]) - lse);
-    row[v] = from_f32<T>(loss_scale * (pv - (v == lab ? 1.f : 0.f)));
+  __syncthreads();
+  const int KTA = (V + KTILE - 1) / KTILE, KTT = (L + KTILE - 1) / KTILE;
+  const int RG = (L + 15) / 16, VS = (V + 15) / 16;
+  for (int v0 = 0; v0 < V; v0 += CB) {
+    // 32 rows x CB columns of dlogits into LDS, E columns per thread and step
+    for (int idx = t; idx < 32 * (CB / E); idx += NTH) {
+      const int rr = idx / (CB / E), cc = (idx - rr * (CB / E)) * E;
+      const int v = v0 + cc, lab = s_lab[rr];
+      T out[E];
+      if (lab >= 0 && v < V) {
+        const u32x4 q = ldg16(logits + (long)(i0 + rr) * V + v);
+        T x[E];
+        __builtin_memcpy(x, &q, 16);
+        const float lse = s_lse[rr];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          out[e] = from_f32<T>(loss_scale * (__expf(to_f32<T>(x[e]) - lse) - (v + e == lab ? 1.f : 0.f)));
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) out[e] = T(0);
+      }
+      u32x4 o;
+      __builtin_memcpy(&o, out, 16);
+      *reinterpret_cast<u32x4 *>(&tile[rr * PITCH + cc]) = o;
+    }
+    __syncthreads();
+    // (a) tiles of [L][V]: 2 row groups x CB/KTILE k tiles
+    for (int idx = t; idx < 2 * (CB / KTILE) * 64; idx += NTH) {
+      const int ln = idx & 63, f = idx >> 6, rg = f / (CB / KTILE), kk = f - rg * (CB / KTILE);
+      const int grp = (i0 >> 4) + rg, kt = v0 / KTILE + kk;
+      if (grp >= RG || kt >= KTA) continue;
+      const u32x4 o = *reinterpret_cast<const u32x4 *>(&tile[(rg * 16 + (ln & 15)) * PITCH + kk * KTILE + (ln >> 4) * E]);
+      dlA[((long)grp * KTA + kt) * 64 + ln] = o;
+    }
+    // (b) tiles of [V][L]: CB/16 column strips x 32/KTILE k tiles of rows
+    for (int idx = t; idx < (CB / 16) * (32 / KTILE) * 64; idx += NTH) {
+      const int ln = idx & 63, f = idx >> 6, vs = f / (32 / KTILE), kk = f - vs * (32 / KTILE);
+      const int strip = (v0 >> 4) + vs, kt = i0 / KTILE + kk;
+      if (strip >= VS || kt >= KTT) continue;
+      T vals[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) vals[e] = tile[(kk * KTILE + (ln >> 4) * E + e) * PITCH + vs * 16 + (ln & 15)];
+      u32x4 o;
+      __builtin_memcpy(&o, vals, 16);
+      dlT[((long)strip * KTT + kt) * 64 + ln] = o;
+    }
+    __syncthreads();
   }
-  if (t == 0) row_loss[i] = loss_scale * (lse - lab_logit);
 }
 
 __global__ __launch_bounds__(256) void k_sum_acc(const float *x, long n, float *out) {
@@ -552,32 +635,106 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dq(AttnBwdParams p) {
   }
 }
 
-// One workgroup of four waves per (tile of 64 depth-0 key positions, kv
-// head); wave w owns keys 16 w .. 16 w + 15, their K and V fragments in
-// registers.  Query tiles of 64 (row, head) pairs -- 64 / G rows times the
-// G heads of the kv head -- are staged in LDS row-major (Q, dO) and
-// transposed (Q^T, dO^T).  Early key tiles are seen by more queries and are
-// launched first.
+// Query tiles of the dK/dV kernel: tile t of kv head gk holds the 64
+// (row, head) pairs qi = (row t QC + qi / G, head gk G + qi % G), QC = 64 / G.
+// This kernel lays each tile out as the dK/dV kernel's matrix-core operands,
+// so that kernel copies whole 1 KB fragments with no index arithmetic:
+//   [0, 4NC)            A fragments of Q  (rows = pairs 16 qb + c16, k = dims)
+//   [4NC, 8NC)          A fragments of dO
+//   [8NC, 8NC + NT)     A fragments of Q^T (rows = dims, k = pairs in the
+//                       order pack_rows_b gives a C block's rows), NT = ND NKC
+//   [8NC + NT, 8NC+2NT) A fragments of dO^T
+// plus info[gk][t][qi] = (lse, D, anchor) of each pair.  Pairs past QC G or
+// past the last row are zero with anchor -1 (never visible).
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdParams p) {
+__global__ __launch_bounds__(256) void k_pair_tiles(const T *q, const T *dout, const float *lse, const float *D,
+                                                    const int *anc, int L, int nq, int nkv, int G, u32x4 *tiles,
+                                                    float4 *info) {
   constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE, NC = HD / KTILE, ND = HD / 16;
-  constexpr int KS = HD + E, VS = 64 + 4, CPR = HD / E;
-  constexpr int NKC = sizeof(T) == 2 ? 2 : 4;
-  __shared__ __attribute__((aligned(16))) T Qs[64 * KS];
-  __shared__ __attribute__((aligned(16))) T Ds[64 * KS];
-  __shared__ __attribute__((aligned(16))) T Qt[HD * VS];
-  __shared__ __attribute__((aligned(16))) T Dt[HD * VS];
-  __shared__ float s_lse[64], s_D[64];
-  __shared__ int s_anc[64];
-  const int G = p.G, QC = 64 / G;  // rows per query tile
-  const int p0 = blockIdx.x * 64, gk = blockIdx.y;
+  constexpr int NKC = sizeof(T) == 2 ? 2 : 4, NT = ND * NKC, NFR = 8 * NC + 2 * NT;
+  const int QC = 64 / G, Tq = (L + QC - 1) / QC;
+  const long total = (long)nkv * Tq * NFR * 64;
+  for (long idx = (long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long)gridDim.x * 256) {
+    const int lane = (int)(idx & 63);
+    const long f = idx >> 6;
+    const int fr = (int)(f % NFR);
+    const long tile = f / NFR;
+    const int t = (int)(tile % Tq), gk = (int)(tile / Tq);
+    const int c16 = lane & 15, g = lane >> 4;
+    T a[E];
+    if (fr < 8 * NC) {
+      const T *src = fr < 4 * NC ? q : dout;
+      const int ff = fr % (4 * NC), qb = ff / NC, c = ff - qb * NC;
+      const int qi = qb * 16 + c16, row = t * QC + qi / G;
+      const bool ok = qi < QC * G && row < L;
+      const long off = ((long)row * nq + gk * G + qi % G) * HD + c * KTILE + g * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) a[e] = ok ? src[off + e] : T(0);
+    } else {
+      const T *src = fr < 8 * NC + NT ? q : dout;
+      const int ff = (fr - 8 * NC) % NT, d = ff / NKC, kc = ff - d * NKC;
+      const int dim = d * 16 + c16;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int qi = sizeof(T) == 2 ? 32 * kc + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4) : 16 * kc + 4 * g + e;
+        const int row = t * QC + qi / G;
+        const bool ok = qi < QC * G && row < L;
+        a[e] = ok ? src[((long)row * nq + gk * G + qi % G) * HD + dim] : T(0);
+      }
+    }
+    u32x4 v;
+    __builtin_memcpy(&v, a, 16);
+    tiles[idx] = v;
+    if (fr == 0) {
+      const int row = t * QC + lane / G;
+      const bool ok = lane < QC * G && row < L;
+      const long pi = (long)row * nq + gk * G + lane % G;
+      info[tile * 64 + lane] = ok ? make_float4(lse[pi], D[pi], __int_as_float(anc[row]), 0.f)
+                                  : make_float4(0.f, 0.f, __int_as_float(-1), 0.f);
+    }
+  }
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  // A workgroup barrier that waits for this wave's LDS operations only:
+  // global loads in flight (the next tiles) stay in flight.
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One workgroup of eight waves per (tile of 128 depth-0 key positions, kv
+// head, share of the query tiles); wave w owns keys 16 w .. 16 w + 15, their
+// K and V fragments in registers.  Query tiles (above) move HBM/L2 ->
+// registers STAGES tiles ahead of use and registers -> LDS at the top of
+// their iteration; per tile every wave runs S = Q K^T, dP = dO V^T,
+// dV^T += dO^T P and dK^T += Q^T dS on the matrix cores.  The rows that see
+// a key tile (all rows from its first position on) are split into qsplit
+// shares of the query tiles -- the same range of global tiles for every key
+// tile, so key tiles running together read the same tiles from L2 -- and
+// each share writes its partial dK, dV by key position, summed in order by
+// k_attn_bwd_reduce.
+template <typename T, int HD>
+__global__ __launch_bounds__(512) void k_attn_bwd_dkdv(AttnBwdParams p) {
+  constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE, NC = HD / KTILE, ND = HD / 16;
+  constexpr int NKC = sizeof(T) == 2 ? 2 : 4, NT = ND * NKC, NFR = 8 * NC + 2 * NT;
+  constexpr int PER = NFR * 64 / 512;  // fragment lanes per thread and tile
+  constexpr int STAGES = PER <= 4 ? 2 : 1;
+  __shared__ u32x4 F[NFR * 64];
+  __shared__ float4 s_info[64];
+  const int G = p.G, QC = 64 / G;
+  const int Tq = (p.L + QC - 1) / QC;
+  const int p0 = blockIdx.x * 128, gk = blockIdx.y, qs = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  if (p0 >= p.n) return;
-  const int r0 = p.inv[(long)p0 * p.K];  // first row at position >= p0 (rows are position-major)
-  if (r0 < 0) return;                      // no depth-0 row here: no query sees these positions
   const long kvs = (long)p.nkv * HD;
-  const int kp = p0 + 16 * w + c16;        // this lane's key position (B-operand column)
-  const bool kvalid = kp < p.n && p.inv[(long)kp * p.K] >= 0;
+  const int kp = p0 + 16 * w + c16;  // this lane's key position (B-operand column)
+  const int r0 = p0 < p.n ? p.inv[(long)p0 * p.K] : -1;  // first row at position >= p0
+  const bool kvalid = r0 >= 0 && kp < p.n && p.inv[(long)kp * p.K] >= 0;
+  int t_begin = Tq, t_end = Tq;
+  if (r0 >= 0) {
+    const int per = (Tq + p.qsplit - 1) / p.qsplit;
+    t_begin = min(Tq, max(r0 / QC, qs * per));
+    t_end = min(Tq, (qs + 1) * per);
+    if (t_end < t_begin) t_end = t_begin;
+  }
   u32x4 kf[NC], vf[NC];
   {
     const T *kr = reinterpret_cast<const T *>(p.k0) + (long)(kvalid ? kp : 0) * kvs + gk * HD;
@@ -591,37 +748,25 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdParams p) {
   floatx4 dkT[ND], dvT[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) dkT[d] = dvT[d] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  for (int c0 = r0; c0 < p.L; c0 += QC) {
-    // Stage 64 (row, head) pairs: pair qi = (row c0 + qi / G, head gk G + qi % G).
-    for (int id = tid; id < 64 * CPR; id += 256) {
-      const int qi = id / CPR, cc = id - qi * CPR;
-      const int rr = c0 + qi / G;
-      const bool ok = qi < QC * G && rr < p.L;
-      const long off = ((long)(ok ? rr : 0) * p.nq + gk * G + qi % G) * HD + cc * E;
-      const u32x4 qv = ok ? ldg16(reinterpret_cast<const T *>(p.q) + off) : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 dv = ok ? ldg16(reinterpret_cast<const T *>(p.dout) + off) : u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4 *>(&Qs[qi * KS + cc * E]) = qv;
-      *reinterpret_cast<u32x4 *>(&Ds[qi * KS + cc * E]) = dv;
-      T qa[E], da[E];
-      __builtin_memcpy(qa, &qv, 16);
-      __builtin_memcpy(da, &dv, 16);
+  const u32x4 *tg = p.qt + (long)gk * Tq * NFR * 64;
+  const float4 *ig = p.qinfo + (long)gk * Tq * 64;
+  struct Stage {
+    u32x4 v[PER];
+    float4 info;
+  };
+  // Loads are unconditional: past the last tile they re-read the last tile.
+  auto fetch = [&](int tq, Stage &st) {
+    const int tc = min(tq, Tq - 1);
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        Qt[(cc * E + e) * VS + qi] = qa[e];
-        Dt[(cc * E + e) * VS + qi] = da[e];
-      }
-    }
-    if (tid < 64) {
-      const int rr = c0 + tid / G;
-      const bool ok = tid < QC * G && rr < p.L;
-      const long pi = (long)(ok ? rr : 0) * p.nq + gk * G + tid % G;
-      s_lse[tid] = ok ? p.lse[pi] : 0.f;
-      s_D[tid] = ok ? p.D[pi] : 0.f;
-      s_anc[tid] = ok ? p.anc[rr] : -1;
-    }
-    __syncthreads();
-    // S and dP blocks: rows = pairs 16 qb + 4g + r, column = this lane's key.
+    for (int i = 0; i < PER; ++i) st.v[i] = tg[(long)tc * NFR * 64 + tid + i * 512];
+    if (w == 0) st.info = ig[(long)tc * 64 + lane];
+  };
+  auto put = [&](const Stage &st) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) F[tid + i * 512] = st.v[i];
+    if (w == 0) s_info[lane] = st.info;
+  };
+  auto compute = [&]() {
     floatx4 sacc[4], pacc[4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) sacc[qb] = pacc[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -629,21 +774,19 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdParams p) {
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const u32x4 qa = lds16b(&Qs[(qb * 16 + c16) * KS + c * KTILE + g * E]);
-        const u32x4 da = lds16b(&Ds[(qb * 16 + c16) * KS + c * KTILE + g * E]);
-        sacc[qb] = Mma<T>::run(qa, kf[c], sacc[qb]);
-        pacc[qb] = Mma<T>::run(da, vf[c], pacc[qb]);
+        sacc[qb] = Mma<T>::run(F[(qb * NC + c) * 64 + lane], kf[c], sacc[qb]);
+        pacc[qb] = Mma<T>::run(F[(4 * NC + qb * NC + c) * 64 + lane], vf[c], pacc[qb]);
       }
     float pv[4][4], ds[4][4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int qi = qb * 16 + 4 * g + r;
-        const bool vis = kvalid && kp <= s_anc[qi];
-        const float pr = vis ? fast_exp2(fmaf(sacc[qb][r], p.scale_log2, -s_lse[qi])) : 0.f;
+        const float4 in = s_info[qb * 16 + 4 * g + r];
+        const bool vis = kvalid && kp <= __float_as_int(in.z);
+        const float pr = vis ? fast_exp2(fmaf(sacc[qb][r], p.scale_log2, -in.x)) : 0.f;
         pv[qb][r] = pr;
-        ds[qb][r] = pr * (pacc[qb][r] - s_D[qi]);
+        ds[qb][r] = pr * (pacc[qb][r] - in.y);
       }
     u32x4 pf[4], dsf[4];
     pack_rows_b<T>(pv, pf);
@@ -652,21 +795,64 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdParams p) {
     for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        dvT[d] = Mma<T>::run(lds_t_frag<T, VS>(Dt, d, c16, g, kc), pf[kc], dvT[d]);
-        dkT[d] = Mma<T>::run(lds_t_frag<T, VS>(Qt, d, c16, g, kc), dsf[kc], dkT[d]);
+        dkT[d] = Mma<T>::run(F[(8 * NC + d * NKC + kc) * 64 + lane], dsf[kc], dkT[d]);
+        dvT[d] = Mma<T>::run(F[(8 * NC + NT + d * NKC + kc) * 64 + lane], pf[kc], dvT[d]);
       }
-    __syncthreads();
-  }
-  if (kvalid) {
-    const int cell = p.inv[(long)kp * p.K];
-    float *dk = p.dk + ((long)cell * p.nkv + gk) * HD;
-    float *dv = p.dv + ((long)cell * p.nkv + gk) * HD;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      *reinterpret_cast<floatx4 *>(dk + d * 16 + 4 * g) = dkT[d] * p.scale;
-      *reinterpret_cast<floatx4 *>(dv + d * 16 + 4 * g) = dvT[d];
+  };
+  if constexpr (STAGES == 2) {
+    Stage st0, st1;
+    fetch(t_begin, st0);
+    fetch(t_begin + 1, st1);
+    for (int tq = t_begin; tq < t_end; tq += 2) {
+      put(st0);
+      lds_barrier();
+      fetch(tq + 2, st0);
+      compute();
+      lds_barrier();
+      if (tq + 1 >= t_end) break;
+      put(st1);
+      lds_barrier();
+      fetch(tq + 3, st1);
+      compute();
+      lds_barrier();
+    }
+  } else {
+    Stage st0;
+    fetch(t_begin, st0);
+    for (int tq = t_begin; tq < t_end; ++tq) {
+      put(st0);
+      lds_barrier();
+      fetch(tq + 1, st0);
+      compute();
+      lds_barrier();
     }
   }
+  if (kp < p.n) {
+    // every share writes its slot (zeros when it saw no rows)
+    const long o = (((long)qs * p.n + kp) * p.nkv + gk) * HD;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      *reinterpret_cast<floatx4 *>(p.pk + o + d * 16 + 4 * g) = dkT[d];
+      *reinterpret_cast<floatx4 *>(p.pv + o + d * 16 + 4 * g) = dvT[d];
+    }
+  }
+}
+
+// dK, dV of the depth-0 rows: the shares' partials summed in share order.
+__global__ __launch_bounds__(256) void k_attn_bwd_reduce(AttnBwdParams p) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const long per = (long)p.nkv * p.hd;
+  if (idx >= (long)p.n * per) return;
+  const long pos = idx / per, r = idx - pos * per;
+  const int cell = p.inv[pos * p.K];
+  if (cell < 0) return;
+  float a = 0.f, b = 0.f;
+  for (int qs = 0; qs < p.qsplit; ++qs) {
+    a += p.pk[(long)qs * p.n * per + idx];
+    b += p.pv[(long)qs * p.n * per + idx];
+  }
+  p.dk[(long)cell * per + r] = a * p.scale;
+  p.dv[(long)cell * per + r] = b;
 }
 
 // dK, dV of the rollout cells (depth >= 1): cell c = (a + j, j) is seen by
@@ -753,15 +939,20 @@ hipError_t launch_pack_t(int dtype, int src_kind, const void *src, long ld, int 
   return hipGetLastError();
 }
 
-hipError_t launch_ce_rows(int dtype, void *logits, int L, int V, const int *anc, const int *dep,
-                          const int *labels, int n, int n_lead, float loss_scale, float *row_loss, hipStream_t s) {
+hipError_t launch_ce_tiles(int dtype, const void *logits, int L, int V, const int *anc, const int *dep,
+                           const int *labels, int n, int n_lead, float loss_scale, float *row_loss, void *dlA,
+                           void *dlT, hipStream_t s) {
   if (L <= 0) return hipSuccess;
+  if (V % 8) return hipErrorInvalidValue;
+  const dim3 grid(nblocks(L, 32));
   if (dtype == 1)
-    hipLaunchKernelGGL(k_ce_rows<bf16_t>, dim3(L), dim3(256), 0, s, reinterpret_cast<bf16_t *>(logits), V, anc,
-                       dep, labels, n, n_lead, loss_scale, row_loss);
+    hipLaunchKernelGGL(k_ce_tiles<bf16_t>, grid, dim3(512), 0, s, reinterpret_cast<const bf16_t *>(logits), L, V, anc,
+                       dep, labels, n, n_lead, loss_scale, row_loss, reinterpret_cast<u32x4 *>(dlA),
+                       reinterpret_cast<u32x4 *>(dlT));
   else
-    hipLaunchKernelGGL(k_ce_rows<float>, dim3(L), dim3(256), 0, s, reinterpret_cast<float *>(logits), V, anc,
-                       dep, labels, n, n_lead, loss_scale, row_loss);
+    hipLaunchKernelGGL(k_ce_tiles<float>, grid, dim3(512), 0, s, reinterpret_cast<const float *>(logits), L, V, anc,
+                       dep, labels, n, n_lead, loss_scale, row_loss, reinterpret_cast<u32x4 *>(dlA),
+                       reinterpret_cast<u32x4 *>(dlT));
   return hipGetLastError();
 }
 
@@ -860,6 +1051,12 @@ hipError_t launch_attn_bwd_pre(int dtype, const float *dout, const void *out, in
   return hipGetLastError();
 }
 
+size_t attn_bwd_tile_bytes(int L, int nkv, int G, int hd, int dtype) {
+  const int QC = 64 / G, Tq = (L + QC - 1) / QC;
+  const int kt = dtype == 1 ? 32 : 16, NC = hd / kt, ND = hd / 16, NKC = dtype == 1 ? 2 : 4;
+  return (size_t)nkv * Tq * ((8 * NC + 2 * ND * NKC) * 1024 + 64 * 16);
+}
+
 hipError_t launch_attn_bwd(int dtype, const AttnBwdParams &p, hipStream_t s) {
   if (p.L <= 0) return hipSuccess;
   if (p.hd != 64 && p.hd != 128) return hipErrorInvalidValue;
@@ -879,18 +1076,37 @@ hipError_t launch_attn_bwd(int dtype, const AttnBwdParams &p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (G > 64) return hipErrorInvalidValue;
+  if (G > 64 || p.qsplit < 1) return hipErrorInvalidValue;
   {
-    const dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)p.nkv);
+    const int QC = 64 / G, Tq = (p.L + QC - 1) / QC;
+    const int kt = dtype == 1 ? 32 : 16, NC = p.hd / kt, ND = p.hd / 16, NKC = dtype == 1 ? 2 : 4;
+    const long frags = (long)p.nkv * Tq * (8 * NC + 2 * ND * NKC) * 64;
+    const unsigned b = (unsigned)std::min<long>(65536, (frags + 255) / 256);
     if (dtype == 1) {
-      if (p.hd == 64) hipLaunchKernelGGL((k_attn_bwd_dkdv<bf16_t, 64>), grid, dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((k_attn_bwd_dkdv<bf16_t, 128>), grid, dim3(256), 0, s, p);
+      if (p.hd == 64)
+        hipLaunchKernelGGL((k_pair_tiles<bf16_t, 64>), dim3(b), dim3(256), 0, s, reinterpret_cast<const bf16_t *>(p.q),
+                           reinterpret_cast<const bf16_t *>(p.dout), p.lse, p.D, p.anc, p.L, p.nq, p.nkv, G, p.qt,
+                           p.qinfo);
+      else
+        hipLaunchKernelGGL((k_pair_tiles<bf16_t, 128>), dim3(b), dim3(256), 0, s,
+                           reinterpret_cast<const bf16_t *>(p.q), reinterpret_cast<const bf16_t *>(p.dout), p.lse, p.D,
+                           p.anc, p.L, p.nq, p.nkv, G, p.qt, p.qinfo);
     } else {
-      hipLaunchKernelGGL((k_attn_bwd_dkdv<float, 64>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((k_pair_tiles<float, 64>), dim3(b), dim3(256), 0, s, reinterpret_cast<const float *>(p.q),
+                         reinterpret_cast<const float *>(p.dout), p.lse, p.D, p.anc, p.L, p.nq, p.nkv, G, p.qt,
+                         p.qinfo);
+    }
+    const dim3 grid((unsigned)((p.n + 127) / 128), (unsigned)p.nkv, (unsigned)p.qsplit);
+    if (dtype == 1) {
+      if (p.hd == 64) hipLaunchKernelGGL((k_attn_bwd_dkdv<bf16_t, 64>), grid, dim3(512), 0, s, p);
+      else hipLaunchKernelGGL((k_attn_bwd_dkdv<bf16_t, 128>), grid, dim3(512), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((k_attn_bwd_dkdv<float, 64>), grid, dim3(512), 0, s, p);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  hipLaunchKernelGGL(k_attn_bwd_reduce, dim3(nblocks((long)p.n * p.nkv * p.hd, 256)), dim3(256), 0, s, p);
   {
     const unsigned b = nblocks((long)p.L * p.nkv, 4);
     if (dtype == 1) hipLaunchKernelGGL(k_attn_bwd_chain<bf16_t>, dim3(b), dim3(256), 0, s, p);
