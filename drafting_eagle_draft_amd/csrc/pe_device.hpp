@@ -85,6 +85,11 @@ __device__ __forceinline__ long frag_off(int m, int k, int KT) {
   return ((long)((m >> 4) * KT + k / KTILE) * 64 + ((k % KTILE) / E) * 16 + (m & 15)) * E + (k % E);
 }
 
+// Workgroup barrier that waits for this wave's LDS operations only, so
+// global loads already issued (prefetched tiles) stay in flight; the plain
+// __syncthreads() also waits for every outstanding global access.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ u32x4 ldg16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }

@@ -302,7 +302,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
 #pragma unroll
         for (int e = 0; e < E; ++e) Vt[(cc * E + e) * VS + key] = vals[e];
       }
-      __syncthreads();
+      lds_barrier();
       if (jt + 64 * PF < nkeys) gload(jt + 64 * PF, kreg[u], vreg[u]);
       // A wave whose rows all sit before this tile has nothing to add.
       if (jt <= wave_amax) {
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
             }
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
 

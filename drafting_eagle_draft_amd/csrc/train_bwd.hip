@@ -519,68 +519,97 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dq(AttnBwdParams p) {
 #pragma unroll
     for (int d = 0; d < ND; ++d) dqacc[qb][d] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int jt = 0; jt < nkeys; jt += 64) {
-    // Stage the tile: K and V row-major, K transposed.
+  // Key/value tiles move HBM/L2 -> registers two tiles ahead of use, then
+  // registers -> LDS (K and V row-major, K transposed) at the top of their
+  // iteration.
+  struct KV {
+    u32x4 k[MAXC], v[MAXC];
+  };
+  auto fetch = [&](int jt, KV &st) {
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int id = tid + i * NT;
+      const int key = id / CPR, cc = id - key * CPR;
+      const int jj = jt + key;
+      const bool ok = id < 64 * CPR && jj < nkeys;
+      st.k[i] = ok ? ldg16(k0 + (long)jj * kvs + cc * E) : u32x4{0u, 0u, 0u, 0u};
+      st.v[i] = ok ? ldg16(v0 + (long)jj * kvs + cc * E) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto put = [&](const KV &st) {
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
       const int id = tid + i * NT;
       if (id >= 64 * CPR) break;
       const int key = id / CPR, cc = id - key * CPR;
-      const int jj = jt + key;
-      const bool ok = jj < nkeys;
-      const u32x4 kv = ok ? ldg16(k0 + (long)jj * kvs + cc * E) : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 vv = ok ? ldg16(v0 + (long)jj * kvs + cc * E) : u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4 *>(&Ks[key * KS + cc * E]) = kv;
-      *reinterpret_cast<u32x4 *>(&Vs[key * KS + cc * E]) = vv;
+      *reinterpret_cast<u32x4 *>(&Ks[key * KS + cc * E]) = st.k[i];
+      *reinterpret_cast<u32x4 *>(&Vs[key * KS + cc * E]) = st.v[i];
       T vals[E];
-      __builtin_memcpy(vals, &kv, 16);
+      __builtin_memcpy(vals, &st.k[i], 16);
 #pragma unroll
       for (int e = 0; e < E; ++e) Kt[(cc * E + e) * VS + key] = vals[e];
     }
-    __syncthreads();
-    if (jt <= wave_amax) {
-      floatx4 sacc[QB][4], pacc[QB][4];
+  };
+  auto compute = [&](int jt) {
+    if (jt > wave_amax) return;  // every row of this wave sits before the tile
+    floatx4 sacc[QB][4], pacc[QB][4];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) sacc[qb][kb] = pacc[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 4; ++kb) sacc[qb][kb] = pacc[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 kf = lds16b(&Ks[(kb * 16 + c16) * KS + c * KTILE + g * E]);
+        const u32x4 vf = lds16b(&Vs[(kb * 16 + c16) * KS + c * KTILE + g * E]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          sacc[qb][kb] = Mma<T>::run(kf, qf[qb][c], sacc[qb][kb]);
+          pacc[qb][kb] = Mma<T>::run(vf, df[qb][c], pacc[qb][kb]);
+        }
+      }
+    u32x4 dsf[QB][4];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float ds[4][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const u32x4 kf = lds16b(&Ks[(kb * 16 + c16) * KS + c * KTILE + g * E]);
-          const u32x4 vf = lds16b(&Vs[(kb * 16 + c16) * KS + c * KTILE + g * E]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            sacc[qb][kb] = Mma<T>::run(kf, qf[qb][c], sacc[qb][kb]);
-            pacc[qb][kb] = Mma<T>::run(vf, df[qb][c], pacc[qb][kb]);
-          }
+        for (int r = 0; r < 4; ++r) {
+          const int jj = jt + kb * 16 + 4 * g + r;
+          const bool vis = valid[qb] && jj < nkeys && jj <= a_q[qb];
+          const float pr = vis ? fast_exp2(fmaf(sacc[qb][kb][r], p.scale_log2, -lse[qb])) : 0.f;
+          ds[kb][r] = pr * (pacc[qb][kb][r] - Dq[qb]);
         }
-      u32x4 dsf[QB][4];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float ds[4][4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int jj = jt + kb * 16 + 4 * g + r;
-            const bool vis = valid[qb] && jj < nkeys && jj <= a_q[qb];
-            const float pr = vis ? fast_exp2(fmaf(sacc[qb][kb][r], p.scale_log2, -lse[qb])) : 0.f;
-            ds[kb][r] = pr * (pacc[qb][kb][r] - Dq[qb]);
-          }
-        pack_rows_b<T>(ds, dsf[qb]);
-      }
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          const u32x4 kf = lds_t_frag<T, VS>(Kt, d, c16, g, kc);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) dqacc[qb][d] = Mma<T>::run(kf, dsf[qb][kc], dqacc[qb][d]);
-        }
+      pack_rows_b<T>(ds, dsf[qb]);
     }
-    __syncthreads();
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const u32x4 kf = lds_t_frag<T, VS>(Kt, d, c16, g, kc);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) dqacc[qb][d] = Mma<T>::run(kf, dsf[qb][kc], dqacc[qb][d]);
+      }
+  };
+  {
+    KV st0, st1;
+    fetch(0, st0);
+    fetch(64, st1);
+    for (int jt = 0; jt < nkeys; jt += 128) {
+      put(st0);
+      lds_barrier();
+      fetch(jt + 128, st0);
+      compute(jt);
+      lds_barrier();
+      if (jt + 64 >= nkeys) break;
+      put(st1);
+      lds_barrier();
+      fetch(jt + 192, st1);
+      compute(jt + 64);
+      lds_barrier();
+    }
   }
 
   // Rollout cells (a + j, j), 1 <= j <= d, on the vector units.
@@ -693,12 +722,6 @@ __global__ __launch_bounds__(256) void k_pair_tiles(const T *q, const T *dout, c
                                   : make_float4(0.f, 0.f, __int_as_float(-1), 0.f);
     }
   }
-}
-
-__device__ __forceinline__ void lds_barrier() {
-  // A workgroup barrier that waits for this wave's LDS operations only:
-  // global loads in flight (the next tiles) stay in flight.
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // One workgroup of eight waves per (tile of 128 depth-0 key positions, kv
