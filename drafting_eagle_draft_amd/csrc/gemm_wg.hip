@@ -124,14 +124,11 @@ __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) best[f] = 0ull;
 
-  u32x4 abuf[D][MAXKW];
-#pragma unroll
-  for (int d = 0; d < D; ++d)
-#pragma unroll
-    for (int j = 0; j < MAXKW; ++j)
-      abuf[d][j] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)tile_off(d, j), 0, 0);
-  // Their activation fragments are the same for every strip, so they stay in
-  // registers for the whole kernel (loaded after the weight prefetch above).
+  // The activation fragments of this wave's k-tiles are the same for every
+  // strip, so they stay in registers for the whole kernel.  They are loaded
+  // before the weight prefetch: the loads in flight at the strip loop's head
+  // are then the weight ring alone, in issue order, and each slot waits only
+  // for itself.
   u32x4 breg[MAXKW][NF];
 #pragma unroll
   for (int j = 0; j < MAXKW; ++j) {
@@ -142,6 +139,12 @@ __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
       breg[j][f] = (jok[j] && row && k < p.K) ? ldg16(row + k) : u32x4{0u, 0u, 0u, 0u};
     }
   }
+  u32x4 abuf[D][MAXKW];
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+#pragma unroll
+    for (int j = 0; j < MAXKW; ++j)
+      abuf[d][j] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)tile_off(d, j), 0, 0);
   if (p.ssq) block_rstd(p, 16 * NF, rsh, scratch);
   float rs[NF];
 #pragma unroll
@@ -158,10 +161,12 @@ __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
       for (int f = 0; f < NF; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < MAXKW; ++j) {
-        const u32x4 a = abuf[d][j];
-        abuf[d][j] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)tile_off(i + D, j), 0, 0);
+        // Use the slot, then refill it: the old and new tile never live at
+        // once, so each slot keeps one register across iterations (no copies
+        // that would have to wait for the refill).
 #pragma unroll
-        for (int f = 0; f < NF; ++f) acc[f] = Mma<T>::run(a, breg[j][f], acc[f]);
+        for (int f = 0; f < NF; ++f) acc[f] = Mma<T>::run(abuf[d][j], breg[j][f], acc[f]);
+        abuf[d][j] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)tile_off(i + D, j), 0, 0);
       }
       if (i < ns) {
         const int s = (int)blockIdx.x + i * G;
