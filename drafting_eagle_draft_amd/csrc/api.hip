@@ -108,7 +108,7 @@ GemmPlan plan_gemm(const pe_model *m, const Tiled &t, int Mv, int nf) {
   GemmPlan g{};
   g.Mv = Mv;
   g.nf = nf;
-  const int W = 8;
+  const int W = kGemmWaves;
   const int max_slots = nf == 1 ? 18 : nf == 2 ? 8 : nf == 3 ? 4 : 2;  // as the kernel's buckets
   // One workgroup per CU (8 waves at up to 256 VGPRs).  Each K split adds
   // a finalize kernel, priced like ~100 extra tiles per CU; choose the split

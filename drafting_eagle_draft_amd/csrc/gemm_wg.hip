@@ -33,11 +33,11 @@ __device__ __forceinline__ u32x4 lds_ld16(const void *p) { return *reinterpret_c
 
 // rstd of the first `rows` activation rows (16*NF) from the producer's
 // per-strip sums of squares, into rsh[rows] (block-wide; ends with a
-// barrier).  Thread t folds row t % rows over strips t / rows + k*nparts with
-// four independent loads per step, then one thread per row folds the
-// nparts partials.  scratch holds blockDim.x floats.
-__device__ void block_rstd(const GemmParams &p, int rows, float *rsh, float *scratch) {
-  const int tid = threadIdx.x, nparts = blockDim.x / rows;
+// barrier).  Thread t of the nthr threads folds row t % rows over strips
+// t / rows + k*nparts with four independent loads per step, then one thread
+// per row folds the nparts partials.  scratch holds nthr floats.
+__device__ void block_rstd(const GemmParams &p, int rows, int nthr, float *rsh, float *scratch) {
+  const int tid = threadIdx.x, nparts = nthr / rows;
   const int m = tid % rows, part = tid / rows;
   float a = 0.f;
   if (part < nparts) {
@@ -59,6 +59,60 @@ __device__ void block_rstd(const GemmParams &p, int rows, float *rsh, float *scr
   __syncthreads();
 }
 
+// The same statistics for the streaming kernel, in two steps around the
+// weight ring: rstd_issue loads the first RPRE strips of each thread's
+// share before the ring is issued (through a buffer resource, so strips
+// past the end read zero without a branch) and rstd_finish folds them
+// after it, so waiting for them does not wait for the ring.  Thread t folds
+// row t % ROWS over strips t / ROWS + r*NPARTS; rstd_finish ends with a
+// barrier.
+template <int NF>
+struct Rstd {
+  static constexpr int ROWS = 16 * NF, NPARTS = 64 * kGemmWaves / ROWS, RPRE = 8;
+  float v[RPRE];
+};
+
+template <int NF>
+__device__ __forceinline__ void rstd_issue(const GemmParams &p, Rstd<NF> &r) {
+  using R = Rstd<NF>;
+  const int tid = threadIdx.x, m = tid % R::ROWS, part = tid / R::ROWS;
+  const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(p.ssq), 0, p.ssq_strips * kMaxRows * 4, 0x00020000);
+#pragma unroll
+  for (int q = 0; q < R::RPRE; ++q) {
+    const int t = part + q * R::NPARTS;
+    const unsigned off = (part < R::NPARTS && t < p.ssq_strips) ? (unsigned)(t * kMaxRows + m) * 4u : 0x7FFFFFF0u;
+    r.v[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(res, (int)off, 0, 0));
+  }
+}
+
+template <int NF>
+__device__ void rstd_finish(const GemmParams &p, const Rstd<NF> &r, float *rsh, float *scratch) {
+  using R = Rstd<NF>;
+  const int tid = threadIdx.x, m = tid % R::ROWS, part = tid / R::ROWS;
+  float v[R::RPRE];
+  // Keep the use of the early loads here, after the loads issued since:
+  // otherwise the sum is scheduled (and waited for) ahead of them.
+#pragma unroll
+  for (int q = 0; q < R::RPRE; ++q) {
+    v[q] = r.v[q];
+    asm volatile("" : "+v"(v[q]) : : "memory");
+  }
+  float a = 0.f;
+#pragma unroll
+  for (int q = 0; q < R::RPRE; ++q) a += v[q];
+  if (part < R::NPARTS)
+    for (int t = part + R::RPRE * R::NPARTS; t < p.ssq_strips; t += R::NPARTS) a += p.ssq[t * kMaxRows + m];
+  scratch[tid] = a;
+  __syncthreads();
+  if (tid < R::ROWS) {
+    float sum = 0.f;
+    for (int q = 0; q < R::NPARTS; ++q) sum += scratch[q * R::ROWS + tid];
+    rsh[tid] = rsqrtf(sum * p.inv_width + p.eps);
+  }
+  __syncthreads();
+}
+
 template <typename T>
 __device__ __forceinline__ const T *act_row(const GemmParams &p, int m) {
   if (m < p.act_rows) return reinterpret_cast<const T *>(p.act) + (long)m * p.act_ld;
@@ -69,8 +123,8 @@ __device__ __forceinline__ const T *act_row(const GemmParams &p, int m) {
 // Block-wide best argmax key per row -> blk_best[blockIdx.x + blockIdx.y*gridDim.x][64].
 template <int NF>
 __device__ void block_argmax_out(const GemmParams &p, const unsigned long long (&best)[NF],
-                                 unsigned long long *sh) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+                                 unsigned long long *sh, int nw) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if ((lane >> 4) == 0) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) sh[w * 64 + 16 * f + (lane & 15)] = best[f];
@@ -84,11 +138,14 @@ __device__ void block_argmax_out(const GemmParams &p, const unsigned long long (
   }
 }
 
-template <typename T, int NF, int MAXKW>
+template <typename T, int NF, int MAXKW, int EK>
 __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
   constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE, D = Ring<MAXKW>::D;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int W = blockDim.x >> 6;
+  // The wave count is a constant of the launch, not read from the dispatch:
+  // blockDim.x is loaded from memory, and waiting for that load would put a
+  // full memory latency ahead of the first weight loads.
+  constexpr int W = kGemmWaves;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c16 = lane & 15, g = lane >> 4;
   const int chunk = blockIdx.y;
   const int kt0 = chunk * p.kc;
@@ -125,10 +182,10 @@ __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
   for (int f = 0; f < NF; ++f) best[f] = 0ull;
 
   // The activation fragments of this wave's k-tiles are the same for every
-  // strip, so they stay in registers for the whole kernel.  They are loaded
-  // before the weight prefetch: the loads in flight at the strip loop's head
-  // are then the weight ring alone, in issue order, and each slot waits only
-  // for itself.
+  // strip, so they stay in registers for the whole kernel.  They (and the
+  // RMSNorm statistics) are loaded before the weight prefetch: the loads in
+  // flight at the strip loop's head are then the weight ring alone, in issue
+  // order, and each slot waits only for itself.
   u32x4 breg[MAXKW][NF];
 #pragma unroll
   for (int j = 0; j < MAXKW; ++j) {
@@ -139,13 +196,15 @@ __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
       breg[j][f] = (jok[j] && row && k < p.K) ? ldg16(row + k) : u32x4{0u, 0u, 0u, 0u};
     }
   }
+  Rstd<NF> rq;
+  if (p.ssq) rstd_issue<NF>(p, rq);
   u32x4 abuf[D][MAXKW];
 #pragma unroll
   for (int d = 0; d < D; ++d)
 #pragma unroll
     for (int j = 0; j < MAXKW; ++j)
       abuf[d][j] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)tile_off(d, j), 0, 0);
-  if (p.ssq) block_rstd(p, 16 * NF, rsh, scratch);
+  if (p.ssq) rstd_finish<NF>(p, rq, rsh, scratch);
   float rs[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) rs[f] = p.ssq ? rsh[16 * f + c16] : 1.f;
@@ -185,42 +244,42 @@ __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
         }
         __syncthreads();
         if (reducer) {
-          if (p.KS == 1) {
-            finish_strip<T, NF>(p, s, lane, res, rs, best);
-          } else {
+          if constexpr (EK == EPI_PARTIAL) {
 #pragma unroll
             for (int f = 0; f < NF; ++f)
               p.part[(((long)chunk * p.NT + s) * NF + f) * 64 + lane] = res[f];
+          } else {
+            finish_strip<T, NF, EK>(p, s, lane, res, rs, best);
           }
         }
       }
     }
   }
-  if (p.epi == EPI_ARGMAX && p.KS == 1)
-    block_argmax_out<NF>(p, best, reinterpret_cast<unsigned long long *>(red));
+  if constexpr (EK == EPI_ARGMAX)
+    block_argmax_out<NF>(p, best, reinterpret_cast<unsigned long long *>(red), W);
 }
 
-template <typename T, int NF, int MAXKW>
-__global__ __launch_bounds__(512) void k_gemm_wg(GemmParams p) {
-  gemm_wg_body<T, NF, MAXKW>(p);
+template <typename T, int NF, int MAXKW, int EK>
+__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_wg(GemmParams p) {
+  gemm_wg_body<T, NF, MAXKW, EK>(p);
 }
 
 // The LM head: the same weight-streaming body with the fused argmax (its
 // own symbol, so profiles report it apart from the layer projections).
-template <typename T, int NF, int MAXKW>
-__global__ __launch_bounds__(512) void k_lm_head_argmax(GemmParams p) {
-  gemm_wg_body<T, NF, MAXKW>(p);
+template <typename T, int NF, int MAXKW, int EK>
+__global__ __launch_bounds__(64 * kGemmWaves) void k_lm_head_argmax(GemmParams p) {
+  gemm_wg_body<T, NF, MAXKW, EK>(p);
 }
 
 // KS > 1: one wave per strip sums the chunk partials in chunk order and runs
 // the epilogue.
-template <typename T, int NF>
+template <typename T, int NF, int EK>
 __global__ __launch_bounds__(256) void k_gemm_finalize(GemmParams p) {
   __shared__ float rsh[64];
   __shared__ float scratch[256];
   __shared__ unsigned long long sh[4 * 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c16 = lane & 15;
-  if (p.ssq) block_rstd(p, 16 * NF, rsh, scratch);
+  if (p.ssq) block_rstd(p, 16 * NF, 256, rsh, scratch);
   float rs[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) rs[f] = p.ssq ? rsh[16 * f + c16] : 1.f;
@@ -235,9 +294,9 @@ __global__ __launch_bounds__(256) void k_gemm_finalize(GemmParams p) {
     for (int c = 0; c < p.KS; ++c)
 #pragma unroll
       for (int f = 0; f < NF; ++f) res[f] += p.part[(((long)c * p.NT + s) * NF + f) * 64 + lane];
-    finish_strip<T, NF>(p, s, lane, res, rs, best);
+    finish_strip<T, NF, EK>(p, s, lane, res, rs, best);
   }
-  if (p.epi == EPI_ARGMAX) block_argmax_out<NF>(p, best, sh);
+  if constexpr (EK == EPI_ARGMAX) block_argmax_out<NF>(p, best, sh, 4);
 }
 
 // Final argmax over the per-workgroup best keys: one 1024-thread workgroup;
@@ -267,12 +326,44 @@ __global__ __launch_bounds__(1024) void k_argmax_final(const unsigned long long 
   }
 }
 
+template <typename T, int NF, int MAXKW, int EK>
+hipError_t launch_one(const GemmParams &p, const GemmLaunch &L, hipStream_t s) {
+  const dim3 grid(L.grid, p.KS), block(L.waves * 64);
+  if constexpr (EK == EPI_ARGMAX || EK == EPI_PARTIAL) {
+    if (p.epi == EPI_ARGMAX) {
+      hipLaunchKernelGGL((k_lm_head_argmax<T, NF, MAXKW, EK>), grid, block, L.lds, s, p);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (EK != EPI_ARGMAX) hipLaunchKernelGGL((k_gemm_wg<T, NF, MAXKW, EK>), grid, block, L.lds, s, p);
+  return hipGetLastError();
+}
+
 template <typename T, int NF, int MAXKW>
 hipError_t launch_main(const GemmParams &p, const GemmLaunch &L, hipStream_t s) {
-  if (p.epi == EPI_ARGMAX)
-    hipLaunchKernelGGL((k_lm_head_argmax<T, NF, MAXKW>), dim3(L.grid, p.KS), dim3(L.waves * 64), L.lds, s, p);
-  else
-    hipLaunchKernelGGL((k_gemm_wg<T, NF, MAXKW>), dim3(L.grid, p.KS), dim3(L.waves * 64), L.lds, s, p);
+  if (L.waves != kGemmWaves) return hipErrorInvalidValue;
+  if (p.KS > 1) return launch_one<T, NF, MAXKW, EPI_PARTIAL>(p, L, s);
+  switch (p.epi) {
+    case EPI_FC: return launch_one<T, NF, MAXKW, EPI_FC>(p, L, s);
+    case EPI_QKV: return launch_one<T, NF, MAXKW, EPI_QKV>(p, L, s);
+    case EPI_RESID: return launch_one<T, NF, MAXKW, EPI_RESID>(p, L, s);
+    case EPI_SWIGLU: return launch_one<T, NF, MAXKW, EPI_SWIGLU>(p, L, s);
+    case EPI_ARGMAX: return launch_one<T, NF, MAXKW, EPI_ARGMAX>(p, L, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int NF>
+hipError_t launch_finalize(const GemmParams &p, hipStream_t s) {
+  const dim3 grid((p.NT + 3) / 4);
+  switch (p.epi) {
+    case EPI_FC: hipLaunchKernelGGL((k_gemm_finalize<T, NF, EPI_FC>), grid, dim3(256), 0, s, p); break;
+    case EPI_QKV: hipLaunchKernelGGL((k_gemm_finalize<T, NF, EPI_QKV>), grid, dim3(256), 0, s, p); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_gemm_finalize<T, NF, EPI_RESID>), grid, dim3(256), 0, s, p); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_finalize<T, NF, EPI_SWIGLU>), grid, dim3(256), 0, s, p); break;
+    case EPI_ARGMAX: hipLaunchKernelGGL((k_gemm_finalize<T, NF, EPI_ARGMAX>), grid, dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -304,14 +395,13 @@ hipError_t launch_t(int nf, const GemmParams &p, const GemmLaunch &L, hipStream_
     case 4: e = launch_kw<T, 4>(p, L, s); break;
   }
   if (e != hipSuccess || p.KS == 1) return e;
-  const dim3 grid((p.NT + 3) / 4);
   switch (nf) {
-    case 1: hipLaunchKernelGGL((k_gemm_finalize<T, 1>), grid, dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((k_gemm_finalize<T, 2>), grid, dim3(256), 0, s, p); break;
-    case 3: hipLaunchKernelGGL((k_gemm_finalize<T, 3>), grid, dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((k_gemm_finalize<T, 4>), grid, dim3(256), 0, s, p); break;
+    case 1: return launch_finalize<T, 1>(p, s);
+    case 2: return launch_finalize<T, 2>(p, s);
+    case 3: return launch_finalize<T, 3>(p, s);
+    case 4: return launch_finalize<T, 4>(p, s);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

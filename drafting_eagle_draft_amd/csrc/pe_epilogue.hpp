@@ -264,7 +264,11 @@ __device__ void epi_argmax(const GemmParams &p, int s, int lane, const floatx4 (
 
 // Apply the RMSNorm row scale (when the input was a raw residual copy) and
 // run the epilogue selected by p.epi.
-template <typename T, int NF>
+// EK is the epilogue of the kernel instance (an Epi), fixed at compile time:
+// a kernel compiles only its own epilogue, because a load in an epilogue the
+// kernel never runs still costs the compiler's wait counting its precision
+// (it then waits for every weight tile in flight at the next strip).
+template <typename T, int NF, int EK>
 __device__ __forceinline__ void finish_strip(const GemmParams &p, int s, int lane, floatx4 (&res)[NF],
                                              const float (&rs)[NF],
                                              unsigned long long (&best)[NF]) {
@@ -272,13 +276,11 @@ __device__ __forceinline__ void finish_strip(const GemmParams &p, int s, int lan
 #pragma unroll
     for (int f = 0; f < NF; ++f) res[f] *= rs[f];
   }
-  switch (p.epi) {
-    case EPI_FC: epi_fc<T, NF>(p, s, lane, res); break;
-    case EPI_QKV: epi_qkv<T, NF>(p, s, lane, res); break;
-    case EPI_RESID: epi_resid<T, NF>(p, s, lane, res); break;
-    case EPI_SWIGLU: epi_swiglu<T, NF>(p, s, lane, res); break;
-    default: epi_argmax<NF>(p, s, lane, res, best); break;
-  }
+  if constexpr (EK == EPI_FC) epi_fc<T, NF>(p, s, lane, res);
+  else if constexpr (EK == EPI_QKV) epi_qkv<T, NF>(p, s, lane, res);
+  else if constexpr (EK == EPI_RESID) epi_resid<T, NF>(p, s, lane, res);
+  else if constexpr (EK == EPI_SWIGLU) epi_swiglu<T, NF>(p, s, lane, res);
+  else epi_argmax<NF>(p, s, lane, res, best);
 }
 
 }  // namespace pe

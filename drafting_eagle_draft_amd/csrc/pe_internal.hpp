@@ -16,6 +16,8 @@ enum Epi : int {
   EPI_RESID = 2,   // x += y (O and down projections)
   EPI_SWIGLU = 3,  // h = silu(gate) * up
   EPI_ARGMAX = 4,  // LM head: optional logits, fused argmax
+  EPI_PARTIAL = 5, // (kernel instances only) KS > 1: fp32 partial strips; the
+                   // epilogue of p.epi runs in the finalize kernel
 };
 
 // Row orders of the tiled weight copies (applied when the tiles are built).
@@ -26,6 +28,7 @@ enum RowMap : int {
 };
 
 constexpr int kMaxRows = 64;  // decode activation rows (B*K and B+1)
+constexpr int kGemmWaves = 8;  // waves per workgroup of the weight-streaming GEMM
 
 struct GemmParams {
   // Weights, tiled: fragment (nt, kt, lane) at wt[(nt*KT + kt)*64 + lane].
