@@ -167,7 +167,9 @@ __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
       const_cast<u32x4 *>(p.wt), 0, (int)p.wbytes, 0x00020000);
   const unsigned kOOB = 0x7FFFFFF0u;
   const int G = gridDim.x;
-  const int ns = (p.NT - (int)blockIdx.x + G - 1) / G;  // strips of this workgroup
+  // This workgroup's strips: base, base + step, ... (ns of them).
+  int base = (int)blockIdx.x, step = G;
+  int ns = (p.NT - (int)blockIdx.x + G - 1) / G;
   unsigned joff[MAXKW];  // byte offset of tile j within a strip (kOOB when empty)
 #pragma unroll
   for (int j = 0; j < MAXKW; ++j)
@@ -175,7 +177,7 @@ __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
   const unsigned strip_bytes = (unsigned)p.KT * 1024u;
   auto tile_off = [&](int i, int j) -> unsigned {
     // Tile j of this workgroup's i-th strip, or kOOB past the last strip.
-    return (i < ns && jok[j]) ? (unsigned)((int)blockIdx.x + i * G) * strip_bytes + joff[j] : kOOB;
+    return (i < ns && jok[j]) ? (unsigned)(base + i * step) * strip_bytes + joff[j] : kOOB;
   };
   unsigned long long best[NF];
 #pragma unroll
@@ -198,6 +200,19 @@ __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
   }
   Rstd<NF> rq;
   if (p.ssq) rstd_issue<NF>(p, rq);
+  // Strips in one contiguous range per XCD (workgroup b runs on XCD
+  // b % kXcds): the XCD's G/kXcds workgroups interleave over NT/kXcds
+  // neighbouring strips, with the same strips per workgroup as the plain
+  // interleave b, b + G, ...  Measured on the LM head: 2.4% faster than the
+  // plain interleave (and faster than ranges sized by each XCD's rate in
+  // the previous call: the per-XCD rates move from call to call).
+  if (p.KS == 1 && G % kXcds == 0) {
+    const int x = (int)blockIdx.x % kXcds, r = (int)blockIdx.x / kXcds;
+    const int a0 = (int)((long)p.NT * x / kXcds), a1 = (int)((long)p.NT * (x + 1) / kXcds);
+    step = G / kXcds;
+    base = a0 + r;
+    ns = base < a1 ? (a1 - base + step - 1) / step : 0;
+  }
   u32x4 abuf[D][MAXKW];
 #pragma unroll
   for (int d = 0; d < D; ++d)
@@ -228,7 +243,7 @@ __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
         abuf[d][j] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)tile_off(i + D, j), 0, 0);
       }
       if (i < ns) {
-        const int s = (int)blockIdx.x + i * G;
+        const int s = base + i * step;
         // Sum the W partial tiles in wave order; wave i%W finishes the strip.
 #pragma unroll
         for (int f = 0; f < NF; ++f) red[(w * NF + f) * 64 + lane] = acc[f];

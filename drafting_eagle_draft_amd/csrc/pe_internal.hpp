@@ -29,6 +29,7 @@ enum RowMap : int {
 
 constexpr int kMaxRows = 64;  // decode activation rows (B*K and B+1)
 constexpr int kGemmWaves = 8;  // waves per workgroup of the weight-streaming GEMM
+constexpr int kXcds = 8;        // accelerator complex dies; workgroup b runs on die b % kXcds
 
 struct GemmParams {
   // Weights, tiled: fragment (nt, kt, lane) at wt[(nt*KT + kt)*64 + lane].
