@@ -95,26 +95,31 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {
   const T *kbk = reinterpret_cast<const T *>(p.kb) + bg * p.Kb * HD;
   const T *vbk = reinterpret_cast<const T *>(p.vb) + bg * p.Kb * HD;
 
-  // Key tiles of this split are loaded NBUF at a time into registers, so a
-  // split's whole HBM traffic is in flight together; each tile then goes
-  // through LDS (K row-major, V transposed) to the matrix cores.
+  // Keys of this split: the cached keys [j0, min(j1, ctx)) stream through
+  // a ring of NBUF tiles in registers, each reloaded with the tile NBUF
+  // ahead as soon as it has been staged in LDS, so loads stay in flight
+  // while earlier tiles are computed.  The loads go through buffer
+  // resources with no branch (offsets past the end read zero): a branch per
+  // key would make the compiler wait for the whole ring before the first
+  // tile.  The block's own keys [max(j0, ctx), j1) (at most K_MAX) follow
+  // as one more tile from the block buffers.  Each tile goes through LDS (K
+  // row-major, V transposed) to the matrix cores.
   constexpr int NBUF = S::NBUF;
+  constexpr unsigned OOB = 0x7FFFFFF0u;
+  const int jc1 = min(j1, ctx);  // end of this split's cached keys
+  const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T *>(kc), 0, (int)(p.C * HD * (long)sizeof(T)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T *>(vc), 0, (int)(p.C * HD * (long)sizeof(T)), 0x00020000);
   u32x4 kreg[NBUF][MAXC], vreg[NBUF][MAXC];
-  auto gload = [&](int jt, u32x4 (&kr)[MAXC], u32x4 (&vr)[MAXC]) {
+  auto gload_cache = [&](int jt, u32x4 (&kr)[MAXC], u32x4 (&vr)[MAXC]) {
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
       const int id = tid + i * S::NTHR;
-      const int key = id / CPR, cc = id - key * CPR;
-      const int jj = jt + key;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (jj < j1) {
-        const T *ks = (jj < ctx) ? kc + (long)jj * HD : kbk + (long)(jj - ctx) * HD;
-        const T *vs = (jj < ctx) ? vc + (long)jj * HD : vbk + (long)(jj - ctx) * HD;
-        kv = ldg16(ks + cc * E);
-        vv = ldg16(vs + cc * E);
-      }
-      kr[i] = kv;
-      vr[i] = vv;
+      const int jj = jt + id / CPR, cc = id % CPR;
+      const unsigned off = jj < jc1 ? (unsigned)(jj * HD + cc * E) * (unsigned)sizeof(T) : OOB;
+      kr[i] = __builtin_amdgcn_raw_buffer_load_b128(rkc, (int)off, 0, 0);
+      vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rvc, (int)off, 0, 0);
     }
   };
   auto lstore = [&](const u32x4 (&kr)[MAXC], const u32x4 (&vr)[MAXC]) {
@@ -135,95 +140,132 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {
   for (int d = 0; d < ND; ++d) oacc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_lane = 0.f;
 
-  for (int jr = j0; jr < j1; jr += 64 * NBUF) {
+  // One staged tile: S^T = K Q^T over its 64 keys, fp32 online softmax, O^T
+  // += V^T P^T.  Key kb*16 + 4g + r of the tile is visible when kbase +
+  // kb*16 + 4g + r < lim (a select per score, applied when masked).
+  auto tile = [&](int kbase, int lim, bool masked) {
+    floatx4 sacc[4];
 #pragma unroll
-    for (int b2 = 0; b2 < NBUF; ++b2) gload(jr + 64 * b2, kreg[b2], vreg[b2]);
+    for (int kb = 0; kb < 4; ++kb) {
+      sacc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 a = lds16(&Ks[(kb * 16 + c16) * KS + c * KTILE + g * E]);
+        sacc[kb] = Mma<T>::run(a, qf[c], sacc[kb]);
+      }
+    }
+    if (masked) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[kb][r] = kbase + kb * 16 + 4 * g + r < lim ? sacc[kb][r] : -INFINITY;
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sacc[kb][r]);
+    mt = fmaxf(mt, shfl_xor_f(mt, 16));
+    mt = fmaxf(mt, shfl_xor_f(mt, 32));
+    // Running maximum in the exp2 domain (the scale is positive, so scaling
+    // commutes with the maximum); weights 2^(s*scale - m).
+    const float m_new = fmaxf(m_run, mt * p.scale_log2);
+    const float msub = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - msub);
+    float pv[4][4];
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[kb][r] = fast_exp2(fmaf(sacc[kb][r], p.scale_log2, -msub));
+        ps += pv[kb][r];
+      }
+    l_lane = l_lane * alpha + ps;
+    m_run = m_new;
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+    }
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const u32x4 bf = {pack_bf16x2(pv[2 * c2][0], pv[2 * c2][1]), pack_bf16x2(pv[2 * c2][2], pv[2 * c2][3]),
+                          pack_bf16x2(pv[2 * c2 + 1][0], pv[2 * c2 + 1][1]),
+                          pack_bf16x2(pv[2 * c2 + 1][2], pv[2 * c2 + 1][3])};
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const T *vrow = &Vt[(d * 16 + c16) * VS + 32 * c2 + 4 * g];
+          const uint2 lo = lds8(vrow), hi = lds8(vrow + 16);
+          const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+          oacc[d] = Mma<T>::run(a, bf, oacc[d]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const u32x4 bf = {__float_as_uint(pv[kb][0]), __float_as_uint(pv[kb][1]),
+                          __float_as_uint(pv[kb][2]), __float_as_uint(pv[kb][3])};
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const u32x4 a = lds16(&Vt[(d * 16 + c16) * VS + 16 * kb + 4 * g]);
+          oacc[d] = Mma<T>::run(a, bf, oacc[d]);
+        }
+      }
+    }
+  };
+
+  // Cached keys.  The scheduling barriers keep each tile's loads in ring
+  // order (loads complete in issue order, so a tile waits only for itself
+  // and the older tiles).
+#pragma unroll
+  for (int b2 = 0; b2 < NBUF; ++b2) {
+    gload_cache(j0 + 64 * b2, kreg[b2], vreg[b2]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Whole rounds (every tile of the round holds a key) carry no branch per
+  // tile, which keeps the compiler's wait for each tile exact across the
+  // loop; the last, partial round follows.
+  int jr = j0;
+  for (; jr + 64 * (NBUF - 1) < jc1; jr += 64 * NBUF) {
 #pragma unroll
     for (int b2 = 0; b2 < NBUF; ++b2) {
       const int jt = jr + 64 * b2;
-      if (jt < j1) {
-        lstore(kreg[b2], vreg[b2]);
-        __syncthreads();
-        if (computes) {
-          floatx4 sacc[4];
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            sacc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-              const u32x4 a = lds16(&Ks[(kb * 16 + c16) * KS + c * KTILE + g * E]);
-              sacc[kb] = Mma<T>::run(a, qf[c], sacc[kb]);
-            }
-          }
-          // Keys beyond the split's end or block rows after the query's
-          // own position are masked; cache-only tiles need no test.
-          if (jt + 63 >= j1 || jt + 63 >= ctx) {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int jj = jt + kb * 16 + 4 * g + r;
-                if (!(jj < j1 && (jj < ctx || jj - ctx <= kp_q))) sacc[kb][r] = -INFINITY;
-              }
-          }
-          float mt = -INFINITY;
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sacc[kb][r]);
-          mt = fmaxf(mt, shfl_xor_f(mt, 16));
-          mt = fmaxf(mt, shfl_xor_f(mt, 32));
-          // Running maximum in the exp2 domain (the scale is positive, so
-          // scaling commutes with the maximum); weights 2^(s*scale - m).
-          const float m_new = fmaxf(m_run, mt * p.scale_log2);
-          const float msub = m_new == -INFINITY ? 0.f : m_new;
-          const float alpha = fast_exp2(m_run - msub);
-          float pv[4][4];
-          float ps = 0.f;
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              pv[kb][r] = fast_exp2(fmaf(sacc[kb][r], p.scale_log2, -msub));
-              ps += pv[kb][r];
-            }
-          l_lane = l_lane * alpha + ps;
-          m_run = m_new;
-          if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-            for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
-          }
-          if constexpr (sizeof(T) == 2) {
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-              const u32x4 bf = {pack_bf16x2(pv[2 * c2][0], pv[2 * c2][1]),
-                                pack_bf16x2(pv[2 * c2][2], pv[2 * c2][3]),
-                                pack_bf16x2(pv[2 * c2 + 1][0], pv[2 * c2 + 1][1]),
-                                pack_bf16x2(pv[2 * c2 + 1][2], pv[2 * c2 + 1][3])};
-#pragma unroll
-              for (int d = 0; d < ND; ++d) {
-                const T *vrow = &Vt[(d * 16 + c16) * VS + 32 * c2 + 4 * g];
-                const uint2 lo = lds8(vrow), hi = lds8(vrow + 16);
-                const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
-                oacc[d] = Mma<T>::run(a, bf, oacc[d]);
-              }
-            }
-          } else {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-              const u32x4 bf = {__float_as_uint(pv[kb][0]), __float_as_uint(pv[kb][1]),
-                                __float_as_uint(pv[kb][2]), __float_as_uint(pv[kb][3])};
-#pragma unroll
-              for (int d = 0; d < ND; ++d) {
-                const u32x4 a = lds16(&Vt[(d * 16 + c16) * VS + 16 * kb + 4 * g]);
-                oacc[d] = Mma<T>::run(a, bf, oacc[d]);
-              }
-            }
-          }
-        }
-        __syncthreads();
-      }
+      lstore(kreg[b2], vreg[b2]);
+      gload_cache(jt + 64 * NBUF, kreg[b2], vreg[b2]);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      if (computes) tile(jt, jc1, jt + 63 >= jc1);
+      __syncthreads();
     }
+  }
+#pragma unroll
+  for (int b2 = 0; b2 < NBUF - 1; ++b2) {
+    const int jt = jr + 64 * b2;
+    if (jt < jc1) {
+      lstore(kreg[b2], vreg[b2]);
+      __syncthreads();
+      if (computes) tile(jt, jc1, jt + 63 >= jc1);
+      __syncthreads();
+    }
+  }
+  // The block's own keys of this split: block rows q in [q0, q1) (q = key -
+  // ctx); query row kp_q sees q <= kp_q.
+  const int q0 = max(j0 - ctx, 0), q1 = j1 - ctx;
+  if (q1 > q0) {
+    u32x4 kr[MAXC], vr[MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int id = tid + i * S::NTHR;
+      const int q = q0 + id / CPR, cc = id % CPR;
+      const bool in = q < q1;
+      kr[i] = in ? ldg16(kbk + (long)q * HD + cc * E) : u32x4{0u, 0u, 0u, 0u};
+      vr[i] = in ? ldg16(vbk + (long)q * HD + cc * E) : u32x4{0u, 0u, 0u, 0u};
+    }
+    lstore(kr, vr);
+    __syncthreads();
+    if (computes) tile(q0, min(q1, kp_q + 1), true);
+    __syncthreads();
   }
 
   float l_tot = l_lane;
