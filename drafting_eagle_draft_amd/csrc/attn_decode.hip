@@ -37,7 +37,10 @@ struct AttnShape {
   static constexpr int CHUNKS = 64 * CPR; // chunks per 64-key tile
   static constexpr int NTHR = 256;        // threads per workgroup
   static constexpr int MAXC = CHUNKS / NTHR;
-  static constexpr int NBUF = MAXC <= 2 ? 4 : 2;  // 64-key tiles prefetched per round
+  // 64-key tiles in flight.  bf16 head_dim 64 keeps two, within 128 VGPRs,
+  // so four workgroups share a CU (AttnOcc): their per-tile chains overlap.
+  static constexpr int NBUF = (sizeof(T) == 2 && HD == 64) ? 2 : (MAXC <= 2 ? 4 : 2);
+  static constexpr int WAVES_PER_EU = (sizeof(T) == 2 && HD == 64) ? 4 : 2;
 };
 
 __device__ __forceinline__ u32x4 lds16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
@@ -58,7 +61,8 @@ __device__ __forceinline__ void store_out4<bf16_t>(bf16_t *dst, const float v[4]
 }
 
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(AttnShape<T, HD>::WAVES_PER_EU)))
+void k_attn_decode(AttnParams p) {
   using S = AttnShape<T, HD>;
   constexpr int E = S::E, KTILE = S::KTILE, NC = S::NC, ND = S::ND, KS = S::KS, VS = S::VS;
   constexpr int CPR = S::CPR, CHUNKS = S::CHUNKS, MAXC = S::MAXC;
