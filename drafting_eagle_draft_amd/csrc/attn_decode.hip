@@ -37,10 +37,11 @@ struct AttnShape {
   static constexpr int CHUNKS = 64 * CPR; // chunks per 64-key tile
   static constexpr int NTHR = 256;        // threads per workgroup
   static constexpr int MAXC = CHUNKS / NTHR;
-  // 64-key tiles in flight.  bf16 head_dim 64 keeps two, within 128 VGPRs,
-  // so four workgroups share a CU (AttnOcc): their per-tile chains overlap.
-  static constexpr int NBUF = (sizeof(T) == 2 && HD == 64) ? 2 : (MAXC <= 2 ? 4 : 2);
-  static constexpr int WAVES_PER_EU = (sizeof(T) == 2 && HD == 64) ? 4 : 2;
+  // 64-key tiles in flight.  bf16 keeps few (two at head_dim 64 within 128
+  // VGPRs, one at 128 within 168), so four or three workgroups share a CU
+  // and their per-tile chains overlap.
+  static constexpr int NBUF = sizeof(T) == 2 ? (HD == 64 ? 2 : 1) : (MAXC <= 2 ? 4 : 2);
+  static constexpr int WAVES_PER_EU = sizeof(T) == 2 ? (HD == 64 ? 4 : 3) : 2;
 };
 
 __device__ __forceinline__ u32x4 lds16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
