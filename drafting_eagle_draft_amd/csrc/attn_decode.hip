@@ -45,6 +45,15 @@ struct AttnShape {
 };
 
 __device__ __forceinline__ u32x4 lds16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// Key-column swizzle of the transposed V tile (row chunk cc = row / E): key
+// bits 3..5 flip by cc & 7 for bf16 head_dim 64, bits 2..5 by cc & 15
+// otherwise.  Either keeps each 4-key group contiguous.
+template <typename T, int HD>
+__device__ __forceinline__ int vswz(int cc) {
+  if constexpr (sizeof(T) == 2 && HD == 64) return (cc & 7) << 3;
+  else return (cc & 15) << 2;
+}
 __device__ __forceinline__ uint2 lds8(const void *p) { return *reinterpret_cast<const uint2 *>(p); }
 
 template <typename T>
@@ -127,6 +136,12 @@ void k_attn_decode(AttnParams p) {
       vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rvc, (int)off, 0, 0);
     }
   };
+  // V is staged transposed, Vt[d][key], with the key column XOR-swizzled
+  // by the row's 16-byte chunk (vswz): the 2-byte transposing stores of one
+  // wave then spread over all banks (unswizzled, the 8-16 chunks of a wave
+  // shared 2 bank offsets and the stores were 8-way conflicted).  The
+  // swizzle flips key bits 2..5 only, so each 4-key group read by the
+  // matrix cores stays contiguous.
   auto lstore = [&](const u32x4 (&kr)[MAXC], const u32x4 (&vr)[MAXC]) {
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
@@ -135,8 +150,9 @@ void k_attn_decode(AttnParams p) {
       *reinterpret_cast<u32x4 *>(&Ks[key * KS + cc * E]) = kr[i];
       T vals[E];
       __builtin_memcpy(vals, &vr[i], 16);
+      const int kcol = key ^ vswz<T, HD>(cc);
 #pragma unroll
-      for (int e = 0; e < E; ++e) Vt[(cc * E + e) * VS + key] = vals[e];
+      for (int e = 0; e < E; ++e) Vt[(cc * E + e) * VS + kcol] = vals[e];
     }
   };
 
@@ -200,8 +216,22 @@ void k_attn_decode(AttnParams p) {
                           pack_bf16x2(pv[2 * c2 + 1][2], pv[2 * c2 + 1][3])};
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          const T *vrow = &Vt[(d * 16 + c16) * VS + 32 * c2 + 4 * g];
-          const uint2 lo = lds8(vrow), hi = lds8(vrow + 16);
+          const int vd = d * 16 + c16;
+          const T *vrow = &Vt[vd * VS];
+          int clo, chi;  // swizzled columns of keys 32 c2 + 4g and 32 c2 + 16 + 4g
+          if constexpr (HD == 64) {
+            // row chunk = 2d + c16/8 <= 7: the lane's bits (2..3) and the
+            // unrolled loop's bits (4..5) do not mix, so the offsets fold
+            // into immediates.
+            const int lanebits = (4 * g) ^ (8 * (c16 >> 3));
+            clo = lanebits | ((32 * c2) ^ (16 * d));
+            chi = lanebits | ((32 * c2 + 16) ^ (16 * d));
+          } else {
+            const int sw = vswz<T, HD>(vd / E);
+            clo = (32 * c2 + 4 * g) ^ sw;
+            chi = (32 * c2 + 16 + 4 * g) ^ sw;
+          }
+          const uint2 lo = lds8(vrow + clo), hi = lds8(vrow + chi);
           const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
           oacc[d] = Mma<T>::run(a, bf, oacc[d]);
         }
@@ -213,7 +243,8 @@ void k_attn_decode(AttnParams p) {
                           __float_as_uint(pv[kb][2]), __float_as_uint(pv[kb][3])};
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          const u32x4 a = lds16(&Vt[(d * 16 + c16) * VS + 16 * kb + 4 * g]);
+          const int vd = d * 16 + c16;
+          const u32x4 a = lds16(&Vt[vd * VS + ((16 * kb + 4 * g) ^ vswz<T, HD>(vd / E))]);
           oacc[d] = Mma<T>::run(a, bf, oacc[d]);
         }
       }
