@@ -124,6 +124,22 @@ def test_bf16_small(kw):
     run_case(cfg, w, inp)
 
 
+@pytest.mark.parametrize("kw", [
+    dict(name="small_bf16_straddle"),
+    dict(name="small_bf16_straddle_hd128", n_q_heads=8, n_kv_heads=2, head_dim=128, seed=2006),
+])
+def test_bf16_block_keys_across_splits(kw):
+    # With a 256-position cache the attention splits hold 64 keys each.  The
+    # contexts put the K = 8 block keys across a split boundary (60: keys
+    # 60..67; 250: keys 250..257), at the start of a split with no cached keys
+    # (128), and alone (empty context).
+    cfg = small_bf16(**kw)
+    w = synth.drafter_weights(cfg, gain_jitter=0.1)
+    inp = synth.decode_inputs(cfg, batch=4, ctx_lens=[60, 128, 0, 250], ctx_stride=256, tag="straddle")
+    log(f"{cfg.name} ctx={inp['ctx_lens'].tolist()} stride={inp['ctx_stride']}")
+    run_case(cfg, w, inp)
+
+
 def test_bf16_small_k16_wide_group():
     # K * G = 128 query rows per kv head: two 64-row query partitions.
     cfg = small_bf16(name="small_bf16_k16", n_q_heads=16, n_kv_heads=2, seed=2004, K=16, batch=2)
