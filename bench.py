@@ -11,6 +11,8 @@ in HBM.  Prints one JSON line:
              bytes per launch / mean launch time from HIP events recorded
              around it on the forward's stream during the timed steps
   forward_roofline  the whole forward's algorithmic bytes / step time
+  step_distribution p10 / median / p90 of single forwards timed one by one
+                    after the bracketed steps
   cpu_baseline      the CPU oracle on the same workload (host cores)
   train_forward     the training-shape forward (one drafter layer over a COD
                     layout of 8192 positions, K = 8, about 34K kept rows,
@@ -363,6 +365,19 @@ def main():
     n_lm, lm_ms = pe.pe_profile_read(drafter.handle)
     pe.pe_profile_enable(drafter.handle, False)
 
+    # Distribution of single steps (after the timed bracket, which alone
+    # gives `value`): one event pair around each of another `steps` forwards.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(a.steps)]
+    for e0, e1 in evs:
+        e0.record()
+        buf.launch(drafter)
+        e1.record()
+    torch.cuda.synchronize()
+    per_step = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    step_dist = {"p10_ms": float(np.percentile(per_step, 10)), "median_ms": float(np.median(per_step)),
+                 "p90_ms": float(np.percentile(per_step, 90)), "steps": int(a.steps)}
+
     graph_ms = None
     if a.graph:
         g = torch.cuda.CUDAGraph()
@@ -413,6 +428,7 @@ def main():
         "forward_roofline": {"bound": "hbm", "achieved": fwd_gbs, "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": fwd_gbs / HBM_PEAK_GBS,
                              "algorithmic_bytes": nbytes["total"]},
+        "step_distribution": step_dist,
     }
     if graph_ms is not None:
         out["graph_ms_per_step"] = graph_ms
