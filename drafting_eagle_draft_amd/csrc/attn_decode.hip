@@ -46,14 +46,15 @@ struct AttnShape {
 
 __device__ __forceinline__ u32x4 lds16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
-// Key-column swizzle of the transposed V tile (row chunk cc = row / E): key
-// bits 3..5 flip by cc & 7 for bf16 head_dim 64, bits 2..5 by cc & 15
-// otherwise.  Either keeps each 4-key group contiguous.
+// V-tile swizzle (pe_device.hpp): bits 3..5 for bf16 head_dim 64, bits 2..5
+// otherwise (fewer store conflicts at head_dim 128 in a CPU bank model).
 template <typename T, int HD>
-__device__ __forceinline__ int vswz(int cc) {
-  if constexpr (sizeof(T) == 2 && HD == 64) return (cc & 7) << 3;
-  else return (cc & 15) << 2;
+__device__ __forceinline__ int vt_sw(int cc) {
+  if constexpr (sizeof(T) == 2 && HD == 64) return vt_swizzle_b3(cc);
+  else return vt_swizzle_b2(cc);
 }
+
+
 __device__ __forceinline__ uint2 lds8(const void *p) { return *reinterpret_cast<const uint2 *>(p); }
 
 template <typename T>
@@ -136,12 +137,10 @@ void k_attn_decode(AttnParams p) {
       vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rvc, (int)off, 0, 0);
     }
   };
-  // V is staged transposed, Vt[d][key], with the key column XOR-swizzled
-  // by the row's 16-byte chunk (vswz): the 2-byte transposing stores of one
-  // wave then spread over all banks (unswizzled, the 8-16 chunks of a wave
-  // shared 2 bank offsets and the stores were 8-way conflicted).  The
-  // swizzle flips key bits 2..5 only, so each 4-key group read by the
-  // matrix cores stays contiguous.
+  // V is staged transposed, Vt[d][key], with the key column swizzled by
+  // the row's 16-byte chunk (vt_sw): unswizzled, the 8-16 chunks of a
+  // wave shared 2 bank offsets and the transposing stores were 8-way
+  // conflicted.
   auto lstore = [&](const u32x4 (&kr)[MAXC], const u32x4 (&vr)[MAXC]) {
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
@@ -150,7 +149,7 @@ void k_attn_decode(AttnParams p) {
       *reinterpret_cast<u32x4 *>(&Ks[key * KS + cc * E]) = kr[i];
       T vals[E];
       __builtin_memcpy(vals, &vr[i], 16);
-      const int kcol = key ^ vswz<T, HD>(cc);
+      const int kcol = key ^ vt_sw<T, HD>(cc);
 #pragma unroll
       for (int e = 0; e < E; ++e) Vt[(cc * E + e) * VS + kcol] = vals[e];
     }
@@ -227,7 +226,7 @@ void k_attn_decode(AttnParams p) {
             clo = lanebits | ((32 * c2) ^ (16 * d));
             chi = lanebits | ((32 * c2 + 16) ^ (16 * d));
           } else {
-            const int sw = vswz<T, HD>(vd / E);
+            const int sw = vt_sw<T, HD>(vd / E);
             clo = (32 * c2 + 4 * g) ^ sw;
             chi = (32 * c2 + 16 + 4 * g) ^ sw;
           }
@@ -244,7 +243,7 @@ void k_attn_decode(AttnParams p) {
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
           const int vd = d * 16 + c16;
-          const u32x4 a = lds16(&Vt[vd * VS + ((16 * kb + 4 * g) ^ vswz<T, HD>(vd / E))]);
+          const u32x4 a = lds16(&Vt[vd * VS + ((16 * kb + 4 * g) ^ vt_sw<T, HD>(vd / E))]);
           oacc[d] = Mma<T>::run(a, bf, oacc[d]);
         }
       }

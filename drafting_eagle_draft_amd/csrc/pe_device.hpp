@@ -85,6 +85,18 @@ __device__ __forceinline__ long frag_off(int m, int k, int KT) {
   return ((long)((m >> 4) * KT + k / KTILE) * 64 + ((k % KTILE) / E) * 16 + (m & 15)) * E + (k % E);
 }
 
+// Key-column swizzles of an attention V tile staged transposed in LDS,
+// Vt[d][key] (64 keys), for the row's 16-byte chunk cc = d / E: key bits
+// 3..5 flip by cc & 7 (vt_swizzle_b3) or bits 2..5 by cc & 15
+// (vt_swizzle_b2).  A wave's 2-byte transposing stores then spread over
+// the banks (without a swizzle they hit two bank offsets), and each 4-key
+// group read by the matrix cores stays contiguous (bits 0..1 are kept).
+// For bf16 with 8 elements per chunk, b3 leaves a read column as per-lane
+// bits (2..3) OR'ed with bits that depend only on the unrolled d and key
+// offset (4..5), so the offsets fold into immediates.
+__device__ __forceinline__ int vt_swizzle_b3(int cc) { return (cc & 7) << 3; }
+__device__ __forceinline__ int vt_swizzle_b2(int cc) { return (cc & 15) << 2; }
+
 // Workgroup barrier that waits for this wave's LDS operations only, so
 // global loads already issued (prefetched tiles) stay in flight; the plain
 // __syncthreads() also waits for every outstanding global access.

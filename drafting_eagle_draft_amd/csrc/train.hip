@@ -299,8 +299,10 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
         *reinterpret_cast<u32x4 *>(&Ks[key * KS + cc * E]) = kreg[u][i];
         T vals[E];
         __builtin_memcpy(vals, &vreg[u][i], 16);
+        // bank-spread transposed V (pe_device.hpp): bits 3..5 for bf16, 2..5 for fp32
+        const int kcol = key ^ (sizeof(T) == 2 ? vt_swizzle_b3(cc) : vt_swizzle_b2(cc));
 #pragma unroll
-        for (int e = 0; e < E; ++e) Vt[(cc * E + e) * VS + key] = vals[e];
+        for (int e = 0; e < E; ++e) Vt[(cc * E + e) * VS + kcol] = vals[e];
       }
       lds_barrier();
       if (jt + 64 * PF < nkeys) gload(jt + 64 * PF, kreg[u], vreg[u]);
@@ -379,8 +381,14 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
           for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
             for (int d = 0; d < ND; ++d) {
-              const T *vrow = &Vt[(d * 16 + c16) * VS + 32 * c2 + 4 * g];
-              const uint2 lo = lds8t(vrow), hi = lds8t(vrow + 16);
+              const int vd = d * 16 + c16;
+              const T *vrow = &Vt[vd * VS];
+              // Swizzled columns of keys 32 c2 + 4g and 32 c2 + 16 + 4g (row
+              // chunk 2d + c16/8): lane bits 2..3, loop-constant bits 4..5.
+              const int lanebits = (4 * g) ^ (8 * (c16 >> 3));
+              const int clo = lanebits | ((32 * c2) ^ ((16 * d) & 48));
+              const int chi = lanebits | ((32 * c2 + 16) ^ ((16 * d) & 48));
+              const uint2 lo = lds8t(vrow + clo), hi = lds8t(vrow + chi);
               const u32x4 vf = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
               for (int qb = 0; qb < QB; ++qb) oacc[qb][d] = Mma<T>::run(vf, pbf[qb][c2], oacc[qb][d]);
@@ -390,7 +398,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int d = 0; d < ND; ++d) {
-              const u32x4 vf = lds16t(&Vt[(d * 16 + c16) * VS + 16 * kb + 4 * g]);
+              const int vd = d * 16 + c16;
+              const u32x4 vf = lds16t(&Vt[vd * VS + ((16 * kb + 4 * g) ^ vt_swizzle_b2(vd / E))]);
 #pragma unroll
               for (int qb = 0; qb < QB; ++qb) oacc[qb][d] = Mma<T>::run(vf, pbf[qb][kb], oacc[qb][d]);
             }
