@@ -194,25 +194,27 @@ __device__ void epi_resid(const GemmParams &p, int s, int lane, const floatx4 (&
   const int c16 = lane & 15, g = lane >> 4;
   const int n0 = s * 16 + 4 * g;
   const int H = p.H;
-  float gn[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) gn[r] = p.gnext[n0 + r];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const int m = 16 * f + c16;
     const bool valid = m < p.M;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    // Every load is consumed inside the branch that issued it: a load still
+    // pending where the branch rejoins would make the next strip's head
+    // wait for every weight tile in flight (its registers may be reused).
+    float v[4] = {0.f, 0.f, 0.f, 0.f}, xgv[4] = {0.f, 0.f, 0.f, 0.f};
     if (valid) {
-      float x[4];
+      float x[4], gn[4];
       load4<float>(p.xres + (long)m * H + n0, x);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = x[r] + res[f][r];
+      for (int r = 0; r < 4; ++r) gn[r] = p.gnext[n0 + r];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = x[r] + res[f][r];
+        xgv[r] = v[r] * gn[r];
+      }
     }
     float sq = sum_groups(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]);
     if (valid) {
-      float xgv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) xgv[r] = v[r] * gn[r];
       store4<float>(p.xres + (long)m * H + n0, v);
       store4<T>(reinterpret_cast<T *>(p.xg) + (long)m * H + n0, xgv);
       if (g == 0) p.ssq_out[s * kMaxRows + m] = sq;

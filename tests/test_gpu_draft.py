@@ -115,6 +115,11 @@ def test_k1_matches_eagle3_step():
     dict(),                                                   # hd 64, G 4
     dict(name="small_bf16_hd128", n_q_heads=8, n_kv_heads=2, head_dim=128, seed=2002),
     dict(name="small_bf16_g8", n_q_heads=16, n_kv_heads=2, head_dim=64, seed=2003, batch=3),
+    # Hidden 2048: fc's contraction (3 x 2048) is split over two workgroup
+    # columns, so the shared row h_shared goes through the split-K instance;
+    # the LM head's 515 strips give its workgroups two or three strips each.
+    dict(name="small_bf16_h2048", hidden=2048, n_layers=1, n_q_heads=32, n_kv_heads=4, head_dim=64,
+         intermediate=2048, seed=2007),
 ])
 def test_bf16_small(kw):
     cfg = small_bf16(**kw)
