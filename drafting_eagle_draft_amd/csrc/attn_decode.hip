@@ -342,15 +342,18 @@ void k_attn_decode(AttnParams p) {
 
 // Merge the split partials of each (sequence, kv head, query partition):
 // o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  One workgroup per 16
-// query rows; its 4 waves take splits w, w+4, ... with a running (online)
-// merge, then wave 0 merges the 4 wave results in wave order.
+// query rows and 32 output columns (the partials are read once, spread over
+// HD/32 times more workgroups than whole rows would give); its 4 waves take
+// splits w, w+4, ... with a running (online) merge, then wave 0 merges the 4
+// wave results in wave order.
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p) {
-  constexpr int ND = HD / 16;
+  constexpr int ND = HD / 16, NDC = 2, HC = ND / NDC;
   __shared__ float sm[4][64], sl[4][64];
-  __shared__ floatx4 so[4][ND][64];
+  __shared__ floatx4 so[4][NDC][64];
   const int QP = (p.RP + 63) / 64;
-  const int bgq = blockIdx.x >> 2, qgrp = blockIdx.x & 3;
+  const int hc = blockIdx.x % HC, bq = blockIdx.x / HC;
+  const int bgq = bq >> 2, qgrp = bq & 3;
   const int b = bgq / (p.nkv * QP), rem = bgq - b * (p.nkv * QP);
   const int gk = rem / QP, qp = rem - gk * QP;
   const int ctx = min(max(p.ctx_lens[b], 0) + p.ctx_off, (int)p.C);
@@ -361,16 +364,17 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p) {
   const long stride = 64L * HD + 128;
   const float *base = p.part + (long)bgq * p.S * stride;
   float M = -INFINITY, l = 0.f;
-  floatx4 o[ND];
+  floatx4 o[NDC];
 #pragma unroll
-  for (int d = 0; d < ND; ++d) o[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < NDC; ++d) o[d] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int sp = w; sp < Sb; sp += 4) {
     const float *pp = base + sp * stride;
     const float ms = pp[64L * HD + rl], ls = pp[64L * HD + 64 + rl];
-    floatx4 ov[ND];
+    floatx4 ov[NDC];
 #pragma unroll
-    for (int d = 0; d < ND; ++d) ov[d] = reinterpret_cast<const floatx4 *>(pp)[(qgrp * ND + d) * 64 + lane];
+    for (int d = 0; d < NDC; ++d)
+      ov[d] = reinterpret_cast<const floatx4 *>(pp)[(qgrp * ND + hc * NDC + d) * 64 + lane];
     // A split may hold no key this query can see (only block rows beyond its
     // own position): its maximum is -inf and it contributes nothing.
     const float Mn = fmaxf(M, ms);
@@ -378,34 +382,34 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p) {
     const float c = ms == -INFINITY ? 0.f : fast_exp2(ms - Mn);
     l = l * a + ls * c;
 #pragma unroll
-    for (int d = 0; d < ND; ++d) o[d] = o[d] * a + ov[d] * c;
+    for (int d = 0; d < NDC; ++d) o[d] = o[d] * a + ov[d] * c;
     M = Mn;
   }
   sm[w][lane] = M;
   sl[w][lane] = l;
 #pragma unroll
-  for (int d = 0; d < ND; ++d) so[w][d][lane] = o[d];
+  for (int d = 0; d < NDC; ++d) so[w][d][lane] = o[d];
   __syncthreads();
   if (w != 0 || rq >= p.R) return;
   float Mt = sm[0][lane];
   for (int q = 1; q < 4; ++q) Mt = fmaxf(Mt, sm[q][lane]);
   float lt = 0.f;
-  floatx4 ot[ND];
+  floatx4 ot[NDC];
 #pragma unroll
-  for (int d = 0; d < ND; ++d) ot[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < NDC; ++d) ot[d] = floatx4{0.f, 0.f, 0.f, 0.f};
   for (int q = 0; q < 4; ++q) {
     const float sc = sm[q][lane] == -INFINITY ? 0.f : fast_exp2(sm[q][lane] - Mt);
     lt += sc * sl[q][lane];
 #pragma unroll
-    for (int d = 0; d < ND; ++d) ot[d] += sc * so[q][d][lane];
+    for (int d = 0; d < NDC; ++d) ot[d] += sc * so[q][d][lane];
   }
   const float inv_l = 1.0f / lt;
   const int kp = rq / p.G, hl = rq - kp * p.G;
   T *dst = reinterpret_cast<T *>(p.out) + (long)(b * p.Kb + kp) * (p.nq * HD) + (gk * p.G + hl) * HD;
 #pragma unroll
-  for (int d = 0; d < ND; ++d) {
+  for (int d = 0; d < NDC; ++d) {
     const float v[4] = {ot[d][0] * inv_l, ot[d][1] * inv_l, ot[d][2] * inv_l, ot[d][3] * inv_l};
-    store_out4<T>(dst + d * 16 + 4 * g, v);
+    store_out4<T>(dst + (hc * NDC + d) * 16 + 4 * g, v);
   }
 }
 
@@ -415,7 +419,7 @@ hipError_t launch_typed(const AttnParams &p, hipStream_t s) {
   hipLaunchKernelGGL((k_attn_decode<T, HD>), dim3(p.S, p.nkv * QP, p.B), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S <= 1) return e;
-  hipLaunchKernelGGL((k_attn_combine<T, HD>), dim3(p.B * p.nkv * QP * 4), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_attn_combine<T, HD>), dim3(p.B * p.nkv * QP * 4 * (HD / 32)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
