@@ -342,13 +342,13 @@ void k_attn_decode(AttnParams p) {
 
 // Merge the split partials of each (sequence, kv head, query partition):
 // o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  One workgroup per 16
-// query rows and 32 output columns (the partials are read once, spread over
-// HD/32 times more workgroups than whole rows would give); its 4 waves take
+// query rows and 16 output columns (the partials are read once, spread over
+// HD/16 times more workgroups than whole rows would give); its 4 waves take
 // splits w, w+4, ... with a running (online) merge, then wave 0 merges the 4
 // wave results in wave order.
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p) {
-  constexpr int ND = HD / 16, NDC = 2, HC = ND / NDC;
+  constexpr int ND = HD / 16, NDC = 1, HC = ND / NDC;
   __shared__ float sm[4][64], sl[4][64];
   __shared__ floatx4 so[4][NDC][64];
   const int QP = (p.RP + 63) / 64;
@@ -419,7 +419,7 @@ hipError_t launch_typed(const AttnParams &p, hipStream_t s) {
   hipLaunchKernelGGL((k_attn_decode<T, HD>), dim3(p.S, p.nkv * QP, p.B), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S <= 1) return e;
-  hipLaunchKernelGGL((k_attn_combine<T, HD>), dim3(p.B * p.nkv * QP * 4 * (HD / 32)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_attn_combine<T, HD>), dim3(p.B * p.nkv * QP * 4 * (HD / 16)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
