@@ -286,6 +286,36 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_lm_head_argmax(GemmParams p
   gemm_wg_body<T, NF, MAXKW, EK>(p);
 }
 
+// Sum of strip s's KS chunk partials in chunk order, CB chunks in flight at
+// a time.  Chunks past KS read zero through the buffer resource without a
+// memory access and are not added.
+template <int NF, int CB>
+__device__ __forceinline__ void sum_chunks(const GemmParams &p, int s, int lane, floatx4 (&res)[NF]) {
+  const __amdgpu_buffer_rsrc_t pres = __builtin_amdgcn_make_buffer_rsrc(
+      p.part, 0, (int)((unsigned)p.KS * (unsigned)p.NT * (unsigned)NF * 1024u), 0x00020000);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) res[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < p.KS; c0 += CB) {
+    u32x4 v[CB][NF];
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const unsigned off = c0 + c < p.KS
+            ? ((((unsigned)(c0 + c) * (unsigned)p.NT + (unsigned)s) * NF + f) * 64u + (unsigned)lane) * 16u
+            : 0x7FFFFFF0u;
+        v[c][f] = __builtin_amdgcn_raw_buffer_load_b128(pres, (int)off, 0, 0);
+      }
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const floatx4 x = __builtin_bit_cast(floatx4, v[c][f]);
+        if (c0 + c < p.KS) res[f] += x;
+      }
+  }
+}
+
 // KS > 1: one wave per strip sums the chunk partials in chunk order and runs
 // the epilogue.
 template <typename T, int NF, int EK>
@@ -303,12 +333,13 @@ __global__ __launch_bounds__(256) void k_gemm_finalize(GemmParams p) {
   for (int f = 0; f < NF; ++f) best[f] = 0ull;
   const int s = blockIdx.x * 4 + w;
   if (s < p.NT) {
+    // The chunk partials of a batch are all in flight at once (a loop that
+    // adds each load as it arrives waits for one memory round trip per
+    // chunk), in batches of 2, 4 or 8 as KS needs.
     floatx4 res[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) res[f] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < p.KS; ++c)
-#pragma unroll
-      for (int f = 0; f < NF; ++f) res[f] += p.part[(((long)c * p.NT + s) * NF + f) * 64 + lane];
+    if (p.KS <= 2) sum_chunks<NF, 2>(p, s, lane, res);
+    else if (p.KS <= 4) sum_chunks<NF, 4>(p, s, lane, res);
+    else sum_chunks<NF, 8>(p, s, lane, res);
     finish_strip<T, NF, EK>(p, s, lane, res, rs, best);
   }
   if constexpr (EK == EPI_ARGMAX) block_argmax_out<NF>(p, best, sh, 4);
