@@ -336,32 +336,50 @@ __global__ __launch_bounds__(256) void k_gemm_finalize(GemmParams p) {
     // The chunk partials of a batch are all in flight at once (a loop that
     // adds each load as it arrives waits for one memory round trip per
     // chunk), in batches of 2, 4 or 8 as KS needs.
+    // The residual epilogue's operands are loaded first, so they arrive
+    // with the partials instead of one round trip after them.
+    ResidIn<NF> rin;
+    if constexpr (EK == EPI_RESID) resid_load<NF>(p, s, lane, rin);
     floatx4 res[NF];
     if (p.KS <= 2) sum_chunks<NF, 2>(p, s, lane, res);
     else if (p.KS <= 4) sum_chunks<NF, 4>(p, s, lane, res);
     else sum_chunks<NF, 8>(p, s, lane, res);
-    finish_strip<T, NF, EK>(p, s, lane, res, rs, best);
+    if constexpr (EK == EPI_RESID) {
+      if (p.ssq) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) res[f] *= rs[f];
+      }
+      epi_resid_in<T, NF>(p, s, lane, res, rin);
+    } else {
+      finish_strip<T, NF, EK>(p, s, lane, res, rs, best);
+    }
   }
   if constexpr (EK == EPI_ARGMAX) block_argmax_out<NF>(p, best, sh, 4);
 }
 
 // Final argmax over the per-workgroup best keys: one 1024-thread workgroup;
-// thread t folds rows t%64 of workgroups t/64, t/64+16, ... (loads unrolled
-// so they are in flight together), then 16 partials per row are folded.
+// thread t folds rows t%64 of workgroups t/64, t/64+16, ... with 16 loads in
+// flight per batch of 256 workgroups (blocks past nblk read zero, the
+// identity of the max, through the buffer resource), then 16 partials per
+// row are folded.
 __global__ __launch_bounds__(1024) void k_argmax_final(const unsigned long long *blk_best, int nblk,
                                                        int M, int *draft_out) {
   __shared__ unsigned long long sh[16 * 64];
   const int tid = threadIdx.x, m = tid & 63, part = tid >> 6;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned long long *>(blk_best), 0, (int)((unsigned)nblk * kMaxRows * 8u), 0x00020000);
   unsigned long long b = 0ull;
-  int q = part;
-  for (; q + 48 < nblk; q += 64) {
-    const unsigned long long v0 = blk_best[(long)q * kMaxRows + m];
-    const unsigned long long v1 = blk_best[(long)(q + 16) * kMaxRows + m];
-    const unsigned long long v2 = blk_best[(long)(q + 32) * kMaxRows + m];
-    const unsigned long long v3 = blk_best[(long)(q + 48) * kMaxRows + m];
-    b = umax64(b, umax64(umax64(v0, v1), umax64(v2, v3)));
+  for (int q0 = 0; q0 < nblk; q0 += 256) {
+    unsigned long long v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = q0 + part + 16 * i;
+      const unsigned off = q < nblk ? ((unsigned)q * kMaxRows + (unsigned)m) * 8u : 0x7FFFFFF0u;
+      v[i] = __builtin_bit_cast(unsigned long long, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) b = umax64(b, v[i]);
   }
-  for (; q < nblk; q += 16) b = umax64(b, blk_best[(long)q * kMaxRows + m]);
   sh[part * 64 + m] = b;
   __syncthreads();
   if (tid < 64) {

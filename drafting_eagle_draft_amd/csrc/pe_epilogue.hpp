@@ -222,6 +222,56 @@ __device__ void epi_resid(const GemmParams &p, int s, int lane, const floatx4 (&
   }
 }
 
+// The residual epilogue with its operands loaded ahead (the split-K
+// finalize issues these loads before the chunk partials): x rows of the
+// strip's 16*NF activation rows (zero past M) and the next norm's gains.
+template <int NF>
+struct ResidIn {
+  float x[NF][4];
+  float gn[4];
+};
+
+template <int NF>
+__device__ __forceinline__ void resid_load(const GemmParams &p, int s, int lane, ResidIn<NF> &in) {
+  const int c16 = lane & 15, g = lane >> 4;
+  const int n0 = s * 16 + 4 * g;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) in.gn[r] = p.gnext[n0 + r];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int m = 16 * f + c16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) in.x[f][r] = 0.f;
+    if (m < p.M) load4<float>(p.xres + (long)m * p.H + n0, in.x[f]);
+  }
+}
+
+template <typename T, int NF>
+__device__ void epi_resid_in(const GemmParams &p, int s, int lane, const floatx4 (&res)[NF], const ResidIn<NF> &in) {
+  const int c16 = lane & 15, g = lane >> 4;
+  const int n0 = s * 16 + 4 * g;
+  const int H = p.H;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int m = 16 * f + c16;
+    const bool valid = m < p.M;
+    float v[4] = {0.f, 0.f, 0.f, 0.f}, xgv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = in.x[f][r] + res[f][r];
+        xgv[r] = v[r] * in.gn[r];
+      }
+    }
+    float sq = sum_groups(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]);
+    if (valid) {
+      store4<float>(p.xres + (long)m * H + n0, v);
+      store4<T>(reinterpret_cast<T *>(p.xg) + (long)m * H + n0, xgv);
+      if (g == 0) p.ssq_out[s * kMaxRows + m] = sq;
+    }
+  }
+}
+
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
 template <typename T, int NF>
