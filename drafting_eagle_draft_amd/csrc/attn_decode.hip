@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(AttnShape<T
 void k_attn_decode(AttnParams p) {
   using S = AttnShape<T, HD>;
   constexpr int E = S::E, KTILE = S::KTILE, NC = S::NC, ND = S::ND, KS = S::KS, VS = S::VS;
-  constexpr int CPR = S::CPR, CHUNKS = S::CHUNKS, MAXC = S::MAXC;
+  constexpr int CPR = S::CPR, MAXC = S::MAXC;
   __shared__ __attribute__((aligned(16))) T Ks[64 * KS];
   __shared__ __attribute__((aligned(16))) T Vt[HD * VS];
 
