@@ -32,7 +32,7 @@ EXPORTS = (
     "pe_profile_read", "pe_mask_create", "pe_mask_destroy", "pe_mask_materialize",
     "pe_train_workspace_size", "pe_train_forward", "pe_cod_rows", "pe_partition",
     "pe_draft_extend", "pe_partition_chunk", "pe_train_forward_chunk", "pe_model_prepare_backward",
-    "pe_train_step_workspace_size", "pe_train_step",
+    "pe_train_step_workspace_size", "pe_train_step", "pe_draft_shape_check",
 )
 
 
@@ -91,6 +91,7 @@ def load(path: str = LIB_PATH):
                             ctypes.POINTER(vp)],
         "pe_model_destroy": [vp],
         "pe_draft_workspace_size": [vp, i32, i32, i64, ctypes.POINTER(sz)],
+        "pe_draft_shape_check": [ctypes.POINTER(PeConfig), i32, i32, i64, i32],
         "pe_workspace_init": [vp, sz, vp],
         "pe_draft_forward": [vp, i32, i32, i32, vp, vp, vp, vp, vp, i64, ctypes.POINTER(vp),
                              ctypes.POINTER(vp), vp, vp, vp, sz, vp],
@@ -156,6 +157,11 @@ def pe_draft_workspace_size(model: int, B: int, K: int, ctx_stride: int) -> int:
     _check("pe_draft_workspace_size",
            load().pe_draft_workspace_size(model, B, K, ctx_stride, ctypes.byref(n)))
     return n.value
+
+
+def pe_draft_shape_check(cfg: PeConfig, B: int, K: int, ctx_stride: int, num_cus: int) -> None:
+    """Host-only: raises PeagleError when the draft forward cannot run this shape."""
+    _check("pe_draft_shape_check", load().pe_draft_shape_check(ctypes.byref(cfg), B, K, ctx_stride, num_cus))
 
 
 def pe_workspace_init(workspace: int, ws_bytes: int, stream: int = 0) -> None:

@@ -65,6 +65,38 @@ struct LayerT {
   Tiled qkvT, oT, guT, downT;
 };
 
+// Tile counts of an [N, K] weight in the fragment-tile layout.
+struct TileDims {
+  int NT, KT;
+};
+TileDims tile_dims(int N, int K, int ktile) { return {(N + 15) / 16, (K + ktile - 1) / ktile}; }
+
+// Everything the decode planners need, derived from the configuration and
+// the device's compute-unit count alone (no device memory).
+struct DecodeShape {
+  pe_config cfg;
+  int cus, attn_bpc, ktile;
+  size_t esz;
+  TileDims fc, lm, qkv, o, gateup, down;
+};
+
+DecodeShape decode_shape(const pe_config &c, int cus, int attn_bpc) {
+  DecodeShape d;
+  d.cfg = c;
+  d.cus = cus;
+  d.attn_bpc = attn_bpc;
+  d.ktile = c.dtype == PE_BF16 ? 32 : 16;
+  d.esz = c.dtype == PE_BF16 ? 2 : 4;
+  const int H = c.hidden, I = c.intermediate, hd = c.head_dim;
+  d.fc = tile_dims(H, 3 * H, d.ktile);
+  d.lm = tile_dims(c.vocab, H, d.ktile);
+  d.qkv = tile_dims((c.n_q_heads + 2 * c.n_kv_heads) * hd, H, d.ktile);
+  d.o = tile_dims(H, c.n_q_heads * hd, d.ktile);
+  d.gateup = tile_dims(2 * I, H, d.ktile);
+  d.down = tile_dims(H, I, d.ktile);
+  return d;
+}
+
 }  // namespace
 
 struct pe_model {
@@ -74,6 +106,7 @@ struct pe_model {
   int num_cus = 256;
   size_t lds_budget = 159 * 1024;  // dynamic LDS per GEMM workgroup
   int attn_blocks_per_cu = 2;
+  DecodeShape shape;   // tile counts and device size the decode planners use
   Tiled fc, lm;
   Tiled fcT, lmT;      // transposed tiles (backward)
   bool has_bwd = false;
@@ -98,13 +131,16 @@ namespace {
 // Work split of one GEMM: 8-wave workgroups; each wave keeps nkw weight
 // tiles per strip in flight and the matching activation fragments in
 // registers, so nkw is capped by the register budget (more activation rows,
-// fewer slots).  Larger K is split over KS workgroup columns.
+// fewer slots).  Larger K is split over KS workgroup columns.  KS == 0 marks
+// a contraction no split up to kMaxSplits can serve.
 struct GemmPlan {
   GemmLaunch L;
   int KS, kc, nkw, Mv, nf;
 };
 
-GemmPlan plan_gemm(const pe_model *m, const Tiled &t, int Mv, int nf) {
+constexpr int kMaxSplits = 64;
+
+GemmPlan plan_gemm(int cus, int NT, int KT, int Mv, int nf) {
   GemmPlan g{};
   g.Mv = Mv;
   g.nf = nf;
@@ -113,17 +149,16 @@ GemmPlan plan_gemm(const pe_model *m, const Tiled &t, int Mv, int nf) {
   // One workgroup per CU (8 waves at up to 256 VGPRs).  Each K split adds
   // a finalize kernel, priced like ~100 extra tiles per CU; choose the split
   // with the smallest modelled makespan (strip rounds x tiles per chunk).
-  const int cus = m->num_cus;
   long best = -1;
-  for (int KS = 1; KS <= 16 && KS <= t.KT; ++KS) {
-    const int kc = (t.KT + KS - 1) / KS;
+  for (int KS = 1; KS <= kMaxSplits && KS <= KT; ++KS) {
+    const int kc = (KT + KS - 1) / KS;
     const int nkw = (kc + W - 1) / W;
     if (nkw > max_slots) continue;
-    const int ks = (t.KT + kc - 1) / kc;  // no empty chunk
+    const int ks = (KT + kc - 1) / kc;  // no empty chunk
     int G = cus / ks;
     if (G < 1) G = 1;
-    if (G > t.NT) G = t.NT;
-    const long rounds = (t.NT + G - 1) / G;
+    if (G > NT) G = NT;
+    const long rounds = (NT + G - 1) / G;
     const long cost = rounds * kc + (ks > 1 ? 100 : 0);
     if (best < 0 || cost < best) {
       best = cost;
@@ -140,13 +175,13 @@ struct AttnPlan {
   int L, S;
 };
 
-// Split-KV plan: about attn_blocks_per_cu workgroups per CU over all
-// (sequence, kv head, query partition) units, splits a multiple of 64 keys.
-AttnPlan plan_attn(const pe_model *m, int B, int K, long C) {
-  const int G = m->cfg.n_q_heads / m->cfg.n_kv_heads;
+// Split-KV plan: about attn_bpc workgroups per CU over all (sequence, kv
+// head, query partition) units, splits a multiple of 64 keys.
+AttnPlan plan_attn(const DecodeShape &m, int B, int K, long C) {
+  const int G = m.cfg.n_q_heads / m.cfg.n_kv_heads;
   const int qparts = ((K * G + 15) / 16 * 16 + 63) / 64;
-  const long units = (long)B * m->cfg.n_kv_heads * qparts;
-  long target = ((long)m->num_cus * m->attn_blocks_per_cu + units - 1) / units;
+  const long units = (long)B * m.cfg.n_kv_heads * qparts;
+  long target = ((long)m.cus * m.attn_bpc + units - 1) / units;
   if (target < 1) target = 1;
   const long keys = C + K;
   const long tiles = (keys + 63) / 64;
@@ -163,34 +198,46 @@ struct WsLayout {
   size_t xres, xg, ssq, q, kb, vb, attn_out, mlp_h, gpart, apart, blk, total;
   int RP;
   AttnPlan ap;
+  const char *unsupported;  // non-NULL: why this shape cannot run
 };
 
-WsLayout layout(const pe_model *m, int B, int K, long C) {
-  const pe_config &c = m->cfg;
-  WsLayout w;
+// The attention kernel addresses one (sequence, kv head) cache slice of
+// ctx_stride * head_dim elements through a buffer resource whose
+// out-of-range offset must lie beyond the slice.
+constexpr long kCacheSliceBytesMax = 0x7FFF0000L;
+
+WsLayout layout(const DecodeShape &m, int B, int K, long C) {
+  const pe_config &c = m.cfg;
+  WsLayout w{};
   const int G = c.n_q_heads / c.n_kv_heads;
   const int R = K * G;
   const int M = B * K, nf = (M + 15) / 16, nf_fc = (B + 1 + 15) / 16;
   w.RP = (R + 15) / 16 * 16;
   w.ap = plan_attn(m, B, K, C);
+  if (C * c.head_dim * (long)m.esz > kCacheSliceBytesMax)
+    w.unsupported = "ctx_stride * head_dim * element size exceeds the 2 GiB cache slice limit";
   size_t part = 0, blk = 0;
-  auto upd = [&](const Tiled &t, int Mv, int nfr, bool lm) {
-    const GemmPlan g = plan_gemm(m, t, Mv, nfr);
+  auto upd = [&](const TileDims &t, int Mv, int nfr, bool lm) {
+    const GemmPlan g = plan_gemm(m.cus, t.NT, t.KT, Mv, nfr);
+    if (g.KS == 0) {
+      w.unsupported = "a projection's contraction is too long for the activation rows held in registers";
+      return;
+    }
     if (g.KS > 1) part = std::max(part, (size_t)g.KS * t.NT * nfr * 1024);
     if (lm) {
       const size_t nb = g.KS > 1 ? (size_t)(t.NT + 3) / 4 : (size_t)g.L.grid;
       blk = std::max(blk, nb * kMaxRows * 8);
     }
   };
-  upd(m->fc, B + 1, nf_fc, false);
-  upd(m->fc, M, nf, false);  // cache extension: one fc row per block row
-  for (const LayerT &L : m->layers) {
-    upd(L.qkv, M, nf, false); upd(L.o, M, nf, false); upd(L.gateup, M, nf, false); upd(L.down, M, nf, false);
+  upd(m.fc, B + 1, nf_fc, false);
+  upd(m.fc, M, nf, false);  // cache extension: one fc row per block row
+  if (c.n_layers > 0) {
+    upd(m.qkv, M, nf, false); upd(m.o, M, nf, false); upd(m.gateup, M, nf, false); upd(m.down, M, nf, false);
   }
-  upd(m->lm, M, nf, true);
+  upd(m.lm, M, nf, true);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
-  const size_t H = c.hidden, esz = m->esz;
+  const size_t H = c.hidden, esz = m.esz;
   w.xres = take((size_t)kMaxRows * H * 4);
   w.xg = take((size_t)kMaxRows * H * esz);
   w.ssq = take((size_t)(H / 16) * kMaxRows * 4);
@@ -199,6 +246,8 @@ WsLayout layout(const pe_model *m, int B, int K, long C) {
   w.vb = take((size_t)B * c.n_kv_heads * K * c.head_dim * esz);
   w.attn_out = take((size_t)kMaxRows * c.n_q_heads * c.head_dim * esz);
   w.mlp_h = take((size_t)kMaxRows * c.intermediate * esz);
+  if (part > (size_t)kCacheSliceBytesMax)
+    w.unsupported = "the split-K partial strips exceed 2 GiB";
   w.gpart = take(std::max(part, (size_t)256));
   const size_t qparts = (size_t)(w.RP + 63) / 64;
   w.apart = take((size_t)B * c.n_kv_heads * qparts * w.ap.S * (64 * (size_t)c.head_dim + 128) * 4);
@@ -365,7 +414,7 @@ pe_status enqueue_draft(const pe_model *m, const WsLayout &W, const DraftCall &d
   int lm_blocks = 0;
   auto run = [&](const Tiled &t, int epi, int nfr, GemmParams p) -> pe_status {
     const int Mv = p.act_rows + (p.act_extra ? 1 : 0);
-    const GemmPlan pl = plan_gemm(m, t, Mv, nfr);
+    const GemmPlan pl = plan_gemm(m->num_cus, t.NT, t.KT, Mv, nfr);
     p.wt = t.ptr; p.wbytes = (unsigned)((size_t)t.NT * t.KT * 1024); p.NT = t.NT; p.KT = t.KT;
     p.N = t.N; p.K = t.K;
     p.epi = epi; p.KS = pl.KS; p.kc = pl.kc; p.nkw = pl.nkw; p.Mv = Mv;
@@ -513,6 +562,7 @@ pe_status pe_model_create(const pe_config *cfg, const pe_weights *w, void *strea
   m->num_cus = cus > 0 ? cus : 256;
   m->attn_blocks_per_cu = env_int("PE_ATTN_BLOCKS_PER_CU", 2);
   if (m->attn_blocks_per_cu < 1) m->attn_blocks_per_cu = 1;
+  m->shape = decode_shape(*cfg, m->num_cus, m->attn_blocks_per_cu);
   e = gemm_set_lds_limits();
   if (e != hipSuccess) { destroy(m); return hip_fail(e, "hipFuncSetAttribute(LDS)"); }
 
@@ -583,7 +633,26 @@ pe_status pe_draft_workspace_size(const pe_model *m, int32_t B, int32_t K, int64
     return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d outside 1<=K<=%d, B*K<=%d, B+1<=%d", B, K, PE_K_MAX,
                 PE_DECODE_ROWS_MAX, PE_DECODE_ROWS_MAX);
   if (ctx_stride < 0) return fail(PE_ERR_INVALID_ARGUMENT, "ctx_stride must be >= 0");
-  *bytes = layout(m, B, K, ctx_stride).total;
+  const WsLayout W = layout(m->shape, B, K, ctx_stride);
+  if (W.unsupported) return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d ctx_stride=%ld: %s", B, K, (long)ctx_stride,
+                                 W.unsupported);
+  *bytes = W.total;
+  return PE_OK;
+}
+
+pe_status pe_draft_shape_check(const pe_config *cfg, int32_t B, int32_t K, int64_t ctx_stride,
+                               int32_t num_cus) {
+  if (!cfg) return fail(PE_ERR_INVALID_ARGUMENT, "cfg must be non-NULL");
+  pe_status st = check_cfg(cfg);
+  if (st != PE_OK) return st;
+  if (num_cus < 1) return fail(PE_ERR_INVALID_ARGUMENT, "num_cus must be >= 1");
+  if (B < 1 || K < 1 || K > PE_K_MAX || B * K > PE_DECODE_ROWS_MAX || B + 1 > PE_DECODE_ROWS_MAX)
+    return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d outside 1<=K<=%d, B*K<=%d, B+1<=%d", B, K, PE_K_MAX,
+                PE_DECODE_ROWS_MAX, PE_DECODE_ROWS_MAX);
+  if (ctx_stride < 0) return fail(PE_ERR_INVALID_ARGUMENT, "ctx_stride must be >= 0");
+  const WsLayout W = layout(decode_shape(*cfg, num_cus, 2), B, K, ctx_stride);
+  if (W.unsupported) return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d ctx_stride=%ld: %s", B, K, (long)ctx_stride,
+                                 W.unsupported);
   return PE_OK;
 }
 
@@ -624,7 +693,9 @@ pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K, c
       (logits_out && misaligned(logits_out)) || misaligned(workspace))
     return fail(PE_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
   if (!workspace) return fail(PE_ERR_WORKSPACE, "workspace is NULL");
-  const WsLayout W = layout(m, B, K, ctx_stride);
+  const WsLayout W = layout(m->shape, B, K, ctx_stride);
+  if (W.unsupported) return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d ctx_stride=%ld: %s", B, K, (long)ctx_stride,
+                                 W.unsupported);
   if (ws_bytes < W.total)
     return fail(PE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
 
@@ -668,7 +739,9 @@ pe_status pe_draft_extend(const pe_model *m, int32_t N, int32_t B, int32_t T, co
       misaligned(workspace))
     return fail(PE_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
   if (!workspace) return fail(PE_ERR_WORKSPACE, "workspace is NULL");
-  const WsLayout W = layout(m, B, T, ctx_stride);
+  const WsLayout W = layout(m->shape, B, T, ctx_stride);
+  if (W.unsupported) return fail(PE_ERR_UNSUPPORTED, "B=%d T=%d ctx_stride=%ld: %s", B, T, (long)ctx_stride,
+                                 W.unsupported);
   if (ws_bytes < W.total)
     return fail(PE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
   DraftCall d{};

@@ -141,22 +141,4 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   return ((unsigned long long)hi << 32) | lo;
 }
 
-// Release this wave's global stores at device scope, then count arrival at
-// *ctr; returns the counter value before the increment (same in all lanes).
-__device__ __forceinline__ int arrive(int *ctr) {
-  __threadfence();
-  int old = 0;
-  if (__lane_id() == 0)
-    old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  old = __shfl(old, 0, 64);
-  return old;
-}
-
-// Acquire side: make other waves' released stores visible to this wave.
-__device__ __forceinline__ void acquire() { __threadfence(); }
-
-__device__ __forceinline__ void reset_counter(int *ctr) {
-  if (__lane_id() == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 }  // namespace pe

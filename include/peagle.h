@@ -103,6 +103,18 @@ pe_status pe_model_destroy(pe_model *m);
 pe_status pe_draft_workspace_size(const pe_model *m, int32_t B, int32_t K, int64_t ctx_stride,
                                   size_t *bytes);
 
+/* Host-only check, no device access: whether pe_draft_forward and
+ * pe_draft_extend can run B sequences of block K over caches of stride
+ * ctx_stride for this configuration on a device with num_cus compute units.
+ * PE_ERR_UNSUPPORTED (with the reason in pe_last_error) when a projection's
+ * contraction cannot be split into chunks whose activation fragments fit the
+ * GEMM's registers, when one (sequence, kv head) cache slice of
+ * ctx_stride * head_dim elements exceeds 2 GiB, or when B and K exceed the
+ * build limits; pe_draft_workspace_size, pe_draft_forward and
+ * pe_draft_extend return the same status for such shapes. */
+pe_status pe_draft_shape_check(const pe_config *cfg, int32_t B, int32_t K, int64_t ctx_stride,
+                               int32_t num_cus);
+
 /* Zero a workspace (device, ws_bytes) on the stream with a fill kernel (no
  * memset node, so it may sit in a captured graph).  Every kernel writes what
  * it later reads, so this only makes a fresh workspace's contents defined. */
@@ -154,7 +166,7 @@ pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K,
  *     tokens): step 0 takes the new token and the target's hidden state,
  *     step j > 0 takes step j-1's draft token and its final-norm output
  *     (input_kind PE_INPUT_DRAFTER; "EAGLE-4", "EAGLE-4 overview": the
- *     drafter feeds its normalized output back), with pos_offset = j.
+ *     final-norm state of one step is the next step's input), with pos_offset = j.
  *
  *   N, B, T     layers (0..n_layers), sequences, rows per sequence;
  *               1 <= T <= PE_K_MAX, B*T <= PE_DECODE_ROWS_MAX
@@ -381,7 +393,11 @@ const char *pe_version(void);
 /* Optional per-stage timing of pe_draft_forward: when enabled, the model
  * records HIP events around its LM-head launch on the forward's stream.
  * pe_profile_read synchronises on the last event and returns the number of
- * recorded launches and their mean duration in milliseconds, then clears. */
+ * recorded launches and their mean duration in milliseconds, then clears.
+ * The event slots belong to the model: while profiling is enabled, forwards
+ * of that model must be issued from one host thread at a time (they may use
+ * any stream).  With profiling disabled (the default) a model is only read
+ * by the forward calls, and several threads and streams may share it. */
 pe_status pe_profile_enable(pe_model *m, int32_t enable);
 pe_status pe_profile_read(pe_model *m, int32_t *count, double *mean_ms);
 

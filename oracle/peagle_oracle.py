@@ -267,7 +267,7 @@ def _rotate_once(a, pos, theta, half):
 #   [TD] "Technical Architecture: From Sequential to Parallel": EAGLE needs K
 #   sequential forward passes for K draft tokens.  [PN] section 2: each step
 #   depends on the previous step's token and hidden state.  [E4] "EAGLE-4":
-#   the drafter feeds its normalized output back as the next step's input.
+#   each drafting step takes the previous step's final-norm state as its input.
 # ---------------------------------------------------------------------------
 
 

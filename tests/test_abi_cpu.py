@@ -108,3 +108,50 @@ def test_train_entry_points_reject_null_handles():
         pe.pe_train_workspace_size(None, 8, 8, 8)
     with pytest.raises(pe.PeagleError):
         pe.pe_mask_destroy(None)
+
+
+def _llama8b(**kw):
+    """A LLaMA-3-8B-shaped drafter layer (H 4096, I 14336, 32 q / 8 kv heads of 128)."""
+    base = dict(hidden=4096, n_layers=1, n_q_heads=32, n_kv_heads=8, head_dim=128, intermediate=14336,
+                vocab=128256, rope_theta=5e5, rms_eps=1e-5, dtype=pe.PE_BF16)
+    base.update(kw)
+    return pe.PeConfig(**base)
+
+
+@pytest.mark.parametrize("B,K", [(1, 1), (2, 8), (4, 8), (8, 8), (4, 16), (63, 1)])
+def test_shape_check_plans_long_contractions(B, K):
+    """Every projection of a LLaMA-3-8B-shaped drafter has a K split whose
+    activation fragments fit in registers, up to 64 activation rows (the
+    14336-wide down projection at B*K = 64 needs more than 16 splits)."""
+    pe.pe_draft_shape_check(_llama8b(), B, K, 8192, 256)
+    pe.pe_draft_shape_check(_llama8b(), B, K, 8192, 80)
+
+
+def test_shape_check_rejects_infeasible_contraction():
+    # 64 activation rows leave 2 tile slots per wave: chunks of 16 k-tiles, at
+    # most 64 of them, so a 65536-wide contraction cannot be planned.
+    with pytest.raises(pe.PeagleError) as ei:
+        pe.pe_draft_shape_check(_llama8b(intermediate=65536), 8, 8, 4096, 256)
+    assert ei.value.status == pe.PE_ERR_UNSUPPORTED and "contraction" in ei.value.message
+    pe.pe_draft_shape_check(_llama8b(intermediate=65536), 1, 8, 4096, 256)  # 8 rows: more slots
+
+
+def test_shape_check_bounds_the_cache_slice():
+    # One (sequence, kv head) slice of ctx_stride * 128 bf16 elements must
+    # stay below 2 GiB.
+    pe.pe_draft_shape_check(_llama8b(), 2, 8, 1 << 22, 256)
+    with pytest.raises(pe.PeagleError) as ei:
+        pe.pe_draft_shape_check(_llama8b(), 2, 8, 1 << 23, 256)
+    assert ei.value.status == pe.PE_ERR_UNSUPPORTED and "cache slice" in ei.value.message
+
+
+def test_shape_check_rejects_bad_arguments():
+    with pytest.raises(pe.PeagleError) as ei:
+        pe.pe_draft_shape_check(_llama8b(), 8, 9, 4096, 256)
+    assert ei.value.status == pe.PE_ERR_UNSUPPORTED
+    with pytest.raises(pe.PeagleError) as ei:
+        pe.pe_draft_shape_check(_llama8b(head_dim=96), 2, 8, 4096, 256)
+    assert ei.value.status == pe.PE_ERR_UNSUPPORTED
+    with pytest.raises(pe.PeagleError) as ei:
+        pe.pe_draft_shape_check(_llama8b(), 2, 8, -1, 256)
+    assert ei.value.status == pe.PE_ERR_INVALID_ARGUMENT
