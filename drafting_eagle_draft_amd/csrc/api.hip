@@ -43,12 +43,6 @@ pe_status hip_fail(hipError_t e, const char *what) {
 
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
-int env_int(const char *name, int dflt) {
-  const char *v = getenv(name);
-  if (!v || !*v) return dflt;
-  return atoi(v);
-}
-
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr int kPipe = 8;  // tile loads in flight per GEMM wave (kernel constant)
@@ -75,16 +69,15 @@ TileDims tile_dims(int N, int K, int ktile) { return {(N + 15) / 16, (K + ktile 
 // the device's compute-unit count alone (no device memory).
 struct DecodeShape {
   pe_config cfg;
-  int cus, attn_bpc, ktile;
+  int cus, ktile;
   size_t esz;
   TileDims fc, lm, qkv, o, gateup, down;
 };
 
-DecodeShape decode_shape(const pe_config &c, int cus, int attn_bpc) {
+DecodeShape decode_shape(const pe_config &c, int cus) {
   DecodeShape d;
   d.cfg = c;
   d.cus = cus;
-  d.attn_bpc = attn_bpc;
   d.ktile = c.dtype == PE_BF16 ? 32 : 16;
   d.esz = c.dtype == PE_BF16 ? 2 : 4;
   const int H = c.hidden, I = c.intermediate, hd = c.head_dim;
@@ -105,7 +98,6 @@ struct pe_model {
   size_t esz = 2;      // bytes per dtype element
   int num_cus = 256;
   size_t lds_budget = 159 * 1024;  // dynamic LDS per GEMM workgroup
-  int attn_blocks_per_cu = 2;
   DecodeShape shape;   // tile counts and device size the decode planners use
   Tiled fc, lm;
   Tiled fcT, lmT;      // transposed tiles (backward)
@@ -149,8 +141,10 @@ GemmPlan plan_gemm(int cus, int NT, int KT, int Mv, int nf) {
   // One workgroup per CU (8 waves at up to 256 VGPRs).  Each K split adds
   // a finalize kernel, priced like ~100 extra tiles per CU; choose the split
   // with the smallest modelled makespan (strip rounds x tiles per chunk).
+  // Splits beyond 16 are only searched when no split up to 16 fits (their
+  // short chunks leave few tile slots per wave).
   long best = -1;
-  for (int KS = 1; KS <= kMaxSplits && KS <= KT; ++KS) {
+  for (int KS = 1; KS <= kMaxSplits && KS <= KT && (KS <= 16 || best < 0); ++KS) {
     const int kc = (KT + KS - 1) / KS;
     const int nkw = (kc + W - 1) / W;
     if (nkw > max_slots) continue;
@@ -175,18 +169,24 @@ struct AttnPlan {
   int L, S;
 };
 
-// Split-KV plan: about attn_bpc workgroups per CU over all (sequence, kv
-// head, query partition) units, splits a multiple of 64 keys.
+// Split-KV plan: splits of a whole number of 64-key tiles.  Each split ends
+// in a partial the combine kernel reads, so fewer, longer splits win until
+// the grid no longer covers the chip: measured on the MI355X (kernel plus
+// combine), 5 tiles per split at the 4K context and 9 at 16K (head_dim 64,
+// register-ring kernel), 4 tiles at head_dim 128 (LDS-ring kernel, two
+// workgroups per CU).
 AttnPlan plan_attn(const DecodeShape &m, int B, int K, long C) {
   const int G = m.cfg.n_q_heads / m.cfg.n_kv_heads;
   const int qparts = ((K * G + 15) / 16 * 16 + 63) / 64;
   const long units = (long)B * m.cfg.n_kv_heads * qparts;
-  long target = ((long)m.cus * m.attn_bpc + units - 1) / units;
-  if (target < 1) target = 1;
   const long keys = C + K;
   const long tiles = (keys + 63) / 64;
-  long per = (tiles + target - 1) / target;
-  if (per < 1) per = 1;
+  const bool lds_ring = m.cfg.dtype == PE_BF16 && m.cfg.head_dim == 128;
+  const long min_tp = lds_ring ? 4 : 5;
+  const long wg_target = (long)m.cus * (lds_ring ? 4 : 2);
+  long per = (units * tiles + wg_target - 1) / wg_target;
+  if (per < min_tp) per = min_tp;
+  if (per > tiles) per = tiles;
   AttnPlan a;
   a.L = (int)(per * 64);
   a.S = (int)((keys + a.L - 1) / a.L);
@@ -560,10 +560,9 @@ pe_status pe_model_create(const pe_config *cfg, const pe_weights *w, void *strea
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) { destroy(m); return hip_fail(e, "hipDeviceGetAttribute"); }
   m->num_cus = cus > 0 ? cus : 256;
-  m->attn_blocks_per_cu = env_int("PE_ATTN_BLOCKS_PER_CU", 2);
-  if (m->attn_blocks_per_cu < 1) m->attn_blocks_per_cu = 1;
-  m->shape = decode_shape(*cfg, m->num_cus, m->attn_blocks_per_cu);
+  m->shape = decode_shape(*cfg, m->num_cus);
   e = gemm_set_lds_limits();
+  if (e == hipSuccess) e = attn_set_lds_limits();
   if (e != hipSuccess) { destroy(m); return hip_fail(e, "hipFuncSetAttribute(LDS)"); }
 
   const int H = cfg->hidden, hd = cfg->head_dim, nq = cfg->n_q_heads, nkv = cfg->n_kv_heads;
@@ -650,7 +649,7 @@ pe_status pe_draft_shape_check(const pe_config *cfg, int32_t B, int32_t K, int64
     return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d outside 1<=K<=%d, B*K<=%d, B+1<=%d", B, K, PE_K_MAX,
                 PE_DECODE_ROWS_MAX, PE_DECODE_ROWS_MAX);
   if (ctx_stride < 0) return fail(PE_ERR_INVALID_ARGUMENT, "ctx_stride must be >= 0");
-  const WsLayout W = layout(decode_shape(*cfg, num_cus, 2), B, K, ctx_stride);
+  const WsLayout W = layout(decode_shape(*cfg, num_cus), B, K, ctx_stride);
   if (W.unsupported) return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d ctx_stride=%ld: %s", B, K, (long)ctx_stride,
                                  W.unsupported);
   return PE_OK;

@@ -13,6 +13,20 @@
 // over workgroups (split-KV); each split keeps an fp32 online softmax and
 // writes its partial, and k_attn_combine merges the splits in split order.
 //
+// Two kernels stage the tiles:
+//   k_attn_decode (fp32, and bf16 at head_dim 64): tiles stream through a
+//   ring of registers into LDS, values transposed on the store.
+//   k_attn_decode_lds (bf16, head_dim 128): the query rows, key tiles and
+//   value tiles go from HBM straight into a ring of LDS stages (buffer loads
+//   with the LDS bit: no registers, no transposing stores).  Keys and values
+//   stay row-major in LDS with each row's 16-byte chunks permuted by the key
+//   (conflict-free reads in a 64-bank model); the value operand of O^T is
+//   read transposed by ds_read_b64_tr_b16, whose lane layout within each
+//   16-lane group is: result element j of lane i = element i % 4 of the 8
+//   bytes addressed by lane 4j + i / 4.  At head_dim 128 it runs 10-25%
+//   faster than the register ring (one tile in flight there); at head_dim
+//   64 the register ring, with four workgroups per CU, is faster.
+//
 // Fragment mappings (see pe_device.hpp): for S^T the contraction over head
 // dims uses 16-byte runs of a key row; for O^T the contraction over keys
 // uses the layout S^T leaves in registers -- lane group g holds keys
@@ -340,6 +354,324 @@ void k_attn_decode(AttnParams p) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16: tiles DMA'd from HBM into a ring of LDS stages.
+// ---------------------------------------------------------------------------
+
+// Buffer descriptor in scalar registers for the inline-assembly loads.
+__device__ __forceinline__ u32x4 sgpr_rsrc(const void *base, unsigned bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  return u32x4{(unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a),
+               (unsigned)__builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xFFFFu)),
+               (unsigned)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
+}
+
+// 16 bytes per lane from rsrc + voffset into LDS at lds + 16 * lane (offsets
+// past the extent write zeros).  Inline assembly, so the compiler neither
+// counts these loads nor guards later LDS reads with waits for them: the
+// kernel waits with explicit vmcnt counts.
+__device__ __forceinline__ void dma16(const u32x4 &rsrc, unsigned lds, unsigned voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// 8 bytes per lane read transposed across each 16-lane group (see the file
+// comment), from LDS byte address a.
+__device__ __forceinline__ uint2 lds_tr8(unsigned a) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(size_t)a);
+  return __builtin_bit_cast(uint2, v);
+}
+
+__device__ __forceinline__ u32x4 lds_b128(unsigned a) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((size_t)a);
+}
+
+template <int HD>
+struct DmaAttn {
+  static constexpr int CPR = HD / 8;              // 16-byte chunks per key row
+  static constexpr int NC = HD / 32;              // q fragments per query row
+  static constexpr int ND = HD / 16;              // 16-dim output blocks
+  static constexpr int TILE = 64 * HD * 2;        // bytes of 64 key (or value, or query) rows
+  static constexpr int BLK = TILE / 1024;         // 1 KB wave-loads per TILE
+  static constexpr int LPW = BLK / 2;             // wave-loads per wave per key tile (K and V, 4 waves)
+  static constexpr int QPW = BLK / 4;             // wave-loads per wave for the query rows
+  // Stages of the ring (each one key tile plus one value tile): two at
+  // head_dim 128 (64 KB, two workgroups per CU) measured faster than three
+  // or four stages at one workgroup per CU.
+  static constexpr int NB = 2;
+  static constexpr int LDS = NB * 2 * TILE;
+};
+
+// Chunk permutation of key row k (depends on k % 16 only): XOR of the
+// row's chunk index; conflict-free K-operand reads (16 keys, one chunk) and
+// transposed V reads (8 keys x 2 chunks per 32 lanes) in a 64-bank model.
+template <int HD>
+__device__ __forceinline__ int kv_sw(int k) {
+  if constexpr (HD == 64) return (2 * ((k >> 1) & 3)) ^ ((k >> 3) & 1);
+  else return (2 * (k & 7)) ^ ((k >> 3) & 1);
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_decode_lds(AttnParams p) {
+  using S = DmaAttn<HD>;
+  constexpr int CPR = S::CPR, NC = S::NC, ND = S::ND, TILE = S::TILE, BLK = S::BLK;
+  constexpr int LPW = S::LPW, QPW = S::QPW, NB = S::NB;
+  constexpr unsigned OOB = 0x7FFFFFF0u;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+
+  // blockIdx.y = kv head * QP + query partition (64 query rows each).
+  const int QP = (p.RP + 63) / 64;
+  const int split = blockIdx.x, gk = blockIdx.y / QP, qp = blockIdx.y - gk * QP, b = blockIdx.z;
+  // out-of-range lengths are clamped
+  const int ctx = min(max(p.ctx_lens[b], 0) + p.ctx_off, (int)p.C);
+  const int total = ctx + p.Kb;
+  const int Sb = (total + p.L - 1) / p.L;
+  if (split >= Sb) return;
+  const int j0 = split * p.L;
+  const int j1 = min(j0 + p.L, total);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rq = 64 * qp + 16 * w + c16;    // this lane's query row in the group
+  const bool computes = 64 * qp + 16 * w < p.RP;
+  const int kp_q = rq / p.G;                // its block position
+
+  const long bg = (long)b * p.nkv + gk;
+  const unsigned lds0 = (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char *)smem;
+  const u32x4 rkc = sgpr_rsrc(reinterpret_cast<const bf16_t *>(p.kc) + bg * p.C * HD,
+                              (unsigned)(p.C * HD * 2));
+  const u32x4 rvc = sgpr_rsrc(reinterpret_cast<const bf16_t *>(p.vc) + bg * p.C * HD,
+                              (unsigned)(p.C * HD * 2));
+  const u32x4 rkb = sgpr_rsrc(reinterpret_cast<const bf16_t *>(p.kb) + bg * p.Kb * HD,
+                              (unsigned)(p.Kb * HD * 2));
+  const u32x4 rvb = sgpr_rsrc(reinterpret_cast<const bf16_t *>(p.vb) + bg * p.Kb * HD,
+                              (unsigned)(p.Kb * HD * 2));
+  // Query rows of this partition that exist: [64 qp, min(64 qp + 64, R)).
+  const int qrows = min(64, p.R - 64 * qp);
+  const u32x4 rq_res = sgpr_rsrc(reinterpret_cast<const bf16_t *>(p.q) + (bg * p.RP + 64 * qp) * HD,
+                                 (unsigned)(max(qrows, 0) * HD * 2));
+
+  // This lane's row and permuted chunk in each of the wave's 1 KB blocks:
+  // LDS slot 64 blk + lane holds chunk (slot % CPR) ^ kv_sw(row) of row
+  // slot / CPR.  Wave w loads blocks w, w + 4, ... of each region.
+  unsigned loff[BLK / 4];  // byte offset of the lane's chunk within a 64-row region of global rows
+  int lrow[BLK / 4];
+#pragma unroll
+  for (int i = 0; i < BLK / 4; ++i) {
+    const int slot = (w + 4 * i) * 64 + lane;
+    const int row = slot / CPR, pc = slot % CPR;
+    lrow[i] = row;
+    loff[i] = (unsigned)(row * HD * 2 + ((pc ^ kv_sw<HD>(row)) * 16));
+  }
+
+  // Keys of this split: cached keys [j0, jc1) in 64-key tiles, then the
+  // block's own keys [q0, q1) (block row index, at most K_MAX) as one tile.
+  const int jc1 = min(j1, ctx);
+  const int nct = jc1 > j0 ? (jc1 - j0 + 63) / 64 : 0;
+  const int q0 = max(j0 - ctx, 0), q1 = j1 - ctx;
+  const int ntiles = nct + (q1 > q0 ? 1 : 0);
+
+  auto stage_addr = [&](int st) -> unsigned { return lds0 + (unsigned)(st * 2 * TILE); };
+  // Tile t into stage st: this wave's LPW wave-loads (keys, then values).
+  auto issue = [&](int t, int st) {
+    const unsigned sk = stage_addr(st), sv = sk + TILE;
+    if (t < nct) {
+      const int jt = j0 + 64 * t;
+#pragma unroll
+      for (int i = 0; i < BLK / 4; ++i) {
+        const unsigned off = jt + lrow[i] < jc1 ? (unsigned)(jt * HD * 2) + loff[i] : OOB;
+        dma16(rkc, sk + (unsigned)((w + 4 * i) * 1024), off);
+        dma16(rvc, sv + (unsigned)((w + 4 * i) * 1024), off);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < BLK / 4; ++i) {
+        const unsigned off = q0 + lrow[i] < q1 ? (unsigned)(q0 * HD * 2) + loff[i] : OOB;
+        dma16(rkb, sk + (unsigned)((w + 4 * i) * 1024), off);
+        dma16(rvb, sv + (unsigned)((w + 4 * i) * 1024), off);
+      }
+    }
+  };
+
+  // Prologue: the query rows into the last stage (free until the first
+  // refill), then tiles 0 .. NB-2.
+  {
+    const unsigned sq = stage_addr(NB - 1);
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      const int blk = w + 4 * i;
+      const int slot = blk * 64 + lane;
+      const int row = slot / CPR, pc = slot % CPR;
+      const unsigned off = row < qrows ? (unsigned)(row * HD * 2 + (pc ^ kv_sw<HD>(row)) * 16) : OOB;
+      dma16(rq_res, sq + (unsigned)(blk * 1024), off);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NB - 1; ++t)
+    if (t < ntiles) issue(t, t);
+
+  // Per-lane LDS byte offsets of the operand reads within a stage.
+  //   K operand (S^T): key kb*16 + c16, chunk c*4 + g.
+  //   V operand (O^T, transposed read): key 32 c2 + 16 h + 4 g + c16/4,
+  //   chunk 2 d + (c16 % 4) / 2, half (c16 % 4) % 2.
+  unsigned koff[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) koff[c] = (unsigned)((c16 * CPR + ((c * 4 + g) ^ kv_sw<HD>(c16))) * 16);
+  const int vkey = 4 * g + (c16 >> 2);
+  unsigned voff[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+    voff[d] = (unsigned)(TILE + (vkey * CPR + ((2 * d + ((c16 & 3) >> 1)) ^ kv_sw<HD>(vkey))) * 16 +
+                         (c16 & 1) * 8);
+
+  u32x4 qf[NC];
+  floatx4 oacc[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) oacc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_lane = 0.f;
+
+  // One staged tile: S^T = K Q^T over its 64 keys, fp32 online softmax, O^T
+  // += V^T P^T.  Key kb*16 + 4g + r of the tile is visible when kbase +
+  // kb*16 + 4g + r < lim (a select per score, applied when masked).
+  auto tile = [&](unsigned sk, int kbase, int lim, bool masked) {
+    floatx4 sacc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sacc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 a = lds_b128(sk + (unsigned)(kb * 16 * CPR * 16) + koff[c]);
+        sacc[kb] = Mma<bf16_t>::run(a, qf[c], sacc[kb]);
+      }
+    }
+    if (masked) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[kb][r] = kbase + kb * 16 + 4 * g + r < lim ? sacc[kb][r] : -INFINITY;
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sacc[kb][r]);
+    mt = fmaxf(mt, shfl_xor_f(mt, 16));
+    mt = fmaxf(mt, shfl_xor_f(mt, 32));
+    // Running maximum in the exp2 domain (the scale is positive, so scaling
+    // commutes with the maximum); weights 2^(s*scale - m).
+    const float m_new = fmaxf(m_run, mt * p.scale_log2);
+    const float msub = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - msub);
+    float pv[4][4];
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[kb][r] = fast_exp2(fmaf(sacc[kb][r], p.scale_log2, -msub));
+        ps += pv[kb][r];
+      }
+    l_lane = l_lane * alpha + ps;
+    m_run = m_new;
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+    }
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const u32x4 bf = {pack_bf16x2(pv[2 * c2][0], pv[2 * c2][1]), pack_bf16x2(pv[2 * c2][2], pv[2 * c2][3]),
+                        pack_bf16x2(pv[2 * c2 + 1][0], pv[2 * c2 + 1][1]),
+                        pack_bf16x2(pv[2 * c2 + 1][2], pv[2 * c2 + 1][3])};
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const unsigned a0 = sk + (unsigned)(32 * c2 * CPR * 16) + voff[d];
+        const uint2 lo = lds_tr8(a0), hi = lds_tr8(a0 + (unsigned)(16 * CPR * 16));
+        const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+        oacc[d] = Mma<bf16_t>::run(a, bf, oacc[d]);
+      }
+    }
+  };
+
+  for (int t = 0; t < ntiles; ++t) {
+    // Wait for this wave's loads of tile t: the tiles issued after it may
+    // stay in flight (min(NB - 2, ntiles - 1 - t) of them).
+    const int after = min(NB - 2, ntiles - 1 - t);
+    if (after >= 3) wait_vm<3 * LPW>();
+    else if (after == 2) wait_vm<2 * LPW>();
+    else if (after == 1) wait_vm<LPW>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();  // every wave's loads of tile t are in LDS
+    if (t == 0) {
+      const unsigned sq = stage_addr(NB - 1);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qf[c] = lds_b128(sq + (unsigned)(16 * w * CPR * 16) + koff[c]);
+      // The query stage is refilled next: every wave must hold its rows first.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+    }
+    // The stage of tile t - 1 is free (every wave is past it): refill it
+    // with tile t + NB - 1.
+    if (t + NB - 1 < ntiles) issue(t + NB - 1, (t + NB - 1) % NB);
+    const unsigned sk = stage_addr(t % NB);
+    if (computes) {
+      if (t < nct) {
+        const int jt = j0 + 64 * t;
+        tile(sk, jt, jc1, jt + 63 >= jc1);
+      } else {
+        // block rows q in [q0, q1); query row kp_q sees q <= kp_q
+        tile(sk, q0, min(q1, kp_q + 1), true);
+      }
+    }
+  }
+  static_assert(NB >= 2 && NB - 2 <= 3, "wait ladder covers at most three tiles after the current one");
+  (void)BLK;
+
+  float l_tot = l_lane;
+  l_tot += shfl_xor_f(l_tot, 16);
+  l_tot += shfl_xor_f(l_tot, 32);
+
+  const int hq = p.nq * HD;
+  if (Sb == 1) {
+    if (!computes || rq >= p.R) return;
+    const int kp = rq / p.G, hl = rq - kp * p.G;
+    bf16_t *dst = reinterpret_cast<bf16_t *>(p.out) + (long)(b * p.Kb + kp) * hq + (gk * p.G + hl) * HD;
+    const float inv_l = 1.0f / l_tot;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const float v[4] = {oacc[d][0] * inv_l, oacc[d][1] * inv_l, oacc[d][2] * inv_l, oacc[d][3] * inv_l};
+      store_out4<bf16_t>(dst + d * 16 + 4 * g, v);
+    }
+    return;
+  }
+
+  // Partials of one split: 64 query rows x HD outputs, then 64 maxima and
+  // 64 sums; k_attn_combine merges them after this kernel.
+  const long stride = 64L * HD + 128;
+  const long bgq = bg * QP + qp;
+  const int rl = rq - 64 * qp;  // row within the partition
+  float *pp = p.part + (bgq * p.S + split) * stride;
+  if (computes) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d) reinterpret_cast<floatx4 *>(pp)[(w * ND + d) * 64 + lane] = oacc[d];
+    if (g == 0) {
+      pp[64L * HD + rl] = m_run;
+      pp[64L * HD + 64 + rl] = l_tot;
+    }
+  }
+}
+
 // Merge the split partials of each (sequence, kv head, query partition):
 // o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  One workgroup per 16
 // query rows and 16 output columns (the partials are read once, spread over
@@ -416,7 +748,13 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams p) {
 template <typename T, int HD>
 hipError_t launch_typed(const AttnParams &p, hipStream_t s) {
   const int QP = (p.RP + 63) / 64;
-  hipLaunchKernelGGL((k_attn_decode<T, HD>), dim3(p.S, p.nkv * QP, p.B), dim3(256), 0, s, p);
+  const dim3 grid(p.S, p.nkv * QP, p.B);
+  if constexpr (sizeof(T) == 2 && HD == 128) {
+    constexpr int lds = DmaAttn<HD>::LDS;
+    hipLaunchKernelGGL((k_attn_decode_lds<HD>), grid, dim3(256), lds, s, p);
+  } else {
+    hipLaunchKernelGGL((k_attn_decode<T, HD>), grid, dim3(256), 0, s, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S <= 1) return e;
   hipLaunchKernelGGL((k_attn_combine<T, HD>), dim3(p.B * p.nkv * QP * 4 * (HD / 16)), dim3(256), 0, s, p);
@@ -424,6 +762,11 @@ hipError_t launch_typed(const AttnParams &p, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t attn_set_lds_limits() {
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_attn_decode_lds<128>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, DmaAttn<128>::LDS);
+}
 
 hipError_t launch_attention(int dtype, const AttnParams &p, hipStream_t s) {
   if (dtype == 1) {

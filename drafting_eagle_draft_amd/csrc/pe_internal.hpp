@@ -127,6 +127,8 @@ struct AttnParams {
 };
 
 hipError_t launch_attention(int dtype, const AttnParams &p, hipStream_t s);
+// Allow the bf16 attention kernels their dynamic LDS (above the 64 KB default).
+hipError_t attn_set_lds_limits();
 
 // Cache extension fed back from the drafter: x = E[tok] + z for M rows (z
 // fp32 [M][H]); writes x (fp32), x * gnext (dtype) and per-strip sums of
