@@ -23,6 +23,7 @@ PE_F32 = 0
 PE_BF16 = 1
 PE_K_MAX = 16
 PE_DECODE_ROWS_MAX = 64
+PE_NOALLOC_SCRATCH_BYTES = 32 << 20
 PE_INPUT_TARGET = 0
 PE_INPUT_DRAFTER = 1
 
@@ -32,7 +33,7 @@ EXPORTS = (
     "pe_profile_read", "pe_mask_create", "pe_mask_destroy", "pe_mask_materialize",
     "pe_train_workspace_size", "pe_train_forward", "pe_cod_rows", "pe_partition",
     "pe_draft_extend", "pe_partition_chunk", "pe_train_forward_chunk", "pe_model_prepare_backward",
-    "pe_train_step_workspace_size", "pe_train_step", "pe_draft_shape_check",
+    "pe_train_step_workspace_size", "pe_train_step", "pe_draft_shape_check", "pe_draft_forward_noalloc",
 )
 
 
@@ -95,6 +96,8 @@ def load(path: str = LIB_PATH):
         "pe_workspace_init": [vp, sz, vp],
         "pe_draft_forward": [vp, i32, i32, i32, vp, vp, vp, vp, vp, i64, ctypes.POINTER(vp),
                              ctypes.POINTER(vp), vp, vp, vp, sz, vp],
+        "pe_draft_forward_noalloc": [vp, i32, i32, i32, vp, vp, vp, vp, vp, i64, ctypes.POINTER(vp),
+                                     ctypes.POINTER(vp), vp, vp, vp],
         "pe_accept": [i32, i32, vp, vp, vp, vp, vp],
         "pe_profile_enable": [vp, i32],
         "pe_profile_read": [vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)],
@@ -187,6 +190,20 @@ def pe_draft_forward(model: int, N: int, B: int, K: int, hidden3: int, token_ids
         ctypes.cast(kc, ctypes.POINTER(ctypes.c_void_p)) if kc is not None else None,
         ctypes.cast(vc, ctypes.POINTER(ctypes.c_void_p)) if vc is not None else None,
         draft_out, logits_out, workspace, ws_bytes, stream))
+
+
+def pe_draft_forward_noalloc(model: int, N: int, B: int, K: int, hidden3: int, token_ids: int,
+                             mask_emb: int, h_shared: int, ctx_lens: int, ctx_stride: int,
+                             k_cache, v_cache, draft_out: int, logits_out: int | None,
+                             stream: int = 0) -> None:
+    """pe_draft_forward on the library's per-device scratch (no workspace)."""
+    kc = _ptr_array(list(k_cache)) if k_cache is not None else None
+    vc = _ptr_array(list(v_cache)) if v_cache is not None else None
+    _check("pe_draft_forward_noalloc", load().pe_draft_forward_noalloc(
+        model, N, B, K, hidden3, token_ids, mask_emb, h_shared, ctx_lens, ctx_stride,
+        ctypes.cast(kc, ctypes.POINTER(ctypes.c_void_p)) if kc is not None else None,
+        ctypes.cast(vc, ctypes.POINTER(ctypes.c_void_p)) if vc is not None else None,
+        draft_out, logits_out, stream))
 
 
 def pe_draft_extend(model: int, N: int, B: int, T: int, inputs: int, input_kind: int, token_ids: int,

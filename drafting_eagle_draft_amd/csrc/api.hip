@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -662,11 +663,16 @@ pe_status pe_workspace_init(void *workspace, size_t ws_bytes, void *stream) {
   return PE_OK;
 }
 
-pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K, const void *hidden3,
-                           const int32_t *token_ids, const void *mask_emb, const void *h_shared,
-                           const int32_t *ctx_lens, int64_t ctx_stride, const void *const *k_cache,
-                           const void *const *v_cache, int32_t *draft_out, float *logits_out,
-                           void *workspace, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the parallel-drafting forward shared by both entry
+// points (everything except the workspace).
+pe_status check_forward(const pe_model *m, int32_t N, int32_t B, int32_t K, const void *hidden3,
+                        const int32_t *token_ids, const void *mask_emb, const void *h_shared,
+                        const int32_t *ctx_lens, int64_t ctx_stride, const void *const *k_cache,
+                        const void *const *v_cache, int32_t *draft_out, float *logits_out) {
   if (!m) return fail(PE_ERR_INVALID_ARGUMENT, "model is NULL");
   const pe_config &c = m->cfg;
   if (N < 0 || N > c.n_layers)
@@ -689,22 +695,101 @@ pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K, c
     }
   }
   if (misaligned(hidden3) || misaligned(mask_emb) || misaligned(h_shared) ||
-      (logits_out && misaligned(logits_out)) || misaligned(workspace))
+      (logits_out && misaligned(logits_out)))
     return fail(PE_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
-  if (!workspace) return fail(PE_ERR_WORKSPACE, "workspace is NULL");
-  const WsLayout W = layout(m->shape, B, K, ctx_stride);
-  if (W.unsupported) return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d ctx_stride=%ld: %s", B, K, (long)ctx_stride,
-                                 W.unsupported);
-  if (ws_bytes < W.total)
-    return fail(PE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
+  return PE_OK;
+}
 
+DraftCall forward_call(int32_t N, int32_t B, int32_t K, const void *hidden3, const int32_t *token_ids,
+                       const void *mask_emb, const void *h_shared, const int32_t *ctx_lens, int64_t ctx_stride,
+                       const void *const *k_cache, const void *const *v_cache, int32_t *draft_out,
+                       float *logits_out) {
   DraftCall d{};
   d.N = N; d.B = B; d.K = K; d.mode = DRAFT_PARALLEL;
   d.in = hidden3; d.tok = token_ids; d.mask_emb = mask_emb; d.h_shared = h_shared;
   d.ctx_lens = ctx_lens; d.C = ctx_stride; d.pos_off = 0;
   d.kc = k_cache; d.vc = v_cache;
   d.draft_out = draft_out; d.logits_out = logits_out;
+  return d;
+}
+
+// Scratch of the allocation-free forward: one array per device, in the
+// library's code object (allocated when the module loads, held until the
+// process ends).  Host code never passes `scratch` itself to a kernel: the
+// name is a host-side stand-in, and the device address comes from
+// hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = PE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address; the first call on a device also
+// zeroes it on `s` (a fill kernel, no allocation).
+pe_status scratch_for_device(hipStream_t s, void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PE_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    e = launch_zero(ptr, kScratchBytes, s);
+    if (e != hipSuccess) return hip_fail(e, "scratch zero launch");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K, const void *hidden3,
+                           const int32_t *token_ids, const void *mask_emb, const void *h_shared,
+                           const int32_t *ctx_lens, int64_t ctx_stride, const void *const *k_cache,
+                           const void *const *v_cache, int32_t *draft_out, float *logits_out,
+                           void *workspace, size_t ws_bytes, void *stream) {
+  pe_status st = check_forward(m, N, B, K, hidden3, token_ids, mask_emb, h_shared, ctx_lens, ctx_stride, k_cache,
+                               v_cache, draft_out, logits_out);
+  if (st != PE_OK) return st;
+  if (misaligned(workspace)) return fail(PE_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  if (!workspace) return fail(PE_ERR_WORKSPACE, "workspace is NULL");
+  const WsLayout W = layout(m->shape, B, K, ctx_stride);
+  if (W.unsupported) return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d ctx_stride=%ld: %s", B, K, (long)ctx_stride,
+                                 W.unsupported);
+  if (ws_bytes < W.total)
+    return fail(PE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
+  const DraftCall d = forward_call(N, B, K, hidden3, token_ids, mask_emb, h_shared, ctx_lens, ctx_stride, k_cache,
+                                   v_cache, draft_out, logits_out);
   return enqueue_draft(m, W, d, reinterpret_cast<char *>(workspace), reinterpret_cast<hipStream_t>(stream));
+}
+
+pe_status pe_draft_forward_noalloc(const pe_model *m, int32_t N, int32_t B, int32_t K, const void *hidden3,
+                                   const int32_t *token_ids, const void *mask_emb, const void *h_shared,
+                                   const int32_t *ctx_lens, int64_t ctx_stride, const void *const *k_cache,
+                                   const void *const *v_cache, int32_t *draft_out, float *logits_out,
+                                   void *stream) {
+  pe_status st = check_forward(m, N, B, K, hidden3, token_ids, mask_emb, h_shared, ctx_lens, ctx_stride, k_cache,
+                               v_cache, draft_out, logits_out);
+  if (st != PE_OK) return st;
+  const WsLayout W = layout(m->shape, B, K, ctx_stride);
+  if (W.unsupported) return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d ctx_stride=%ld: %s", B, K, (long)ctx_stride,
+                                 W.unsupported);
+  if (W.total > kScratchBytes)
+    return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d ctx_stride=%ld needs %zu bytes of scratch; the allocation-free "
+                "forward holds %zu (use pe_draft_forward with a workspace)", B, K, (long)ctx_stride, W.total,
+                kScratchBytes);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void *ws = nullptr;
+  if ((st = scratch_for_device(s, &ws)) != PE_OK) return st;
+  const DraftCall d = forward_call(N, B, K, hidden3, token_ids, mask_emb, h_shared, ctx_lens, ctx_stride, k_cache,
+                                   v_cache, draft_out, logits_out);
+  return enqueue_draft(m, W, d, reinterpret_cast<char *>(ws), s);
 }
 
 pe_status pe_draft_extend(const pe_model *m, int32_t N, int32_t B, int32_t T, const void *inputs,

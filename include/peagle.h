@@ -154,6 +154,29 @@ pe_status pe_draft_forward(const pe_model *m, int32_t N, int32_t B, int32_t K,
                            void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * pe_draft_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The same kernels run on a scratch
+ * array of PE_NOALLOC_SCRATCH_BYTES bytes that the library holds per device
+ * in its own code object (there from module load until the process ends);
+ * this call allocates and frees nothing.  The first call on a device looks
+ * the array's address up and clears it with a fill kernel on `stream`.
+ * Arguments, layouts and outputs as pe_draft_forward.  Errors as
+ * pe_draft_forward; PE_ERR_UNSUPPORTED also when the shape needs more
+ * scratch than the array holds (the message gives both sizes; the
+ * workspace forward serves such shapes).  Every call on one device shares
+ * that device's array: calls that may overlap in time on one device (other
+ * streams, other threads) race on it and must be ordered by the caller.
+ */
+#define PE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pe_status pe_draft_forward_noalloc(const pe_model *m, int32_t N, int32_t B, int32_t K,
+                                   const void *hidden3, const int32_t *token_ids,
+                                   const void *mask_emb, const void *h_shared,
+                                   const int32_t *ctx_lens, int64_t ctx_stride,
+                                   const void *const *k_cache, const void *const *v_cache,
+                                   int32_t *draft_out, float *logits_out, void *stream);
+
+/*
  * Drafter-cache extension: T real rows per sequence ("Speeding LLM inference
  * with P-EAGLE in vLLM Speculators", "Flex-attention mask": depth-0
  * positions carry real tokens and real hidden states and attend causally to
