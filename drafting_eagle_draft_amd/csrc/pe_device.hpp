@@ -125,9 +125,11 @@ __device__ __forceinline__ float unordered_bits(unsigned o) {
   return __uint_as_float(u);
 }
 
-// Argmax key: the larger value wins, then the lower index.
+// Argmax key: the larger value wins, then the lower index.  -0.0 + 0.0 is
+// +0.0 (round to nearest), so the two zeros, equal as values, get one key and
+// a tie between them also goes to the lower index.
 __device__ __forceinline__ unsigned long long argmax_key(float v, unsigned idx) {
-  return ((unsigned long long)ordered_bits(v) << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
+  return ((unsigned long long)ordered_bits(v + 0.0f) << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
 }
 
 __device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {

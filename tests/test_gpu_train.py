@@ -168,12 +168,13 @@ def test_train_repeat_is_identical_and_argmax_only():
     mask = runner.TrainMask(cfg.n_max, cfg.K)
     buf = runner.TrainBuffers(d, mask, inp, rows)
     outs = []
-    for _ in range(2):
+    for _ in range(20):  # repeat-run bit identity over 20 runs
         buf.launch(d, mask)
         torch.cuda.synchronize()
         outs.append((buf.argmax.cpu().numpy().copy(), buf.logits.float().cpu().numpy().copy()))
-    np.testing.assert_array_equal(outs[0][0], outs[1][0])
-    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+    for a, lg in outs[1:]:
+        np.testing.assert_array_equal(a, outs[0][0])
+        np.testing.assert_array_equal(lg, outs[0][1])
     nolog = runner.TrainBuffers(d, mask, inp, rows, want_logits=False)
     nolog.launch(d, mask)
     torch.cuda.synchronize()
@@ -252,8 +253,8 @@ def test_train_chunk_rejects_bad_lead_and_missing_rows():
 @pytest.mark.timeout(400)
 def test_train_full_size_sampled_rows():
     """GPT-OSS-20B-shaped drafter layer, n = 8192, K = 8, COD r = 0.8: every
-    row runs on the GPU; a seeded sample of 32 rows per depth is checked
-    against the oracle, run on the rows those depend on."""
+    row runs on the GPU; a seeded sample of 256 rows per depth (2048 rows)
+    is checked against the oracle, run on the rows those depend on."""
     cfg = synth.config("train_gptoss20b_n8192_k8")
     n, K = cfg.seq_len, cfg.K
     t0 = time.time()
@@ -269,7 +270,7 @@ def test_train_full_size_sampled_rows():
     torch.cuda.synchronize()
     rng = np.random.default_rng(11)
     D = rows % K
-    sample = np.sort(np.concatenate([rng.choice(np.flatnonzero(D == dd), 32, replace=False)
+    sample = np.sort(np.concatenate([rng.choice(np.flatnonzero(D == dd), 256, replace=False)
                                      for dd in range(K)]))
     idx = torch.from_numpy(sample).cuda()
     logits = buf.logits[idx].float().cpu().numpy()
