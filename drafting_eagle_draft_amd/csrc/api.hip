@@ -207,16 +207,25 @@ struct WsLayout {
 // out-of-range offset must lie beyond the slice.
 constexpr long kCacheSliceBytesMax = 0x7FFF0000L;
 
+// B sequences of block K within the build limits; B is bounded before the
+// product is formed, so no argument overflows it.
+bool decode_rows_ok(int B, int K) {
+  return B >= 1 && B <= PE_DECODE_ROWS_MAX - 1 && K >= 1 && K <= PE_K_MAX && B * K <= PE_DECODE_ROWS_MAX;
+}
+
 WsLayout layout(const DecodeShape &m, int B, int K, long C) {
   const pe_config &c = m.cfg;
   WsLayout w{};
+  // Compared by division, so that no ctx_stride overflows the product.
+  if (C > kCacheSliceBytesMax / ((long)c.head_dim * (long)m.esz)) {
+    w.unsupported = "ctx_stride * head_dim * element size exceeds the 2 GiB cache slice limit";
+    return w;
+  }
   const int G = c.n_q_heads / c.n_kv_heads;
   const int R = K * G;
   const int M = B * K, nf = (M + 15) / 16, nf_fc = (B + 1 + 15) / 16;
   w.RP = (R + 15) / 16 * 16;
   w.ap = plan_attn(m, B, K, C);
-  if (C * c.head_dim * (long)m.esz > kCacheSliceBytesMax)
-    w.unsupported = "ctx_stride * head_dim * element size exceeds the 2 GiB cache slice limit";
   size_t part = 0, blk = 0;
   auto upd = [&](const TileDims &t, int Mv, int nfr, bool lm) {
     const GemmPlan g = plan_gemm(m.cus, t.NT, t.KT, Mv, nfr);
@@ -629,7 +638,7 @@ pe_status pe_model_destroy(pe_model *m) {
 pe_status pe_draft_workspace_size(const pe_model *m, int32_t B, int32_t K, int64_t ctx_stride,
                                   size_t *bytes) {
   if (!m || !bytes) return fail(PE_ERR_INVALID_ARGUMENT, "model and bytes must be non-NULL");
-  if (B < 1 || K < 1 || K > PE_K_MAX || B * K > PE_DECODE_ROWS_MAX || B + 1 > PE_DECODE_ROWS_MAX)
+  if (!decode_rows_ok(B, K))
     return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d outside 1<=K<=%d, B*K<=%d, B+1<=%d", B, K, PE_K_MAX,
                 PE_DECODE_ROWS_MAX, PE_DECODE_ROWS_MAX);
   if (ctx_stride < 0) return fail(PE_ERR_INVALID_ARGUMENT, "ctx_stride must be >= 0");
@@ -646,7 +655,7 @@ pe_status pe_draft_shape_check(const pe_config *cfg, int32_t B, int32_t K, int64
   pe_status st = check_cfg(cfg);
   if (st != PE_OK) return st;
   if (num_cus < 1) return fail(PE_ERR_INVALID_ARGUMENT, "num_cus must be >= 1");
-  if (B < 1 || K < 1 || K > PE_K_MAX || B * K > PE_DECODE_ROWS_MAX || B + 1 > PE_DECODE_ROWS_MAX)
+  if (!decode_rows_ok(B, K))
     return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d outside 1<=K<=%d, B*K<=%d, B+1<=%d", B, K, PE_K_MAX,
                 PE_DECODE_ROWS_MAX, PE_DECODE_ROWS_MAX);
   if (ctx_stride < 0) return fail(PE_ERR_INVALID_ARGUMENT, "ctx_stride must be >= 0");
@@ -677,7 +686,7 @@ pe_status check_forward(const pe_model *m, int32_t N, int32_t B, int32_t K, cons
   const pe_config &c = m->cfg;
   if (N < 0 || N > c.n_layers)
     return fail(PE_ERR_INVALID_ARGUMENT, "N=%d outside [0, n_layers=%d]", N, c.n_layers);
-  if (B < 1 || K < 1 || K > PE_K_MAX || B * K > PE_DECODE_ROWS_MAX || B + 1 > PE_DECODE_ROWS_MAX)
+  if (!decode_rows_ok(B, K))
     return fail(PE_ERR_UNSUPPORTED, "B=%d K=%d outside 1<=K<=%d, B*K<=%d, B+1<=%d", B, K, PE_K_MAX,
                 PE_DECODE_ROWS_MAX, PE_DECODE_ROWS_MAX);
   if (!hidden3 || !token_ids || !mask_emb || !h_shared || !draft_out)
@@ -801,7 +810,7 @@ pe_status pe_draft_extend(const pe_model *m, int32_t N, int32_t B, int32_t T, co
   const pe_config &c = m->cfg;
   if (N < 0 || N > c.n_layers)
     return fail(PE_ERR_INVALID_ARGUMENT, "N=%d outside [0, n_layers=%d]", N, c.n_layers);
-  if (B < 1 || T < 1 || T > PE_K_MAX || B * T > PE_DECODE_ROWS_MAX)
+  if (B < 1 || B > PE_DECODE_ROWS_MAX || T < 1 || T > PE_K_MAX || B * T > PE_DECODE_ROWS_MAX)
     return fail(PE_ERR_UNSUPPORTED, "B=%d T=%d outside 1<=T<=%d, B*T<=%d", B, T, PE_K_MAX, PE_DECODE_ROWS_MAX);
   if (input_kind != PE_INPUT_TARGET && input_kind != PE_INPUT_DRAFTER)
     return fail(PE_ERR_INVALID_ARGUMENT, "input_kind %d is neither PE_INPUT_TARGET nor PE_INPUT_DRAFTER",

@@ -371,12 +371,19 @@ __device__ __forceinline__ u32x4 sgpr_rsrc(const void *base, unsigned bytes) {
 // past the extent write zeros).  Inline assembly, so the compiler neither
 // counts these loads nor guards later LDS reads with waits for them: the
 // kernel waits with explicit vmcnt counts.
+// M0 is a register the compiler reserves: it warns that the clobber is not
+// honoured.  No code it generates for these kernels keeps a value in M0
+// (every M0 write is this asm's, checked on the assembly by a test), so
+// the warning is silenced here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const u32x4 &rsrc, unsigned lds, unsigned voffset) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds), "v"(voffset), "s"(rsrc)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {

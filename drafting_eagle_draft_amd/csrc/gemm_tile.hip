@@ -110,34 +110,31 @@ __device__ __forceinline__ u32x4 make_rsrc(const void *base, size_t bytes) {
                (unsigned)__builtin_amdgcn_readfirstlane((int)n), 0x00020000u};
 }
 
-// 16 bytes per lane from rsrc + voffset into registers, untracked by the
-// compiler like load_to_lds: the caller waits with an explicit vmcnt and
-// then passes the registers through an empty asm before their first use.
-__device__ __forceinline__ u32x4 load_to_reg(const u32x4 &rsrc, int voffset) {
-  u32x4 v;
-  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(voffset), "s"(rsrc) : "memory");
-  return v;
-}
-
 // 16 bytes per lane from rsrc + voffset into LDS at lds + 16 * lane.  Issued
 // as inline assembly so that the compiler neither counts it nor guards later
 // LDS reads with a wait for it: callers wait with explicit vmcnt counts.
+// M0 is a register the compiler reserves: it warns that the clobber is not
+// honoured.  No code it generates for these kernels keeps a value in M0
+// (every M0 write is this asm's, checked on the assembly by a test), so
+// the warning is silenced here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void load_to_lds(const u32x4 &rsrc, unsigned lds, int voffset) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds), "v"(voffset), "s"(rsrc)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <typename T, int EPI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_tile(TileGemmParams p) {
   constexpr int KTILE = Frag<T>::KTILE, E = Frag<T>::E;
   constexpr int NSTAGE = 4;
-  // Stage layout: the tile's 16 row groups of 16 activation rows; each
-  // fragment is 64 lanes x 16 bytes.  Weight fragments bypass LDS: each wave
-  // loads its own four strips' fragments into a ring of registers.
-  __shared__ u32x4 smem[NSTAGE][16][64];
+  // Stage layout: fragments 0..15 are weight strips s0..s0+15, 16..31 are
+  // row groups of 16 activation rows; each fragment is 64 lanes x 16 bytes.
+  __shared__ u32x4 smem[NSTAGE][32][64];
   // LM head: per-wave staging of RCH logits rows (row pitch 64 elements +
   // 16 bytes) and the per-quarter argmax keys of the tile's 256 rows.  Kept
   // apart from the stages so the next tile's loads run during the epilogue.
@@ -157,20 +154,20 @@ void k_gemm_tile(TileGemmParams p) {
   const int G = gridDim.x, b = blockIdx.x;
   const int slot = (G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
   const size_t lda_b = (size_t)p.lda * sizeof(T);
-  // Activation fragments: wave w fetches row groups 2w, 2w + 1 of each stage
-  // into LDS.  Byte offset of this lane's 16 bytes within the wave's first
-  // fragment at k tile 0; fragment q and k tile kt add qstride*q + kstep*kt.
-  // Tiled activations: 1 KB fragments, k tiles 1 KB apart, groups KT KB
-  // apart.  Row-major activations: 16 rows of lda elements.
-  const int lanebase = p.a_tiled ? lane * 16 : c16 * (int)lda_b + g * E * (int)sizeof(T);
-  const int qstride = p.a_tiled ? p.KT * 1024 : 16 * (int)lda_b;
-  const int fbase = 2 * w * qstride;
-  const int kstep = p.a_tiled ? 1024 : KTILE * (int)sizeof(T);
+  const bool wave_w = w < 4;  // waves 0-3 fetch weight strips, 4-7 row groups, 4 each
+  // Byte offset of this lane's 16 bytes within the wave's first fragment at
+  // k tile 0; fragment q and k tile kt add the wave-uniform
+  // fbase + qstride*q + kstep*kt.
+  // Weights and tiled activations: 1 KB fragments, k tiles 1 KB apart,
+  // groups KT KB apart.  Row-major activations: 16 rows of lda elements.
+  const bool frag = wave_w || p.a_tiled;
+  const int lanebase = frag ? lane * 16 : c16 * (int)lda_b + g * E * (int)sizeof(T);
+  const int qstride = frag ? p.KT * 1024 : 16 * (int)lda_b;
+  const int fbase = (w & 3) * 4 * qstride;
+  const int kstep = frag ? 1024 : KTILE * (int)sizeof(T);
   const unsigned lds0 = (unsigned)__builtin_amdgcn_readfirstlane(
-      (int)(unsigned)(size_t)(lds_void *)&smem[0][2 * w][0]);
-  constexpr int stage_bytes = 16 * 64 * 16;
-  // Weight fragments of strip wn*4 + i, k tile kt: offset ((wn*4 + i) KT + kt) KB.
-  const int wbase = (wn * 4) * p.KT * 1024 + lane * 16;
+      (int)(unsigned)(size_t)(lds_void *)&smem[0][(w >> 2) * 16 + (w & 3) * 4][0]);
+  constexpr int stage_bytes = 32 * 64 * 16;
 
   // Tile t -> (first activation row, first weight strip); bands of four row
   // blocks, columns inside a band.
@@ -182,51 +179,31 @@ void k_gemm_tile(TileGemmParams p) {
     s0 = cb * 16;
   };
   const int MG = (p.M + 15) >> 4;  // 16-row groups of a tiled A
-  auto a_rsrc = [&](int m0) {
+  auto tile_rsrc = [&](int m0, int s0) {
+    if (wave_w)
+      return make_rsrc(reinterpret_cast<const char *>(p.wt) + (size_t)s0 * p.KT * 1024,
+                       (size_t)(p.NT - s0) * p.KT * 1024);
     if (p.a_tiled)
       return make_rsrc(reinterpret_cast<const char *>(p.A) + (size_t)(m0 >> 4) * p.KT * 1024,
                        (size_t)(MG - (m0 >> 4)) * p.KT * 1024);
     return make_rsrc(reinterpret_cast<const char *>(p.A) + (size_t)m0 * lda_b, (size_t)(p.M - m0) * lda_b);
   };
-  auto w_rsrc = [&](int s0) {
-    return make_rsrc(reinterpret_cast<const char *>(p.wt) + (size_t)s0 * p.KT * 1024,
-                     (size_t)(p.NT - s0) * p.KT * 1024);
-  };
-  // Per k step and lane: two activation loads into LDS, then (after the
-  // step's products) four weight loads into the ring slot just used; the
-  // loads of step kt are issued during step kt - 3.  Loads past the last k
-  // tile use an offset beyond the extent: zero, no memory access, but
-  // counted like the others, so every step waits for the same vmcnt.
-  auto issue_a = [&](const u32x4 &rs, int kt) {
+  auto issue = [&](const u32x4 &rs, int kt) {
     const unsigned dst = lds0 + (unsigned)((kt & (NSTAGE - 1)) * stage_bytes);
     const bool live = kt < p.KT;
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < 4; ++q)
       load_to_lds(rs, dst + q * 1024, live ? lanebase + (fbase + q * qstride + kt * kstep) : kOobOffset);
   };
-  auto issue_w = [&](const u32x4 &rs, int kt, u32x4 (&slot)[4]) {
-    const bool live = kt < p.KT;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      slot[i] = load_to_reg(rs, live ? wbase + (i * p.KT + kt) * 1024 : kOobOffset);
-  };
 
-  u32x4 ring0[4], ring1[4], ring2[4];
   int t = slot, m0 = 0, s0 = 0;
-  u32x4 rsa = {0u, 0u, 0u, 0u}, rsw = {0u, 0u, 0u, 0u};
-  auto prologue = [&]() {
-    issue_a(rsa, 0);
-    issue_w(rsw, 0, ring0);
-    issue_a(rsa, 1);
-    issue_w(rsw, 1, ring1);
-    issue_a(rsa, 2);
-    issue_w(rsw, 2, ring2);
-  };
+  u32x4 rs = {0u, 0u, 0u, 0u};
   if (t < tiles) {
     tile_origin(t, m0, s0);
-    rsa = a_rsrc(m0);
-    rsw = w_rsrc(s0);
-    prologue();
+    rs = tile_rsrc(m0, s0);
+    issue(rs, 0);
+    issue(rs, 1);
+    issue(rs, 2);
   }
   while (t < tiles) {
     floatx4 acc[4][8];
@@ -235,31 +212,25 @@ void k_gemm_tile(TileGemmParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // Step kt: wait until this lane's loads of step kt are in (the twelve
-    // younger ones of steps kt+1 and kt+2 may still be loading), barrier so
-    // every wave's activation loads of the stage are in LDS, issue step
-    // kt+3's activation loads, read the 8 activation fragments, multiply with
-    // the ring slot's weight fragments, then refill that slot with step
-    // kt+3's weights.  The second wave on each SIMD covers this wave's waits.
-    auto step = [&](int kt, u32x4 (&wf)[4]) {
-      asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
-      // The ring registers are valid only from here on.
-      asm volatile("" : "+v"(wf[0]), "+v"(wf[1]), "+v"(wf[2]), "+v"(wf[3]));
-      issue_a(rsa, kt + 3);
+    // Three stages in flight ahead of the one being multiplied (the first
+    // three were issued before this tile started).  Step kt waits for its
+    // own stage (two younger stages may still be loading), refills the
+    // buffer of stage kt-1 (read into registers before this barrier) with
+    // stage kt+3, then reads its 12 fragments and multiplies; the second
+    // wave on each SIMD covers this wave's waits.
+    for (int kt = 0; kt < p.KT; ++kt) {
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+      issue(rs, kt + 3);
       const int st = kt & (NSTAGE - 1);
-      u32x4 af[8];
+      u32x4 wf[4], af[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) af[j] = smem[st][wm * 8 + j][lane];
+      for (int i = 0; i < 4; ++i) wf[i] = smem[st][wn * 4 + i][lane];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) af[j] = smem[st][16 + wm * 8 + j][lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = Mma<T>::run(wf[i], af[j], acc[i][j]);
-      issue_w(rsw, kt + 3, wf);
-    };
-    for (int kt = 0; kt < p.KT; kt += 3) {
-      step(kt, ring0);
-      if (kt + 1 < p.KT) step(kt + 1, ring1);
-      if (kt + 2 < p.KT) step(kt + 2, ring2);
     }
     // Drain the look-ahead loads (they target stages the next tile reuses),
     // then start the next tile's first three stages so that they load while
@@ -269,9 +240,10 @@ void k_gemm_tile(TileGemmParams p) {
     t += G;
     if (t < tiles) {
       tile_origin(t, m0, s0);
-      rsa = a_rsrc(m0);
-      rsw = w_rsrc(s0);
-      prologue();
+      rs = tile_rsrc(m0, s0);
+      issue(rs, 0);
+      issue(rs, 1);
+      issue(rs, 2);
     }
     {
     const int m0 = tm0, s0 = ts0;
