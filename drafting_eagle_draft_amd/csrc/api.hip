@@ -196,7 +196,7 @@ AttnPlan plan_attn(const DecodeShape &m, int B, int K, long C) {
 }
 
 struct WsLayout {
-  size_t xres, xg, ssq, q, kb, vb, attn_out, mlp_h, gpart, apart, blk, total;
+  size_t xres, xg, ssq, q, kb, vb, attn_out, mlp_h, gpart, apart, blk, cnt, keys, total;
   int RP;
   AttnPlan ap;
   const char *unsupported;  // non-NULL: why this shape cannot run
@@ -262,6 +262,12 @@ WsLayout layout(const DecodeShape &m, int B, int K, long C) {
   const size_t qparts = (size_t)(w.RP + 63) / 64;
   w.apart = take((size_t)B * c.n_kv_heads * qparts * w.ap.S * (64 * (size_t)c.head_dim + 128) * 4);
   w.blk = take(std::max(blk, (size_t)256));
+  // Arrival counters (one per weight strip of the split projections; the LM
+  // head uses the first) and the LM head's row keys: zero from
+  // pe_workspace_init on, and every launch leaves them at zero.
+  const int nt_max = std::max({m.fc.NT, m.qkv.NT, m.o.NT, m.gateup.NT, m.down.NT, 1});
+  w.cnt = take((size_t)nt_max * 4);
+  w.keys = take((size_t)kMaxRows * 8);
   w.total = off;
   return w;
 }
@@ -421,7 +427,9 @@ pe_status enqueue_draft(const pe_model *m, const WsLayout &W, const DraftCall &d
   base.eps = c.rms_eps;
   base.inv_width = 1.0f / (float)H;
 
+  unsigned *cnt = reinterpret_cast<unsigned *>(ws + W.cnt);
   int lm_blocks = 0;
+  bool tokens_written = false;  // the LM head wrote draft_out itself
   auto run = [&](const Tiled &t, int epi, int nfr, GemmParams p) -> pe_status {
     const int Mv = p.act_rows + (p.act_extra ? 1 : 0);
     const GemmPlan pl = plan_gemm(m->num_cus, t.NT, t.KT, Mv, nfr);
@@ -429,6 +437,15 @@ pe_status enqueue_draft(const pe_model *m, const WsLayout &W, const DraftCall &d
     p.N = t.N; p.K = t.K;
     p.epi = epi; p.KS = pl.KS; p.kc = pl.kc; p.nkw = pl.nkw; p.Mv = Mv;
     lm_blocks = pl.KS > 1 ? (t.NT + 3) / 4 : pl.L.grid;
+    // Split FC and residual projections finish their strips in-kernel; an
+    // unsplit LM head writes the tokens itself.
+    if (pl.KS > 1 && (epi == EPI_FC || epi == EPI_RESID)) p.cnt = cnt;
+    if (epi == EPI_ARGMAX && pl.KS == 1 && d.draft_out) {
+      p.cnt = cnt;
+      p.keys = reinterpret_cast<unsigned long long *>(ws + W.keys);
+      p.draft_out = d.draft_out;
+      tokens_written = true;
+    }
     hipError_t e = launch_gemm(c.dtype, nfr, p, pl.L, s);
     if (e != hipSuccess) return hip_fail(e, "GEMM launch");
     return PE_OK;
@@ -522,7 +539,7 @@ pe_status enqueue_draft(const pe_model *m, const WsLayout &W, const DraftCall &d
       (void)hipEventRecord(m->ev1[m->nrec], s);
       ++m->nrec;
     }
-    if (d.draft_out) {
+    if (d.draft_out && !tokens_written) {
       hipError_t e = launch_argmax_final(p.blk_best, lm_blocks, M, d.draft_out, s);
       if (e != hipSuccess) return hip_fail(e, "argmax launch");
     }

@@ -14,10 +14,13 @@
 //     issued without branches (buffer loads past the end read zero).
 //   * Partial 16x(16*NF) tiles are summed through LDS in wave order
 //     (deterministic) by one wave per strip, which runs the epilogue.
-//   * Nothing crosses workgroups inside a kernel: there is no device-scope
-//     fence or counter.  When the activations do not fit in LDS the K range
-//     is split over KS workgroup columns that write fp32 partial strips, and
-//     k_gemm_finalize sums them in chunk order and runs the epilogue.
+//   * Long contractions are split over KS workgroup columns that write fp32
+//     partial strips.  With arrival counters (the FC and residual
+//     epilogues) the workgroup that completes a strip last sums its
+//     partials in chunk order and runs the epilogue after its strip loop;
+//     otherwise k_gemm_finalize does.  The LM head folds its argmax the same
+//     way (64-bit atomic maximum per row, last workgroup writes the tokens).
+//     Counters and keys start at zero and every launch leaves them at zero.
 #include "pe_epilogue.hpp"
 
 namespace pe {
@@ -138,7 +141,126 @@ __device__ void block_argmax_out(const GemmParams &p, const unsigned long long (
   }
 }
 
-template <typename T, int NF, int MAXKW, int EK>
+// Sum of strip s's KS chunk partials in chunk order, CB chunks in flight at
+// a time.  Chunks past KS read zero through the buffer resource without a
+// memory access and are not added.
+// Cache policy of a buffer access at device scope (SC1): a store writes
+// through to the level every XCD reads, and a load reads the value there.
+constexpr int kDeviceScope = 16;
+
+template <int NF, int CB, int AUX = 0>
+__device__ __forceinline__ void sum_chunks(const GemmParams &p, int s, int lane, floatx4 (&res)[NF]) {
+  const __amdgpu_buffer_rsrc_t pres = __builtin_amdgcn_make_buffer_rsrc(
+      p.part, 0, (int)((unsigned)p.KS * (unsigned)p.NT * (unsigned)NF * 1024u), 0x00020000);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) res[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < p.KS; c0 += CB) {
+    u32x4 v[CB][NF];
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const unsigned off = c0 + c < p.KS
+            ? ((((unsigned)(c0 + c) * (unsigned)p.NT + (unsigned)s) * NF + f) * 64u + (unsigned)lane) * 16u
+            : 0x7FFFFFF0u;
+        v[c][f] = __builtin_amdgcn_raw_buffer_load_b128(pres, (int)off, 0, AUX);
+      }
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const floatx4 x = __builtin_bit_cast(floatx4, v[c][f]);
+        if (c0 + c < p.KS) res[f] += x;
+      }
+  }
+}
+
+// Split-K without a finalize kernel.  The partial strips of such an
+// instance are written at device scope (through to the level every XCD
+// reads).  After its strip loop each wave waits for its own stores to
+// complete, so they are visible to every workgroup; then the workgroup
+// counts itself in on each of its strips' arrival counters (agent-scope
+// atomics).  The workgroup that brings a strip's count to KS read every
+// other count after that strip's partials were complete: it sums them in
+// chunk order with device-scope loads (as k_gemm_finalize does), runs the
+// epilogue FIN and returns the counter to zero for the next launch.  This
+// runs after the strip loop because nothing is in flight there: a counter
+// update inside the loop would make the wave wait for its whole ring of
+// weight tiles (the atomic's result is counted behind them).  No cache
+// writeback or invalidation is needed (measured: the agent-scope fences
+// that would do them cost about 20 us per launch).  flag: LDS for
+// 64 * kGemmWaves words.
+template <typename T, int NF, int FIN>
+__device__ void finalize_last(const GemmParams &p, int base, int step, int ns, const float (&rs)[NF],
+                              unsigned *flag) {
+  constexpr int NTH = 64 * kGemmWaves;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int i0 = 0; i0 < ns; i0 += NTH) {
+    const int nb = min(NTH, ns - i0);
+    if (tid < nb) {
+      const int s = base + (i0 + tid) * step;
+      const unsigned old = __hip_atomic_fetch_add(p.cnt + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      flag[tid] = old == (unsigned)(p.KS - 1) ? 1u : 0u;
+    }
+    __syncthreads();
+    for (int j = w; j < nb; j += kGemmWaves) {
+      if (flag[j]) {
+        const int s = base + (i0 + j) * step;
+        floatx4 res[NF];
+        if (p.KS <= 2) sum_chunks<NF, 2, kDeviceScope>(p, s, lane, res);
+        else if (p.KS <= 4) sum_chunks<NF, 4, kDeviceScope>(p, s, lane, res);
+        else sum_chunks<NF, 8, kDeviceScope>(p, s, lane, res);
+        unsigned long long unused[NF];
+        finish_strip<T, NF, FIN>(p, s, lane, res, rs, unused);
+        if (lane == 0) __hip_atomic_store(p.cnt + s, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();  // flags are rewritten by the next batch
+  }
+}
+
+// The LM head's argmax without a second kernel.  Each workgroup folds its
+// best key per row into keys[row] with a 64-bit atomic maximum, waits for
+// them to complete and counts itself in; the launch's last workgroup reads
+// the M keys (agent-scope atomic loads), writes the token ids and returns
+// keys and counter to zero for the next launch.
+template <int NF>
+__device__ void argmax_last(const GemmParams &p, const unsigned long long (&best)[NF],
+                            unsigned long long *sh, int nw) {
+  __shared__ unsigned last;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if ((lane >> 4) == 0) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) sh[w * 64 + 16 * f + (lane & 15)] = best[f];
+    for (int f = NF; f < 4; ++f) sh[w * 64 + 16 * f + (lane & 15)] = 0ull;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    unsigned long long b = 0ull;
+    for (int q = 0; q < nw; ++q) b = umax64(b, sh[q * 64 + tid]);
+    // Every real key is nonzero (its low word is 0xFFFFFFFF - index).
+    if (tid < p.M && b) __hip_atomic_fetch_max(p.keys + tid, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  if (tid == 0) {
+    const unsigned total = gridDim.x * gridDim.y;
+    const unsigned old = __hip_atomic_fetch_add(p.cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = old == total - 1 ? 1u : 0u;
+  }
+  __syncthreads();
+  if (last && tid < 64) {
+    if (tid < p.M) {
+      const unsigned long long k = __hip_atomic_load(p.keys + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      p.draft_out[tid] = (int)(0xFFFFFFFFu - (unsigned)(k & 0xFFFFFFFFull));
+      __hip_atomic_store(p.keys + tid, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0) __hip_atomic_store(p.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <typename T, int NF, int MAXKW, int EK, int FIN>
 __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
   constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE, D = Ring<MAXKW>::D;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -269,7 +391,17 @@ __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
         }
         __syncthreads();
         if (reducer) {
-          if constexpr (EK == EPI_PARTIAL) {
+          if constexpr (EK == EPI_PARTIAL && FIN != EPI_PARTIAL) {
+            // Read by another workgroup in this launch: device scope.
+            const __amdgpu_buffer_rsrc_t pres = __builtin_amdgcn_make_buffer_rsrc(
+                p.part, 0, (int)((unsigned)p.KS * (unsigned)p.NT * (unsigned)NF * 1024u), 0x00020000);
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  __builtin_bit_cast(u32x4, res[f]), pres,
+                  (int)(((((unsigned)chunk * (unsigned)p.NT + (unsigned)s) * NF + f) * 64u + (unsigned)lane) * 16u),
+                  0, kDeviceScope);
+          } else if constexpr (EK == EPI_PARTIAL) {
 #pragma unroll
             for (int f = 0; f < NF; ++f)
               p.part[(((long)chunk * p.NT + s) * NF + f) * 64 + lane] = res[f];
@@ -290,50 +422,24 @@ __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
       }
     }
   }
-  if constexpr (EK == EPI_ARGMAX)
-    block_argmax_out<NF>(p, best, reinterpret_cast<unsigned long long *>(red), W);
+  if constexpr (EK == EPI_PARTIAL && FIN != EPI_PARTIAL)
+    finalize_last<T, NF, FIN>(p, base, step, ns, rs, reinterpret_cast<unsigned *>(red));
+  if constexpr (EK == EPI_ARGMAX) {
+    if (p.keys) argmax_last<NF>(p, best, reinterpret_cast<unsigned long long *>(red), W);
+    else block_argmax_out<NF>(p, best, reinterpret_cast<unsigned long long *>(red), W);
+  }
 }
 
-template <typename T, int NF, int MAXKW, int EK>
+template <typename T, int NF, int MAXKW, int EK, int FIN>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_wg(GemmParams p) {
-  gemm_wg_body<T, NF, MAXKW, EK>(p);
+  gemm_wg_body<T, NF, MAXKW, EK, FIN>(p);
 }
 
 // The LM head: the same weight-streaming body with the fused argmax (its
 // own symbol, so profiles report it apart from the layer projections).
 template <typename T, int NF, int MAXKW, int EK>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_lm_head_argmax(GemmParams p) {
-  gemm_wg_body<T, NF, MAXKW, EK>(p);
-}
-
-// Sum of strip s's KS chunk partials in chunk order, CB chunks in flight at
-// a time.  Chunks past KS read zero through the buffer resource without a
-// memory access and are not added.
-template <int NF, int CB>
-__device__ __forceinline__ void sum_chunks(const GemmParams &p, int s, int lane, floatx4 (&res)[NF]) {
-  const __amdgpu_buffer_rsrc_t pres = __builtin_amdgcn_make_buffer_rsrc(
-      p.part, 0, (int)((unsigned)p.KS * (unsigned)p.NT * (unsigned)NF * 1024u), 0x00020000);
-#pragma unroll
-  for (int f = 0; f < NF; ++f) res[f] = floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < p.KS; c0 += CB) {
-    u32x4 v[CB][NF];
-#pragma unroll
-    for (int c = 0; c < CB; ++c)
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const unsigned off = c0 + c < p.KS
-            ? ((((unsigned)(c0 + c) * (unsigned)p.NT + (unsigned)s) * NF + f) * 64u + (unsigned)lane) * 16u
-            : 0x7FFFFFF0u;
-        v[c][f] = __builtin_amdgcn_raw_buffer_load_b128(pres, (int)off, 0, 0);
-      }
-#pragma unroll
-    for (int c = 0; c < CB; ++c)
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const floatx4 x = __builtin_bit_cast(floatx4, v[c][f]);
-        if (c0 + c < p.KS) res[f] += x;
-      }
-  }
+  gemm_wg_body<T, NF, MAXKW, EK, EPI_PARTIAL>(p);
 }
 
 // KS > 1: one wave per strip sums the chunk partials in chunk order and runs
@@ -410,23 +516,30 @@ __global__ __launch_bounds__(1024) void k_argmax_final(const unsigned long long 
   }
 }
 
-template <typename T, int NF, int MAXKW, int EK>
+// FIN: the epilogue a split-K (EK == EPI_PARTIAL) instance runs itself on
+// each strip's last arrival, or EPI_PARTIAL when k_gemm_finalize runs it.
+template <typename T, int NF, int MAXKW, int EK, int FIN = EPI_PARTIAL>
 hipError_t launch_one(const GemmParams &p, const GemmLaunch &L, hipStream_t s) {
   const dim3 grid(L.grid, p.KS), block(L.waves * 64);
-  if constexpr (EK == EPI_ARGMAX || EK == EPI_PARTIAL) {
+  if constexpr (EK == EPI_ARGMAX || (EK == EPI_PARTIAL && FIN == EPI_PARTIAL)) {
     if (p.epi == EPI_ARGMAX) {
       hipLaunchKernelGGL((k_lm_head_argmax<T, NF, MAXKW, EK>), grid, block, L.lds, s, p);
       return hipGetLastError();
     }
   }
-  if constexpr (EK != EPI_ARGMAX) hipLaunchKernelGGL((k_gemm_wg<T, NF, MAXKW, EK>), grid, block, L.lds, s, p);
+  if constexpr (EK != EPI_ARGMAX)
+    hipLaunchKernelGGL((k_gemm_wg<T, NF, MAXKW, EK, FIN>), grid, block, L.lds, s, p);
   return hipGetLastError();
 }
 
 template <typename T, int NF, int MAXKW>
 hipError_t launch_main(const GemmParams &p, const GemmLaunch &L, hipStream_t s) {
   if (L.waves != kGemmWaves) return hipErrorInvalidValue;
-  if (p.KS > 1) return launch_one<T, NF, MAXKW, EPI_PARTIAL>(p, L, s);
+  if (p.KS > 1) {
+    if (p.cnt && p.epi == EPI_FC) return launch_one<T, NF, MAXKW, EPI_PARTIAL, EPI_FC>(p, L, s);
+    if (p.cnt && p.epi == EPI_RESID) return launch_one<T, NF, MAXKW, EPI_PARTIAL, EPI_RESID>(p, L, s);
+    return launch_one<T, NF, MAXKW, EPI_PARTIAL>(p, L, s);
+  }
   switch (p.epi) {
     case EPI_FC: return launch_one<T, NF, MAXKW, EPI_FC>(p, L, s);
     case EPI_QKV: return launch_one<T, NF, MAXKW, EPI_QKV>(p, L, s);
@@ -478,7 +591,8 @@ hipError_t launch_t(int nf, const GemmParams &p, const GemmLaunch &L, hipStream_
     case 3: e = launch_kw<T, 3>(p, L, s); break;
     case 4: e = launch_kw<T, 4>(p, L, s); break;
   }
-  if (e != hipSuccess || p.KS == 1) return e;
+  // Split-K instances with arrival counters finish their strips themselves.
+  if (e != hipSuccess || p.KS == 1 || p.cnt) return e;
   switch (nf) {
     case 1: return launch_finalize<T, 1>(p, s);
     case 2: return launch_finalize<T, 2>(p, s);

@@ -85,6 +85,12 @@ struct GemmParams {
   float *logits;                  // [M][V] or null
   unsigned long long *blk_best;   // [workgroups][kMaxRows] best key per row
   int V;
+  // In-kernel completion (zero between launches): per-strip arrival
+  // counters of a split-K GEMM that finishes its own strips, or counter 0 of
+  // an LM head that writes the tokens itself from keys[kMaxRows].
+  unsigned *cnt;
+  unsigned long long *keys;
+  int *draft_out;
 };
 
 struct GemmLaunch {

@@ -116,8 +116,10 @@ pe_status pe_draft_shape_check(const pe_config *cfg, int32_t B, int32_t K, int64
                                int32_t num_cus);
 
 /* Zero a workspace (device, ws_bytes) on the stream with a fill kernel (no
- * memset node, so it may sit in a captured graph).  Every kernel writes what
- * it later reads, so this only makes a fresh workspace's contents defined. */
+ * memset node, so it may sit in a captured graph).  Required once before a
+ * workspace's first use: it holds arrival counters and argmax keys that must
+ * start at zero, and every completed call leaves them at zero again.  After
+ * a call that failed on the device, initialise the workspace again. */
 pe_status pe_workspace_init(void *workspace, size_t ws_bytes, void *stream);
 
 /*
