@@ -15,7 +15,9 @@
 //
 // Two kernels stage the tiles:
 //   k_attn_decode (fp32, and bf16 at head_dim 64): tiles stream through a
-//   ring of registers into LDS, values transposed on the store.
+//   ring of registers into LDS.  bf16 keeps keys and values row-major with
+//   permuted chunks (as below) and reads the values transposed; fp32
+//   transposes the values on the store.
 //   k_attn_decode_lds (bf16, head_dim 128): the query rows, key tiles and
 //   value tiles go from HBM straight into a ring of LDS stages (buffer loads
 //   with the LDS bit: no registers, no transposing stores).  Keys and values
@@ -60,16 +62,10 @@ struct AttnShape {
 
 __device__ __forceinline__ u32x4 lds16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
-// V-tile swizzle (pe_device.hpp): bits 3..5 for bf16 head_dim 64, bits 2..5
-// otherwise (fewer store conflicts at head_dim 128 in a CPU bank model).
+// fp32 V-tile swizzle (pe_device.hpp): the transposing stores' key column
+// XORed with bits 2..5 of the row's chunk.
 template <typename T, int HD>
-__device__ __forceinline__ int vt_sw(int cc) {
-  if constexpr (sizeof(T) == 2 && HD == 64) return vt_swizzle_b3(cc);
-  else return vt_swizzle_b2(cc);
-}
-
-
-__device__ __forceinline__ uint2 lds8(const void *p) { return *reinterpret_cast<const uint2 *>(p); }
+__device__ __forceinline__ int vt_sw(int cc) { return vt_swizzle_b2(cc); }
 
 template <typename T>
 __device__ __forceinline__ void store_out4(T *dst, const float v[4]);
@@ -85,14 +81,42 @@ __device__ __forceinline__ void store_out4<bf16_t>(bf16_t *dst, const float v[4]
   *reinterpret_cast<uint2 *>(dst) = w;
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// 8 bytes per lane read transposed across each 16-lane group (see the file
+// comment), from LDS byte address a.
+__device__ __forceinline__ uint2 lds_tr8(unsigned a) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(size_t)a);
+  return __builtin_bit_cast(uint2, v);
+}
+
+__device__ __forceinline__ u32x4 lds_b128(unsigned a) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((size_t)a);
+}
+
+// Chunk permutation of key row k (depends on k % 16 only): XOR of the
+// row's chunk index; conflict-free K-operand reads (16 keys, one chunk) and
+// transposed V reads (8 keys x 2 chunks per 32 lanes) in a 64-bank model.
+template <int HD>
+__device__ __forceinline__ int kv_sw(int k) {
+  if constexpr (HD == 64) return (2 * ((k >> 1) & 3)) ^ ((k >> 3) & 1);
+  else return (2 * (k & 7)) ^ ((k >> 3) & 1);
+}
+
 template <typename T, int HD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(AttnShape<T, HD>::WAVES_PER_EU)))
 void k_attn_decode(AttnParams p) {
   using S = AttnShape<T, HD>;
   constexpr int E = S::E, KTILE = S::KTILE, NC = S::NC, ND = S::ND, KS = S::KS, VS = S::VS;
   constexpr int CPR = S::CPR, MAXC = S::MAXC;
-  __shared__ __attribute__((aligned(16))) T Ks[64 * KS];
-  __shared__ __attribute__((aligned(16))) T Vt[HD * VS];
+  // bf16: key and value rows row-major in LDS with each row's 16-byte
+  // chunks permuted by kv_sw (one 16-byte store per chunk, conflict-free
+  // operand reads), values read transposed by ds_read_b64_tr_b16.  fp32:
+  // padded key rows; values transposed on the store (Vt[d][key]).
+  constexpr bool TR = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) T Ks[TR ? 64 * HD : 64 * KS];
+  __shared__ __attribute__((aligned(16))) T Vt[TR ? 64 * HD : HD * VS];
 
   // blockIdx.y = kv head * QP + query partition (64 query rows each).
   const int QP = (p.RP + 63) / 64;
@@ -160,6 +184,12 @@ void k_attn_decode(AttnParams p) {
     for (int i = 0; i < MAXC; ++i) {
       const int id = tid + i * S::NTHR;
       const int key = id / CPR, cc = id - key * CPR;
+      if constexpr (TR) {
+        const int o = key * HD * 2 + (cc ^ kv_sw<HD>(key)) * 16;
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(Ks) + o) = kr[i];
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(Vt) + o) = vr[i];
+        continue;
+      }
       *reinterpret_cast<u32x4 *>(&Ks[key * KS + cc * E]) = kr[i];
       T vals[E];
       __builtin_memcpy(vals, &vr[i], 16);
@@ -174,6 +204,23 @@ void k_attn_decode(AttnParams p) {
   for (int d = 0; d < ND; ++d) oacc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_lane = 0.f;
 
+  // bf16 operand reads (LDS byte addresses):
+  //   K (S^T): key kb*16 + c16, chunk c*4 + g;
+  //   V (O^T, transposed read): key 32 c2 + 16 h + 4 g + c16/4, chunk
+  //   2 d + (c16 % 4) / 2, half (c16 % 4) % 2.
+  const unsigned kl = (unsigned)(size_t)(__attribute__((address_space(3))) T *)Ks;
+  const unsigned vl = (unsigned)(size_t)(__attribute__((address_space(3))) T *)Vt;
+  unsigned koff[NC], voff[ND];
+  if constexpr (TR) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) koff[c] = kl + (unsigned)((c16 * CPR + ((c * 4 + g) ^ kv_sw<HD>(c16))) * 16);
+    const int vkey = 4 * g + (c16 >> 2);
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+      voff[d] = vl + (unsigned)((vkey * CPR + ((2 * d + ((c16 & 3) >> 1)) ^ kv_sw<HD>(vkey))) * 16 +
+                                (c16 & 1) * 8);
+  }
+
   // One staged tile: S^T = K Q^T over its 64 keys, fp32 online softmax, O^T
   // += V^T P^T.  Key kb*16 + 4g + r of the tile is visible when kbase +
   // kb*16 + 4g + r < lim (a select per score, applied when masked).
@@ -184,7 +231,9 @@ void k_attn_decode(AttnParams p) {
       sacc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const u32x4 a = lds16(&Ks[(kb * 16 + c16) * KS + c * KTILE + g * E]);
+        u32x4 a;
+        if constexpr (TR) a = lds_b128(koff[c] + (unsigned)(kb * 16 * CPR * 16));
+        else a = lds16(&Ks[(kb * 16 + c16) * KS + c * KTILE + g * E]);
         sacc[kb] = Mma<T>::run(a, qf[c], sacc[kb]);
       }
     }
@@ -229,22 +278,8 @@ void k_attn_decode(AttnParams p) {
                           pack_bf16x2(pv[2 * c2 + 1][2], pv[2 * c2 + 1][3])};
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          const int vd = d * 16 + c16;
-          const T *vrow = &Vt[vd * VS];
-          int clo, chi;  // swizzled columns of keys 32 c2 + 4g and 32 c2 + 16 + 4g
-          if constexpr (HD == 64) {
-            // row chunk = 2d + c16/8 <= 7: the lane's bits (2..3) and the
-            // unrolled loop's bits (4..5) do not mix, so the offsets fold
-            // into immediates.
-            const int lanebits = (4 * g) ^ (8 * (c16 >> 3));
-            clo = lanebits | ((32 * c2) ^ (16 * d));
-            chi = lanebits | ((32 * c2 + 16) ^ (16 * d));
-          } else {
-            const int sw = vt_sw<T, HD>(vd / E);
-            clo = (32 * c2 + 4 * g) ^ sw;
-            chi = (32 * c2 + 16 + 4 * g) ^ sw;
-          }
-          const uint2 lo = lds8(vrow + clo), hi = lds8(vrow + chi);
+          const unsigned a0 = voff[d] + (unsigned)(32 * c2 * CPR * 16);
+          const uint2 lo = lds_tr8(a0), hi = lds_tr8(a0 + (unsigned)(16 * CPR * 16));
           const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
           oacc[d] = Mma<T>::run(a, bf, oacc[d]);
         }
@@ -390,20 +425,6 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// 8 bytes per lane read transposed across each 16-lane group (see the file
-// comment), from LDS byte address a.
-__device__ __forceinline__ uint2 lds_tr8(unsigned a) {
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(size_t)a);
-  return __builtin_bit_cast(uint2, v);
-}
-
-__device__ __forceinline__ u32x4 lds_b128(unsigned a) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((size_t)a);
-}
-
 template <int HD>
 struct DmaAttn {
   static constexpr int CPR = HD / 8;              // 16-byte chunks per key row
@@ -419,15 +440,6 @@ struct DmaAttn {
   static constexpr int NB = 2;
   static constexpr int LDS = NB * 2 * TILE;
 };
-
-// Chunk permutation of key row k (depends on k % 16 only): XOR of the
-// row's chunk index; conflict-free K-operand reads (16 keys, one chunk) and
-// transposed V reads (8 keys x 2 chunks per 32 lanes) in a 64-bank model.
-template <int HD>
-__device__ __forceinline__ int kv_sw(int k) {
-  if constexpr (HD == 64) return (2 * ((k >> 1) & 3)) ^ ((k >> 3) & 1);
-  else return (2 * (k & 7)) ^ ((k >> 3) & 1);
-}
 
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_decode_lds(AttnParams p) {
