@@ -81,29 +81,6 @@ __device__ __forceinline__ void store_out4<bf16_t>(bf16_t *dst, const float v[4]
   *reinterpret_cast<uint2 *>(dst) = w;
 }
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// 8 bytes per lane read transposed across each 16-lane group (see the file
-// comment), from LDS byte address a.
-__device__ __forceinline__ uint2 lds_tr8(unsigned a) {
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(size_t)a);
-  return __builtin_bit_cast(uint2, v);
-}
-
-__device__ __forceinline__ u32x4 lds_b128(unsigned a) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((size_t)a);
-}
-
-// Chunk permutation of key row k (depends on k % 16 only): XOR of the
-// row's chunk index; conflict-free K-operand reads (16 keys, one chunk) and
-// transposed V reads (8 keys x 2 chunks per 32 lanes) in a 64-bank model.
-template <int HD>
-__device__ __forceinline__ int kv_sw(int k) {
-  if constexpr (HD == 64) return (2 * ((k >> 1) & 3)) ^ ((k >> 3) & 1);
-  else return (2 * (k & 7)) ^ ((k >> 3) & 1);
-}
-
 template <typename T, int HD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(AttnShape<T, HD>::WAVES_PER_EU)))
 void k_attn_decode(AttnParams p) {

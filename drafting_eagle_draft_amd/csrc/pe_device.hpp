@@ -85,16 +85,11 @@ __device__ __forceinline__ long frag_off(int m, int k, int KT) {
   return ((long)((m >> 4) * KT + k / KTILE) * 64 + ((k % KTILE) / E) * 16 + (m & 15)) * E + (k % E);
 }
 
-// Key-column swizzles of an attention V tile staged transposed in LDS,
+// Key-column swizzle of an fp32 attention V tile staged transposed in LDS,
 // Vt[d][key] (64 keys), for the row's 16-byte chunk cc = d / E: key bits
-// 3..5 flip by cc & 7 (vt_swizzle_b3) or bits 2..5 by cc & 15
-// (vt_swizzle_b2).  A wave's 2-byte transposing stores then spread over
-// the banks (without a swizzle they hit two bank offsets), and each 4-key
-// group read by the matrix cores stays contiguous (bits 0..1 are kept).
-// For bf16 with 8 elements per chunk, b3 leaves a read column as per-lane
-// bits (2..3) OR'ed with bits that depend only on the unrolled d and key
-// offset (4..5), so the offsets fold into immediates.
-__device__ __forceinline__ int vt_swizzle_b3(int cc) { return (cc & 7) << 3; }
+// 2..5 flip by cc & 15.  A wave's transposing stores then spread over the
+// banks (without a swizzle they hit two bank offsets), and each 4-key group
+// read by the matrix cores stays contiguous (bits 0..1 are kept).
 __device__ __forceinline__ int vt_swizzle_b2(int cc) { return (cc & 15) << 2; }
 
 // Workgroup barrier that waits for this wave's LDS operations only, so
@@ -141,6 +136,32 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   lo = __shfl_xor(lo, mask, 64);
   hi = __shfl_xor(hi, mask, 64);
   return ((unsigned long long)hi << 32) | lo;
+}
+
+// Row-major LDS tiles of bf16 keys/values with permuted chunks and their
+// transposed reads (decode and training attention).
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// ds_read_b64_tr_b16 from LDS byte address a: within each 16-lane group,
+// result element j of lane i is element i % 4 of the 8 bytes addressed by
+// lane 4j + i / 4.
+__device__ __forceinline__ uint2 lds_tr8(unsigned a) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(size_t)a);
+  return __builtin_bit_cast(uint2, v);
+}
+
+__device__ __forceinline__ u32x4 lds_b128(unsigned a) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((size_t)a);
+}
+
+// Chunk permutation of key row k (depends on k % 16 only): XOR of the
+// row's chunk index; conflict-free K-operand reads (16 keys, one chunk) and
+// transposed V reads (8 keys x 2 chunks per 32 lanes) in a 64-bank model.
+template <int HD>
+__device__ __forceinline__ int kv_sw(int k) {
+  if constexpr (HD == 64) return (2 * ((k >> 1) & 3)) ^ ((k >> 3) & 1);
+  else return (2 * (k & 7)) ^ ((k >> 3) & 1);
 }
 
 }  // namespace pe

@@ -203,15 +203,18 @@ template <> __device__ __forceinline__ void store_vals4<bf16_t>(bf16_t *dst, con
 }
 
 __device__ __forceinline__ u32x4 lds16t(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
-__device__ __forceinline__ uint2 lds8t(const void *p) { return *reinterpret_cast<const uint2 *>(p); }
 
 template <typename T, int HD, int NW, int QB>
 __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
   constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE, NC = HD / KTILE, ND = HD / 16;
   constexpr int NT = 64 * NW;  // threads
   constexpr int KS = HD + E, VS = 64 + 4, CPR = HD / E, MAXC = (64 * CPR + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) T Ks[64 * KS];
-  __shared__ __attribute__((aligned(16))) T Vt[HD * VS];
+  // bf16: key and value rows row-major with permuted 16-byte chunks
+  // (kv_sw), values read transposed; fp32: padded key rows, values
+  // transposed on the store (Vt[d][key]).
+  constexpr bool TR = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) T Ks[TR ? 64 * HD : 64 * KS];
+  __shared__ __attribute__((aligned(16))) T Vt[TR ? 64 * HD : HD * VS];
   __shared__ int s_amax[NW];
   const int G = p.G, QT = 16 * QB * NW / G;
   const int gk = blockIdx.y;
@@ -268,8 +271,24 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
     l_lane[qb] = 0.f;
   }
 
+  // bf16 operand reads (LDS byte addresses): K key kb*16 + c16, chunk
+  // c*4 + g; V (transposed read) key 32 c2 + 16 h + 4 g + c16/4, chunk
+  // 2 d + (c16 % 4) / 2, half (c16 % 4) % 2.
+  unsigned koff[NC], voff[ND];
+  if constexpr (TR) {
+    const unsigned kl = (unsigned)(size_t)(__attribute__((address_space(3))) T *)Ks;
+    const unsigned vl = (unsigned)(size_t)(__attribute__((address_space(3))) T *)Vt;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) koff[c] = kl + (unsigned)((c16 * CPR + ((c * 4 + g) ^ kv_sw<HD>(c16))) * 16);
+    const int vkey = 4 * g + (c16 >> 2);
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+      voff[d] = vl + (unsigned)((vkey * CPR + ((2 * d + ((c16 & 3) >> 1)) ^ kv_sw<HD>(vkey))) * 16 +
+                                (c16 & 1) * 8);
+  }
+
   // Key/value tiles are loaded PF tiles ahead into a register ring; tile t
-  // goes through LDS (K row-major, V transposed) to the matrix cores.
+  // goes through LDS to the matrix cores.
   constexpr int PF = 3;
   u32x4 kreg[PF][MAXC], vreg[PF][MAXC];
   auto gload = [&](int jt, u32x4 (&kr)[MAXC], u32x4 (&vr)[MAXC]) {
@@ -296,11 +315,17 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
         const int id = tid + i * NT;
         if (id >= 64 * CPR) break;
         const int key = id / CPR, cc = id - key * CPR;
+        if constexpr (TR) {
+          const int o = key * HD * 2 + (cc ^ kv_sw<HD>(key)) * 16;
+          *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(Ks) + o) = kreg[u][i];
+          *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(Vt) + o) = vreg[u][i];
+          continue;
+        }
         *reinterpret_cast<u32x4 *>(&Ks[key * KS + cc * E]) = kreg[u][i];
         T vals[E];
         __builtin_memcpy(vals, &vreg[u][i], 16);
-        // bank-spread transposed V (pe_device.hpp): bits 3..5 for bf16, 2..5 for fp32
-        const int kcol = key ^ (sizeof(T) == 2 ? vt_swizzle_b3(cc) : vt_swizzle_b2(cc));
+        // bank-spread transposed V (pe_device.hpp)
+        const int kcol = key ^ vt_swizzle_b2(cc);
 #pragma unroll
         for (int e = 0; e < E; ++e) Vt[(cc * E + e) * VS + kcol] = vals[e];
       }
@@ -317,7 +342,9 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
-            const u32x4 kf = lds16t(&Ks[(kb * 16 + c16) * KS + c * KTILE + g * E]);
+            u32x4 kf;
+            if constexpr (TR) kf = lds_b128(koff[c] + (unsigned)(kb * 16 * CPR * 16));
+            else kf = lds16t(&Ks[(kb * 16 + c16) * KS + c * KTILE + g * E]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = Mma<T>::run(kf, qf[qb][c], sacc[qb][kb]);
           }
@@ -381,14 +408,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
           for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
             for (int d = 0; d < ND; ++d) {
-              const int vd = d * 16 + c16;
-              const T *vrow = &Vt[vd * VS];
-              // Swizzled columns of keys 32 c2 + 4g and 32 c2 + 16 + 4g (row
-              // chunk 2d + c16/8): lane bits 2..3, loop-constant bits 4..5.
-              const int lanebits = (4 * g) ^ (8 * (c16 >> 3));
-              const int clo = lanebits | ((32 * c2) ^ ((16 * d) & 48));
-              const int chi = lanebits | ((32 * c2 + 16) ^ ((16 * d) & 48));
-              const uint2 lo = lds8t(vrow + clo), hi = lds8t(vrow + chi);
+              const unsigned a0 = voff[d] + (unsigned)(32 * c2 * CPR * 16);
+              const uint2 lo = lds_tr8(a0), hi = lds_tr8(a0 + (unsigned)(16 * CPR * 16));
               const u32x4 vf = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
               for (int qb = 0; qb < QB; ++qb) oacc[qb][d] = Mma<T>::run(vf, pbf[qb][c2], oacc[qb][d]);
