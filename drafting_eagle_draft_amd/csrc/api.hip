@@ -133,31 +133,52 @@ struct GemmPlan {
 
 constexpr int kMaxSplits = 64;
 
-GemmPlan plan_gemm(int cus, int NT, int KT, int Mv, int nf) {
+// Modelled cost of a K split in tile-times per CU: the in-kernel
+// completion's tail (fc, QKV and residual epilogues), a finalize kernel
+// (other epilogues), or, for the LM head, a cost that keeps it whole unless
+// nothing else fits (its argmax is folded only when it is not split).
+constexpr int kSplitCostInKernel = 90;
+constexpr int kSplitCostKernel = 100;
+constexpr int kSplitCostLmHead = 1000;
+
+bool finishes_in_kernel(int epi) { return epi == EPI_FC || epi == EPI_RESID || epi == EPI_QKV; }
+
+GemmPlan plan_gemm(int cus, int NT, int KT, int Mv, int nf, int epi) {
   GemmPlan g{};
   g.Mv = Mv;
   g.nf = nf;
   const int W = kGemmWaves;
   const int max_slots = nf == 1 ? 18 : nf == 2 ? 8 : nf == 3 ? 4 : 2;  // as the kernel's buckets
-  // One workgroup per CU (8 waves at up to 256 VGPRs).  Each K split adds
-  // a finalize kernel, priced like ~100 extra tiles per CU; choose the split
-  // with the smallest modelled makespan (strip rounds x tiles per chunk).
-  // Splits beyond 16 are only searched when no split up to 16 fits (their
-  // short chunks leave few tile slots per wave).
+  // One workgroup per CU (8 waves at up to 256 VGPRs).  The modelled
+  // makespan of a plan is what the busiest workgroup streams: its strip
+  // rounds x tiles per chunk, plus the activation slice it loads before its
+  // first strip (nf x tiles per chunk: every workgroup loads its own, and
+  // these bytes set the ramp of the short projections), plus the split's
+  // cost.  Splits that leave a wave fewer than 4 tile slots keep too few
+  // loads in flight; they are only planned when nothing else fits, and
+  // splits beyond 16 only when no split up to 16 fits.  Fitted to A/B runs
+  // on the MI355X: QKV split 3 ways at 16 rows and 2 ways at 32 rows, O 4
+  // ways at 32 rows, down unchanged.
+  const int split_cost = epi == EPI_ARGMAX ? kSplitCostLmHead
+                         : finishes_in_kernel(epi) ? kSplitCostInKernel : kSplitCostKernel;
+  const int floor_slots = max_slots < 4 ? max_slots : 4;
   long best = -1;
-  for (int KS = 1; KS <= kMaxSplits && KS <= KT && (KS <= 16 || best < 0); ++KS) {
-    const int kc = (KT + KS - 1) / KS;
-    const int nkw = (kc + W - 1) / W;
-    if (nkw > max_slots) continue;
-    const int ks = (KT + kc - 1) / kc;  // no empty chunk
-    int G = cus / ks;
-    if (G < 1) G = 1;
-    if (G > NT) G = NT;
-    const long rounds = (NT + G - 1) / G;
-    const long cost = rounds * kc + (ks > 1 ? 100 : 0);
-    if (best < 0 || cost < best) {
-      best = cost;
-      g.KS = ks; g.kc = kc; g.nkw = nkw; g.L.grid = G;
+  for (int pass = 0; pass < 2 && best < 0; ++pass) {
+    for (int KS = 1; KS <= kMaxSplits && KS <= KT && (KS <= 16 || best < 0); ++KS) {
+      const int kc = (KT + KS - 1) / KS;
+      const int nkw = (kc + W - 1) / W;
+      if (nkw > max_slots) continue;
+      const int ks = (KT + kc - 1) / kc;  // no empty chunk
+      if (pass == 0 && ks > 1 && nkw < floor_slots) continue;
+      int G = cus / ks;
+      if (G < 1) G = 1;
+      if (G > NT) G = NT;
+      const long rounds = (NT + G - 1) / G;
+      const long cost = rounds * kc + (long)nf * kc + (ks > 1 ? split_cost : 0);
+      if (best < 0 || cost < best) {
+        best = cost;
+        g.KS = ks; g.kc = kc; g.nkw = nkw; g.L.grid = G;
+      }
     }
   }
   g.L.waves = W;
@@ -227,8 +248,9 @@ WsLayout layout(const DecodeShape &m, int B, int K, long C) {
   w.RP = (R + 15) / 16 * 16;
   w.ap = plan_attn(m, B, K, C);
   size_t part = 0, blk = 0;
-  auto upd = [&](const TileDims &t, int Mv, int nfr, bool lm) {
-    const GemmPlan g = plan_gemm(m.cus, t.NT, t.KT, Mv, nfr);
+  auto upd = [&](const TileDims &t, int Mv, int nfr, int epi) {
+    const bool lm = epi == EPI_ARGMAX;
+    const GemmPlan g = plan_gemm(m.cus, t.NT, t.KT, Mv, nfr, epi);
     if (g.KS == 0) {
       w.unsupported = "a projection's contraction is too long for the activation rows held in registers";
       return;
@@ -239,12 +261,13 @@ WsLayout layout(const DecodeShape &m, int B, int K, long C) {
       blk = std::max(blk, nb * kMaxRows * 8);
     }
   };
-  upd(m.fc, B + 1, nf_fc, false);
-  upd(m.fc, M, nf, false);  // cache extension: one fc row per block row
+  upd(m.fc, B + 1, nf_fc, EPI_FC);
+  upd(m.fc, M, nf, EPI_FC);  // cache extension: one fc row per block row
   if (c.n_layers > 0) {
-    upd(m.qkv, M, nf, false); upd(m.o, M, nf, false); upd(m.gateup, M, nf, false); upd(m.down, M, nf, false);
+    upd(m.qkv, M, nf, EPI_QKV); upd(m.o, M, nf, EPI_RESID); upd(m.gateup, M, nf, EPI_SWIGLU);
+    upd(m.down, M, nf, EPI_RESID);
   }
-  upd(m.lm, M, nf, true);
+  upd(m.lm, M, nf, EPI_ARGMAX);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
   const size_t H = c.hidden, esz = m.esz;
@@ -432,14 +455,14 @@ pe_status enqueue_draft(const pe_model *m, const WsLayout &W, const DraftCall &d
   bool tokens_written = false;  // the LM head wrote draft_out itself
   auto run = [&](const Tiled &t, int epi, int nfr, GemmParams p) -> pe_status {
     const int Mv = p.act_rows + (p.act_extra ? 1 : 0);
-    const GemmPlan pl = plan_gemm(m->num_cus, t.NT, t.KT, Mv, nfr);
+    const GemmPlan pl = plan_gemm(m->num_cus, t.NT, t.KT, Mv, nfr, epi);
     p.wt = t.ptr; p.wbytes = (unsigned)((size_t)t.NT * t.KT * 1024); p.NT = t.NT; p.KT = t.KT;
     p.N = t.N; p.K = t.K;
     p.epi = epi; p.KS = pl.KS; p.kc = pl.kc; p.nkw = pl.nkw; p.Mv = Mv;
     lm_blocks = pl.KS > 1 ? (t.NT + 3) / 4 : pl.L.grid;
     // Split FC and residual projections finish their strips in-kernel; an
     // unsplit LM head writes the tokens itself.
-    if (pl.KS > 1 && (epi == EPI_FC || epi == EPI_RESID)) p.cnt = cnt;
+    if (pl.KS > 1 && finishes_in_kernel(epi)) p.cnt = cnt;
     if (epi == EPI_ARGMAX && pl.KS == 1 && d.draft_out) {
       p.cnt = cnt;
       p.keys = reinterpret_cast<unsigned long long *>(ws + W.keys);

@@ -15,7 +15,7 @@
 //   * Partial 16x(16*NF) tiles are summed through LDS in wave order
 //     (deterministic) by one wave per strip, which runs the epilogue.
 //   * Long contractions are split over KS workgroup columns that write fp32
-//     partial strips.  With arrival counters (the FC and residual
+//     partial strips.  With arrival counters (the FC, QKV and residual
 //     epilogues) the workgroup that completes a strip last sums its
 //     partials in chunk order and runs the epilogue after its strip loop;
 //     otherwise k_gemm_finalize does.  The LM head folds its argmax the same
@@ -538,6 +538,7 @@ hipError_t launch_main(const GemmParams &p, const GemmLaunch &L, hipStream_t s) 
   if (p.KS > 1) {
     if (p.cnt && p.epi == EPI_FC) return launch_one<T, NF, MAXKW, EPI_PARTIAL, EPI_FC>(p, L, s);
     if (p.cnt && p.epi == EPI_RESID) return launch_one<T, NF, MAXKW, EPI_PARTIAL, EPI_RESID>(p, L, s);
+    if (p.cnt && p.epi == EPI_QKV) return launch_one<T, NF, MAXKW, EPI_PARTIAL, EPI_QKV>(p, L, s);
     return launch_one<T, NF, MAXKW, EPI_PARTIAL>(p, L, s);
   }
   switch (p.epi) {
