@@ -133,6 +133,19 @@ def test_extend_bf16_small(T, kind, off):
     _check_extend(cfg, w, inp, T, kind, off, seed=20 + T)
 
 
+@pytest.mark.parametrize("T,kind,off", [(8, 0, 0), (1, 1, 3)])
+def test_extend_bf16_split_projections(T, kind, off):
+    """One GPT-OSS-shaped layer (H 2880, 64q/8kv, hd 64) with I = 4096 and a
+    small vocabulary: the planner splits fc, QKV (3 ways), O and down (4
+    ways) over K, so every split projection finishes in-kernel, QKV writing
+    the appended cache rows from the strip's last workgroup."""
+    cfg = small_bf16("ext_split_bf16", seed=2301, hidden=2880, n_layers=1, n_q_heads=64, n_kv_heads=8,
+                     intermediate=4096, vocab=8192 + 48)
+    w = synth.drafter_weights(cfg, gain_jitter=0.1)
+    inp = synth.decode_inputs(cfg)
+    _check_extend(cfg, w, inp, T, kind, off, seed=40 + T)
+
+
 def _check_chain(cfg, w, inp, K):
     d = runner.Drafter(cfg, w)
     ch = runner.Eagle3Chain(d, inp, K, want_logits=True)
