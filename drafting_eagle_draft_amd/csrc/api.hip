@@ -133,6 +133,14 @@ struct GemmPlan {
 
 constexpr int kMaxSplits = 64;
 
+// Share of the LM head's strips handed out at run time instead of by XCD
+// range (per cent): the XCDs' streaming rates differ from call to call, so
+// their static ranges end up to 20-30 us apart.  Measured in alternating
+// runs: 6% takes the GPT-OSS-shaped forward from 490.4 to 485.5 us (16K
+// context 528.8 -> 524.5, Qwen3-Coder shape 407.6 -> 406.3); 8-10% gain the
+// same or less.
+constexpr int kLmPoolPercent = 6;
+
 // Modelled cost of a K split in tile-times per CU: the in-kernel
 // completion's tail (fc, QKV and residual epilogues), a finalize kernel
 // (other epilogues), or, for the LM head, a cost that keeps it whole unless
@@ -467,6 +475,9 @@ pe_status enqueue_draft(const pe_model *m, const WsLayout &W, const DraftCall &d
       p.cnt = cnt;
       p.keys = reinterpret_cast<unsigned long long *>(ws + W.keys);
       p.draft_out = d.draft_out;
+      // Only where workgroups stream many strips: with a few strips each the
+      // ranges barely drift apart, and the ticket round trip would be a cost.
+      p.pool = t.NT >= 8 * pl.L.grid ? t.NT * kLmPoolPercent / 100 : 0;
       tokens_written = true;
     }
     hipError_t e = launch_gemm(c.dtype, nfr, p, pl.L, s);

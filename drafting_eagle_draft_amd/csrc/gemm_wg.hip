@@ -256,7 +256,10 @@ __device__ void argmax_last(const GemmParams &p, const unsigned long long (&best
       p.draft_out[tid] = (int)(0xFFFFFFFFu - (unsigned)(k & 0xFFFFFFFFull));
       __hip_atomic_store(p.keys + tid, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (tid == 0) __hip_atomic_store(p.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      __hip_atomic_store(p.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (p.pool > 0) __hip_atomic_store(p.cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -289,9 +292,12 @@ __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
       const_cast<u32x4 *>(p.wt), 0, (int)p.wbytes, 0x00020000);
   const unsigned kOOB = 0x7FFFFFF0u;
   const int G = gridDim.x;
+  // Statically assigned strips [0, NTs); an LM head leaves the last p.pool
+  // strips to whichever workgroups finish first (after the strip loop).
+  const int NTs = p.NT - p.pool;
   // This workgroup's strips: base, base + step, ... (ns of them).
   int base = (int)blockIdx.x, step = G;
-  int ns = (p.NT - (int)blockIdx.x + G - 1) / G;
+  int ns = (NTs - (int)blockIdx.x + G - 1) / G;
   unsigned joff[MAXKW];  // byte offset of tile j within a strip (kOOB when empty)
 #pragma unroll
   for (int j = 0; j < MAXKW; ++j)
@@ -313,7 +319,7 @@ __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
   // the previous call: the per-XCD rates move from call to call).
   if (p.KS == 1 && G % kXcds == 0) {
     const int x = (int)blockIdx.x % kXcds, r = (int)blockIdx.x / kXcds;
-    const int a0 = (int)((long)p.NT * x / kXcds), a1 = (int)((long)p.NT * (x + 1) / kXcds);
+    const int a0 = (int)((long)NTs * x / kXcds), a1 = (int)((long)NTs * (x + 1) / kXcds);
     step = G / kXcds;
     base = a0 + r;
     ns = base < a1 ? (a1 - base + step - 1) / step : 0;
@@ -424,6 +430,50 @@ __device__ __forceinline__ void gemm_wg_body(const GemmParams &p) {
   }
   if constexpr (EK == EPI_PARTIAL && FIN != EPI_PARTIAL)
     finalize_last<T, NF, FIN>(p, base, step, ns, rs, reinterpret_cast<unsigned *>(red));
+  if constexpr (EK == EPI_ARGMAX) {
+    // The pool: one strip per ticket from counter 1 until the tickets pass
+    // p.pool.  The XCDs' streaming rates differ from call to call, so the
+    // static ranges end at different times; the pool goes to the workgroups
+    // that are free first.  Nothing is in flight here, so waiting for the
+    // ticket costs no weight stream.
+    if (p.pool > 0) {
+      __shared__ int s_ticket;
+      for (;;) {
+        if (tid == 0)
+          s_ticket = (int)__hip_atomic_fetch_add(p.cnt + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int t = s_ticket;
+        if (t >= p.pool) break;
+        const int s = NTs + t;
+        floatx4 acc[NF];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+        u32x4 tl[MAXKW];
+#pragma unroll
+        for (int j = 0; j < MAXKW; ++j)
+          tl[j] = __builtin_amdgcn_raw_buffer_load_b128(
+              wres, (int)(jok[j] ? (unsigned)s * strip_bytes + joff[j] : kOOB), 0, 0);
+#pragma unroll
+        for (int j = 0; j < MAXKW; ++j)
+#pragma unroll
+          for (int f = 0; f < NF; ++f) acc[f] = Mma<T>::run(tl[j], breg[j][f], acc[f]);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) red[(w * NF + f) * 64 + lane] = acc[f];
+        __syncthreads();
+        const bool reducer = (w == t % W);
+        floatx4 res[NF];
+        if (reducer) {
+#pragma unroll
+          for (int f = 0; f < NF; ++f) res[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+          for (int q = 0; q < W; ++q)
+#pragma unroll
+            for (int f = 0; f < NF; ++f) res[f] += red[(q * NF + f) * 64 + lane];
+        }
+        __syncthreads();
+        if (reducer) finish_strip<T, NF, EK>(p, s, lane, res, rs, best);
+      }
+    }
+  }
   if constexpr (EK == EPI_ARGMAX) {
     if (p.keys) argmax_last<NF>(p, best, reinterpret_cast<unsigned long long *>(red), W);
     else block_argmax_out<NF>(p, best, reinterpret_cast<unsigned long long *>(red), W);

@@ -91,6 +91,7 @@ struct GemmParams {
   unsigned *cnt;
   unsigned long long *keys;
   int *draft_out;
+  int pool;  // LM head: strips [NT - pool, NT) handed out by counter 1 (0: none)
 };
 
 struct GemmLaunch {
