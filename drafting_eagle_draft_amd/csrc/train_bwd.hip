@@ -12,6 +12,7 @@
 // holds the steps between the GEMMs (cross-entropy, RMSNorm, SwiGLU, RoPE,
 // input-fusion backward), the packing kernel, and the attention backward.
 #include <algorithm>
+#include <climits>
 
 #include "pe_internal.hpp"
 
@@ -742,7 +743,10 @@ __global__ __launch_bounds__(512) void k_attn_bwd_dkdv(AttnBwdParams p) {
   constexpr int PER = NFR * 64 / 512;  // fragment lanes per thread and tile
   constexpr int STAGES = PER <= 4 ? 2 : 1;
   __shared__ u32x4 F[NFR * 64];
-  __shared__ float4 s_info[64];
+  // (lse, D, anchor) of the tile's 64 pairs, one array each, so a lane reads
+  // the four rows 4g .. 4g + 3 of a 16-row block with one 16-byte load.
+  __shared__ __attribute__((aligned(16))) float s_lse[64], s_D[64];
+  __shared__ __attribute__((aligned(16))) int s_anc[64];
   const int G = p.G, QC = 64 / G;
   const int Tq = (p.L + QC - 1) / QC;
   const int p0 = blockIdx.x * 128, gk = blockIdx.y, qs = blockIdx.z;
@@ -751,6 +755,8 @@ __global__ __launch_bounds__(512) void k_attn_bwd_dkdv(AttnBwdParams p) {
   const int kp = p0 + 16 * w + c16;  // this lane's key position (B-operand column)
   const int r0 = p0 < p.n ? p.inv[(long)p0 * p.K] : -1;  // first row at position >= p0
   const bool kvalid = r0 >= 0 && kp < p.n && p.inv[(long)kp * p.K] >= 0;
+  // a pair sees this key when kq <= its anchor (never for an invalid key)
+  const int kq = kvalid ? kp : INT_MAX;
   int t_begin = Tq, t_end = Tq;
   if (r0 >= 0) {
     const int per = (Tq + p.qsplit - 1) / p.qsplit;
@@ -787,7 +793,11 @@ __global__ __launch_bounds__(512) void k_attn_bwd_dkdv(AttnBwdParams p) {
   auto put = [&](const Stage &st) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) F[tid + i * 512] = st.v[i];
-    if (w == 0) s_info[lane] = st.info;
+    if (w == 0) {
+      s_lse[lane] = st.info.x;
+      s_D[lane] = st.info.y;
+      s_anc[lane] = __float_as_int(st.info.z);
+    }
   };
   auto compute = [&]() {
     floatx4 sacc[4], pacc[4];
@@ -800,16 +810,26 @@ __global__ __launch_bounds__(512) void k_attn_bwd_dkdv(AttnBwdParams p) {
         sacc[qb] = Mma<T>::run(F[(qb * NC + c) * 64 + lane], kf[c], sacc[qb]);
         pacc[qb] = Mma<T>::run(F[(4 * NC + qb * NC + c) * 64 + lane], vf[c], pacc[qb]);
       }
+    // Every operand is loaded before use and masking is a select, so the
+    // compiler emits no per-row branch with its own LDS round trip.
+    floatx4 lq[4], dq[4];
+    int aq[4][4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      lq[qb] = *reinterpret_cast<const floatx4 *>(&s_lse[qb * 16 + 4 * g]);
+      dq[qb] = *reinterpret_cast<const floatx4 *>(&s_D[qb * 16 + 4 * g]);
+      const int4 a4 = *reinterpret_cast<const int4 *>(&s_anc[qb * 16 + 4 * g]);
+      aq[qb][0] = a4.x; aq[qb][1] = a4.y; aq[qb][2] = a4.z; aq[qb][3] = a4.w;
+    }
     float pv[4][4], ds[4][4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float4 in = s_info[qb * 16 + 4 * g + r];
-        const bool vis = kvalid && kp <= __float_as_int(in.z);
-        const float pr = vis ? fast_exp2(fmaf(sacc[qb][r], p.scale_log2, -in.x)) : 0.f;
+        const float e = fast_exp2(fmaf(sacc[qb][r], p.scale_log2, -lq[qb][r]));
+        const float pr = kq <= aq[qb][r] ? e : 0.f;
         pv[qb][r] = pr;
-        ds[qb][r] = pr * (pacc[qb][r] - in.y);
+        ds[qb][r] = pr * (pacc[qb][r] - dq[qb][r]);
       }
     u32x4 pf[4], dsf[4];
     pack_rows_b<T>(pv, pf);
