@@ -1142,7 +1142,7 @@ struct StepLayout {
   std::vector<StepLayer> off;  // byte offsets stored in the pointer fields
   size_t xN = 0, z = 0, logits = 0, dlA = 0, row_loss = 0;
   size_t dx = 0, dx2 = 0, dxt = 0, gbuf = 0, dgu = 0, doutt = 0, D = 0, dq = 0, dk = 0, dv = 0, dqkv = 0;
-  size_t packA = 0, packB = 0, part = 0, dntp = 0, dshared = 0, pk = 0, pv = 0, qt = 0;
+  size_t packA = 0, packB = 0, part = 0, dntp = 0, dshared = 0, pk = 0, pv = 0, qt = 0, kpart = 0, kpart_bytes = 0;
   int qsplit = 1;
   size_t total = 0;
 };
@@ -1217,6 +1217,23 @@ StepLayout step_layout(const pe_model *m, int N, long n, int K, long L) {
   t.pk = take((size_t)t.qsplit * n * nkv * hd * 4);
   t.pv = take((size_t)t.qsplit * n * nkv * hd * 4);
   t.qt = take(attn_bwd_tile_bytes((int)L, (int)nkv, (int)(nq / nkv), (int)hd, c.dtype));
+  // K-split partials of the data-gradient GEMMs (C = dY W over L rows, the
+  // transposed weight [N][K]), the largest that any of them plans
+  size_t kp = 0;
+  auto ksplit_need = [&](size_t Nw, size_t Kw) {
+    const TileDims d = tile_dims((int)Nw, (int)Kw, kt);
+    const int ks = tile_gemm_ksplit(L, d.NT, d.KT, m->num_cus);
+    kp = std::max(kp, (size_t)(ks - 1) * L * Nw * 4);
+  };
+  ksplit_need(H, V);
+  if (N > 0) {
+    ksplit_need(I, H);
+    ksplit_need(H, 2 * I);
+    ksplit_need(nq * hd, H);
+    ksplit_need(H, (nq + 2 * nkv) * hd);
+  }
+  t.kpart = take(kp);
+  t.kpart_bytes = kp;
   t.total = off;
   return t;
 }
@@ -1250,7 +1267,19 @@ pe_status enqueue_backward(const pe_model *m, int32_t N, int32_t n, int32_t K, c
     p.A = A; p.a_tiled = a_tiled; p.lda = lda; p.M = M;
     p.wt = Bt; p.NT = NT; p.KT = KT; p.N = Nn; p.K = Kk;
     p.C = C; p.ldc = ldc;
-    return chk(launch_gemm_tile(dt, epi, p, m->num_cus, s), "backward GEMM launch");
+    if (epi == BEPI_STORE) {
+      // split over K when the tiles alone leave CUs idle (partials summed after)
+      const int ks = tile_gemm_ksplit(M, NT, KT, m->num_cus);
+      if (ks > 1 && (size_t)(ks - 1) * M * ldc * 4 <= SL.kpart_bytes) {
+        p.ksplit = ks;
+        p.kpart = F(SL.kpart);
+        p.kpart_stride = (long)M * ldc;
+      }
+    }
+    pe_status r = chk(launch_gemm_tile(dt, epi, p, m->num_cus, s), "backward GEMM launch");
+    if (r == PE_OK && p.ksplit > 1)
+      r = chk(launch_ksum(C, ldc, M, Nn, p.kpart, p.kpart_stride, p.ksplit, s), "K-split sum launch");
+    return r;
   };
   auto dgrad = [&](const void *dY, long ld, const Tiled &WT, float *out) {  // out [L][WT.N] = dY W
     return gemm(dY, 0, ld, L, WT.ptr, WT.NT, WT.KT, WT.N, WT.K, BEPI_STORE, out, WT.N);

@@ -24,6 +24,8 @@
 //  * persistent grid of one workgroup per CU walking tiles in bands of four
 //    row blocks, with the tile index spread so that the 32 CUs of one XCD
 //    work on one 4 x 8 patch of tiles at a time (shared L2 panels).
+#include <cmath>
+
 #include "pe_epilogue.hpp"
 
 namespace pe {
@@ -150,7 +152,10 @@ void k_gemm_tile(TileGemmParams p) {
   // strips wn*4 .. +4 of the tile: 4 x 8 MFMA tiles, 128 accumulators.
   const int wm = w >> 2, wn = w & 3;
   const int RB = (p.M + 255) >> 8, CB = (p.NT + 15) >> 4;
-  const int tiles = RB * CB;
+  // Work units: ksplit chunks of the k tiles for every output tile, chunk
+  // by chunk (all tiles' chunk 0 first).
+  const int tiles = RB * CB, units = tiles * p.ksplit;
+  const int KTc = (p.KT + p.ksplit - 1) / p.ksplit;  // k tiles per chunk
   const int G = gridDim.x, b = blockIdx.x;
   const int slot = (G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
   const size_t lda_b = (size_t)p.lda * sizeof(T);
@@ -169,9 +174,11 @@ void k_gemm_tile(TileGemmParams p) {
       (int)(unsigned)(size_t)(lds_void *)&smem[0][(w >> 2) * 16 + (w & 3) * 4][0]);
   constexpr int stage_bytes = 32 * 64 * 16;
 
-  // Tile t -> (first activation row, first weight strip); bands of four row
-  // blocks, columns inside a band.
-  auto tile_origin = [&](int t, int &m0, int &s0) {
+  // Unit u -> (first activation row, first weight strip, chunk); tiles in
+  // bands of four row blocks, columns inside a band.
+  auto tile_origin = [&](int u, int &m0, int &s0, int &ks) {
+    ks = u / tiles;
+    const int t = u - ks * tiles;
     const int band = t / (4 * CB), rem = t - band * 4 * CB;
     const int rows_in = min(4, RB - band * 4);
     const int cb = rem / rows_in, rb = band * 4 + rem % rows_in;
@@ -179,33 +186,40 @@ void k_gemm_tile(TileGemmParams p) {
     s0 = cb * 16;
   };
   const int MG = (p.M + 15) >> 4;  // 16-row groups of a tiled A
-  auto tile_rsrc = [&](int m0, int s0) {
+  // The resource starts at the chunk's first k tile kt0 (the k tiles of a
+  // chunk are loaded as 0 .. nk - 1).
+  auto tile_rsrc = [&](int m0, int s0, int kt0) {
+    const size_t k0 = (size_t)kt0 * kstep;
     if (wave_w)
-      return make_rsrc(reinterpret_cast<const char *>(p.wt) + (size_t)s0 * p.KT * 1024,
-                       (size_t)(p.NT - s0) * p.KT * 1024);
+      return make_rsrc(reinterpret_cast<const char *>(p.wt) + (size_t)s0 * p.KT * 1024 + k0,
+                       (size_t)(p.NT - s0) * p.KT * 1024 - k0);
     if (p.a_tiled)
-      return make_rsrc(reinterpret_cast<const char *>(p.A) + (size_t)(m0 >> 4) * p.KT * 1024,
-                       (size_t)(MG - (m0 >> 4)) * p.KT * 1024);
-    return make_rsrc(reinterpret_cast<const char *>(p.A) + (size_t)m0 * lda_b, (size_t)(p.M - m0) * lda_b);
+      return make_rsrc(reinterpret_cast<const char *>(p.A) + (size_t)(m0 >> 4) * p.KT * 1024 + k0,
+                       (size_t)(MG - (m0 >> 4)) * p.KT * 1024 - k0);
+    return make_rsrc(reinterpret_cast<const char *>(p.A) + (size_t)m0 * lda_b + k0, (size_t)(p.M - m0) * lda_b - k0);
   };
+  int nk = 0;  // k tiles of the current unit
   auto issue = [&](const u32x4 &rs, int kt) {
     const unsigned dst = lds0 + (unsigned)((kt & (NSTAGE - 1)) * stage_bytes);
-    const bool live = kt < p.KT;
+    const bool live = kt < nk;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       load_to_lds(rs, dst + q * 1024, live ? lanebase + (fbase + q * qstride + kt * kstep) : kOobOffset);
   };
 
-  int t = slot, m0 = 0, s0 = 0;
+  int t = slot, m0 = 0, s0 = 0, ks = 0;
   u32x4 rs = {0u, 0u, 0u, 0u};
-  if (t < tiles) {
-    tile_origin(t, m0, s0);
-    rs = tile_rsrc(m0, s0);
+  auto start_unit = [&]() {
+    tile_origin(t, m0, s0, ks);
+    const int kt0 = ks * KTc;
+    nk = min(KTc, p.KT - kt0);
+    rs = tile_rsrc(m0, s0, kt0);
     issue(rs, 0);
     issue(rs, 1);
     issue(rs, 2);
-  }
-  while (t < tiles) {
+  };
+  if (t < units) start_unit();
+  while (t < units) {
     floatx4 acc[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -221,7 +235,7 @@ void k_gemm_tile(TileGemmParams p) {
     // the barrier they cost 3% more (measured on the LM head: 33.8 against
     // 32.8 ms); the scheduling barriers keep the compiler from regrouping
     // them.  The second wave on each SIMD covers this wave's waits.
-    for (int kt = 0; kt < p.KT; ++kt) {
+    for (int kt = 0; kt < nk; ++kt) {
       asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
       const int st = kt & (NSTAGE - 1);
       u32x4 wf[4], af[8];
@@ -230,7 +244,7 @@ void k_gemm_tile(TileGemmParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) af[j] = smem[st][16 + wm * 8 + j][lane];
       const unsigned dst = lds0 + (unsigned)(((kt + 3) & (NSTAGE - 1)) * stage_bytes);
-      const bool live = kt + 3 < p.KT;
+      const bool live = kt + 3 < nk;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_barrier(0);
@@ -244,17 +258,13 @@ void k_gemm_tile(TileGemmParams p) {
     // then start the next tile's first three stages so that they load while
     // this tile's epilogue runs.
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    const int tm0 = m0, ts0 = s0;
+    const int tm0 = m0, ts0 = s0, tks = ks;
     t += G;
-    if (t < tiles) {
-      tile_origin(t, m0, s0);
-      rs = tile_rsrc(m0, s0);
-      issue(rs, 0);
-      issue(rs, 1);
-      issue(rs, 2);
-    }
+    if (t < units) start_unit();
     {
     const int m0 = tm0, s0 = ts0;
+    // chunk 0 stores to C, chunk c > 0 to its own partial block
+    float *const C = tks == 0 ? p.C : p.kpart + (size_t)(tks - 1) * p.kpart_stride;
     // acc[i][j][r] = C[m = m0 + (wm*8 + j)*16 + c16][n = (s0 + wn*4 + i)*16 + 4g + r]
     if constexpr (LMH) {
       // Output row of activation row m, or -1 when it is not written (the
@@ -344,7 +354,7 @@ void k_gemm_tile(TileGemmParams p) {
           const int n = s * 16 + 4 * g;
           if (m < p.M && s < p.NT) {
             if constexpr (EPI == BEPI_STORE) {
-              *reinterpret_cast<floatx4 *>(p.C + (long)m * p.ldc + n) = acc[i][j];
+              *reinterpret_cast<floatx4 *>(C + (long)m * p.ldc + n) = acc[i][j];
             } else if constexpr (EPI == BEPI_ACCUM) {
               floatx4 *dst = reinterpret_cast<floatx4 *>(p.C + (long)m * p.ldc + n);
               *dst = *dst + acc[i][j];
@@ -363,11 +373,59 @@ void k_gemm_tile(TileGemmParams p) {
   }
 }
 
+// C += the K-split partials: one thread per 4 columns of a row.
+__global__ __launch_bounds__(256) void k_ksum(float *C, long ldc, int M, int N4, const float *kpart, long stride,
+                                              int ksplit) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)M * N4) return;
+  const long r = idx / N4, c = (idx - r * N4) * 4;
+  floatx4 *dst = reinterpret_cast<floatx4 *>(C + r * ldc + c);
+  floatx4 a = *dst;
+  for (int k = 0; k < ksplit - 1; ++k) a += *reinterpret_cast<const floatx4 *>(kpart + k * stride + r * ldc + c);
+  *dst = a;
+}
+
 }  // namespace
+
+int tile_gemm_ksplit(long M, int NT, int KT, int num_cus) {
+  // Cost in k steps of one round of tiles (about 0.8 us each on a 256 x 256
+  // tile): rounds of units times k tiles per unit, plus the summing pass,
+  // which moves ks + 1 fp32 blocks (256 KB per tile each; about 15 us per
+  // round of 256 tiles at 4.5 TB/s, i.e. 19 k steps).
+  constexpr double kSumStepsPerBlock = 19.0;
+  const long tiles = ((M + 255) / 256) * (long)((NT + 15) / 16);
+  int best = 1;
+  double best_cost = std::ceil((double)tiles / num_cus) * KT;
+  for (int ks = 2; ks <= 8 && ks <= KT; ++ks) {
+    if ((ks - 1) * ((KT + ks - 1) / ks) >= KT) continue;  // every chunk gets k tiles
+    const double rounds = std::ceil((double)tiles * ks / num_cus);
+    const double cost =
+        rounds * std::ceil((double)KT / ks) + (ks + 1) * kSumStepsPerBlock * (double)tiles / num_cus;
+    if (cost < best_cost * 0.98) {
+      best = ks;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+hipError_t launch_ksum(float *C, long ldc, int M, int N, const float *kpart, long kpart_stride, int ksplit,
+                       hipStream_t s) {
+  if (ksplit <= 1 || M < 1 || N < 1) return hipSuccess;
+  if (N % 4 || ldc % 4 || kpart_stride % 4) return hipErrorInvalidValue;
+  const long n = (long)M * (N / 4);
+  hipLaunchKernelGGL(k_ksum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, C, ldc, M, N / 4, kpart,
+                     kpart_stride, ksplit);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_tile(int dtype, int epi, const TileGemmParams &p, int num_cus, hipStream_t s) {
   if (p.M < 1 || p.NT < 1 || p.KT < 1) return hipSuccess;
-  const long tiles = (long)((p.M + 255) / 256) * ((p.NT + 15) / 16);
+  if (p.ksplit < 1 ||
+      (p.ksplit > 1 && (epi != BEPI_STORE || !p.kpart || (p.ksplit - 1) * ((p.KT + p.ksplit - 1) / p.ksplit) >= p.KT)))
+    return hipErrorInvalidValue;
+  const long tiles = (long)((p.M + 255) / 256) * ((p.NT + 15) / 16) * p.ksplit;
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(tiles < num_cus ? tiles : num_cus));
 #define PE_TILE_CASE(T, E) \
   case E: hipLaunchKernelGGL((k_gemm_tile<T, E>), grid, dim3(512), 0, s, p); break;

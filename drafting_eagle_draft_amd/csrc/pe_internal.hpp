@@ -173,6 +173,12 @@ struct TileGemmParams {
   int a_tiled;          // A in the fragment-tile layout: [ceil(M/16)][KT] 1 KB fragments
   float *C;
   long ldc;
+  // K split (STORE only; 1 = none): the k tiles in ksplit chunks of
+  // ceil(KT / ksplit); chunk 0 writes C, chunk c > 0 writes the same layout
+  // at kpart + (c - 1) * kpart_stride.  C is their sum (launch_ksum).
+  int ksplit = 1;
+  float *kpart;
+  long kpart_stride;
   void *logits;
   unsigned long long *keys;  // [M], zeroed before the launch; atomically maxed
   // LM head output rows: row m goes to logits row out_rows[m - row_skip]
@@ -193,6 +199,14 @@ struct TileGemmParams {
 };
 
 hipError_t launch_gemm_tile(int dtype, int epi, const TileGemmParams &p, int num_cus, hipStream_t s);
+// C[r][0..N) += sum over c = 1 .. ksplit - 1 of the K-split partials, in
+// chunk order, for rows r < M (row stride ldc; N a multiple of 4).
+hipError_t launch_ksum(float *C, long ldc, int M, int N, const float *kpart, long kpart_stride, int ksplit,
+                       hipStream_t s);
+// K split of a STORE tile GEMM (M rows, NT strips, KT k tiles) over num_cus
+// workgroups: the chunk count, up to 8, with the fewest k tiles per CU
+// counting the summing pass; 1 when a split does not pay.
+int tile_gemm_ksplit(long M, int NT, int KT, int num_cus);
 // out[r(m)] = argmax of keys[m], r(m) as for the LM head's output rows (out_rows NULL: r(m) = m).
 hipError_t launch_argmax_rows(const unsigned long long *keys, int M, int *out, const int *out_rows,
                               int row_skip, int out_M, hipStream_t s);
