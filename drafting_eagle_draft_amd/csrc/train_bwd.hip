@@ -464,9 +464,10 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dq(AttnBwdParams p) {
   constexpr int NT = 64 * NW;
   constexpr int KS = HD + E, VS = 64 + 4, CPR = HD / E, MAXC = (64 * CPR + NT - 1) / NT;
   constexpr int NKC = sizeof(T) == 2 ? 2 : 4;  // reduction chunks over 64 keys
-  __shared__ __attribute__((aligned(16))) T Ks[64 * KS];
-  __shared__ __attribute__((aligned(16))) T Vs[64 * KS];
-  __shared__ __attribute__((aligned(16))) T Kt[HD * VS];
+  // Two buffers of each: one key tile is multiplied while the next is stored.
+  __shared__ __attribute__((aligned(16))) T Ks[2][64 * KS];
+  __shared__ __attribute__((aligned(16))) T Vs[2][64 * KS];
+  __shared__ __attribute__((aligned(16))) T Kt[2][HD * VS];
   __shared__ int s_amax[NW];
   const int G = p.G, QT = 16 * QB * NW / G;
   const int gk = blockIdx.y;
@@ -537,21 +538,21 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dq(AttnBwdParams p) {
       st.v[i] = ok ? ldg16(v0 + (long)jj * kvs + cc * E) : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  auto put = [&](const KV &st) {
+  auto put = [&](const KV &st, int bf) {
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
       const int id = tid + i * NT;
       if (id >= 64 * CPR) break;
       const int key = id / CPR, cc = id - key * CPR;
-      *reinterpret_cast<u32x4 *>(&Ks[key * KS + cc * E]) = st.k[i];
-      *reinterpret_cast<u32x4 *>(&Vs[key * KS + cc * E]) = st.v[i];
+      *reinterpret_cast<u32x4 *>(&Ks[bf][key * KS + cc * E]) = st.k[i];
+      *reinterpret_cast<u32x4 *>(&Vs[bf][key * KS + cc * E]) = st.v[i];
       T vals[E];
       __builtin_memcpy(vals, &st.k[i], 16);
 #pragma unroll
-      for (int e = 0; e < E; ++e) Kt[(cc * E + e) * VS + key] = vals[e];
+      for (int e = 0; e < E; ++e) Kt[bf][(cc * E + e) * VS + key] = vals[e];
     }
   };
-  auto compute = [&](int jt) {
+  auto compute = [&](int jt, int bf) {
     if (jt > wave_amax) return;  // every row of this wave sits before the tile
     floatx4 sacc[QB][4], pacc[QB][4];
 #pragma unroll
@@ -562,8 +563,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dq(AttnBwdParams p) {
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const u32x4 kf = lds16b(&Ks[(kb * 16 + c16) * KS + c * KTILE + g * E]);
-        const u32x4 vf = lds16b(&Vs[(kb * 16 + c16) * KS + c * KTILE + g * E]);
+        const u32x4 kf = lds16b(&Ks[bf][(kb * 16 + c16) * KS + c * KTILE + g * E]);
+        const u32x4 vf = lds16b(&Vs[bf][(kb * 16 + c16) * KS + c * KTILE + g * E]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           sacc[qb][kb] = Mma<T>::run(kf, qf[qb][c], sacc[qb][kb]);
@@ -589,27 +590,33 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dq(AttnBwdParams p) {
     for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        const u32x4 kf = lds_t_frag<T, VS>(Kt, d, c16, g, kc);
+        const u32x4 kf = lds_t_frag<T, VS>(Kt[bf], d, c16, g, kc);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) dqacc[qb][d] = Mma<T>::run(kf, dsf[qb][kc], dqacc[qb][d]);
       }
   };
-  {
+  // Key tile jt sits in buffer (jt / 64) & 1.  After multiplying a tile, a
+  // wave stores the next one (loaded into registers earlier) into the other
+  // buffer; one barrier per tile then finds that tile stored by every wave
+  // and the buffer just multiplied free for the tile after.
+  if (nkeys > 0) {
     KV st0, st1;
     fetch(0, st0);
     fetch(64, st1);
-    for (int jt = 0; jt < nkeys; jt += 128) {
-      put(st0);
-      lds_barrier();
-      fetch(jt + 128, st0);
-      compute(jt);
-      lds_barrier();
-      if (jt + 64 >= nkeys) break;
-      put(st1);
+    put(st0, 0);
+    lds_barrier();
+    fetch(128, st0);
+    for (int jt = 0;; jt += 128) {
+      compute(jt, 0);
+      put(st1, 1);
       lds_barrier();
       fetch(jt + 192, st1);
-      compute(jt + 64);
+      if (jt + 64 >= nkeys) break;
+      compute(jt + 64, 1);
+      put(st0, 0);
       lds_barrier();
+      fetch(jt + 256, st0);
+      if (jt + 128 >= nkeys) break;
     }
   }
 
@@ -728,8 +735,8 @@ __global__ __launch_bounds__(256) void k_pair_tiles(const T *q, const T *dout, c
 // One workgroup of eight waves per (tile of 128 depth-0 key positions, kv
 // head, share of the query tiles); wave w owns keys 16 w .. 16 w + 15, their
 // K and V fragments in registers.  Query tiles (above) move HBM/L2 ->
-// registers STAGES tiles ahead of use and registers -> LDS at the top of
-// their iteration; per tile every wave runs S = Q K^T, dP = dO V^T,
+// registers STAGES tiles ahead of use and registers -> LDS (two buffers)
+// while the tile before is multiplied; per tile every wave runs S = Q K^T, dP = dO V^T,
 // dV^T += dO^T P and dK^T += Q^T dS on the matrix cores.  The rows that see
 // a key tile (all rows from its first position on) are split into qsplit
 // shares of the query tiles -- the same range of global tiles for every key
@@ -742,11 +749,12 @@ __global__ __launch_bounds__(512) void k_attn_bwd_dkdv(AttnBwdParams p) {
   constexpr int NKC = sizeof(T) == 2 ? 2 : 4, NT = ND * NKC, NFR = 8 * NC + 2 * NT;
   constexpr int PER = NFR * 64 / 512;  // fragment lanes per thread and tile
   constexpr int STAGES = PER <= 4 ? 2 : 1;
-  __shared__ u32x4 F[NFR * 64];
+  // Two LDS buffers: one query tile is multiplied while the next is stored.
+  __shared__ u32x4 F[2][NFR * 64];
   // (lse, D, anchor) of the tile's 64 pairs, one array each, so a lane reads
   // the four rows 4g .. 4g + 3 of a 16-row block with one 16-byte load.
-  __shared__ __attribute__((aligned(16))) float s_lse[64], s_D[64];
-  __shared__ __attribute__((aligned(16))) int s_anc[64];
+  __shared__ __attribute__((aligned(16))) float s_lse[2][64], s_D[2][64];
+  __shared__ __attribute__((aligned(16))) int s_anc[2][64];
   const int G = p.G, QC = 64 / G;
   const int Tq = (p.L + QC - 1) / QC;
   const int p0 = blockIdx.x * 128, gk = blockIdx.y, qs = blockIdx.z;
@@ -790,16 +798,16 @@ __global__ __launch_bounds__(512) void k_attn_bwd_dkdv(AttnBwdParams p) {
     for (int i = 0; i < PER; ++i) st.v[i] = tg[(long)tc * NFR * 64 + tid + i * 512];
     if (w == 0) st.info = ig[(long)tc * 64 + lane];
   };
-  auto put = [&](const Stage &st) {
+  auto put = [&](const Stage &st, int bf) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) F[tid + i * 512] = st.v[i];
+    for (int i = 0; i < PER; ++i) F[bf][tid + i * 512] = st.v[i];
     if (w == 0) {
-      s_lse[lane] = st.info.x;
-      s_D[lane] = st.info.y;
-      s_anc[lane] = __float_as_int(st.info.z);
+      s_lse[bf][lane] = st.info.x;
+      s_D[bf][lane] = st.info.y;
+      s_anc[bf][lane] = __float_as_int(st.info.z);
     }
   };
-  auto compute = [&]() {
+  auto compute = [&](int bf) {
     floatx4 sacc[4], pacc[4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) sacc[qb] = pacc[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -807,8 +815,8 @@ __global__ __launch_bounds__(512) void k_attn_bwd_dkdv(AttnBwdParams p) {
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        sacc[qb] = Mma<T>::run(F[(qb * NC + c) * 64 + lane], kf[c], sacc[qb]);
-        pacc[qb] = Mma<T>::run(F[(4 * NC + qb * NC + c) * 64 + lane], vf[c], pacc[qb]);
+        sacc[qb] = Mma<T>::run(F[bf][(qb * NC + c) * 64 + lane], kf[c], sacc[qb]);
+        pacc[qb] = Mma<T>::run(F[bf][(4 * NC + qb * NC + c) * 64 + lane], vf[c], pacc[qb]);
       }
     // Every operand is loaded before use and masking is a select, so the
     // compiler emits no per-row branch with its own LDS round trip.
@@ -816,9 +824,9 @@ __global__ __launch_bounds__(512) void k_attn_bwd_dkdv(AttnBwdParams p) {
     int aq[4][4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      lq[qb] = *reinterpret_cast<const floatx4 *>(&s_lse[qb * 16 + 4 * g]);
-      dq[qb] = *reinterpret_cast<const floatx4 *>(&s_D[qb * 16 + 4 * g]);
-      const int4 a4 = *reinterpret_cast<const int4 *>(&s_anc[qb * 16 + 4 * g]);
+      lq[qb] = *reinterpret_cast<const floatx4 *>(&s_lse[bf][qb * 16 + 4 * g]);
+      dq[qb] = *reinterpret_cast<const floatx4 *>(&s_D[bf][qb * 16 + 4 * g]);
+      const int4 a4 = *reinterpret_cast<const int4 *>(&s_anc[bf][qb * 16 + 4 * g]);
       aq[qb][0] = a4.x; aq[qb][1] = a4.y; aq[qb][2] = a4.z; aq[qb][3] = a4.w;
     }
     float pv[4][4], ds[4][4];
@@ -838,36 +846,47 @@ __global__ __launch_bounds__(512) void k_attn_bwd_dkdv(AttnBwdParams p) {
     for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        dkT[d] = Mma<T>::run(F[(8 * NC + d * NKC + kc) * 64 + lane], dsf[kc], dkT[d]);
-        dvT[d] = Mma<T>::run(F[(8 * NC + NT + d * NKC + kc) * 64 + lane], pf[kc], dvT[d]);
+        dkT[d] = Mma<T>::run(F[bf][(8 * NC + d * NKC + kc) * 64 + lane], dsf[kc], dkT[d]);
+        dvT[d] = Mma<T>::run(F[bf][(8 * NC + NT + d * NKC + kc) * 64 + lane], pf[kc], dvT[d]);
       }
   };
-  if constexpr (STAGES == 2) {
-    Stage st0, st1;
-    fetch(t_begin, st0);
-    fetch(t_begin + 1, st1);
-    for (int tq = t_begin; tq < t_end; tq += 2) {
-      put(st0);
+  // Query tile tq sits in buffer (tq - t_begin) & 1.  After multiplying a
+  // tile, a wave stores the next one (loaded into registers earlier) into
+  // the other buffer; one barrier per tile then finds that tile stored by
+  // every wave and the buffer just multiplied free for the tile after.
+  if (t_begin < t_end) {
+    if constexpr (STAGES == 2) {
+      Stage st0, st1;
+      fetch(t_begin, st0);
+      fetch(t_begin + 1, st1);
+      put(st0, 0);
       lds_barrier();
-      fetch(tq + 2, st0);
-      compute();
+      fetch(t_begin + 2, st0);
+      for (int tq = t_begin;; tq += 2) {
+        compute(0);
+        put(st1, 1);
+        lds_barrier();
+        fetch(tq + 3, st1);
+        if (tq + 1 >= t_end) break;
+        compute(1);
+        put(st0, 0);
+        lds_barrier();
+        fetch(tq + 4, st0);
+        if (tq + 2 >= t_end) break;
+      }
+    } else {
+      Stage st0;
+      fetch(t_begin, st0);
+      put(st0, 0);
       lds_barrier();
-      if (tq + 1 >= t_end) break;
-      put(st1);
-      lds_barrier();
-      fetch(tq + 3, st1);
-      compute();
-      lds_barrier();
-    }
-  } else {
-    Stage st0;
-    fetch(t_begin, st0);
-    for (int tq = t_begin; tq < t_end; ++tq) {
-      put(st0);
-      lds_barrier();
-      fetch(tq + 1, st0);
-      compute();
-      lds_barrier();
+      fetch(t_begin + 1, st0);
+      for (int tq = t_begin; tq < t_end; ++tq) {
+        const int bf = (tq - t_begin) & 1;
+        compute(bf);
+        put(st0, bf ^ 1);
+        lds_barrier();
+        fetch(tq + 2, st0);
+      }
     }
   }
   if (kp < p.n) {
