@@ -1217,20 +1217,28 @@ StepLayout step_layout(const pe_model *m, int N, long n, int K, long L) {
   t.pk = take((size_t)t.qsplit * n * nkv * hd * 4);
   t.pv = take((size_t)t.qsplit * n * nkv * hd * 4);
   t.qt = take(attn_bwd_tile_bytes((int)L, (int)nkv, (int)(nq / nkv), (int)hd, c.dtype));
-  // K-split partials of the data-gradient GEMMs (C = dY W over L rows, the
-  // transposed weight [N][K]), the largest that any of them plans
+  // K-split partials of the backward's GEMMs, the largest that any of them
+  // plans: data gradients C [L][Nw] = dY W (the transposed weight [Nw][Kw])
+  // and weight gradients C [rows][cols] += A^T B over Kr rows
   size_t kp = 0;
-  auto ksplit_need = [&](size_t Nw, size_t Kw) {
+  auto ksplit_need = [&](size_t M, size_t Nw, size_t Kw) {
     const TileDims d = tile_dims((int)Nw, (int)Kw, kt);
-    const int ks = tile_gemm_ksplit(L, d.NT, d.KT, m->num_cus);
-    kp = std::max(kp, (size_t)(ks - 1) * L * Nw * 4);
+    const int ks = tile_gemm_ksplit((long)M, d.NT, d.KT, m->num_cus);
+    kp = std::max(kp, (size_t)(ks - 1) * M * Nw * 4);
   };
-  ksplit_need(H, V);
+  ksplit_need(L, H, V);
+  ksplit_need(V, H, L);
+  ksplit_need(H, 3 * H, n);
   if (N > 0) {
-    ksplit_need(I, H);
-    ksplit_need(H, 2 * I);
-    ksplit_need(nq * hd, H);
-    ksplit_need(H, (nq + 2 * nkv) * hd);
+    ksplit_need(L, I, H);
+    ksplit_need(L, H, 2 * I);
+    ksplit_need(L, nq * hd, H);
+    ksplit_need(L, H, (nq + 2 * nkv) * hd);
+    ksplit_need(H, I, L);
+    ksplit_need(I, H, L);
+    ksplit_need(H, nq * hd, L);
+    ksplit_need(nq * hd, H, L);
+    ksplit_need(nkv * hd, H, L);
   }
   t.kpart = take(kp);
   t.kpart_bytes = kp;
@@ -1267,7 +1275,7 @@ pe_status enqueue_backward(const pe_model *m, int32_t N, int32_t n, int32_t K, c
     p.A = A; p.a_tiled = a_tiled; p.lda = lda; p.M = M;
     p.wt = Bt; p.NT = NT; p.KT = KT; p.N = Nn; p.K = Kk;
     p.C = C; p.ldc = ldc;
-    if (epi == BEPI_STORE) {
+    if (epi == BEPI_STORE || epi == BEPI_ACCUM) {
       // split over K when the tiles alone leave CUs idle (partials summed after)
       const int ks = tile_gemm_ksplit(M, NT, KT, m->num_cus);
       if (ks > 1 && (size_t)(ks - 1) * M * ldc * 4 <= SL.kpart_bytes) {

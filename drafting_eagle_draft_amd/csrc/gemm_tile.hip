@@ -263,7 +263,8 @@ void k_gemm_tile(TileGemmParams p) {
     if (t < units) start_unit();
     {
     const int m0 = tm0, s0 = ts0;
-    // chunk 0 stores to C, chunk c > 0 to its own partial block
+    // chunk 0 stores to (or accumulates into) C, chunk c > 0 stores its own
+    // partial block
     float *const C = tks == 0 ? p.C : p.kpart + (size_t)(tks - 1) * p.kpart_stride;
     // acc[i][j][r] = C[m = m0 + (wm*8 + j)*16 + c16][n = (s0 + wn*4 + i)*16 + 4g + r]
     if constexpr (LMH) {
@@ -356,8 +357,8 @@ void k_gemm_tile(TileGemmParams p) {
             if constexpr (EPI == BEPI_STORE) {
               *reinterpret_cast<floatx4 *>(C + (long)m * p.ldc + n) = acc[i][j];
             } else if constexpr (EPI == BEPI_ACCUM) {
-              floatx4 *dst = reinterpret_cast<floatx4 *>(p.C + (long)m * p.ldc + n);
-              *dst = *dst + acc[i][j];
+              floatx4 *dst = reinterpret_cast<floatx4 *>(C + (long)m * p.ldc + n);
+              *dst = tks == 0 ? *dst + acc[i][j] : acc[i][j];
             } else if constexpr (EPI == BEPI_SWIGLU) {
               epi_tile_swiglu<T, false>(p, m, s, g, acc[i][j]);
             } else if constexpr (EPI == BEPI_SWIGLU_SAVE) {
@@ -394,19 +395,20 @@ int tile_gemm_ksplit(long M, int NT, int KT, int num_cus) {
   // round of 256 tiles at 4.5 TB/s, i.e. 19 k steps).
   constexpr double kSumStepsPerBlock = 19.0;
   const long tiles = ((M + 255) / 256) * (long)((NT + 15) / 16);
+  const double unsplit = std::ceil((double)tiles / num_cus) * KT;
   int best = 1;
-  double best_cost = std::ceil((double)tiles / num_cus) * KT;
+  double best_cost = unsplit;
   for (int ks = 2; ks <= 8 && ks <= KT; ++ks) {
     if ((ks - 1) * ((KT + ks - 1) / ks) >= KT) continue;  // every chunk gets k tiles
     const double rounds = std::ceil((double)tiles * ks / num_cus);
     const double cost =
         rounds * std::ceil((double)KT / ks) + (ks + 1) * kSumStepsPerBlock * (double)tiles / num_cus;
-    if (cost < best_cost * 0.98) {
+    if (cost < best_cost) {
       best = ks;
       best_cost = cost;
     }
   }
-  return best;
+  return best_cost < unsplit * 0.98 ? best : 1;  // a split must save 2%
 }
 
 hipError_t launch_ksum(float *C, long ldc, int M, int N, const float *kpart, long kpart_stride, int ksplit,
@@ -421,8 +423,8 @@ hipError_t launch_ksum(float *C, long ldc, int M, int N, const float *kpart, lon
 
 hipError_t launch_gemm_tile(int dtype, int epi, const TileGemmParams &p, int num_cus, hipStream_t s) {
   if (p.M < 1 || p.NT < 1 || p.KT < 1) return hipSuccess;
-  if (p.ksplit < 1 ||
-      (p.ksplit > 1 && (epi != BEPI_STORE || !p.kpart || (p.ksplit - 1) * ((p.KT + p.ksplit - 1) / p.ksplit) >= p.KT)))
+  if (p.ksplit < 1 || (p.ksplit > 1 && ((epi != BEPI_STORE && epi != BEPI_ACCUM) || !p.kpart ||
+                                         (p.ksplit - 1) * ((p.KT + p.ksplit - 1) / p.ksplit) >= p.KT)))
     return hipErrorInvalidValue;
   const long tiles = (long)((p.M + 255) / 256) * ((p.NT + 15) / 16) * p.ksplit;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;

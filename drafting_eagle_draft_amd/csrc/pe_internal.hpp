@@ -173,9 +173,10 @@ struct TileGemmParams {
   int a_tiled;          // A in the fragment-tile layout: [ceil(M/16)][KT] 1 KB fragments
   float *C;
   long ldc;
-  // K split (STORE only; 1 = none): the k tiles in ksplit chunks of
-  // ceil(KT / ksplit); chunk 0 writes C, chunk c > 0 writes the same layout
-  // at kpart + (c - 1) * kpart_stride.  C is their sum (launch_ksum).
+  // K split (STORE and ACCUM; 1 = none): the k tiles in ksplit chunks of
+  // ceil(KT / ksplit); chunk 0 writes (STORE) or adds to (ACCUM) C, chunk
+  // c > 0 stores the same layout at kpart + (c - 1) * kpart_stride, added to
+  // C afterwards in chunk order (launch_ksum).
   int ksplit = 1;
   float *kpart;
   long kpart_stride;
@@ -203,7 +204,7 @@ hipError_t launch_gemm_tile(int dtype, int epi, const TileGemmParams &p, int num
 // chunk order, for rows r < M (row stride ldc; N a multiple of 4).
 hipError_t launch_ksum(float *C, long ldc, int M, int N, const float *kpart, long kpart_stride, int ksplit,
                        hipStream_t s);
-// K split of a STORE tile GEMM (M rows, NT strips, KT k tiles) over num_cus
+// K split of a STORE or ACCUM tile GEMM (M rows, NT strips, KT k tiles) over num_cus
 // workgroups: the chunk count, up to 8, with the fewest k tiles per CU
 // counting the summing pass; 1 when a split does not pay.
 int tile_gemm_ksplit(long M, int NT, int KT, int num_cus);
