@@ -444,6 +444,21 @@ __device__ __forceinline__ void pack_rows_b(const float (&v)[4][4], u32x4 (&out)
   }
 }
 
+// Pack two 16-row C blocks the same way: one bf16 fragment (32 rows) or two
+// fp32 fragments (16 rows each).
+template <typename T>
+__device__ __forceinline__ void pack_rows_b2(const float (&v)[2][4], u32x4 (&out)[sizeof(T) == 2 ? 1 : 2]) {
+  if constexpr (sizeof(T) == 2) {
+    out[0] = u32x4{pack_bf16x2(v[0][0], v[0][1]), pack_bf16x2(v[0][2], v[0][3]), pack_bf16x2(v[1][0], v[1][1]),
+                   pack_bf16x2(v[1][2], v[1][3])};
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      out[kb] = u32x4{__float_as_uint(v[kb][0]), __float_as_uint(v[kb][1]), __float_as_uint(v[kb][2]),
+                      __float_as_uint(v[kb][3])};
+  }
+}
+
 // A fragment of a transposed LDS tile X^T [HD][64 + 4] (rows d*16 + c16) over
 // reduction rows {32 c2 + 4g + r, 32 c2 + 16 + 4g + r} (bf16) or
 // {16 kb + 4g + r} (fp32), matching pack_rows_b.
@@ -733,22 +748,29 @@ __global__ __launch_bounds__(256) void k_pair_tiles(const T *q, const T *dout, c
 }
 
 // One workgroup of eight waves per (tile of 128 depth-0 key positions, kv
-// head, share of the query tiles); wave w owns keys 16 w .. 16 w + 15, their
-// K and V fragments in registers.  Query tiles (above) move HBM/L2 ->
-// registers STAGES tiles ahead of use and registers -> LDS (two buffers)
-// while the tile before is multiplied; per tile every wave runs S = Q K^T, dP = dO V^T,
-// dV^T += dO^T P and dK^T += Q^T dS on the matrix cores.  The rows that see
-// a key tile (all rows from its first position on) are split into qsplit
-// shares of the query tiles -- the same range of global tiles for every key
-// tile, so key tiles running together read the same tiles from L2 -- and
-// each share writes its partial dK, dV by key position, summed in order by
-// k_attn_bwd_reduce.
-template <typename T, int HD>
+// head, share of the query tiles).  PH = 1: wave w owns keys 16 w .. + 15
+// and all 64 pairs of each query tile.  PH = 2: waves 2v and 2v + 1 own
+// keys 32 v .. + 31 (two 16-key blocks) and pairs 0-31 and 32-63 of each
+// tile, so each wave reads half of the tile's fragments from LDS for the
+// same matrix work; the pair of waves adds its two partial sums at the
+// end.  K and V fragments of the wave's keys sit in registers.  Query tiles
+// (above) move HBM/L2 -> registers STAGES tiles ahead of use and registers
+// -> LDS (two buffers) while the tile before is multiplied; per tile every
+// wave runs S = Q K^T, dP = dO V^T, dV^T += dO^T P and dK^T += Q^T dS on
+// the matrix cores.  The rows that see a key tile (all rows from its first
+// position on) are split into qsplit shares of the query tiles -- the same
+// range of global tiles for every key tile, so key tiles running together
+// read the same tiles from L2 -- and each share writes its partial dK, dV
+// by key position, summed in order by k_attn_bwd_reduce.
+template <typename T, int HD, int PH>
 __global__ __launch_bounds__(512) void k_attn_bwd_dkdv(AttnBwdParams p) {
   constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE, NC = HD / KTILE, ND = HD / 16;
   constexpr int NKC = sizeof(T) == 2 ? 2 : 4, NT = ND * NKC, NFR = 8 * NC + 2 * NT;
   constexpr int PER = NFR * 64 / 512;  // fragment lanes per thread and tile
   constexpr int STAGES = PER <= 4 ? 2 : 1;
+  constexpr int KB = PH;               // 16-key blocks per wave
+  constexpr int NQB = 4 / PH;          // 16-pair blocks per wave
+  constexpr int NKW = NKC / PH;        // pair fragments (reduction chunks) per wave
   // Two LDS buffers: one query tile is multiplied while the next is stored.
   __shared__ u32x4 F[2][NFR * 64];
   // (lse, D, anchor) of the tile's 64 pairs, one array each, so a lane reads
@@ -759,12 +781,28 @@ __global__ __launch_bounds__(512) void k_attn_bwd_dkdv(AttnBwdParams p) {
   const int Tq = (p.L + QC - 1) / QC;
   const int p0 = blockIdx.x * 128, gk = blockIdx.y, qs = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int ph = w % PH;           // this wave's pair half
+  const int kw = (w / PH) * KB;    // first 16-key block of this wave
+  const int qb0 = ph * NQB, kc0 = ph * NKW;
   const long kvs = (long)p.nkv * HD;
-  const int kp = p0 + 16 * w + c16;  // this lane's key position (B-operand column)
   const int r0 = p0 < p.n ? p.inv[(long)p0 * p.K] : -1;  // first row at position >= p0
-  const bool kvalid = r0 >= 0 && kp < p.n && p.inv[(long)kp * p.K] >= 0;
-  // a pair sees this key when kq <= its anchor (never for an invalid key)
-  const int kq = kvalid ? kp : INT_MAX;
+  // This lane's key (B-operand column) in each key block, and the position
+  // a pair's anchor must reach to see it (never reached for an invalid key).
+  int kp[KB], kq[KB];
+  u32x4 kf[KB][NC], vf[KB][NC];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    kp[kb] = p0 + 16 * (kw + kb) + c16;
+    const bool kvalid = r0 >= 0 && kp[kb] < p.n && p.inv[(long)kp[kb] * p.K] >= 0;
+    kq[kb] = kvalid ? kp[kb] : INT_MAX;
+    const T *kr = reinterpret_cast<const T *>(p.k0) + (long)(kvalid ? kp[kb] : 0) * kvs + gk * HD;
+    const T *vr = reinterpret_cast<const T *>(p.v0) + (long)(kvalid ? kp[kb] : 0) * kvs + gk * HD;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kf[kb][c] = kvalid ? ldg16(kr + c * KTILE + g * E) : u32x4{0u, 0u, 0u, 0u};
+      vf[kb][c] = kvalid ? ldg16(vr + c * KTILE + g * E) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
   int t_begin = Tq, t_end = Tq;
   if (r0 >= 0) {
     const int per = (Tq + p.qsplit - 1) / p.qsplit;
@@ -772,19 +810,11 @@ __global__ __launch_bounds__(512) void k_attn_bwd_dkdv(AttnBwdParams p) {
     t_end = min(Tq, (qs + 1) * per);
     if (t_end < t_begin) t_end = t_begin;
   }
-  u32x4 kf[NC], vf[NC];
-  {
-    const T *kr = reinterpret_cast<const T *>(p.k0) + (long)(kvalid ? kp : 0) * kvs + gk * HD;
-    const T *vr = reinterpret_cast<const T *>(p.v0) + (long)(kvalid ? kp : 0) * kvs + gk * HD;
+  floatx4 dkT[KB][ND], dvT[KB][ND];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      kf[c] = kvalid ? ldg16(kr + c * KTILE + g * E) : u32x4{0u, 0u, 0u, 0u};
-      vf[c] = kvalid ? ldg16(vr + c * KTILE + g * E) : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  floatx4 dkT[ND], dvT[ND];
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-  for (int d = 0; d < ND; ++d) dkT[d] = dvT[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < ND; ++d) dkT[kb][d] = dvT[kb][d] = floatx4{0.f, 0.f, 0.f, 0.f};
   const u32x4 *tg = p.qt + (long)gk * Tq * NFR * 64;
   const float4 *ig = p.qinfo + (long)gk * Tq * 64;
   struct Stage {
@@ -808,46 +838,68 @@ __global__ __launch_bounds__(512) void k_attn_bwd_dkdv(AttnBwdParams p) {
     }
   };
   auto compute = [&](int bf) {
-    floatx4 sacc[4], pacc[4];
+    floatx4 sacc[KB][NQB], pacc[KB][NQB];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) sacc[qb] = pacc[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
+      for (int q = 0; q < NQB; ++q) sacc[kb][q] = pacc[kb][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // each fragment read from LDS feeds the products of all KB key blocks
+#pragma unroll
+    for (int q = 0; q < NQB; ++q)
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        sacc[qb] = Mma<T>::run(F[bf][(qb * NC + c) * 64 + lane], kf[c], sacc[qb]);
-        pacc[qb] = Mma<T>::run(F[bf][(4 * NC + qb * NC + c) * 64 + lane], vf[c], pacc[qb]);
+        const u32x4 qa = F[bf][((qb0 + q) * NC + c) * 64 + lane];
+        const u32x4 da = F[bf][(4 * NC + (qb0 + q) * NC + c) * 64 + lane];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          sacc[kb][q] = Mma<T>::run(qa, kf[kb][c], sacc[kb][q]);
+          pacc[kb][q] = Mma<T>::run(da, vf[kb][c], pacc[kb][q]);
+        }
       }
     // Every operand is loaded before use and masking is a select, so the
     // compiler emits no per-row branch with its own LDS round trip.
-    floatx4 lq[4], dq[4];
-    int aq[4][4];
+    floatx4 lq[NQB], dq[NQB];
+    int aq[NQB][4];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      lq[qb] = *reinterpret_cast<const floatx4 *>(&s_lse[bf][qb * 16 + 4 * g]);
-      dq[qb] = *reinterpret_cast<const floatx4 *>(&s_D[bf][qb * 16 + 4 * g]);
-      const int4 a4 = *reinterpret_cast<const int4 *>(&s_anc[bf][qb * 16 + 4 * g]);
-      aq[qb][0] = a4.x; aq[qb][1] = a4.y; aq[qb][2] = a4.z; aq[qb][3] = a4.w;
+    for (int q = 0; q < NQB; ++q) {
+      const int r = (qb0 + q) * 16 + 4 * g;
+      lq[q] = *reinterpret_cast<const floatx4 *>(&s_lse[bf][r]);
+      dq[q] = *reinterpret_cast<const floatx4 *>(&s_D[bf][r]);
+      const int4 a4 = *reinterpret_cast<const int4 *>(&s_anc[bf][r]);
+      aq[q][0] = a4.x; aq[q][1] = a4.y; aq[q][2] = a4.z; aq[q][3] = a4.w;
     }
-    float pv[4][4], ds[4][4];
+    u32x4 pf[KB][4], dsf[KB][4];  // first NKW used
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
+    for (int kb = 0; kb < KB; ++kb) {
+      float pv[NQB][4], ds[NQB][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = fast_exp2(fmaf(sacc[qb][r], p.scale_log2, -lq[qb][r]));
-        const float pr = kq <= aq[qb][r] ? e : 0.f;
-        pv[qb][r] = pr;
-        ds[qb][r] = pr * (pacc[qb][r] - dq[qb][r]);
+      for (int q = 0; q < NQB; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = fast_exp2(fmaf(sacc[kb][q][r], p.scale_log2, -lq[q][r]));
+          const float pr = kq[kb] <= aq[q][r] ? e : 0.f;
+          pv[q][r] = pr;
+          ds[q][r] = pr * (pacc[kb][q][r] - dq[q][r]);
+        }
+      if constexpr (PH == 1) {
+        pack_rows_b<T>(pv, pf[kb]);
+        pack_rows_b<T>(ds, dsf[kb]);
+      } else {
+        pack_rows_b2<T>(pv, reinterpret_cast<u32x4 (&)[NKW]>(pf[kb]));
+        pack_rows_b2<T>(ds, reinterpret_cast<u32x4 (&)[NKW]>(dsf[kb]));
       }
-    u32x4 pf[4], dsf[4];
-    pack_rows_b<T>(pv, pf);
-    pack_rows_b<T>(ds, dsf);
+    }
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc)
+    for (int k = 0; k < NKW; ++k)
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        dkT[d] = Mma<T>::run(F[bf][(8 * NC + d * NKC + kc) * 64 + lane], dsf[kc], dkT[d]);
-        dvT[d] = Mma<T>::run(F[bf][(8 * NC + NT + d * NKC + kc) * 64 + lane], pf[kc], dvT[d]);
+        const u32x4 qt = F[bf][(8 * NC + d * NKC + kc0 + k) * 64 + lane];
+        const u32x4 dt = F[bf][(8 * NC + NT + d * NKC + kc0 + k) * 64 + lane];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          dkT[kb][d] = Mma<T>::run(qt, dsf[kb][k], dkT[kb][d]);
+          dvT[kb][d] = Mma<T>::run(dt, pf[kb][k], dvT[kb][d]);
+        }
       }
   };
   // Query tile tq sits in buffer (tq - t_begin) & 1.  After multiplying a
@@ -889,13 +941,41 @@ __global__ __launch_bounds__(512) void k_attn_bwd_dkdv(AttnBwdParams p) {
       }
     }
   }
-  if (kp < p.n) {
-    // every share writes its slot (zeros when it saw no rows)
-    const long o = (((long)qs * p.n + kp) * p.nkv + gk) * HD;
+  if constexpr (PH == 2) {
+    // The second pair half hands its partial sums to the first through LDS
+    // (F is free: every wave has passed the loop's last barrier, or the loop
+    // did not run), which adds them after its own.
+    u32x4 *xch = &F[0][0] + (size_t)(w >> 1) * (KB * ND * 2 * 64);
+    __syncthreads();
+    if (ph == 1) {
 #pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      *reinterpret_cast<floatx4 *>(p.pk + o + d * 16 + 4 * g) = dkT[d];
-      *reinterpret_cast<floatx4 *>(p.pv + o + d * 16 + 4 * g) = dvT[d];
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          xch[((kb * ND + d) * 2 + 0) * 64 + lane] = __builtin_bit_cast(u32x4, dkT[kb][d]);
+          xch[((kb * ND + d) * 2 + 1) * 64 + lane] = __builtin_bit_cast(u32x4, dvT[kb][d]);
+        }
+    }
+    __syncthreads();
+    if (ph == 1) return;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        dkT[kb][d] += __builtin_bit_cast(floatx4, xch[((kb * ND + d) * 2 + 0) * 64 + lane]);
+        dvT[kb][d] += __builtin_bit_cast(floatx4, xch[((kb * ND + d) * 2 + 1) * 64 + lane]);
+      }
+  }
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    if (kp[kb] < p.n) {
+      // every share writes its slot (zeros when it saw no rows)
+      const long o = (((long)qs * p.n + kp[kb]) * p.nkv + gk) * HD;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        *reinterpret_cast<floatx4 *>(p.pk + o + d * 16 + 4 * g) = dkT[kb][d];
+        *reinterpret_cast<floatx4 *>(p.pv + o + d * 16 + 4 * g) = dvT[kb][d];
+      }
     }
   }
 }
@@ -1160,10 +1240,10 @@ hipError_t launch_attn_bwd(int dtype, const AttnBwdParams &p, hipStream_t s) {
     }
     const dim3 grid((unsigned)((p.n + 127) / 128), (unsigned)p.nkv, (unsigned)p.qsplit);
     if (dtype == 1) {
-      if (p.hd == 64) hipLaunchKernelGGL((k_attn_bwd_dkdv<bf16_t, 64>), grid, dim3(512), 0, s, p);
-      else hipLaunchKernelGGL((k_attn_bwd_dkdv<bf16_t, 128>), grid, dim3(512), 0, s, p);
+      if (p.hd == 64) hipLaunchKernelGGL((k_attn_bwd_dkdv<bf16_t, 64, 2>), grid, dim3(512), 0, s, p);
+      else hipLaunchKernelGGL((k_attn_bwd_dkdv<bf16_t, 128, 1>), grid, dim3(512), 0, s, p);  // two key blocks spill at hd 128
     } else {
-      hipLaunchKernelGGL((k_attn_bwd_dkdv<float, 64>), grid, dim3(512), 0, s, p);
+      hipLaunchKernelGGL((k_attn_bwd_dkdv<float, 64, 2>), grid, dim3(512), 0, s, p);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
