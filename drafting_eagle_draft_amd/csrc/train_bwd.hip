@@ -14,7 +14,7 @@
 #include <algorithm>
 #include <climits>
 
-#include "pe_internal.hpp"
+#include "pe_epilogue.hpp"
 
 namespace pe {
 
@@ -234,22 +234,41 @@ __global__ __launch_bounds__(256) void k_sum_acc(const float *x, long n, float *
 // RMSNorm backward: one wave per row; 64 rows per workgroup of 4 waves for
 // the gain partials (each wave walks 16 rows).
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int NCH>
 __global__ __launch_bounds__(256) void k_rms_bwd(const float *x, const float *gain, const float *dy,
                                                  const float *dres, int L, int H, float eps, float *dx, T *dx_t,
                                                  float *part) {
+  // NCH 16-byte chunks of a row per lane (H <= 256 NCH), loaded together so a
+  // wave has the whole row in flight at once; the gain stays in registers.
   extern __shared__ float gpart[];  // [4][H]
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, H4 = H >> 2;
   for (int c = lane; c < H; c += 64) gpart[w * H + c] = 0.f;
+  float4 *gp = reinterpret_cast<float4 *>(gpart + w * H);
+  float4 gv[NCH];
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int c4 = lane + 64 * k;
+    gv[k] = c4 < H4 ? reinterpret_cast<const float4 *>(gain)[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   for (int rr = 0; rr < 16; ++rr) {
     const int i = blockIdx.x * 64 + w * 16 + rr;
     if (i >= L) break;
-    const float *xr = x + (long)i * H, *dyr = dy + (long)i * H;
+    const float4 *xr = reinterpret_cast<const float4 *>(x + (long)i * H);
+    const float4 *dyr = reinterpret_cast<const float4 *>(dy + (long)i * H);
+    float4 xv[NCH], dv[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int c4 = lane + 64 * k;
+      const bool ok = c4 < H4;
+      xv[k] = ok ? xr[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      dv[k] = ok ? dyr[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     float ss = 0.f, sgx = 0.f;
-    for (int c = lane; c < H; c += 64) {
-      const float xv = xr[c];
-      ss += xv * xv;
-      sgx += gain[c] * dyr[c] * xv;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      ss += xv[k].x * xv[k].x + xv[k].y * xv[k].y + xv[k].z * xv[k].z + xv[k].w * xv[k].w;
+      sgx += gv[k].x * dv[k].x * xv[k].x + gv[k].y * dv[k].y * xv[k].y + gv[k].z * dv[k].z * xv[k].z +
+             gv[k].w * dv[k].w * xv[k].w;
     }
     for (int o = 32; o > 0; o >>= 1) {
       ss += __shfl_xor(ss, o, 64);
@@ -257,13 +276,28 @@ __global__ __launch_bounds__(256) void k_rms_bwd(const float *x, const float *ga
     }
     const float r = rsqrtf(ss / (float)H + eps);
     const float coef = r * r * r * sgx / (float)H;
-    for (int c = lane; c < H; c += 64) {
-      const float xv = xr[c], d = dyr[c];
-      float v = r * gain[c] * d - xv * coef;
-      if (dres) v += dres[(long)i * H + c];
-      dx[(long)i * H + c] = v;
-      if (dx_t) dx_t[(long)i * H + c] = from_f32<T>(v);
-      gpart[w * H + c] += d * xv * r;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int c4 = lane + 64 * k;
+      if (c4 >= H4) break;
+      const float4 g4 = gv[k], x4 = xv[k], d4 = dv[k];
+      float4 v = make_float4(r * g4.x * d4.x - x4.x * coef, r * g4.y * d4.y - x4.y * coef,
+                             r * g4.z * d4.z - x4.z * coef, r * g4.w * d4.w - x4.w * coef);
+      if (dres) {
+        const float4 e = reinterpret_cast<const float4 *>(dres + (long)i * H)[c4];
+        v.x += e.x; v.y += e.y; v.z += e.z; v.w += e.w;
+      }
+      reinterpret_cast<float4 *>(dx + (long)i * H)[c4] = v;
+      if (dx_t) {
+        if constexpr (sizeof(T) == 2)
+          *reinterpret_cast<uint2 *>(dx_t + (long)i * H + 4 * c4) =
+              make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+        else
+          *reinterpret_cast<float4 *>(dx_t + (long)i * H + 4 * c4) = v;
+      }
+      float4 a = gp[c4];
+      a.x += d4.x * x4.x * r; a.y += d4.y * x4.y * r; a.z += d4.z * x4.z * r; a.w += d4.w * x4.w * r;
+      gp[c4] = a;
     }
   }
   __syncthreads();
@@ -302,51 +336,87 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_rope_bwd(const float *dq, const float *dk, const float *dv, const int *anc,
                                                   const int *dep, const double *inv_freq, int L, int nq, int nkv,
                                                   int hd, T *out) {
+  // Thread q of a row: four rotation pairs (j .. j+3, j+half ..) of a q or k
+  // head, or four v elements.  The rotation is the forward's (rope_cs),
+  // transposed.  Rows: blockIdx.y, then in steps of gridDim.y.
   const int half = hd >> 1, W = (nq + 2 * nkv) * hd;
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  const long npair = (long)L * (nq + nkv) * half;
-  if (idx < npair) {
-    const long i = idx / ((nq + nkv) * half);
-    const int rem = (int)(idx - i * (nq + nkv) * half);
-    const int hh = rem / half, j = rem - hh * half;
-    const float *src = hh < nq ? dq + (i * nq + hh) * hd : dk + (i * nkv + (hh - nq)) * hd;
-    const double ang = (double)(anc[i] + dep[i]) * inv_freq[j];
-    const float c = (float)cos(ang), sn = (float)sin(ang);
-    const float lo = src[j], hi = src[j + half];
-    T *o = out + i * W + hh * hd;
-    o[j] = from_f32<T>(lo * c + hi * sn);
-    o[j + half] = from_f32<T>(hi * c - lo * sn);
-  } else if (idx < npair + (long)L * nkv * hd) {
-    const long e = idx - npair;
-    const long i = e / (nkv * hd);
-    const int r = (int)(e - i * nkv * hd);
-    out[i * W + (nq + nkv) * hd + r] = from_f32<T>(dv[e]);
+  const int QH = half / 4, QR = (nq + nkv) * QH, QV = nkv * hd / 4;
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= QR + QV) return;
+  for (int i = blockIdx.y; i < L; i += gridDim.y) {
+    T *orow = out + (long)i * W;
+    if (q < QR) {
+      const int hh = q / QH, j = (q - hh * QH) * 4;
+      const float *src = hh < nq ? dq + ((long)i * nq + hh) * hd : dk + ((long)i * nkv + (hh - nq)) * hd;
+      const float4 lo = *reinterpret_cast<const float4 *>(src + j);
+      const float4 hi = *reinterpret_cast<const float4 *>(src + j + half);
+      const float l4[4] = {lo.x, lo.y, lo.z, lo.w}, h4[4] = {hi.x, hi.y, hi.z, hi.w};
+      const int pos = anc[i] + dep[i];
+      float ol[4], oh[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float c, sn;
+        rope_cs(pos, inv_freq[j + e], c, sn);
+        ol[e] = l4[e] * c + h4[e] * sn;
+        oh[e] = h4[e] * c - l4[e] * sn;
+      }
+      store4<T>(orow + hh * hd + j, ol);
+      store4<T>(orow + hh * hd + j + half, oh);
+    } else {
+      const int r = (q - QR) * 4;
+      const float4 v = *reinterpret_cast<const float4 *>(dv + (long)i * nkv * hd + r);
+      const float v4[4] = {v.x, v.y, v.z, v.w};
+      store4<T>(orow + (nq + nkv) * hd + r, v4);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Input-fusion backward (64 rows per workgroup for the deeper-row partials).
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int NCH>
 __global__ __launch_bounds__(256) void k_fuse_bwd(const float *dx0, const int *anc, const int *dep, int L, int n,
                                                   int H, T *d_ntp, float *embed_rows, float *part) {
+  // NCH 16-byte chunks of a row per lane (H <= 256 NCH), loaded together.
   extern __shared__ float gpart[];  // [4][H]
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, H4 = H >> 2;
   for (int c = lane; c < H; c += 64) gpart[w * H + c] = 0.f;
+  float4 *gp = reinterpret_cast<float4 *>(gpart + w * H);
   for (int rr = 0; rr < 16; ++rr) {
     const int i = blockIdx.x * 64 + w * 16 + rr;
     if (i >= L) break;
     const int d = dep[i], pos = anc[i] + d;
-    const float *src = dx0 + (long)i * H;
+    if (d == 0 && (pos < 0 || pos >= n)) continue;
+    const float4 *src = reinterpret_cast<const float4 *>(dx0 + (long)i * H);
+    float4 v[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int c4 = lane + 64 * k;
+      v[k] = c4 < H4 ? src[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     if (d == 0) {
-      if (pos < 0 || pos >= n) continue;
-      for (int c = lane; c < H; c += 64) {
-        const float v = src[c];
-        d_ntp[(long)pos * H + c] = from_f32<T>(v);
-        if (embed_rows) embed_rows[(long)pos * H + c] += v;
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) {
+        const int c4 = lane + 64 * k;
+        if (c4 >= H4) break;
+        const float v4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+        store4<T>(d_ntp + (long)pos * H + 4 * c4, v4);
+        if (embed_rows) {
+          float4 *e = reinterpret_cast<float4 *>(embed_rows + (long)pos * H) + c4;
+          float4 a = *e;
+          a.x += v[k].x; a.y += v[k].y; a.z += v[k].z; a.w += v[k].w;
+          *e = a;
+        }
       }
     } else {
-      for (int c = lane; c < H; c += 64) gpart[w * H + c] += src[c];
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) {
+        const int c4 = lane + 64 * k;
+        if (c4 >= H4) break;
+        float4 a = gp[c4];
+        a.x += v[k].x; a.y += v[k].y; a.z += v[k].z; a.w += v[k].w;
+        gp[c4] = a;
+      }
     }
   }
   __syncthreads();
@@ -394,21 +464,40 @@ __global__ __launch_bounds__(256) void k_matvec_acc(const u32x4 *wt, int NT, int
 template <typename T>
 __global__ __launch_bounds__(256) void k_attn_bwd_pre(const float *dout, const T *out, int L, int nq, int hd,
                                                       T *dout_t, float *D) {
-  // one wave per (row, head)
-  const long wid = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (wid >= (long)L * nq) return;
-  const long i = wid / nq;
-  const int h = (int)(wid - i * nq);
-  const int KTo = nq * hd / Frag<T>::KTILE;
+  // One thread per E dimensions of a (row, head): the output's 16-byte
+  // fragment chunk, 4 E bytes of dO; the hd / E threads of a (row, head)
+  // are adjacent lanes and sum their parts with shuffles.
+  constexpr int E = Frag<T>::E;
+  const long t = (long)blockIdx.x * 256 + threadIdx.x;
+  const int per = hd / E;  // threads per (row, head): a power of two <= 64
+  const long wid = t / per;
+  const bool ok = wid < (long)L * nq;
+  const int c = (int)(t - wid * per);
   float a = 0.f;
-  for (int d = lane; d < hd; d += 64) {
-    const float g = dout[(i * nq + h) * hd + d];
-    a += g * to_f32<T>(out[frag_off<T>((int)i, h * hd + d, KTo)]);
-    dout_t[(i * nq + h) * hd + d] = from_f32<T>(g);
+  if (ok) {
+    const long i = wid / nq;
+    const int h = (int)(wid - i * nq);
+    const int KTo = nq * hd / Frag<T>::KTILE;
+    const float *g = dout + wid * hd + c * E;
+    T o[E], gt[E];
+    const u32x4 ov = *reinterpret_cast<const u32x4 *>(out + frag_off<T>((int)i, h * hd + c * E, KTo));
+    __builtin_memcpy(o, &ov, 16);
+#pragma unroll
+    for (int q = 0; q < E / 4; ++q) {
+      const float4 g4 = reinterpret_cast<const float4 *>(g)[q];
+      const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a += gv[e] * to_f32<T>(o[4 * q + e]);
+        gt[4 * q + e] = from_f32<T>(gv[e]);
+      }
+    }
+    u32x4 gv;
+    __builtin_memcpy(&gv, gt, 16);
+    *reinterpret_cast<u32x4 *>(dout_t + wid * hd + c * E) = gv;
   }
-  for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, 64);
-  if (lane == 0) D[wid] = a;
+  for (int o = 1; o < per; o <<= 1) a += __shfl_xor(a, o, 64);
+  if (ok && c == 0) D[wid] = a;
 }
 
 // ---------------------------------------------------------------------------
@@ -1107,13 +1196,25 @@ hipError_t launch_rms_bwd(int dtype, const float *x, const float *gain, const fl
                           int L, int H, float eps, float *dx, void *dx_t, float *part, hipStream_t s) {
   if (L <= 0) return hipSuccess;
   const size_t lds = (size_t)4 * H * sizeof(float);
-  if (lds > 64 * 1024) return hipErrorInvalidValue;
-  if (dtype == 1)
-    hipLaunchKernelGGL(k_rms_bwd<bf16_t>, dim3(nblocks(L, 64)), dim3(256), lds, s, x, gain, dy, dres, L, H, eps,
-                       dx, reinterpret_cast<bf16_t *>(dx_t), part);
-  else
-    hipLaunchKernelGGL(k_rms_bwd<float>, dim3(nblocks(L, 64)), dim3(256), lds, s, x, gain, dy, dres, L, H, eps, dx,
+  if (lds > 64 * 1024 || H % 4) return hipErrorInvalidValue;
+  const dim3 grid(nblocks(L, 64));
+#define PE_RMS_BWD(NCH)                                                                                      \
+  if (dtype == 1)                                                                                             \
+    hipLaunchKernelGGL((k_rms_bwd<bf16_t, NCH>), grid, dim3(256), lds, s, x, gain, dy, dres, L, H, eps, dx,    \
+                       reinterpret_cast<bf16_t *>(dx_t), part);                                               \
+  else                                                                                                        \
+    hipLaunchKernelGGL((k_rms_bwd<float, NCH>), grid, dim3(256), lds, s, x, gain, dy, dres, L, H, eps, dx,     \
                        reinterpret_cast<float *>(dx_t), part);
+  if (H <= 1024) {
+    PE_RMS_BWD(4)
+  } else if (H <= 2048) {
+    PE_RMS_BWD(8)
+  } else if (H <= 3072) {
+    PE_RMS_BWD(12)
+  } else {
+    PE_RMS_BWD(16)
+  }
+#undef PE_RMS_BWD
   return hipGetLastError();
 }
 
@@ -1136,13 +1237,15 @@ hipError_t launch_swiglu_bwd(int dtype, const float *dh, const void *gu, int L, 
 hipError_t launch_rope_bwd(int dtype, const float *dq, const float *dk, const float *dv, const int *anc,
                            const int *dep, const double *inv_freq, int L, int nq, int nkv, int hd, void *out,
                            hipStream_t s) {
-  const long total = (long)L * (nq + nkv) * (hd / 2) + (long)L * nkv * hd;
-  const unsigned b = nblocks(total, 256);
+  if (L <= 0) return hipSuccess;
+  if (hd % 8) return hipErrorInvalidValue;
+  const int per_row = (nq + nkv) * (hd / 8) + nkv * hd / 4;
+  const dim3 b(nblocks(per_row, 256), (unsigned)std::min(L, 65535));
   if (dtype == 1)
-    hipLaunchKernelGGL(k_rope_bwd<bf16_t>, dim3(b), dim3(256), 0, s, dq, dk, dv, anc, dep, inv_freq, L, nq, nkv, hd,
+    hipLaunchKernelGGL(k_rope_bwd<bf16_t>, b, dim3(256), 0, s, dq, dk, dv, anc, dep, inv_freq, L, nq, nkv, hd,
                        reinterpret_cast<bf16_t *>(out));
   else
-    hipLaunchKernelGGL(k_rope_bwd<float>, dim3(b), dim3(256), 0, s, dq, dk, dv, anc, dep, inv_freq, L, nq, nkv, hd,
+    hipLaunchKernelGGL(k_rope_bwd<float>, b, dim3(256), 0, s, dq, dk, dv, anc, dep, inv_freq, L, nq, nkv, hd,
                        reinterpret_cast<float *>(out));
   return hipGetLastError();
 }
@@ -1151,13 +1254,25 @@ hipError_t launch_fuse_bwd(int dtype, const float *dx0, const int *anc, const in
                            void *d_ntp, float *embed_rows, float *part, hipStream_t s) {
   if (L <= 0) return hipSuccess;
   const size_t lds = (size_t)4 * H * sizeof(float);
-  if (lds > 64 * 1024) return hipErrorInvalidValue;
-  if (dtype == 1)
-    hipLaunchKernelGGL(k_fuse_bwd<bf16_t>, dim3(nblocks(L, 64)), dim3(256), lds, s, dx0, anc, dep, L, n, H,
-                       reinterpret_cast<bf16_t *>(d_ntp), embed_rows, part);
-  else
-    hipLaunchKernelGGL(k_fuse_bwd<float>, dim3(nblocks(L, 64)), dim3(256), lds, s, dx0, anc, dep, L, n, H,
+  if (lds > 64 * 1024 || H % 4) return hipErrorInvalidValue;
+  const dim3 grid(nblocks(L, 64));
+#define PE_FUSE_BWD(NCH)                                                                                     \
+  if (dtype == 1)                                                                                             \
+    hipLaunchKernelGGL((k_fuse_bwd<bf16_t, NCH>), grid, dim3(256), lds, s, dx0, anc, dep, L, n, H,            \
+                       reinterpret_cast<bf16_t *>(d_ntp), embed_rows, part);                                  \
+  else                                                                                                        \
+    hipLaunchKernelGGL((k_fuse_bwd<float, NCH>), grid, dim3(256), lds, s, dx0, anc, dep, L, n, H,             \
                        reinterpret_cast<float *>(d_ntp), embed_rows, part);
+  if (H <= 1024) {
+    PE_FUSE_BWD(4)
+  } else if (H <= 2048) {
+    PE_FUSE_BWD(8)
+  } else if (H <= 3072) {
+    PE_FUSE_BWD(12)
+  } else {
+    PE_FUSE_BWD(16)
+  }
+#undef PE_FUSE_BWD
   return hipGetLastError();
 }
 
@@ -1183,7 +1298,9 @@ hipError_t launch_matvec_acc(int dtype, const u32x4 *wt, int NT, int KT, int N, 
 
 hipError_t launch_attn_bwd_pre(int dtype, const float *dout, const void *out, int L, int nq, int hd,
                                void *dout_t, float *D, hipStream_t s) {
-  const unsigned b = nblocks((long)L * nq, 4);
+  const int E = dtype == 1 ? 8 : 4;
+  if (hd % E || hd / E > 64 || ((hd / E) & (hd / E - 1))) return hipErrorInvalidValue;
+  const unsigned b = nblocks((long)L * nq * (hd / E), 256);
   if (dtype == 1)
     hipLaunchKernelGGL(k_attn_bwd_pre<bf16_t>, dim3(b), dim3(256), 0, s, dout, reinterpret_cast<const bf16_t *>(out),
                        L, nq, hd, reinterpret_cast<bf16_t *>(dout_t), D);
