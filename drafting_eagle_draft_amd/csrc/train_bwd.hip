@@ -305,12 +305,21 @@ __global__ __launch_bounds__(256) void k_rms_bwd(const float *x, const float *ga
     part[(long)blockIdx.x * H + c] = gpart[c] + gpart[H + c] + gpart[2 * H + c] + gpart[3 * H + c];
 }
 
+// out[c] += sum over b of part[b][c]: 64 columns per workgroup; wave w sums
+// blocks 8w .. 8w + 7, then every 32nd block on, into eight independent
+// accumulators (eight loads in flight); the sums combine in a fixed order.
 __global__ __launch_bounds__(256) void k_colsum_acc(const float *part, int nblk, int H, float *out) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= H) return;
-  float a = 0.f;
-  for (int b = 0; b < nblk; ++b) a += part[(long)b * H + c];
-  out[c] += a;
+  __shared__ float red[4][64];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, c = blockIdx.x * 64 + lane;
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (c < H)
+    for (int b0 = 8 * w; b0 < nblk; b0 += 32)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (b0 + k < nblk) a[k] += part[(long)(b0 + k) * H + c];
+  red[w][lane] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+  __syncthreads();
+  if (w == 0 && c < H) out[c] += (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
 }
 
 // ---------------------------------------------------------------------------
@@ -791,48 +800,56 @@ template <typename T, int HD>
 __global__ __launch_bounds__(256) void k_pair_tiles(const T *q, const T *dout, const float *lse, const float *D,
                                                     const int *anc, int L, int nq, int nkv, int G, u32x4 *tiles,
                                                     float4 *info) {
+  // One workgroup per tile (blockIdx.x = gk * Tq + t): the tile's Q and dO
+  // rows are read with 16-byte loads (a row's G heads of kv head gk are
+  // contiguous) into LDS, and every fragment lane is then assembled there.
   constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE, NC = HD / KTILE, ND = HD / 16;
   constexpr int NKC = sizeof(T) == 2 ? 2 : 4, NT = ND * NKC, NFR = 8 * NC + 2 * NT;
+  constexpr int RS = HD + E;  // LDS row pitch (elements)
+  __shared__ __attribute__((aligned(16))) T Qs[64 * RS];
+  __shared__ __attribute__((aligned(16))) T Ds[64 * RS];
   const int QC = 64 / G, Tq = (L + QC - 1) / QC;
-  const long total = (long)nkv * Tq * NFR * 64;
-  for (long idx = (long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long)gridDim.x * 256) {
-    const int lane = (int)(idx & 63);
-    const long f = idx >> 6;
-    const int fr = (int)(f % NFR);
-    const long tile = f / NFR;
-    const int t = (int)(tile % Tq), gk = (int)(tile / Tq);
+  const long tile = blockIdx.x;
+  const int t = (int)(tile % Tq), gk = (int)(tile / Tq);
+  constexpr int CPR = HD / E;  // 16-byte chunks per pair row
+  for (int idx = threadIdx.x; idx < 64 * CPR; idx += 256) {
+    const int qi = idx / CPR, c = idx - qi * CPR;
+    const int row = t * QC + qi / G;
+    const bool ok = qi < QC * G && row < L;
+    const long off = ((long)row * nq + gk * G + qi % G) * HD + c * E;
+    *reinterpret_cast<u32x4 *>(&Qs[qi * RS + c * E]) = ok ? ldg16(q + off) : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4 *>(&Ds[qi * RS + c * E]) = ok ? ldg16(dout + off) : u32x4{0u, 0u, 0u, 0u};
+  }
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x, row = t * QC + lane / G;
+    const bool ok = lane < QC * G && row < L;
+    const long pi = (long)row * nq + gk * G + lane % G;
+    info[tile * 64 + lane] = ok ? make_float4(lse[pi], D[pi], __int_as_float(anc[row]), 0.f)
+                                : make_float4(0.f, 0.f, __int_as_float(-1), 0.f);
+  }
+  __syncthreads();
+  u32x4 *dst = tiles + tile * NFR * 64;
+  for (int idx = threadIdx.x; idx < NFR * 64; idx += 256) {
+    const int lane = idx & 63, fr = idx >> 6;
     const int c16 = lane & 15, g = lane >> 4;
-    T a[E];
+    u32x4 v;
     if (fr < 8 * NC) {
-      const T *src = fr < 4 * NC ? q : dout;
+      const T *src = fr < 4 * NC ? Qs : Ds;
       const int ff = fr % (4 * NC), qb = ff / NC, c = ff - qb * NC;
-      const int qi = qb * 16 + c16, row = t * QC + qi / G;
-      const bool ok = qi < QC * G && row < L;
-      const long off = ((long)row * nq + gk * G + qi % G) * HD + c * KTILE + g * E;
-#pragma unroll
-      for (int e = 0; e < E; ++e) a[e] = ok ? src[off + e] : T(0);
+      v = *reinterpret_cast<const u32x4 *>(&src[(qb * 16 + c16) * RS + c * KTILE + g * E]);
     } else {
-      const T *src = fr < 8 * NC + NT ? q : dout;
+      const T *src = fr < 8 * NC + NT ? Qs : Ds;
       const int ff = (fr - 8 * NC) % NT, d = ff / NKC, kc = ff - d * NKC;
       const int dim = d * 16 + c16;
+      T a[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int qi = sizeof(T) == 2 ? 32 * kc + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4) : 16 * kc + 4 * g + e;
-        const int row = t * QC + qi / G;
-        const bool ok = qi < QC * G && row < L;
-        a[e] = ok ? src[((long)row * nq + gk * G + qi % G) * HD + dim] : T(0);
+        a[e] = src[qi * RS + dim];
       }
+      __builtin_memcpy(&v, a, 16);
     }
-    u32x4 v;
-    __builtin_memcpy(&v, a, 16);
-    tiles[idx] = v;
-    if (fr == 0) {
-      const int row = t * QC + lane / G;
-      const bool ok = lane < QC * G && row < L;
-      const long pi = (long)row * nq + gk * G + lane % G;
-      info[tile * 64 + lane] = ok ? make_float4(lse[pi], D[pi], __int_as_float(anc[row]), 0.f)
-                                  : make_float4(0.f, 0.f, __int_as_float(-1), 0.f);
-    }
+    dst[idx] = v;
   }
 }
 
@@ -1219,7 +1236,7 @@ hipError_t launch_rms_bwd(int dtype, const float *x, const float *gain, const fl
 }
 
 hipError_t launch_colsum_acc(const float *part, int nblk, int H, float *out, hipStream_t s) {
-  hipLaunchKernelGGL(k_colsum_acc, dim3(nblocks(H, 256)), dim3(256), 0, s, part, nblk, H, out);
+  hipLaunchKernelGGL(k_colsum_acc, dim3(nblocks(H, 64)), dim3(256), 0, s, part, nblk, H, out);
   return hipGetLastError();
 }
 
@@ -1338,9 +1355,7 @@ hipError_t launch_attn_bwd(int dtype, const AttnBwdParams &p, hipStream_t s) {
   if (G > 64 || p.qsplit < 1) return hipErrorInvalidValue;
   {
     const int QC = 64 / G, Tq = (p.L + QC - 1) / QC;
-    const int kt = dtype == 1 ? 32 : 16, NC = p.hd / kt, ND = p.hd / 16, NKC = dtype == 1 ? 2 : 4;
-    const long frags = (long)p.nkv * Tq * (8 * NC + 2 * ND * NKC) * 64;
-    const unsigned b = (unsigned)std::min<long>(65536, (frags + 255) / 256);
+    const unsigned b = (unsigned)((long)p.nkv * Tq);  // one workgroup per query tile
     if (dtype == 1) {
       if (p.hd == 64)
         hipLaunchKernelGGL((k_pair_tiles<bf16_t, 64>), dim3(b), dim3(256), 0, s, reinterpret_cast<const bf16_t *>(p.q),
