@@ -1043,7 +1043,6 @@ pe_status enqueue_train(const pe_model *m, const pe_mask *mask, int32_t N, int32
                           sv ? sv->layer.empty() ? sv->xN : sv->layer[0].x : xres, s);
     if (e != hipSuccess) return hip_fail(e, "fusion launch");
   }
-  const size_t xbytes = (size_t)L * H * sizeof(float);
   for (int l = 0; l < N; ++l) {
     const LayerT &Lw = m->layers[l];
     StepLayer B;
@@ -1075,12 +1074,10 @@ pe_status enqueue_train(const pe_model *m, const pe_mask *mask, int32_t N, int32
       a.lse = B.lse;
       if ((e = launch_attn_train(dt, a, s)) != hipSuccess) return hip_fail(e, "attention launch");
     }
-    if (B.xm != B.x && (e = hipMemcpyAsync(B.xm, B.x, xbytes, hipMemcpyDeviceToDevice, s)) != hipSuccess)
-      return hip_fail(e, "residual copy");
     {
       TileGemmParams p{};
       p.A = B.attn; p.lda = (long)nq * hd; p.M = L; p.a_tiled = 1;
-      p.C = B.xm; p.ldc = H;
+      p.C = B.xm; p.Cin = B.x; p.ldc = H;  // xm = x + attn W_o (in place when they coincide)
       if ((st = gemm(Lw.o, BEPI_ACCUM, p)) != PE_OK) return st;
     }
     if ((e = launch_rmsnorm_tiled(dt, B.xm, Lw.mlp_norm, L, H, c.rms_eps, B.u2, s)) != hipSuccess)
@@ -1091,12 +1088,10 @@ pe_status enqueue_train(const pe_model *m, const pe_mask *mask, int32_t N, int32
       p.h = B.h; p.I = c.intermediate; p.gu = B.gu;
       if ((st = gemm(Lw.gateup, B.gu ? BEPI_SWIGLU_SAVE : BEPI_SWIGLU, p)) != PE_OK) return st;
     }
-    if (xnext != B.xm && (e = hipMemcpyAsync(xnext, B.xm, xbytes, hipMemcpyDeviceToDevice, s)) != hipSuccess)
-      return hip_fail(e, "residual copy");
     {
       TileGemmParams p{};
       p.A = B.h; p.lda = c.intermediate; p.M = L; p.a_tiled = 1;
-      p.C = xnext; p.ldc = H;
+      p.C = xnext; p.Cin = B.xm; p.ldc = H;  // x' = xm + h W_down
       if ((st = gemm(Lw.down, BEPI_ACCUM, p)) != PE_OK) return st;
     }
   }

@@ -358,7 +358,10 @@ void k_gemm_tile(TileGemmParams p) {
               *reinterpret_cast<floatx4 *>(C + (long)m * p.ldc + n) = acc[i][j];
             } else if constexpr (EPI == BEPI_ACCUM) {
               floatx4 *dst = reinterpret_cast<floatx4 *>(C + (long)m * p.ldc + n);
-              *dst = tks == 0 ? *dst + acc[i][j] : acc[i][j];
+              if (tks == 0)
+                *dst = *reinterpret_cast<const floatx4 *>((p.Cin ? p.Cin : p.C) + (long)m * p.ldc + n) + acc[i][j];
+              else
+                *dst = acc[i][j];
             } else if constexpr (EPI == BEPI_SWIGLU) {
               epi_tile_swiglu<T, false>(p, m, s, g, acc[i][j]);
             } else if constexpr (EPI == BEPI_SWIGLU_SAVE) {

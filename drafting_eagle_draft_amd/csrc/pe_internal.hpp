@@ -173,6 +173,8 @@ struct TileGemmParams {
   int a_tiled;          // A in the fragment-tile layout: [ceil(M/16)][KT] 1 KB fragments
   float *C;
   long ldc;
+  // ACCUM: the addend's rows (same layout as C); C = Cin + A W^T.  Null: C itself.
+  const float *Cin;
   // K split (STORE and ACCUM; 1 = none): the k tiles in ksplit chunks of
   // ceil(KT / ksplit); chunk 0 writes (STORE) or adds to (ACCUM) C, chunk
   // c > 0 stores the same layout at kpart + (c - 1) * kpart_stride, added to
