@@ -71,28 +71,37 @@ __global__ void k_argmax_rows(const unsigned long long *keys, int M, int *out, c
   out[r] = (int)(0xFFFFFFFFu - (unsigned)(keys[m] & 0xFFFFFFFFull));
 }
 
-// y = W x for one vector: one wave per 16-row weight strip; lane (c16, g)
-// holds row c16 and k-slots g*E.. of each fragment, partial sums are folded
-// over the four lane groups.
+// y = W x for one vector: one workgroup per 16-row weight strip; wave w
+// takes k tiles 4w .. 4w + 3, then every 16th on, with four loads in flight;
+// lane (c16, g) holds row c16 and k-slots g*E.. of each fragment.  The
+// partial sums fold over the waves (in order) and the four lane groups.
 template <typename T>
 __global__ __launch_bounds__(256) void k_matvec_tiled(const u32x4 *wt, int NT, int KT, int N, const T *x,
                                                       int K, float *y) {
   constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE;
+  __shared__ float red[4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c16 = lane & 15, g = lane >> 4;
-  const int s = blockIdx.x * 4 + w;
-  if (s >= NT) return;
-  float acc = 0.f;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int k = kt * KTILE + g * E;
-    if (k >= K) continue;
-    const u32x4 wv = wt[((long)s * KT + kt) * 64 + lane];
-    const u32x4 xv = ldg16(x + k);
-    T ww[E], xx[E];
-    __builtin_memcpy(ww, &wv, 16);
-    __builtin_memcpy(xx, &xv, 16);
+  const int s = blockIdx.x;
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int kt0 = 4 * w; kt0 < KT; kt0 += 16) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc += to_f32<T>(ww[e]) * to_f32<T>(xx[e]);
+    for (int u = 0; u < 4; ++u) {
+      const int kt = kt0 + u, k = kt * KTILE + g * E;
+      if (kt < KT && k < K) {
+        const u32x4 wv = wt[((long)s * KT + kt) * 64 + lane];
+        const u32x4 xv = ldg16(x + k);
+        T ww[E], xx[E];
+        __builtin_memcpy(ww, &wv, 16);
+        __builtin_memcpy(xx, &xv, 16);
+#pragma unroll
+        for (int e = 0; e < E; ++e) a[u] += to_f32<T>(ww[e]) * to_f32<T>(xx[e]);
+      }
+    }
   }
+  red[w][lane] = (a[0] + a[1]) + (a[2] + a[3]);
+  __syncthreads();
+  if (w != 0) return;
+  float acc = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
   acc += shfl_xor_f(acc, 16);
   acc += shfl_xor_f(acc, 32);
   const int n = s * 16 + c16;
@@ -535,7 +544,7 @@ hipError_t launch_argmax_rows(const unsigned long long *keys, int M, int *out, c
 
 hipError_t launch_matvec_tiled(int dtype, const u32x4 *wt, int NT, int KT, int N, const void *x, int K,
                                float *y, hipStream_t s) {
-  const dim3 grid((unsigned)((NT + 3) / 4));
+  const dim3 grid((unsigned)NT);
   if (dtype == 1)
     hipLaunchKernelGGL(k_matvec_tiled<bf16_t>, grid, dim3(256), 0, s, wt, NT, KT, N,
                        reinterpret_cast<const bf16_t *>(x), K, y);

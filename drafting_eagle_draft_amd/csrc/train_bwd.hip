@@ -445,21 +445,31 @@ __global__ __launch_bounds__(256) void k_outer_acc(const float *a, const T *b, i
 template <typename T>
 __global__ __launch_bounds__(256) void k_matvec_acc(const u32x4 *wt, int NT, int KT, int N, const float *x, int K,
                                                     float *y) {
+  // One workgroup per 16-row strip; wave w takes k tiles 4w .. 4w + 3, then
+  // every 16th on, four loads in flight; sums fold over waves in order.
   constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE;
+  __shared__ float red[4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c16 = lane & 15, g = lane >> 4;
-  const int s = blockIdx.x * 4 + w;
-  if (s >= NT) return;
-  float acc = 0.f;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int k = kt * KTILE + g * E;
-    if (k >= K) continue;
-    const u32x4 wv = wt[((long)s * KT + kt) * 64 + lane];
-    T ww[E];
-    __builtin_memcpy(ww, &wv, 16);
+  const int s = blockIdx.x;
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int kt0 = 4 * w; kt0 < KT; kt0 += 16) {
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (k + e < K) acc += to_f32<T>(ww[e]) * x[k + e];
+    for (int u = 0; u < 4; ++u) {
+      const int kt = kt0 + u, k = kt * KTILE + g * E;
+      if (kt < KT && k < K) {
+        const u32x4 wv = wt[((long)s * KT + kt) * 64 + lane];
+        T ww[E];
+        __builtin_memcpy(ww, &wv, 16);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (k + e < K) a[u] += to_f32<T>(ww[e]) * x[k + e];
+      }
+    }
   }
+  red[w][lane] = (a[0] + a[1]) + (a[2] + a[3]);
+  __syncthreads();
+  if (w != 0) return;
+  float acc = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
   acc += shfl_xor_f(acc, 16);
   acc += shfl_xor_f(acc, 32);
   const int nrow = s * 16 + c16;
@@ -1305,7 +1315,7 @@ hipError_t launch_outer_acc(int dtype, const float *a, const void *b, int R, int
 
 hipError_t launch_matvec_acc(int dtype, const u32x4 *wt, int NT, int KT, int N, const float *x, int K, float *y,
                              hipStream_t s) {
-  const dim3 grid((unsigned)((NT + 3) / 4));
+  const dim3 grid((unsigned)NT);
   if (dtype == 1)
     hipLaunchKernelGGL(k_matvec_acc<bf16_t>, grid, dim3(256), 0, s, wt, NT, KT, N, x, K, y);
   else
