@@ -1113,8 +1113,10 @@ pe_status enqueue_train(const pe_model *m, const pe_mask *mask, int32_t N, int32
     p.logits = sv ? reinterpret_cast<char *>(logits_out) + (size_t)r0 * c.vocab * m->esz : logits_out;
     p.ldc = c.vocab;
     p.out_rows = out_rows; p.row_skip = n_lead - r0; p.out_M = L_out;
-    p.keys = reinterpret_cast<unsigned long long *>(ws + W.keys);
-    if ((e = launch_zero(p.keys, (size_t)p.M * 8, s)) != hipSuccess) return hip_fail(e, "key reset launch");
+    if (argmax_out) {  // the training step keeps only the logits
+      p.keys = reinterpret_cast<unsigned long long *>(ws + W.keys);
+      if ((e = launch_zero(p.keys, (size_t)p.M * 8, s)) != hipSuccess) return hip_fail(e, "key reset launch");
+    }
     const bool prof = m->prof && m->nrec < (int)m->ev0.size();
     if (prof) (void)hipEventRecord(m->ev0[m->nrec], s);
     if ((st = gemm(m->lm, out_rows ? BEPI_LMHEAD_MAP : BEPI_LMHEAD, p)) != PE_OK) return st;

@@ -276,9 +276,11 @@ void k_gemm_tile(TileGemmParams p) {
         const int r = m < p.row_skip ? -1 : p.out_rows[m - p.row_skip];
         return r < p.out_M ? r : -1;
       };
-      // Argmax keys of the wave's 128 rows over its 64 columns.
+      // Argmax keys of the wave's 128 rows over its 64 columns (skipped when
+      // the caller keeps only the logits: keys null).
+      const bool with_keys = p.keys != nullptr;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 8 && with_keys; ++j) {
         const int m = m0 + (wm * 8 + j) * 16 + c16;
         unsigned long long key = 0ull;
 #pragma unroll
@@ -338,7 +340,7 @@ void k_gemm_tile(TileGemmParams p) {
         }
       }
       __syncthreads();
-      if (tid < 256) {
+      if (tid < 256 && with_keys) {
         const int m = m0 + tid;
         const unsigned long long k4 =
             umax64(umax64(kbuf[0][tid], kbuf[1][tid]), umax64(kbuf[2][tid], kbuf[3][tid]));

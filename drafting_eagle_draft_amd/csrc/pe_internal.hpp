@@ -183,7 +183,7 @@ struct TileGemmParams {
   float *kpart;
   long kpart_stride;
   void *logits;
-  unsigned long long *keys;  // [M], zeroed before the launch; atomically maxed
+  unsigned long long *keys;  // [M], zeroed before the launch; atomically maxed (LM head; null: no keys)
   // LM head output rows: row m goes to logits row out_rows[m - row_skip]
   // (rows m < row_skip, and targets outside [0, out_M), are not written);
   // without out_rows, row m goes to row m.
