@@ -57,49 +57,6 @@ __device__ __forceinline__ void epi_tile_swiglu(const TileGemmParams &p, int m, 
   }
 }
 
-// q|k|v tile rows n..n+3 of row m.  For q and k heads, r = 2t + hi holds
-// dimension 8j + 2g + t (hi = 0) or that dimension + hd/2 (hi = 1), the two
-// halves that one rotation pairs; v heads keep their order.  Row m sits at
-// RoPE position anchor + depth; depth-0 rows also go to k0/v0 by position.
-template <typename T>
-__device__ __forceinline__ void epi_tile_qkv(const TileGemmParams &p, int m, int n, floatx4 v) {
-  const int hd = p.hd, half = hd >> 1;
-  const int hh = n / hd, within = n - hh * hd;
-  const int d = p.dep[m], pos = p.anc[m] + d;
-  const bool depth0 = d == 0 && pos >= 0 && pos < p.n;
-  if (hh < p.nq + p.nkv) {
-    const int dim = 8 * (within >> 4) + (within & 15) / 2;
-    float lo[2], hi[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float c, sn;
-      rope_cs(pos, p.inv_freq[dim + t], c, sn);
-      lo[t] = v[2 * t] * c - v[2 * t + 1] * sn;
-      hi[t] = v[2 * t + 1] * c + v[2 * t] * sn;
-    }
-    T *dst;
-    T *dst0 = nullptr;
-    if (hh < p.nq) {
-      dst = reinterpret_cast<T *>(p.q) + ((long)m * p.nq + hh) * hd;
-    } else {
-      const int gk = hh - p.nq;
-      dst = reinterpret_cast<T *>(p.kall) + ((long)m * p.nkv + gk) * hd;
-      if (depth0) dst0 = reinterpret_cast<T *>(p.k0) + ((long)pos * p.nkv + gk) * hd;
-    }
-    store2<T>(dst + dim, lo[0], lo[1]);
-    store2<T>(dst + dim + half, hi[0], hi[1]);
-    if (dst0) {
-      store2<T>(dst0 + dim, lo[0], lo[1]);
-      store2<T>(dst0 + dim + half, hi[0], hi[1]);
-    }
-  } else {
-    const int gk = hh - p.nq - p.nkv;
-    const float vals[4] = {v[0], v[1], v[2], v[3]};
-    store4<T>(reinterpret_cast<T *>(p.vall) + ((long)m * p.nkv + gk) * hd + within, vals);
-    if (depth0) store4<T>(reinterpret_cast<T *>(p.v0) + ((long)pos * p.nkv + gk) * hd + within, vals);
-  }
-}
-
 constexpr unsigned kRecordsCap = 0x7FFFF000u;  // buffer extent limit per tile
 constexpr int kOobOffset = 0x7FFFFFF0;         // beyond every extent: reads zero
 
@@ -347,6 +304,73 @@ void k_gemm_tile(TileGemmParams p) {
         if (m < p.M) atomicMax(p.keys + m, k4);
       }
       __syncthreads();  // staging and key buffers are reused by the next tile
+    } else if constexpr (EPI == BEPI_QKV) {
+      // The wave's 64 columns are one head (hd 64) or half of one (hd 128).
+      // RoPE'd rows go through the wave's region of stage buffer 3 (idle
+      // until the next tile's first step) and out as whole 16-byte chunks:
+      // written piecewise, the scattered 4-byte stores had cost several
+      // times their bytes in HBM traffic.
+      constexpr int RP = 16;                             // rows per pass
+      constexpr int SP = sizeof(T) == 2 ? 72 : 64;       // staged row pitch (bf16 padded: no bank conflicts)
+      constexpr int EC = 16 / (int)sizeof(T);            // elements per 16-byte chunk
+      constexpr int CHR = 64 / EC;                       // chunks per 64-element row
+      T *stg = reinterpret_cast<T *>(&smem[3][0][0]) + w * (RP * SP);
+      const int hd = p.hd, half = hd >> 1, c0 = (s0 + wn * 4) * 16;
+      const int hh = c0 / hd, within0 = c0 - hh * hd;
+      const bool rot = hh < p.nq + p.nkv;
+      const int lo0 = within0 >> 1;  // first rotated dimension of the wave's columns
+      if (c0 < p.N) {
+#pragma unroll
+        for (int ps = 0; ps < 128 / RP; ++ps) {
+#pragma unroll
+          for (int jj = 0; jj < RP / 16; ++jj) {
+            const int j = ps * (RP / 16) + jj;
+            const int m = m0 + (wm * 8 + j) * 16 + c16;
+            const int pos = m < p.M ? p.anc[m] + p.dep[m] : 0;
+            T *srow = stg + (jj * 16 + c16) * SP;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const floatx4 v = acc[i][j];
+              if (rot) {
+                const int li = 8 * i + 2 * g;  // local index of the lower dimension pair
+                float lo[2], hi[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                  float c, sn;
+                  rope_cs(pos, p.inv_freq[lo0 + li + t], c, sn);
+                  lo[t] = v[2 * t] * c - v[2 * t + 1] * sn;
+                  hi[t] = v[2 * t + 1] * c + v[2 * t] * sn;
+                }
+                store2<T>(srow + li, lo[0], lo[1]);
+                store2<T>(srow + 32 + li, hi[0], hi[1]);
+              } else {
+                const float vals[4] = {v[0], v[1], v[2], v[3]};
+                store4<T>(srow + 16 * i + 4 * g, vals);
+              }
+            }
+          }
+#pragma unroll
+          for (int r0 = 0; r0 < RP; r0 += 64 / CHR) {
+            const int rl = r0 + lane / CHR, ch = lane % CHR, li = ch * EC;
+            const int m = m0 + wm * 128 + ps * RP + rl;
+            const u32x4 val = *reinterpret_cast<const u32x4 *>(stg + rl * SP + li);
+            if (m < p.M) {
+              const int dim = rot ? (li < 32 ? lo0 + li : half + lo0 + li - 32) : within0 + li;
+              const int d = p.dep[m], pos = p.anc[m] + d;
+              const bool depth0 = d == 0 && pos >= 0 && pos < p.n;
+              if (hh < p.nq) {
+                stg16(reinterpret_cast<T *>(p.q) + ((long)m * p.nq + hh) * hd + dim, val);
+              } else {
+                const int gk = rot ? hh - p.nq : hh - p.nq - p.nkv;
+                T *all = reinterpret_cast<T *>(rot ? p.kall : p.vall);
+                T *zero = reinterpret_cast<T *>(rot ? p.k0 : p.v0);
+                stg16(all + ((long)m * p.nkv + gk) * hd + dim, val);
+                if (depth0) stg16(zero + ((long)pos * p.nkv + gk) * hd + dim, val);
+              }
+            }
+          }
+        }
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -368,8 +392,6 @@ void k_gemm_tile(TileGemmParams p) {
               epi_tile_swiglu<T, false>(p, m, s, g, acc[i][j]);
             } else if constexpr (EPI == BEPI_SWIGLU_SAVE) {
               epi_tile_swiglu<T, true>(p, m, s, g, acc[i][j]);
-            } else {
-              epi_tile_qkv<T>(p, m, n, acc[i][j]);
             }
           }
         }
