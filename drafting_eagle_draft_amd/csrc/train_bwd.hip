@@ -675,48 +675,59 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dq(AttnBwdParams p) {
       for (int e = 0; e < E; ++e) Kt[bf][(cc * E + e) * VS + key] = vals[e];
     }
   };
+  // One 32-key (bf16) or 16-key (fp32) reduction chunk of the tile at a
+  // time: its scores and dP for all QB query blocks, then its share of dQ,
+  // so only one chunk's scores are held in registers.
   auto compute = [&](int jt, int bf) {
     if (jt > wave_amax) return;  // every row of this wave sits before the tile
-    floatx4 sacc[QB][4], pacc[QB][4];
+    constexpr int KBC = 4 / NKC;  // 16-key blocks per reduction chunk
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int kc = 0; kc < NKC; ++kc) {
+      floatx4 sacc[QB][KBC], pacc[QB][KBC];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) sacc[qb][kb] = pacc[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+        for (int kl = 0; kl < KBC; ++kl) sacc[qb][kl] = pacc[qb][kl] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const u32x4 kf = lds16b(&Ks[bf][(kb * 16 + c16) * KS + c * KTILE + g * E]);
-        const u32x4 vf = lds16b(&Vs[bf][(kb * 16 + c16) * KS + c * KTILE + g * E]);
+      for (int kl = 0; kl < KBC; ++kl)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          sacc[qb][kb] = Mma<T>::run(kf, qf[qb][c], sacc[qb][kb]);
-          pacc[qb][kb] = Mma<T>::run(vf, df[qb][c], pacc[qb][kb]);
+        for (int c = 0; c < NC; ++c) {
+          const int kb = kc * KBC + kl;
+          const u32x4 kf = lds16b(&Ks[bf][(kb * 16 + c16) * KS + c * KTILE + g * E]);
+          const u32x4 vf = lds16b(&Vs[bf][(kb * 16 + c16) * KS + c * KTILE + g * E]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            sacc[qb][kl] = Mma<T>::run(kf, qf[qb][c], sacc[qb][kl]);
+            pacc[qb][kl] = Mma<T>::run(vf, df[qb][c], pacc[qb][kl]);
+          }
         }
+      u32x4 dsf[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float ds[KBC][4];
+#pragma unroll
+        for (int kl = 0; kl < KBC; ++kl)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int jj = jt + (kc * KBC + kl) * 16 + 4 * g + r;
+            const bool vis = valid[qb] && jj < nkeys && jj <= a_q[qb];
+            const float pr = vis ? fast_exp2(fmaf(sacc[qb][kl][r], p.scale_log2, -lse[qb])) : 0.f;
+            ds[kl][r] = pr * (pacc[qb][kl][r] - Dq[qb]);
+          }
+        if constexpr (KBC == 2)
+          dsf[qb] = u32x4{pack_bf16x2(ds[0][0], ds[0][1]), pack_bf16x2(ds[0][2], ds[0][3]),
+                          pack_bf16x2(ds[1][0], ds[1][1]), pack_bf16x2(ds[1][2], ds[1][3])};
+        else
+          dsf[qb] = u32x4{__float_as_uint(ds[0][0]), __float_as_uint(ds[0][1]), __float_as_uint(ds[0][2]),
+                          __float_as_uint(ds[0][3])};
       }
-    u32x4 dsf[QB][4];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float ds[4][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int jj = jt + kb * 16 + 4 * g + r;
-          const bool vis = valid[qb] && jj < nkeys && jj <= a_q[qb];
-          const float pr = vis ? fast_exp2(fmaf(sacc[qb][kb][r], p.scale_log2, -lse[qb])) : 0.f;
-          ds[kb][r] = pr * (pacc[qb][kb][r] - Dq[qb]);
-        }
-      pack_rows_b<T>(ds, dsf[qb]);
-    }
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         const u32x4 kf = lds_t_frag<T, VS>(Kt[bf], d, c16, g, kc);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) dqacc[qb][d] = Mma<T>::run(kf, dsf[qb][kc], dqacc[qb][d]);
+        for (int qb = 0; qb < QB; ++qb) dqacc[qb][d] = Mma<T>::run(kf, dsf[qb], dqacc[qb][d]);
       }
+    }
   };
   // Key tile jt sits in buffer (jt / 64) & 1.  After multiplying a tile, a
   // wave stores the next one (loaded into registers earlier) into the other
@@ -1348,16 +1359,21 @@ hipError_t launch_attn_bwd(int dtype, const AttnBwdParams &p, hipStream_t s) {
   if (p.hd != 64 && p.hd != 128) return hipErrorInvalidValue;
   if (dtype != 1 && p.hd != 64) return hipErrorInvalidValue;
   const int G = p.G;
-  // dQ: the forward's query tiling (NW waves x QB 16-row blocks).
+  // dQ: NW waves x QB 16-row blocks of query pairs per workgroup (three
+  // blocks where they fit the registers: bf16 at hd 64).
   {
-    constexpr int NW = 8, QB = 2;
-    const int QT = 16 * QB * NW / G;
-    const dim3 grid((unsigned)((p.L + QT - 1) / QT), (unsigned)p.nkv);
+    constexpr int NW = 8;
+    auto grid_for = [&](int QB) {
+      const int QT = 16 * QB * NW / G;
+      return dim3((unsigned)((p.L + QT - 1) / QT), (unsigned)p.nkv);
+    };
     if (dtype == 1) {
-      if (p.hd == 64) hipLaunchKernelGGL((k_attn_bwd_dq<bf16_t, 64, NW, QB>), grid, dim3(64 * NW), 0, s, p);
-      else hipLaunchKernelGGL((k_attn_bwd_dq<bf16_t, 128, NW, QB>), grid, dim3(64 * NW), 0, s, p);
+      if (p.hd == 64)
+        hipLaunchKernelGGL((k_attn_bwd_dq<bf16_t, 64, NW, 3>), grid_for(3), dim3(64 * NW), 0, s, p);
+      else
+        hipLaunchKernelGGL((k_attn_bwd_dq<bf16_t, 128, NW, 2>), grid_for(2), dim3(64 * NW), 0, s, p);
     } else {
-      hipLaunchKernelGGL((k_attn_bwd_dq<float, 64, NW, QB>), grid, dim3(64 * NW), 0, s, p);
+      hipLaunchKernelGGL((k_attn_bwd_dq<float, 64, NW, 2>), grid_for(2), dim3(64 * NW), 0, s, p);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
