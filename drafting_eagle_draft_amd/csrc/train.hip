@@ -222,8 +222,10 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
   // (kv_sw), values read transposed; fp32: padded key rows, values
   // transposed on the store (Vt[d][key]).
   constexpr bool TR = sizeof(T) == 2;
-  __shared__ __attribute__((aligned(16))) T Ks[TR ? 64 * HD : 64 * KS];
-  __shared__ __attribute__((aligned(16))) T Vt[TR ? 64 * HD : HD * VS];
+  // Two buffers of each: one key tile is multiplied while the next is stored.
+  constexpr int KSZ = TR ? 64 * HD : 64 * KS, VSZ = TR ? 64 * HD : HD * VS;
+  __shared__ __attribute__((aligned(16))) T Ks[2][KSZ];
+  __shared__ __attribute__((aligned(16))) T Vt[2][VSZ];
   __shared__ int s_amax[NW];
   const int G = p.G, QT = 16 * QB * NW / G;
   const int gk = blockIdx.y;
@@ -285,8 +287,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
   // 2 d + (c16 % 4) / 2, half (c16 % 4) % 2.
   unsigned koff[NC], voff[ND];
   if constexpr (TR) {
-    const unsigned kl = (unsigned)(size_t)(__attribute__((address_space(3))) T *)Ks;
-    const unsigned vl = (unsigned)(size_t)(__attribute__((address_space(3))) T *)Vt;
+    const unsigned kl = (unsigned)(size_t)(__attribute__((address_space(3))) T *)Ks[0];
+    const unsigned vl = (unsigned)(size_t)(__attribute__((address_space(3))) T *)Vt[0];
 #pragma unroll
     for (int c = 0; c < NC; ++c) koff[c] = kl + (unsigned)((c16 * CPR + ((c * 4 + g) ^ kv_sw<HD>(c16))) * 16);
     const int vkey = 4 * g + (c16 >> 2);
@@ -314,128 +316,147 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
 #pragma unroll
   for (int u = 0; u < PF; ++u)
     if (64 * u < nkeys) gload(64 * u, kreg[u], vreg[u]);
+  // Tile jt's keys and values: register slot (jt / 64) % PF -> LDS buffer
+  // (jt / 64) & 1.
+  auto put = [&](const u32x4 (&kr)[MAXC], const u32x4 (&vr)[MAXC], int bf) {
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int id = tid + i * NT;
+      if (id >= 64 * CPR) break;
+      const int key = id / CPR, cc = id - key * CPR;
+      if constexpr (TR) {
+        const int o = key * HD * 2 + (cc ^ kv_sw<HD>(key)) * 16;
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(Ks[bf]) + o) = kr[i];
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(Vt[bf]) + o) = vr[i];
+        continue;
+      }
+      *reinterpret_cast<u32x4 *>(&Ks[bf][key * KS + cc * E]) = kr[i];
+      T vals[E];
+      __builtin_memcpy(vals, &vr[i], 16);
+      // bank-spread transposed V (pe_device.hpp)
+      const int kcol = key ^ vt_swizzle_b2(cc);
+#pragma unroll
+      for (int e = 0; e < E; ++e) Vt[bf][(cc * E + e) * VS + kcol] = vals[e];
+    }
+  };
+  auto compute = [&](int jt, int bf) {
+    const unsigned kbo = (unsigned)(bf * KSZ * (int)sizeof(T)), vbo = (unsigned)(bf * VSZ * (int)sizeof(T));
+    (void)kbo; (void)vbo;
+    // A wave whose rows all sit before this tile has nothing to add.
+    if (jt <= wave_amax) {
+      floatx4 sacc[QB][4];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) sacc[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          u32x4 kf;
+          if constexpr (TR) kf = lds_b128(koff[c] + kbo + (unsigned)(kb * 16 * CPR * 16));
+          else kf = lds16t(&Ks[bf][(kb * 16 + c16) * KS + c * KTILE + g * E]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = Mma<T>::run(kf, qf[qb][c], sacc[qb][kb]);
+        }
+      // Keys after a row's own anchor (or past the prefix) are masked; tiles
+      // below every anchor of the wave need no test.
+      const bool need_mask = jt + 63 > wave_amin || jt + 63 >= nkeys;
+      u32x4 pbf[QB][4];  // P^T fragments: bf16 uses [qb][0..1], fp32 [qb][0..3]
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (need_mask) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int jj = jt + kb * 16 + 4 * g + r;
+              if (!(jj < nkeys && jj <= a_q[qb])) sacc[qb][kb][r] = -INFINITY;
+            }
+        }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sacc[qb][kb][r]);
+        mt = fmaxf(mt, shfl_xor_f(mt, 16));
+        mt = fmaxf(mt, shfl_xor_f(mt, 32));
+        // Running maximum in the exp2 domain (positive scale commutes with
+        // the maximum); weights 2^(s*scale - m).
+        const float m_new = fmaxf(m_run[qb], mt * p.scale_log2);
+        const float msub = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run[qb] - msub);
+        float pv[4][4];
+        float ps = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pv[kb][r] = fast_exp2(fmaf(sacc[qb][kb][r], p.scale_log2, -msub));
+            ps += pv[kb][r];
+          }
+        l_lane[qb] = l_lane[qb] * alpha + ps;
+        m_run[qb] = m_new;
+        if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+          for (int d = 0; d < ND; ++d) oacc[qb][d] *= alpha;
+        }
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2)
+            pbf[qb][c2] = u32x4{pack_bf16x2(pv[2 * c2][0], pv[2 * c2][1]), pack_bf16x2(pv[2 * c2][2], pv[2 * c2][3]),
+                                pack_bf16x2(pv[2 * c2 + 1][0], pv[2 * c2 + 1][1]),
+                                pack_bf16x2(pv[2 * c2 + 1][2], pv[2 * c2 + 1][3])};
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            pbf[qb][kb] = u32x4{__float_as_uint(pv[kb][0]), __float_as_uint(pv[kb][1]),
+                                __float_as_uint(pv[kb][2]), __float_as_uint(pv[kb][3])};
+        }
+      }
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            const unsigned a0 = voff[d] + vbo + (unsigned)(32 * c2 * CPR * 16);
+            const uint2 lo = lds_tr8(a0), hi = lds_tr8(a0 + (unsigned)(16 * CPR * 16));
+            const u32x4 vf = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) oacc[qb][d] = Mma<T>::run(vf, pbf[qb][c2], oacc[qb][d]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            const int vd = d * 16 + c16;
+            const u32x4 vf = lds16t(&Vt[bf][vd * VS + ((16 * kb + 4 * g) ^ vt_swizzle_b2(vd / E))]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) oacc[qb][d] = Mma<T>::run(vf, pbf[qb][kb], oacc[qb][d]);
+          }
+      }
+    }
+  };
+  // After multiplying a tile, each wave stores the next one into the other
+  // buffer; one barrier per tile then finds it stored by every wave and the
+  // buffer just multiplied free for the tile after.
+  if (nkeys > 0) {
+    put(kreg[0], vreg[0], 0);
+    lds_barrier();
+    if (64 * PF < nkeys) gload(64 * PF, kreg[0], vreg[0]);
+  }
   for (int jt0 = 0; jt0 < nkeys; jt0 += 64 * PF) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int jt = jt0 + 64 * u;
       if (jt >= nkeys) break;
-#pragma unroll
-      for (int i = 0; i < MAXC; ++i) {
-        const int id = tid + i * NT;
-        if (id >= 64 * CPR) break;
-        const int key = id / CPR, cc = id - key * CPR;
-        if constexpr (TR) {
-          const int o = key * HD * 2 + (cc ^ kv_sw<HD>(key)) * 16;
-          *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(Ks) + o) = kreg[u][i];
-          *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(Vt) + o) = vreg[u][i];
-          continue;
-        }
-        *reinterpret_cast<u32x4 *>(&Ks[key * KS + cc * E]) = kreg[u][i];
-        T vals[E];
-        __builtin_memcpy(vals, &vreg[u][i], 16);
-        // bank-spread transposed V (pe_device.hpp)
-        const int kcol = key ^ vt_swizzle_b2(cc);
-#pragma unroll
-        for (int e = 0; e < E; ++e) Vt[(cc * E + e) * VS + kcol] = vals[e];
-      }
+      const int bf = (jt >> 6) & 1;
+      compute(jt, bf);
+      const int un = (u + 1) % PF;  // register slot of tile jt + 64
+      if (jt + 64 < nkeys) put(kreg[un], vreg[un], bf ^ 1);
       lds_barrier();
-      if (jt + 64 * PF < nkeys) gload(jt + 64 * PF, kreg[u], vreg[u]);
-      // A wave whose rows all sit before this tile has nothing to add.
-      if (jt <= wave_amax) {
-        floatx4 sacc[QB][4];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) sacc[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            u32x4 kf;
-            if constexpr (TR) kf = lds_b128(koff[c] + (unsigned)(kb * 16 * CPR * 16));
-            else kf = lds16t(&Ks[(kb * 16 + c16) * KS + c * KTILE + g * E]);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = Mma<T>::run(kf, qf[qb][c], sacc[qb][kb]);
-          }
-        // Keys after a row's own anchor (or past the prefix) are masked; tiles
-        // below every anchor of the wave need no test.
-        const bool need_mask = jt + 63 > wave_amin || jt + 63 >= nkeys;
-        u32x4 pbf[QB][4];  // P^T fragments: bf16 uses [qb][0..1], fp32 [qb][0..3]
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          if (need_mask) {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int jj = jt + kb * 16 + 4 * g + r;
-                if (!(jj < nkeys && jj <= a_q[qb])) sacc[qb][kb][r] = -INFINITY;
-              }
-          }
-          float mt = -INFINITY;
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sacc[qb][kb][r]);
-          mt = fmaxf(mt, shfl_xor_f(mt, 16));
-          mt = fmaxf(mt, shfl_xor_f(mt, 32));
-          // Running maximum in the exp2 domain (positive scale commutes with
-          // the maximum); weights 2^(s*scale - m).
-          const float m_new = fmaxf(m_run[qb], mt * p.scale_log2);
-          const float msub = m_new == -INFINITY ? 0.f : m_new;
-          const float alpha = fast_exp2(m_run[qb] - msub);
-          float pv[4][4];
-          float ps = 0.f;
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              pv[kb][r] = fast_exp2(fmaf(sacc[qb][kb][r], p.scale_log2, -msub));
-              ps += pv[kb][r];
-            }
-          l_lane[qb] = l_lane[qb] * alpha + ps;
-          m_run[qb] = m_new;
-          if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-            for (int d = 0; d < ND; ++d) oacc[qb][d] *= alpha;
-          }
-          if constexpr (sizeof(T) == 2) {
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2)
-              pbf[qb][c2] = u32x4{pack_bf16x2(pv[2 * c2][0], pv[2 * c2][1]), pack_bf16x2(pv[2 * c2][2], pv[2 * c2][3]),
-                                  pack_bf16x2(pv[2 * c2 + 1][0], pv[2 * c2 + 1][1]),
-                                  pack_bf16x2(pv[2 * c2 + 1][2], pv[2 * c2 + 1][3])};
-          } else {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-              pbf[qb][kb] = u32x4{__float_as_uint(pv[kb][0]), __float_as_uint(pv[kb][1]),
-                                  __float_as_uint(pv[kb][2]), __float_as_uint(pv[kb][3])};
-          }
-        }
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-            for (int d = 0; d < ND; ++d) {
-              const unsigned a0 = voff[d] + (unsigned)(32 * c2 * CPR * 16);
-              const uint2 lo = lds_tr8(a0), hi = lds_tr8(a0 + (unsigned)(16 * CPR * 16));
-              const u32x4 vf = {lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-              for (int qb = 0; qb < QB; ++qb) oacc[qb][d] = Mma<T>::run(vf, pbf[qb][c2], oacc[qb][d]);
-            }
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int d = 0; d < ND; ++d) {
-              const int vd = d * 16 + c16;
-              const u32x4 vf = lds16t(&Vt[vd * VS + ((16 * kb + 4 * g) ^ vt_swizzle_b2(vd / E))]);
-#pragma unroll
-              for (int qb = 0; qb < QB; ++qb) oacc[qb][d] = Mma<T>::run(vf, pbf[qb][kb], oacc[qb][d]);
-            }
-        }
-      }
-      lds_barrier();
+      if (jt + 64 + 64 * PF < nkeys) gload(jt + 64 + 64 * PF, kreg[un], vreg[un]);
     }
   }
 
@@ -484,8 +505,10 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
         const int base = d * 16 + 4 * g;
 #pragma unroll
         for (int r = 0; r < 4; ++r) vv[r] = to_f32<T>(vr[base + r]);
+        // One product rounded, stated explicitly: a contraction left to the
+        // compiler may pick either product and change with code layout.
 #pragma unroll
-        for (int r = 0; r < 4; ++r) oacc[qb][d][r] = oacc[qb][d][r] * alpha + pc * vv[r];
+        for (int r = 0; r < 4; ++r) oacc[qb][d][r] = fmaf(pc, vv[r], oacc[qb][d][r] * alpha);
       }
     }
 
