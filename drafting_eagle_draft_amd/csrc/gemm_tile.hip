@@ -86,14 +86,20 @@ __device__ __forceinline__ void load_to_lds(const u32x4 &rsrc, unsigned lds, int
 }
 #pragma clang diagnostic pop
 
-template <typename T, int EPI>
+// NS weight strips per tile: 16, or 20 for the plain STORE / ACCUM
+// epilogues where the strip count pads less (an output of 2880 columns is
+// 9 tiles of 320 against 11.25 of 256).
+template <typename T, int EPI, int NS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_tile(TileGemmParams p) {
+  static_assert(NS == 16 || (NS == 20 && (EPI == BEPI_STORE || EPI == BEPI_ACCUM)), "strips per tile");
   constexpr int KTILE = Frag<T>::KTILE, E = Frag<T>::E;
   constexpr int NSTAGE = 4;
-  // Stage layout: fragments 0..15 are weight strips s0..s0+15, 16..31 are
-  // row groups of 16 activation rows; each fragment is 64 lanes x 16 bytes.
-  __shared__ u32x4 smem[NSTAGE][32][64];
+  constexpr int SW = NS / 4;  // weight strips per wave
+  // Stage layout: fragments 0..NS-1 are weight strips s0..s0+NS-1, NS..NS+15
+  // are row groups of 16 activation rows; each fragment is 64 lanes x 16
+  // bytes.
+  __shared__ u32x4 smem[NSTAGE][NS + 16][64];
   // LM head: per-wave staging of RCH logits rows (row pitch 64 elements +
   // 16 bytes) and the per-quarter argmax keys of the tile's 256 rows.  Kept
   // apart from the stages so the next tile's loads run during the epilogue.
@@ -106,9 +112,9 @@ void k_gemm_tile(TileGemmParams p) {
   const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
   // Wave (wm, wn): activation rows wm*128 .. +128 (8 row groups) and weight
-  // strips wn*4 .. +4 of the tile: 4 x 8 MFMA tiles, 128 accumulators.
+  // strips wn*SW .. +SW of the tile: SW x 8 MFMA tiles, 32 SW accumulators.
   const int wm = w >> 2, wn = w & 3;
-  const int RB = (p.M + 255) >> 8, CB = (p.NT + 15) >> 4;
+  const int RB = (p.M + 255) >> 8, CB = (p.NT + NS - 1) / NS;
   // Work units: ksplit chunks of the k tiles for every output tile, chunk
   // by chunk (all tiles' chunk 0 first).
   const int tiles = RB * CB, units = tiles * p.ksplit;
@@ -116,7 +122,7 @@ void k_gemm_tile(TileGemmParams p) {
   const int G = gridDim.x, b = blockIdx.x;
   const int slot = (G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
   const size_t lda_b = (size_t)p.lda * sizeof(T);
-  const bool wave_w = w < 4;  // waves 0-3 fetch weight strips, 4-7 row groups, 4 each
+  const bool wave_w = w < 4;  // waves 0-3 fetch SW weight strips each, 4-7 four row groups each
   // Byte offset of this lane's 16 bytes within the wave's first fragment at
   // k tile 0; fragment q and k tile kt add the wave-uniform
   // fbase + qstride*q + kstep*kt.
@@ -125,11 +131,11 @@ void k_gemm_tile(TileGemmParams p) {
   const bool frag = wave_w || p.a_tiled;
   const int lanebase = frag ? lane * 16 : c16 * (int)lda_b + g * E * (int)sizeof(T);
   const int qstride = frag ? p.KT * 1024 : 16 * (int)lda_b;
-  const int fbase = (w & 3) * 4 * qstride;
+  const int fbase = (w & 3) * (wave_w ? SW : 4) * qstride;
   const int kstep = frag ? 1024 : KTILE * (int)sizeof(T);
   const unsigned lds0 = (unsigned)__builtin_amdgcn_readfirstlane(
-      (int)(unsigned)(size_t)(lds_void *)&smem[0][(w >> 2) * 16 + (w & 3) * 4][0]);
-  constexpr int stage_bytes = 32 * 64 * 16;
+      (int)(unsigned)(size_t)(lds_void *)&smem[0][wave_w ? (w & 3) * SW : NS + (w & 3) * 4][0]);
+  constexpr int stage_bytes = (NS + 16) * 64 * 16;
 
   // Unit u -> (first activation row, first weight strip, chunk); tiles in
   // bands of four row blocks, columns inside a band.
@@ -140,7 +146,7 @@ void k_gemm_tile(TileGemmParams p) {
     const int rows_in = min(4, RB - band * 4);
     const int cb = rem / rows_in, rb = band * 4 + rem % rows_in;
     m0 = rb * 256;
-    s0 = cb * 16;
+    s0 = cb * NS;
   };
   const int MG = (p.M + 15) >> 4;  // 16-row groups of a tiled A
   // The resource starts at the chunk's first k tile kt0 (the k tiles of a
@@ -160,8 +166,9 @@ void k_gemm_tile(TileGemmParams p) {
     const unsigned dst = lds0 + (unsigned)((kt & (NSTAGE - 1)) * stage_bytes);
     const bool live = kt < nk;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      load_to_lds(rs, dst + q * 1024, live ? lanebase + (fbase + q * qstride + kt * kstep) : kOobOffset);
+    for (int q = 0; q < SW; ++q)
+      if (q < 4 || wave_w)
+        load_to_lds(rs, dst + q * 1024, live ? lanebase + (fbase + q * qstride + kt * kstep) : kOobOffset);
   };
 
   int t = slot, m0 = 0, s0 = 0, ks = 0;
@@ -177,9 +184,9 @@ void k_gemm_tile(TileGemmParams p) {
   };
   if (t < units) start_unit();
   while (t < units) {
-    floatx4 acc[4][8];
+    floatx4 acc[SW][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < SW; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
@@ -193,19 +200,27 @@ void k_gemm_tile(TileGemmParams p) {
     // 32.8 ms); the scheduling barriers keep the compiler from regrouping
     // them.  The second wave on each SIMD covers this wave's waits.
     for (int kt = 0; kt < nk; ++kt) {
-      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+      // Loads of the two younger stages may stay in flight: SW or 4 per stage.
+      if constexpr (NS == 16) {
+        asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+      } else {
+        if (wave_w) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");
+      }
       const int st = kt & (NSTAGE - 1);
-      u32x4 wf[4], af[8];
+      u32x4 wf[SW], af[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wf[i] = smem[st][wn * 4 + i][lane];
+      for (int i = 0; i < SW; ++i) wf[i] = smem[st][wn * SW + i][lane];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) af[j] = smem[st][16 + wm * 8 + j][lane];
+      for (int j = 0; j < 8; ++j) af[j] = smem[st][NS + wm * 8 + j][lane];
       const unsigned dst = lds0 + (unsigned)(((kt + 3) & (NSTAGE - 1)) * stage_bytes);
       const bool live = kt + 3 < nk;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < SW; ++i) {
         __builtin_amdgcn_sched_barrier(0);
-        load_to_lds(rs, dst + i * 1024, live ? lanebase + (fbase + i * qstride + (kt + 3) * kstep) : kOobOffset);
+        if (i < 4 || wave_w)
+          load_to_lds(rs, dst + i * 1024, live ? lanebase + (fbase + i * qstride + (kt + 3) * kstep) : kOobOffset);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = Mma<T>::run(wf[i], af[j], acc[i][j]);
@@ -223,7 +238,7 @@ void k_gemm_tile(TileGemmParams p) {
     // chunk 0 stores to (or accumulates into) C, chunk c > 0 stores its own
     // partial block
     float *const C = tks == 0 ? p.C : p.kpart + (size_t)(tks - 1) * p.kpart_stride;
-    // acc[i][j][r] = C[m = m0 + (wm*8 + j)*16 + c16][n = (s0 + wn*4 + i)*16 + 4g + r]
+    // acc[i][j][r] = C[m = m0 + (wm*8 + j)*16 + c16][n = (s0 + wn*SW + i)*16 + 4g + r]
     if constexpr (LMH) {
       // Output row of activation row m, or -1 when it is not written (the
       // map is a variant of its own so the plain LM head keeps its code).
@@ -376,8 +391,8 @@ void k_gemm_tile(TileGemmParams p) {
       for (int j = 0; j < 8; ++j) {
         const int m = m0 + (wm * 8 + j) * 16 + c16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = s0 + wn * 4 + i;
+        for (int i = 0; i < SW; ++i) {
+          const int s = s0 + wn * SW + i;
           const int n = s * 16 + 4 * g;
           if (m < p.M && s < p.NT) {
             if constexpr (EPI == BEPI_STORE) {
@@ -415,27 +430,63 @@ __global__ __launch_bounds__(256) void k_ksum(float *C, long ldc, int M, int N4,
 
 }  // namespace
 
-int tile_gemm_ksplit(long M, int NT, int KT, int num_cus) {
-  // Cost in k steps of one round of tiles (about 0.8 us each on a 256 x 256
-  // tile): rounds of units times k tiles per unit, plus the summing pass,
-  // which moves ks + 1 fp32 blocks (256 KB per tile each; about 15 us per
-  // round of 256 tiles at 4.5 TB/s, i.e. 19 k steps).
-  constexpr double kSumStepsPerBlock = 19.0;
-  const long tiles = ((M + 255) / 256) * (long)((NT + 15) / 16);
-  const double unsplit = std::ceil((double)tiles / num_cus) * KT;
+namespace {
+
+// Plain (STORE / ACCUM) tile GEMMs take 16 or 20 weight strips per tile.
+// Costs are in k steps of a 16-strip tile (about 0.83 us each on a 256 x
+// 256 tile); a 20-strip step costs 1.24 of them (measured 1.035 against
+// 0.834 us on the 33,927 x 2880 data gradient of the LM head: in
+// proportion to the matrix work, so a 20-strip tile pays only where 16
+// strips pad the output or leave a ragged last round).  A K split adds the
+// summing pass, which moves ks + 1 fp32 copies of the output (256 KB per
+// 256 x 256 block each; about 15 us per round of 256 blocks at 4.5 TB/s,
+// i.e. 19 k steps).
+constexpr double kStepCost20 = 1.24;
+constexpr double kSumStepsPerBlock = 19.0;
+
+double plain_tile_cost(long M, int NT, int KT, int num_cus, int ns, int ks) {
+  const long tiles = ((M + 255) / 256) * (long)((NT + ns - 1) / ns);
+  const double step = ns == 20 ? kStepCost20 : 1.0;
+  const double work = std::ceil((double)tiles * ks / num_cus) * std::ceil((double)KT / ks) * step;
+  if (ks == 1) return work;
+  const double blocks = (double)((M + 255) / 256) * (double)((NT + 15) / 16);
+  return work + (ks + 1) * kSumStepsPerBlock * blocks / num_cus;
+}
+
+// Cheapest K split (1 .. 8, every chunk non-empty) for ns strips per tile;
+// a split must save 2% over none.
+int plain_tile_ksplit(long M, int NT, int KT, int num_cus, int ns, double *cost_out) {
+  const double unsplit = plain_tile_cost(M, NT, KT, num_cus, ns, 1);
   int best = 1;
   double best_cost = unsplit;
   for (int ks = 2; ks <= 8 && ks <= KT; ++ks) {
-    if ((ks - 1) * ((KT + ks - 1) / ks) >= KT) continue;  // every chunk gets k tiles
-    const double rounds = std::ceil((double)tiles * ks / num_cus);
-    const double cost =
-        rounds * std::ceil((double)KT / ks) + (ks + 1) * kSumStepsPerBlock * (double)tiles / num_cus;
-    if (cost < best_cost) {
+    if ((ks - 1) * ((KT + ks - 1) / ks) >= KT) continue;
+    const double c = plain_tile_cost(M, NT, KT, num_cus, ns, ks);
+    if (c < best_cost) {
       best = ks;
-      best_cost = cost;
+      best_cost = c;
     }
   }
-  return best_cost < unsplit * 0.98 ? best : 1;  // a split must save 2%
+  if (best_cost >= unsplit * 0.98) {
+    best = 1;
+    best_cost = unsplit;
+  }
+  *cost_out = best_cost;
+  return best;
+}
+
+// Strips per tile for a given split: 20 only when cheaper than 16.
+int plain_tile_strips(long M, int NT, int KT, int num_cus, int ks) {
+  return plain_tile_cost(M, NT, KT, num_cus, 20, ks) < plain_tile_cost(M, NT, KT, num_cus, 16, ks) ? 20 : 16;
+}
+
+}  // namespace
+
+int tile_gemm_ksplit(long M, int NT, int KT, int num_cus) {
+  double c16, c20;
+  const int k16 = plain_tile_ksplit(M, NT, KT, num_cus, 16, &c16);
+  const int k20 = plain_tile_ksplit(M, NT, KT, num_cus, 20, &c20);
+  return c20 < c16 ? k20 : k16;
 }
 
 hipError_t launch_ksum(float *C, long ldc, int M, int N, const float *kpart, long kpart_stride, int ksplit,
@@ -453,12 +504,19 @@ hipError_t launch_gemm_tile(int dtype, int epi, const TileGemmParams &p, int num
   if (p.ksplit < 1 || (p.ksplit > 1 && ((epi != BEPI_STORE && epi != BEPI_ACCUM) || !p.kpart ||
                                          (p.ksplit - 1) * ((p.KT + p.ksplit - 1) / p.ksplit) >= p.KT)))
     return hipErrorInvalidValue;
-  const long tiles = (long)((p.M + 255) / 256) * ((p.NT + 15) / 16) * p.ksplit;
+  const int ns =
+      epi == BEPI_STORE || epi == BEPI_ACCUM ? plain_tile_strips(p.M, p.NT, p.KT, num_cus, p.ksplit) : 16;
+  const long tiles = (long)((p.M + 255) / 256) * ((p.NT + ns - 1) / ns) * p.ksplit;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(tiles < num_cus ? tiles : num_cus));
 #define PE_TILE_CASE(T, E) \
-  case E: hipLaunchKernelGGL((k_gemm_tile<T, E>), grid, dim3(512), 0, s, p); break;
-  if (dtype == 1) {
+  case E: hipLaunchKernelGGL((k_gemm_tile<T, E, 16>), grid, dim3(512), 0, s, p); break;
+  if (ns == 20) {
+    if (epi == BEPI_STORE && dtype == 1) hipLaunchKernelGGL((k_gemm_tile<bf16_t, BEPI_STORE, 20>), grid, dim3(512), 0, s, p);
+    else if (epi == BEPI_STORE) hipLaunchKernelGGL((k_gemm_tile<float, BEPI_STORE, 20>), grid, dim3(512), 0, s, p);
+    else if (dtype == 1) hipLaunchKernelGGL((k_gemm_tile<bf16_t, BEPI_ACCUM, 20>), grid, dim3(512), 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_tile<float, BEPI_ACCUM, 20>), grid, dim3(512), 0, s, p);
+  } else if (dtype == 1) {
     switch (epi) {
       PE_TILE_CASE(bf16_t, 0) PE_TILE_CASE(bf16_t, 1) PE_TILE_CASE(bf16_t, 2) PE_TILE_CASE(bf16_t, 3)
       PE_TILE_CASE(bf16_t, 4) PE_TILE_CASE(bf16_t, 5) PE_TILE_CASE(bf16_t, 6)

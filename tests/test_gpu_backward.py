@@ -160,6 +160,33 @@ def test_step_bf16_hd128_g4():
     _compare(cfg, grads, rg, loss, rl, f"{cfg.name} n={cfg.seq_len} L={len(rows)}")
 
 
+def test_step_bf16_wide_tiles():
+    """Hidden 640 (40 strips of 16 columns): the plain-store and accumulate
+    GEMMs whose output is hidden wide take 20-strip tiles (2 tiles of 320
+    columns instead of 2.5 of 256), in the forward and the backward."""
+    cfg = train_small(name="bwd_small_h640", seed=4003, hidden=640, n_layers=1, seq_len=120)
+    w = synth.drafter_weights(cfg, gain_jitter=0.1)
+    inp = synth.train_inputs(cfg)
+    rows = _layout(cfg, cfg.seq_len, cfg.K)
+    labels = _labels(cfg, cfg.seq_len, 9)
+    loss, grads = _run(cfg, w, inp, rows, cfg.K, labels, n_max=cfg.n_max)
+    rl, rg = _oracle(cfg, w, inp, rows, cfg.K, labels)
+    _compare(cfg, grads, rg, loss, rl, f"{cfg.name} n={cfg.seq_len} L={len(rows)}")
+
+
+def test_step_f32_wide_tiles():
+    """fp32 with hidden 320 (20 strips: one 20-strip tile instead of two of 16)."""
+    cfg = synth.config("tiny_f32", hidden=320)
+    w = synth.drafter_weights(cfg, gain_jitter=0.1)
+    n, K = 44, 4
+    inp = synth.train_inputs(cfg, n=n, tag="bwide")
+    rows = _layout(cfg, n, K, tag="bwide")
+    labels = _labels(cfg, n, 5)
+    loss, grads = _run(cfg, w, inp, rows, K, labels, n_max=n)
+    rl, rg = _oracle(cfg, w, inp, rows, K, labels)
+    _compare(cfg, grads, rg, loss, rl, f"tiny_f32 hidden 320 n={n} K={K} L={len(rows)}")
+
+
 @pytest.mark.parametrize("S", [2, 3])
 def test_chunked_steps_accumulate_to_whole(S):
     cfg = synth.config("tiny_f32")
