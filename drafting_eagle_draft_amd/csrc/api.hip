@@ -1183,7 +1183,7 @@ StepLayout step_layout(const pe_model *m, int N, long n, int K, long L) {
   t.z = take(Lp * H * esz);
   t.logits = take(L * V * esz);
   t.dlA = take(tiles_bytes(L, (long)V, m->ktile));
-  t.row_loss = take(L * 4);
+  t.row_loss = take(L * 4 * 3);  // row losses, then the cross-entropy's 2L scratch floats
   const size_t wide = std::max(std::max(H, I), nq * hd);
   t.dx = take(L * H * 4);
   t.dx2 = take(L * H * 4);
@@ -1303,7 +1303,8 @@ pe_status enqueue_backward(const pe_model *m, int32_t N, int32_t n, int32_t K, c
 
   // ---- loss and LM head: dlogits as tiles of [L][V] and of [V][L] (packA)
   void *dlA = ws + SL.dlA;
-  if ((st = chk(launch_ce_tiles(dt, sv.logits, L, V, anc, dep, labels, n, n_lead, loss_scale, F(SL.row_loss), dlA,
+  if ((st = chk(launch_ce_tiles(dt, sv.logits, L, V, anc, dep, labels, n, n_lead, loss_scale, F(SL.row_loss),
+                                F(SL.row_loss) + L, dlA,
                                 packA, s), "cross-entropy launch")) != PE_OK) return st;
   if (loss_out && (st = chk(launch_sum_acc(F(SL.row_loss), L, loss_out, s), "loss sum launch")) != PE_OK) return st;
   if ((st = gemm(dlA, 1, V, L, m->lmT.ptr, m->lmT.NT, m->lmT.KT, m->lmT.N, m->lmT.K, BEPI_STORE, gbuf, H)) != PE_OK)

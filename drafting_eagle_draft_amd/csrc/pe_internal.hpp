@@ -259,10 +259,10 @@ hipError_t launch_pack_t(int dtype, int src_kind, const void *src, long ld, int 
 // anc[i] + dep[i] >= 0) dlogits = loss_scale * (softmax - onehot(label)),
 // zero for the others, written as fragment tiles of [L][V] (dlA) and of its
 // transpose [V][L] (dlT); row_loss[i] = loss_scale * (logsumexp -
-// logit[label]) or 0.
+// logit[label]) or 0.  ce_scratch: 2L floats (row log-sum-exps and labels).
 hipError_t launch_ce_tiles(int dtype, const void *logits, int L, int V, const int *anc, const int *dep,
-                           const int *labels, int n, int n_lead, float loss_scale, float *row_loss, void *dlA,
-                           void *dlT, hipStream_t s);
+                           const int *labels, int n, int n_lead, float loss_scale, float *row_loss, float *ce_scratch,
+                           void *dlA, void *dlT, hipStream_t s);
 // *out += sum of x[0..n) in a fixed order.
 hipError_t launch_sum_acc(const float *x, long n, float *out, hipStream_t s);
 

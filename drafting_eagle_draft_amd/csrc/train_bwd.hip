@@ -111,40 +111,43 @@ __global__ __launch_bounds__(256) void k_pack_t(const void *src, long ld, int R,
 // ---------------------------------------------------------------------------
 // Cross-entropy.
 // ---------------------------------------------------------------------------
-// Cross-entropy over a block of 32 kept rows, writing dlogits straight
-// into the two operand layouts of the LM head's backward GEMMs: fragment
-// tiles of [L][V] (A of dz = dlogits W) and of the transpose [V][L] (A of
-// dW = dlogits^T z).  Pass 1: per-row log-sum-exp, one wave per 4 rows at a
-// time with 16-byte loads (a per-lane maximum over each loaded group, then
-// one rescale).  Pass 2: 256-column blocks through LDS, each written as
-// whole 1 KB tiles of both layouts.  Needs V a multiple of 8.
+// Cross-entropy in two passes.  Pass 1 (k_ce_lse): one wave per kept row
+// finds the row's label (-1 when it is not scored), its log-sum-exp and
+// its loss term, each lane keeping UNR 16-byte loads in flight and folding
+// them into a running maximum and sum (a per-lane maximum over each loaded
+// group, then one rescale).  Pass 2 (k_ce_grad): dlogits of 32 rows x 2048
+// columns per workgroup, 256-column blocks through LDS, the next block's
+// logits loaded while the current one is written, each block stored as
+// whole 1 KB tiles of both operand layouts of the LM head's backward GEMMs:
+// fragment tiles of [L][V] (A of dz = dlogits W) and of the transpose
+// [V][L] (A of dW = dlogits^T z).  Small workgroups over a 2-D grid keep
+// every CU busy to the end.  Needs V a multiple of 8.
 template <typename T>
-__global__ __launch_bounds__(512) void k_ce_tiles(const T *logits, int L, int V, const int *anc, const int *dep,
-                                                  const int *labels, int n, int n_lead, float loss_scale,
-                                                  float *row_loss, u32x4 *dlA, u32x4 *dlT) {
-  constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE;
-  constexpr int CB = 256, PITCH = CB + 8;  // columns per block; padded row pitch (elements)
-  constexpr int NTH = 512;
-  __shared__ float s_lse[32];
-  __shared__ int s_lab[32];
-  __shared__ __attribute__((aligned(16))) T tile[32 * PITCH];
-  const int i0 = blockIdx.x * 32, t = threadIdx.x, w = t >> 6, lane = t & 63;
-  // pass 1: wave w takes rows w, w + 8, w + 16, w + 24
-  for (int rr = w; rr < 32; rr += 8) {
-    const int i = i0 + rr;
-    int lab = -1;
-    if (i < L) {
-      const int pos = anc[i] + dep[i];
-      if (i >= n_lead && pos >= 0 && pos < n) lab = labels[pos];
-      if (lab >= V) lab = -1;
-    }
-    float m = -INFINITY, ssum = 0.f;
-    if (lab >= 0) {
-      const T *row = logits + (long)i * V;
-      for (int v = lane * E; v < V; v += 64 * E) {
-        const u32x4 q = ldg16(row + v);
+__global__ __launch_bounds__(256) void k_ce_lse(const T *logits, int L, int V, const int *anc, const int *dep,
+                                                const int *labels, int n, int n_lead, float loss_scale,
+                                                float *row_loss, float *lse_out, int *lab_out) {
+  constexpr int E = Frag<T>::E, UNR = 8;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (i >= L) return;
+  int lab = -1;
+  const int pos = anc[i] + dep[i];
+  if (i >= n_lead && pos >= 0 && pos < n) lab = labels[pos];
+  if (lab >= V) lab = -1;
+  float m = -INFINITY, ssum = 0.f;
+  if (lab >= 0) {
+    const T *row = logits + (long)i * V;
+    for (int v0 = lane * E; v0 < V; v0 += UNR * 64 * E) {
+      u32x4 q[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int v = v0 + u * 64 * E;
+        q[u] = v < V ? ldg16(row + v) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        if (v0 + u * 64 * E >= V) break;
         T x[E];
-        __builtin_memcpy(x, &q, 16);
+        __builtin_memcpy(x, &q[u], 16);
         float f[E], mx = -INFINITY;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -158,33 +161,66 @@ __global__ __launch_bounds__(512) void k_ce_tiles(const T *logits, int L, int V,
         ssum = acc;
         m = mn;
       }
-      for (int o = 32; o > 0; o >>= 1) {
-        const float mo = __shfl_xor(m, o, 64), so = __shfl_xor(ssum, o, 64);
-        const float mn = fmaxf(m, mo);
-        ssum = (m == -INFINITY ? 0.f : ssum * __expf(m - mn)) + (mo == -INFINITY ? 0.f : so * __expf(mo - mn));
-        m = mn;
-      }
     }
-    if (lane == 0) {
-      const float lse = lab >= 0 ? m + __logf(ssum) : 0.f;
-      s_lse[rr] = lse;
-      s_lab[rr] = lab;
-      if (i < L) row_loss[i] = lab >= 0 ? loss_scale * (lse - to_f32<T>(logits[(long)i * V + lab])) : 0.f;
+    for (int o = 32; o > 0; o >>= 1) {
+      const float mo = __shfl_xor(m, o, 64), so = __shfl_xor(ssum, o, 64);
+      const float mn = fmaxf(m, mo);
+      ssum = (m == -INFINITY ? 0.f : ssum * __expf(m - mn)) + (mo == -INFINITY ? 0.f : so * __expf(mo - mn));
+      m = mn;
     }
   }
+  if (lane == 0) {
+    const float lse = lab >= 0 ? m + __logf(ssum) : 0.f;
+    lse_out[i] = lse;
+    lab_out[i] = lab;
+    row_loss[i] = lab >= 0 ? loss_scale * (lse - to_f32<T>(logits[(long)i * V + lab])) : 0.f;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_ce_grad(const T *logits, int L, int V, float loss_scale,
+                                                 const float *lse_in, const int *lab_in, u32x4 *dlA, u32x4 *dlT) {
+  constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE;
+  constexpr int CB = 256, PITCH = CB + 8;  // columns per block; padded row pitch (elements)
+  constexpr int NTH = 256, NBLK = 8;       // threads; blocks per workgroup
+  constexpr int PER = 32 * (CB / E) / NTH; // 16-byte chunks per thread and block
+  __shared__ float s_lse[32];
+  __shared__ int s_lab[32];
+  __shared__ __attribute__((aligned(16))) T tile[32 * PITCH];
+  const int i0 = blockIdx.x * 32, t = threadIdx.x;
+  const int vbeg = blockIdx.y * NBLK * CB, vend = min(V, vbeg + NBLK * CB);
+  if (t < 32) {
+    const int i = i0 + t;
+    s_lab[t] = i < L ? lab_in[i] : -1;
+    s_lse[t] = i < L ? lse_in[i] : 0.f;
+  }
   __syncthreads();
+  // chunk k of this thread: row (t + k NTH) / (CB / E), columns E * ((t + k NTH) % (CB / E)) ..
+  auto load = [&](int v0, u32x4 (&q)[PER]) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = t + k * NTH, rr = idx / (CB / E), cc = (idx - rr * (CB / E)) * E, v = v0 + cc;
+      q[k] = s_lab[rr] >= 0 && v < V ? ldg16(logits + (long)(i0 + rr) * V + v) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
   const int KTA = (V + KTILE - 1) / KTILE, KTT = (L + KTILE - 1) / KTILE;
   const int RG = (L + 15) / 16, VS = (V + 15) / 16;
-  for (int v0 = 0; v0 < V; v0 += CB) {
-    // 32 rows x CB columns of dlogits into LDS, E columns per thread and step
-    for (int idx = t; idx < 32 * (CB / E); idx += NTH) {
-      const int rr = idx / (CB / E), cc = (idx - rr * (CB / E)) * E;
-      const int v = v0 + cc, lab = s_lab[rr];
+  u32x4 nxt[PER];
+  load(vbeg, nxt);
+  for (int v0 = vbeg; v0 < vend; v0 += CB) {
+    u32x4 cur[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) cur[k] = nxt[k];
+    if (v0 + CB < vend) load(v0 + CB, nxt);
+    // 32 rows x CB columns of dlogits into LDS, E columns per chunk
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = t + k * NTH, rr = idx / (CB / E), cc = (idx - rr * (CB / E)) * E, v = v0 + cc;
+      const int lab = s_lab[rr];
       T out[E];
       if (lab >= 0 && v < V) {
-        const u32x4 q = ldg16(logits + (long)(i0 + rr) * V + v);
         T x[E];
-        __builtin_memcpy(x, &q, 16);
+        __builtin_memcpy(x, &cur[k], 16);
         const float lse = s_lse[rr];
 #pragma unroll
         for (int e = 0; e < E; ++e)
@@ -1209,19 +1245,27 @@ hipError_t launch_pack_t(int dtype, int src_kind, const void *src, long ld, int 
 }
 
 hipError_t launch_ce_tiles(int dtype, const void *logits, int L, int V, const int *anc, const int *dep,
-                           const int *labels, int n, int n_lead, float loss_scale, float *row_loss, void *dlA,
-                           void *dlT, hipStream_t s) {
+                           const int *labels, int n, int n_lead, float loss_scale, float *row_loss, float *ce_scratch,
+                           void *dlA, void *dlT, hipStream_t s) {
   if (L <= 0) return hipSuccess;
   if (V % 8) return hipErrorInvalidValue;
-  const dim3 grid(nblocks(L, 32));
-  if (dtype == 1)
-    hipLaunchKernelGGL(k_ce_tiles<bf16_t>, grid, dim3(512), 0, s, reinterpret_cast<const bf16_t *>(logits), L, V, anc,
-                       dep, labels, n, n_lead, loss_scale, row_loss, reinterpret_cast<u32x4 *>(dlA),
-                       reinterpret_cast<u32x4 *>(dlT));
-  else
-    hipLaunchKernelGGL(k_ce_tiles<float>, grid, dim3(512), 0, s, reinterpret_cast<const float *>(logits), L, V, anc,
-                       dep, labels, n, n_lead, loss_scale, row_loss, reinterpret_cast<u32x4 *>(dlA),
-                       reinterpret_cast<u32x4 *>(dlT));
+  float *lse = ce_scratch;
+  int *lab = reinterpret_cast<int *>(ce_scratch + L);
+  const dim3 grid(nblocks(L, 32), nblocks(V, 8 * 256));
+  if (grid.y > 65535) return hipErrorInvalidValue;
+  if (dtype == 1) {
+    const bf16_t *lg = reinterpret_cast<const bf16_t *>(logits);
+    hipLaunchKernelGGL(k_ce_lse<bf16_t>, dim3(nblocks(L, 4)), dim3(256), 0, s, lg, L, V, anc, dep, labels, n, n_lead,
+                       loss_scale, row_loss, lse, lab);
+    hipLaunchKernelGGL(k_ce_grad<bf16_t>, grid, dim3(256), 0, s, lg, L, V, loss_scale, lse, lab,
+                       reinterpret_cast<u32x4 *>(dlA), reinterpret_cast<u32x4 *>(dlT));
+  } else {
+    const float *lg = reinterpret_cast<const float *>(logits);
+    hipLaunchKernelGGL(k_ce_lse<float>, dim3(nblocks(L, 4)), dim3(256), 0, s, lg, L, V, anc, dep, labels, n, n_lead,
+                       loss_scale, row_loss, lse, lab);
+    hipLaunchKernelGGL(k_ce_grad<float>, grid, dim3(256), 0, s, lg, L, V, loss_scale, lse, lab,
+                       reinterpret_cast<u32x4 *>(dlA), reinterpret_cast<u32x4 *>(dlT));
+  }
   return hipGetLastError();
 }
 
