@@ -374,7 +374,7 @@ pe_status check_cfg(const pe_config *c) {
 
 // Workspace of the training-shape forward.
 struct TrainLayout {
-  size_t anc, dep, inv, yfc, xres, u, q, kall, vall, k0, v0, attn, h, keys, total;
+  size_t anc, dep, inv, rope, yfc, xres, u, q, kall, vall, k0, v0, attn, h, keys, total;
 };
 
 TrainLayout train_layout(const pe_model *m, long n, int K, long L) {
@@ -386,6 +386,7 @@ TrainLayout train_layout(const pe_model *m, long n, int K, long L) {
   t.anc = take((size_t)L * 4);
   t.dep = take((size_t)L * 4);
   t.inv = take((size_t)n * K * 4);
+  t.rope = take(c.n_layers > 0 ? (size_t)n * (hd / 2) * 8 : 0);
   t.yfc = take((size_t)(n + 1) * H * 4);
   t.xres = take((size_t)L * H * 4);
   const size_t Lp = (size_t)(L + 15) / 16 * 16;  // tiled activations hold whole 16-row groups
@@ -1043,6 +1044,9 @@ pe_status enqueue_train(const pe_model *m, const pe_mask *mask, int32_t N, int32
                           sv ? sv->layer.empty() ? sv->xN : sv->layer[0].x : xres, s);
     if (e != hipSuccess) return hip_fail(e, "fusion launch");
   }
+  float *rope = reinterpret_cast<float *>(ws + W.rope);
+  if (N > 0 && (e = launch_rope_table(m->inv_freq, n, hd / 2, rope, s)) != hipSuccess)
+    return hip_fail(e, "rotation table launch");
   for (int l = 0; l < N; ++l) {
     const LayerT &Lw = m->layers[l];
     StepLayer B;
@@ -1060,7 +1064,7 @@ pe_status enqueue_train(const pe_model *m, const pe_mask *mask, int32_t N, int32
       TileGemmParams p{};
       p.A = B.u1; p.lda = H; p.M = L; p.a_tiled = 1;
       p.q = B.q; p.kall = B.kall; p.vall = B.vall; p.k0 = B.k0; p.v0 = B.v0;
-      p.anc = anc; p.dep = dep; p.inv_freq = m->inv_freq;
+      p.anc = anc; p.dep = dep; p.rope = rope;
       p.n = n; p.nq = nq; p.nkv = nkv; p.hd = hd;
       if ((st = gemm(Lw.qkv, BEPI_QKV, p)) != PE_OK) return st;
     }
@@ -1159,6 +1163,7 @@ StepLayout step_layout(const pe_model *m, int N, long n, int K, long L) {
   t.tl.anc = take((size_t)L * 4);
   t.tl.dep = take((size_t)L * 4);
   t.tl.inv = take((size_t)n * K * 4);
+  t.tl.rope = take(N > 0 ? (size_t)n * (hd / 2) * 8 : 0);
   t.tl.yfc = take((size_t)(n + 1) * H * 4);
   t.tl.keys = take((size_t)L * 8);
   t.off.resize(N);

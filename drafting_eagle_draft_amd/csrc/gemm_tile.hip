@@ -341,18 +341,22 @@ void k_gemm_tile(TileGemmParams p) {
           for (int jj = 0; jj < RP / 16; ++jj) {
             const int j = ps * (RP / 16) + jj;
             const int m = m0 + (wm * 8 + j) * 16 + c16;
-            const int pos = m < p.M ? p.anc[m] + p.dep[m] : 0;
+            // table row of the position (clamped: rows past M, or cells that
+            // break the layout, read some row of the table)
+            const int pos = min(max(m < p.M ? p.anc[m] + p.dep[m] : 0, 0), p.n - 1);
             T *srow = stg + (jj * 16 + c16) * SP;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const floatx4 v = acc[i][j];
               if (rot) {
                 const int li = 8 * i + 2 * g;  // local index of the lower dimension pair
+                // cos, sin of pairs lo0 + li and lo0 + li + 1
+                const floatx4 cs =
+                    *reinterpret_cast<const floatx4 *>(p.rope + 2 * ((long)pos * half + lo0 + li));
                 float lo[2], hi[2];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                  float c, sn;
-                  rope_cs(pos, p.inv_freq[lo0 + li + t], c, sn);
+                  const float c = cs[2 * t], sn = cs[2 * t + 1];
                   lo[t] = v[2 * t] * c - v[2 * t + 1] * sn;
                   hi[t] = v[2 * t + 1] * c + v[2 * t] * sn;
                 }

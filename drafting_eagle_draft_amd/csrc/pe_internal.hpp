@@ -195,9 +195,11 @@ struct TileGemmParams {
   void *gu;  // SWIGLU_SAVE: gate | up pre-activations [M][2I], row-major dtype
   // QKV: q [M][nq][hd], kall/vall [M][nkv][hd], depth-0 rows also to
   // k0/v0 [n][nkv][hd] at their position.
+  // Rotation: cos and sin of position p and frequency pair i at
+  // rope[2 (p hd/2 + i)] and the float after it, for p < n.
   void *q, *kall, *vall, *k0, *v0;
   const int *anc, *dep;
-  const double *inv_freq;
+  const float *rope;
   int n, nq, nkv, hd;
 };
 
@@ -222,6 +224,10 @@ hipError_t launch_gather_rows(const int2 *table, int nK, const int *rows, int L,
                               int *inv, hipStream_t s);
 hipError_t launch_mask_materialize(const int2 *table, int nK, const int *rows, int L, unsigned char *out,
                                    hipStream_t s);
+// The rotation table of the training-shape QKV epilogue: tab[2 (p half + i)]
+// and the float after it hold the cos and sin that rope_cs gives for
+// position p < n and frequency pair i < half.
+hipError_t launch_rope_table(const double *inv_freq, int n, int half, float *tab, hipStream_t s);
 hipError_t launch_train_fuse(int dtype, const float *Y, const void *embed, const int *tok,
                              const void *mask_emb, const int *anc, const int *dep, int L, int n, int H,
                              int V, float *x, hipStream_t s);

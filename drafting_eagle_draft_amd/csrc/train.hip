@@ -9,7 +9,7 @@
 // Kept cells ("rows") are processed in ascending grid order.  Cell (p, d)
 // attends to depth-0 cells at positions <= a and to the kept cells (a+j, j),
 // 1 <= j <= d, of its own rollout.
-#include "pe_internal.hpp"
+#include "pe_epilogue.hpp"
 
 
 namespace pe {
@@ -531,6 +531,18 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
   }
 }
 
+// Rotation table: one thread per (position, frequency pair), the same
+// fp64 angle reduction and single-precision sincos as the epilogues that
+// rotate in place.
+__global__ __launch_bounds__(256) void k_rope_table(const double *inv_freq, int n, int half, float *tab) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)n * half) return;
+  const int pos = (int)(idx / half), i = (int)(idx - (long)pos * half);
+  float c, sn;
+  rope_cs(pos, inv_freq[i], c, sn);
+  *reinterpret_cast<float2 *>(tab + 2 * idx) = make_float2(c, sn);
+}
+
 unsigned blocks_for(long n, int threads) { return (unsigned)((n + threads - 1) / threads); }
 
 }  // namespace
@@ -574,6 +586,12 @@ hipError_t launch_matvec_tiled(int dtype, const u32x4 *wt, int NT, int KT, int N
   else
     hipLaunchKernelGGL(k_matvec_tiled<float>, grid, dim3(256), 0, s, wt, NT, KT, N,
                        reinterpret_cast<const float *>(x), K, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(const double *inv_freq, int n, int half, float *tab, hipStream_t s) {
+  if (n <= 0 || half <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rope_table, dim3(blocks_for((long)n * half, 256)), dim3(256), 0, s, inv_freq, n, half, tab);
   return hipGetLastError();
 }
 
