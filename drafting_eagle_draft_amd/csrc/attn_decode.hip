@@ -225,8 +225,8 @@ void k_attn_decode(AttnParams p) {
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sacc[kb][r]);
-    mt = fmaxf(mt, shfl_xor_f(mt, 16));
-    mt = fmaxf(mt, shfl_xor_f(mt, 32));
+    mt = xor_max<16>(mt);
+    mt = xor_max<32>(mt);
     // Running maximum in the exp2 domain (the scale is positive, so scaling
     // commutes with the maximum); weights 2^(s*scale - m).
     const float m_new = fmaxf(m_run, mt * p.scale_log2);
@@ -330,8 +330,8 @@ void k_attn_decode(AttnParams p) {
   }
 
   float l_tot = l_lane;
-  l_tot += shfl_xor_f(l_tot, 16);
-  l_tot += shfl_xor_f(l_tot, 32);
+  l_tot = xor_sum<16>(l_tot);
+  l_tot = xor_sum<32>(l_tot);
 
   const int hq = p.nq * HD;
   auto write_out = [&](const floatx4 (&o)[ND], float inv_l) {
@@ -563,8 +563,8 @@ __global__ __launch_bounds__(256) void k_attn_decode_lds(AttnParams p) {
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sacc[kb][r]);
-    mt = fmaxf(mt, shfl_xor_f(mt, 16));
-    mt = fmaxf(mt, shfl_xor_f(mt, 32));
+    mt = xor_max<16>(mt);
+    mt = xor_max<32>(mt);
     // Running maximum in the exp2 domain (the scale is positive, so scaling
     // commutes with the maximum); weights 2^(s*scale - m).
     const float m_new = fmaxf(m_run, mt * p.scale_log2);
@@ -635,8 +635,8 @@ __global__ __launch_bounds__(256) void k_attn_decode_lds(AttnParams p) {
   (void)BLK;
 
   float l_tot = l_lane;
-  l_tot += shfl_xor_f(l_tot, 16);
-  l_tot += shfl_xor_f(l_tot, 32);
+  l_tot = xor_sum<16>(l_tot);
+  l_tot = xor_sum<32>(l_tot);
 
   const int hq = p.nq * HD;
   if (Sb == 1) {

@@ -109,6 +109,38 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// Sum or maximum of v over lane pairs (l, l ^ M), M 16 or 32, through the
+// gfx950 lane-swap instructions (v_permlane16/32_swap: a register move, no
+// LDS round trip).  With both operands v, each lane receives its own value
+// and its partner's, in row order; the two operations commute, so both
+// lanes of a pair get the same result as v op shfl_xor_f(v, M).
+template <int M>
+__device__ __forceinline__ void xor_pair(float v, float &a, float &b) {
+  static_assert(M == 16 || M == 32, "lane-swap distance");
+  const unsigned u = __float_as_uint(v);
+  if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+}
+template <int M>
+__device__ __forceinline__ float xor_sum(float v) {
+  float a, b;
+  xor_pair<M>(v, a, b);
+  return a + b;
+}
+template <int M>
+__device__ __forceinline__ float xor_max(float v) {
+  float a, b;
+  xor_pair<M>(v, a, b);
+  return fmaxf(a, b);
+}
+
 // Order-preserving map of a float onto uint32 (larger float -> larger code).
 __device__ __forceinline__ unsigned ordered_bits(float v) {
   unsigned u = __float_as_uint(v);

@@ -379,8 +379,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sacc[qb][kb][r]);
-        mt = fmaxf(mt, shfl_xor_f(mt, 16));
-        mt = fmaxf(mt, shfl_xor_f(mt, 32));
+        mt = xor_max<16>(mt);
+        mt = xor_max<32>(mt);
         // Running maximum in the exp2 domain (positive scale commutes with
         // the maximum); weights 2^(s*scale - m).
         const float m_new = fmaxf(m_run[qb], mt * p.scale_log2);
@@ -489,8 +489,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
           for (int e = 0; e < E; ++e) part += to_f32<T>(qq[e]) * to_f32<T>(kk[e]);
         }
       }
-      part += shfl_xor_f(part, 16);
-      part += shfl_xor_f(part, 32);
+      part = xor_sum<16>(part);
+      part = xor_sum<32>(part);
       if (ci < 0) continue;
       const float sc = part * p.scale_log2;
       const float m_new = fmaxf(m_run[qb], sc);
@@ -513,8 +513,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
     }
 
     float l_tot = l_lane[qb];
-    l_tot += shfl_xor_f(l_tot, 16);
-    l_tot += shfl_xor_f(l_tot, 32);
+    l_tot = xor_sum<16>(l_tot);
+    l_tot = xor_sum<32>(l_tot);
     // Softmax statistics for the backward: weights are 2^(s * scale_log2 - lse).
     if (p.lse && valid[qb] && g == 0) p.lse[(long)row[qb] * p.nq + gk * G + hl[qb]] = m_run[qb] + log2f(l_tot);
     if (valid[qb]) {
