@@ -47,11 +47,7 @@ __device__ __forceinline__ void load4<bf16_t>(const bf16_t *src, float v[4]) {
   v[3] = __uint_as_float(t.y & 0xFFFF0000u);
 }
 
-__device__ __forceinline__ float sum_groups(float v) {
-  v += shfl_xor_f(v, 16);
-  v += shfl_xor_f(v, 32);
-  return v;
-}
+__device__ __forceinline__ float sum_groups(float v) { return xor_sum<32>(xor_sum<16>(v)); }
 
 // Rotation angle reduced to [-pi, pi] in fp64 before the fp32 sine/cosine.
 __device__ __forceinline__ void rope_cs(int pos, double inv_freq, float &c, float &s) {

@@ -102,8 +102,8 @@ __global__ __launch_bounds__(256) void k_matvec_tiled(const u32x4 *wt, int NT, i
   __syncthreads();
   if (w != 0) return;
   float acc = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
-  acc += shfl_xor_f(acc, 16);
-  acc += shfl_xor_f(acc, 32);
+  acc = xor_sum<16>(acc);
+  acc = xor_sum<32>(acc);
   const int n = s * 16 + c16;
   if (g == 0 && n < N) y[n] = acc;
 }
@@ -273,13 +273,20 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
   const T *v0 = reinterpret_cast<const T *>(p.v0) + gk * HD;
 
   floatx4 oacc[QB][ND];
+  // Row sums of the weights: bf16 accumulates them on the matrix cores
+  // (the P^T fragments times a fragment of ones: every lane holds its
+  // query row's whole sum); fp32 keeps per-lane partial sums on the vector
+  // units, added over the four lane groups at the end.
   float m_run[QB], l_lane[QB];
+  floatx4 lacc[QB];
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
     for (int d = 0; d < ND; ++d) oacc[qb][d] = floatx4{0.f, 0.f, 0.f, 0.f};
     m_run[qb] = -INFINITY;
     l_lane[qb] = 0.f;
+    lacc[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
   // bf16 operand reads (LDS byte addresses): K key kb*16 + c16, chunk
@@ -300,7 +307,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
 
   // Key/value tiles are loaded PF tiles ahead into a register ring; tile t
   // goes through LDS to the matrix cores.
-  constexpr int PF = 3;
+  constexpr int PF = 2;
   u32x4 kreg[PF][MAXC], vreg[PF][MAXC];
   auto gload = [&](int jt, u32x4 (&kr)[MAXC], u32x4 (&vr)[MAXC]) {
 #pragma unroll
@@ -393,13 +400,14 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             pv[kb][r] = fast_exp2(fmaf(sacc[qb][kb][r], p.scale_log2, -msub));
-            ps += pv[kb][r];
+            if constexpr (!TR) ps += pv[kb][r];
           }
-        l_lane[qb] = l_lane[qb] * alpha + ps;
+        if constexpr (!TR) l_lane[qb] = l_lane[qb] * alpha + ps;
         m_run[qb] = m_new;
         if (__ballot(alpha != 1.0f)) {
 #pragma unroll
           for (int d = 0; d < ND; ++d) oacc[qb][d] *= alpha;
+          if constexpr (TR) lacc[qb] *= alpha;
         }
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -425,6 +433,10 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) oacc[qb][d] = Mma<T>::run(vf, pbf[qb][c2], oacc[qb][d]);
           }
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) lacc[qb] = Mma<T>::run(ones, pbf[qb][c2], lacc[qb]);
       } else {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -469,6 +481,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
   T *out = reinterpret_cast<T *>(p.out);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
+    if constexpr (TR) l_lane[qb] = lacc[qb][0];  // the whole row sum, in every lane group
     for (int j = 1; j < p.K; ++j) {
       int ci = -1;
       if (valid[qb] && j <= d_q[qb]) {
@@ -496,7 +509,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
       const float m_new = fmaxf(m_run[qb], sc);
       const float alpha = m_run[qb] == -INFINITY ? 0.f : fast_exp2(m_run[qb] - m_new);
       const float pc = fast_exp2(sc - m_new);
-      l_lane[qb] = l_lane[qb] * alpha + (g == 0 ? pc : 0.f);
+      l_lane[qb] = l_lane[qb] * alpha + (TR || g == 0 ? pc : 0.f);
       m_run[qb] = m_new;
       const T *vr = vall + (long)ci * kvs;
 #pragma unroll
@@ -513,8 +526,10 @@ __global__ __launch_bounds__(64 * NW) void k_attn_train(TrainAttnParams p) {
     }
 
     float l_tot = l_lane[qb];
-    l_tot = xor_sum<16>(l_tot);
-    l_tot = xor_sum<32>(l_tot);
+    if constexpr (!TR) {
+      l_tot = xor_sum<16>(l_tot);
+      l_tot = xor_sum<32>(l_tot);
+    }
     // Softmax statistics for the backward: weights are 2^(s * scale_log2 - lse).
     if (p.lse && valid[qb] && g == 0) p.lse[(long)row[qb] * p.nq + gk * G + hl[qb]] = m_run[qb] + log2f(l_tot);
     if (valid[qb]) {

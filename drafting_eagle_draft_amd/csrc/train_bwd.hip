@@ -506,8 +506,8 @@ __global__ __launch_bounds__(256) void k_matvec_acc(const u32x4 *wt, int NT, int
   __syncthreads();
   if (w != 0) return;
   float acc = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
-  acc += shfl_xor_f(acc, 16);
-  acc += shfl_xor_f(acc, 32);
+  acc = xor_sum<16>(acc);
+  acc = xor_sum<32>(acc);
   const int nrow = s * 16 + c16;
   if (g == 0 && nrow < N) y[nrow] += acc;
 }
@@ -820,10 +820,10 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dq(AttnBwdParams p) {
           }
         }
       }
-      sp += shfl_xor_f(sp, 16);
-      sp += shfl_xor_f(sp, 32);
-      dp += shfl_xor_f(dp, 16);
-      dp += shfl_xor_f(dp, 32);
+      sp = xor_sum<16>(sp);
+      sp = xor_sum<32>(sp);
+      dp = xor_sum<16>(dp);
+      dp = xor_sum<32>(dp);
       if (ci < 0) continue;
       const float pr = fast_exp2(fmaf(sp, p.scale_log2, -lse[qb]));
       const float dsv = pr * (dp - Dq[qb]);
