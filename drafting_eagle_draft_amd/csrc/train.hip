@@ -114,20 +114,26 @@ __global__ __launch_bounds__(256) void k_matvec_tiled(const u32x4 *wt, int NT, i
 
 // x[i] = E[tok[p_i]] + Y[p_i] at depth 0, mask_emb + Y[n] deeper (Y = fc out).
 template <typename T>
-__global__ void k_train_fuse(const float *Y, const T *embed, const int *tok, const T *mask_emb,
-                             const int *anc, const int *dep, int L, int n, int H, int V, float *x) {
+__global__ __launch_bounds__(256) void k_train_fuse(const float *Y, const T *embed, const int *tok,
+                                                    const T *mask_emb, const int *anc, const int *dep, int L,
+                                                    int n, int H, int V, float *x) {
+  // one thread per 4 consecutive columns of a row (H is a multiple of 4)
+  const int H4 = H >> 2;
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long)L * H) return;
-  const int i = (int)(idx / H), c = (int)(idx - (long)i * H);
+  if (idx >= (long)L * H4) return;
+  const int i = (int)(idx / H4), c = (int)(idx - (long)i * H4) * 4;
   const int d = dep[i], pos = min(max(anc[i] + d, 0), n - 1);
-  float v;
+  float e[4];
+  floatx4 y;
   if (d == 0) {
     const int t = min(max(tok[pos], 0), V - 1);
-    v = to_f32<T>(embed[(long)t * H + c]) + Y[(long)pos * H + c];
+    load4<T>(embed + (long)t * H + c, e);
+    y = *reinterpret_cast<const floatx4 *>(Y + (long)pos * H + c);
   } else {
-    v = to_f32<T>(mask_emb[c]) + Y[(long)n * H + c];
+    load4<T>(mask_emb + c, e);
+    y = *reinterpret_cast<const floatx4 *>(Y + (long)n * H + c);
   }
-  x[idx] = v;
+  *reinterpret_cast<floatx4 *>(x + (long)i * H + c) = floatx4{e[0] + y[0], e[1] + y[1], e[2] + y[2], e[3] + y[3]};
 }
 
 // u = x / sqrt(mean(x^2) + eps) * g for one 16-row group per block, written
@@ -613,7 +619,8 @@ hipError_t launch_rope_table(const double *inv_freq, int n, int half, float *tab
 hipError_t launch_train_fuse(int dtype, const float *Y, const void *embed, const int *tok,
                              const void *mask_emb, const int *anc, const int *dep, int L, int n, int H,
                              int V, float *x, hipStream_t s) {
-  const unsigned b = blocks_for((long)L * H, 256);
+  if (H % 4) return hipErrorInvalidValue;
+  const unsigned b = blocks_for((long)L * (H / 4), 256);
   if (dtype == 1)
     hipLaunchKernelGGL(k_train_fuse<bf16_t>, dim3(b), dim3(256), 0, s, Y,
                        reinterpret_cast<const bf16_t *>(embed), tok,
