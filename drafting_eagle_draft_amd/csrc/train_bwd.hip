@@ -291,13 +291,24 @@ __global__ __launch_bounds__(256) void k_rms_bwd(const float *x, const float *ga
     if (i >= L) break;
     const float4 *xr = reinterpret_cast<const float4 *>(x + (long)i * H);
     const float4 *dyr = reinterpret_cast<const float4 *>(dy + (long)i * H);
-    float4 xv[NCH], dv[NCH];
+    float4 xv[NCH], dv[NCH], ev[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const int c4 = lane + 64 * k;
       const bool ok = c4 < H4;
       xv[k] = ok ? xr[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
       dv[k] = ok ? dyr[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    // the residual gradient's row too, in flight with x and dy (up to 12
+    // chunks per lane: beyond, the extra registers would halve the waves)
+    constexpr bool PRE = NCH <= 12;
+    if (PRE && dres) {
+      const float4 *er = reinterpret_cast<const float4 *>(dres + (long)i * H);
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) {
+        const int c4 = lane + 64 * k;
+        ev[k] = c4 < H4 ? er[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
     float ss = 0.f, sgx = 0.f;
 #pragma unroll
@@ -320,7 +331,7 @@ __global__ __launch_bounds__(256) void k_rms_bwd(const float *x, const float *ga
       float4 v = make_float4(r * g4.x * d4.x - x4.x * coef, r * g4.y * d4.y - x4.y * coef,
                              r * g4.z * d4.z - x4.z * coef, r * g4.w * d4.w - x4.w * coef);
       if (dres) {
-        const float4 e = reinterpret_cast<const float4 *>(dres + (long)i * H)[c4];
+        const float4 e = PRE ? ev[k] : reinterpret_cast<const float4 *>(dres + (long)i * H)[c4];
         v.x += e.x; v.y += e.y; v.z += e.z; v.w += e.w;
       }
       reinterpret_cast<float4 *>(dx + (long)i * H)[c4] = v;
@@ -363,15 +374,24 @@ __global__ __launch_bounds__(256) void k_colsum_acc(const float *part, int nblk,
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_swiglu_bwd(const float *dh, const T *gu, int L, int I, T *dgu) {
+  // one thread per four consecutive columns i .. i+3 of a row (I is a multiple of 4)
+  const int I4 = I >> 2;
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long)L * I) return;
-  const long m = idx / I;
-  const int i = (int)(idx - m * I);
-  const float a = to_f32<T>(gu[m * 2 * I + i]), b = to_f32<T>(gu[m * 2 * I + I + i]);
-  const float sg = 1.f / (1.f + __expf(-a));
-  const float d = dh[idx];
-  dgu[m * 2 * I + i] = from_f32<T>(d * b * sg * (1.f + a * (1.f - sg)));
-  dgu[m * 2 * I + I + i] = from_f32<T>(d * a * sg);
+  if (idx >= (long)L * I4) return;
+  const long m = idx / I4;
+  const int i = (int)(idx - m * I4) * 4;
+  float a[4], b[4], dg[4], du[4];
+  load4<T>(gu + m * 2 * I + i, a);
+  load4<T>(gu + m * 2 * I + I + i, b);
+  const floatx4 d = *reinterpret_cast<const floatx4 *>(dh + m * I + i);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float sg = 1.f / (1.f + __expf(-a[e]));
+    dg[e] = d[e] * b[e] * sg * (1.f + a[e] * (1.f - sg));
+    du[e] = d[e] * a[e] * sg;
+  }
+  store4<T>(dgu + m * 2 * I + i, dg);
+  store4<T>(dgu + m * 2 * I + I + i, du);
 }
 
 // ---------------------------------------------------------------------------
@@ -1306,7 +1326,8 @@ hipError_t launch_colsum_acc(const float *part, int nblk, int H, float *out, hip
 }
 
 hipError_t launch_swiglu_bwd(int dtype, const float *dh, const void *gu, int L, int I, void *dgu, hipStream_t s) {
-  const unsigned b = nblocks((long)L * I, 256);
+  if (I % 4) return hipErrorInvalidValue;
+  const unsigned b = nblocks((long)L * (I / 4), 256);
   if (dtype == 1)
     hipLaunchKernelGGL(k_swiglu_bwd<bf16_t>, dim3(b), dim3(256), 0, s, dh, reinterpret_cast<const bf16_t *>(gu), L,
                        I, reinterpret_cast<bf16_t *>(dgu));
