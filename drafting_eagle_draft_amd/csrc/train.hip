@@ -145,25 +145,32 @@ __global__ __launch_bounds__(256) void k_rmsnorm_tiled(const float *x, const flo
   constexpr int E = Frag<T>::E, KTILE = Frag<T>::KTILE;
   __shared__ float rstd[16];
   const int grp = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // Sums of squares: wave w takes rows 4w..4w+3 together (four independent
-  // 16-byte loads per step).
+  // Sums of squares: wave w takes rows 4w..4w+3 together, four column steps
+  // at a time (sixteen independent 16-byte loads in flight per lane, with no
+  // branch around them: rows past M read row 0, whose sums go unused;
+  // columns past H read as zeros).
   {
     float s[4] = {0.f, 0.f, 0.f, 0.f};
     const float *xr[4];
-    bool ok[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = grp * 16 + w * 4 + r;
-      ok[r] = row < M;
-      xr[r] = x + (long)(ok[r] ? row : 0) * H;
+      xr[r] = x + (long)(row < M ? row : 0) * H;
     }
-    for (int c = lane * 4; c < H; c += 256) {
+    for (int c0 = lane * 4; c0 < H; c0 += 4 * 256) {
+      floatx4 v[4][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (!ok[r]) continue;
-        const floatx4 v = *reinterpret_cast<const floatx4 *>(xr[r] + c);
-        s[r] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-      }
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = c0 + 256 * u;
+          v[u][r] = c < H ? *reinterpret_cast<const floatx4 *>(xr[r] + c) : floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s[r] += v[u][r].x * v[u][r].x + v[u][r].y * v[u][r].y + v[u][r].z * v[u][r].z + v[u][r].w * v[u][r].w;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -178,22 +185,33 @@ __global__ __launch_bounds__(256) void k_rmsnorm_tiled(const float *x, const flo
   const int row = grp * 16 + c16;
   const float rs = rstd[c16];
   const float *xrow = x + (long)(row < M ? row : 0) * H;
-  for (int kt = w; kt < KT; kt += 4) {
-    const int k = kt * KTILE + g * E;
-    float xv[E], gv[E];
+  // Four k tiles of the wave at a time: their row and gain loads go out
+  // together before any is used.
+  for (int kt0 = w; kt0 < KT; kt0 += 16) {
+    floatx4 xa[4][E / 4], ga[4][E / 4];
 #pragma unroll
-    for (int q = 0; q < E / 4; ++q) {
-      const floatx4 a = *reinterpret_cast<const floatx4 *>(xrow + k + 4 * q);
-      const floatx4 b = *reinterpret_cast<const floatx4 *>(gain + k + 4 * q);
-      xv[4 * q] = a.x; xv[4 * q + 1] = a.y; xv[4 * q + 2] = a.z; xv[4 * q + 3] = a.w;
-      gv[4 * q] = b.x; gv[4 * q + 1] = b.y; gv[4 * q + 2] = b.z; gv[4 * q + 3] = b.w;
+    for (int t = 0; t < 4; ++t) {
+      const int kt = kt0 + 4 * t;
+      const int k = (kt < KT ? kt : kt0) * KTILE + g * E;
+#pragma unroll
+      for (int q = 0; q < E / 4; ++q) {
+        xa[t][q] = *reinterpret_cast<const floatx4 *>(xrow + k + 4 * q);
+        ga[t][q] = *reinterpret_cast<const floatx4 *>(gain + k + 4 * q);
+      }
     }
-    T vals[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) vals[e] = from_f32<T>(row < M ? xv[e] * rs * gv[e] : 0.f);
-    u32x4 v;
-    __builtin_memcpy(&v, vals, 16);
-    stg16(u + ((long)(grp * KT + kt) * 64 + lane) * E, v);
+    for (int t = 0; t < 4; ++t) {
+      const int kt = kt0 + 4 * t;
+      if (kt >= KT) break;
+      T vals[E];
+#pragma unroll
+      for (int q = 0; q < E / 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vals[4 * q + e] = from_f32<T>(row < M ? xa[t][q][e] * rs * ga[t][q][e] : 0.f);
+      u32x4 v;
+      __builtin_memcpy(&v, vals, 16);
+      stg16(u + ((long)(grp * KT + kt) * 64 + lane) * E, v);
+    }
   }
 }
 

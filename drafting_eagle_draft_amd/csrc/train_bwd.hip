@@ -1183,63 +1183,84 @@ __global__ __launch_bounds__(256) void k_attn_bwd_reduce(AttnBwdParams p) {
 // dK, dV of the rollout cells (depth >= 1): cell c = (a + j, j) is seen by
 // the kept cells (a + d, d), j <= d < K, of its own rollout, each with the G
 // heads of the kv head.  One wave per (cell, kv head); lane = dimension.
-template <typename T>
+template <typename T, int HD>
 __global__ __launch_bounds__(256) void k_attn_bwd_chain(AttnBwdParams p) {
+  // A wave step covers HPW query heads of one deeper cell: LPH lanes per
+  // head row, four dimensions per lane (8-byte loads for bf16), so the
+  // scores' reductions stay within 16- or 32-lane groups, and the loads of
+  // a cell's whole chain go out before any is used.
+  constexpr int LPH = HD / 4, HPW = 64 / LPH;
   const long wid = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wid >= (long)p.L * p.nkv) return;
   const int c = (int)(wid / p.nkv), gk = (int)(wid - (long)c * p.nkv);
   const int j = p.dep[c], a = p.anc[c];
   if (j == 0 || a < 0) return;
-  const int HD = p.hd, G = p.G;
+  const int G = p.G, slot = lane / LPH, d0 = (lane - slot * LPH) * 4;
   const long kvs = (long)p.nkv * HD;
-  const T *kc = reinterpret_cast<const T *>(p.kall) + (long)c * kvs + gk * HD;
-  const T *vc = reinterpret_cast<const T *>(p.vall) + (long)c * kvs + gk * HD;
-  float kd[2], vd[2], dk[2] = {0.f, 0.f}, dv[2] = {0.f, 0.f};
+  float kd[4], vd[4], dk[4] = {0.f, 0.f, 0.f, 0.f}, dv[4] = {0.f, 0.f, 0.f, 0.f};
+  load4<T>(reinterpret_cast<const T *>(p.kall) + (long)c * kvs + gk * HD + d0, kd);
+  load4<T>(reinterpret_cast<const T *>(p.vall) + (long)c * kvs + gk * HD + d0, vd);
+  // the deeper cells of the rollout that see this one: (a + dq, dq), dq = j .. K-1,
+  // up to the first that was not kept (chains are closed); K <= 16
+  constexpr int KMAX = 16;
+  int qis[KMAX];
+  int nq_cells = 0;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int d = lane + 64 * t;
-    kd[t] = d < HD ? to_f32<T>(kc[d]) : 0.f;
-    vd[t] = d < HD ? to_f32<T>(vc[d]) : 0.f;
-  }
-  for (int dq = j; dq < p.K; ++dq) {
+  for (int t = 0; t < KMAX; ++t) {
+    const int dq = j + t;
     const long r = (long)(a + dq) * p.K + dq;
-    if (r >= (long)p.n * p.K) break;
-    const int qi = p.inv[r];
-    if (qi < 0) break;  // chain-closed: no deeper cell of this rollout either
-    for (int h = gk * G; h < gk * G + G; ++h) {
-      const T *qr = reinterpret_cast<const T *>(p.q) + ((long)qi * p.nq + h) * HD;
-      const T *dr = reinterpret_cast<const T *>(p.dout) + ((long)qi * p.nq + h) * HD;
-      float qv[2], dov[2], sp = 0.f, dp = 0.f;
+    qis[t] = dq < p.K && r < (long)p.n * p.K ? p.inv[r] : -1;
+  }
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int d = lane + 64 * t;
-        qv[t] = d < HD ? to_f32<T>(qr[d]) : 0.f;
-        dov[t] = d < HD ? to_f32<T>(dr[d]) : 0.f;
-        sp += qv[t] * kd[t];
-        dp += dov[t] * vd[t];
+  for (int t = 0; t < KMAX; ++t)
+    if (qis[t] >= 0 && nq_cells == t) nq_cells = t + 1;
+  for (int t = 0; t < nq_cells; ++t) {
+    const int qi = qis[t];
+    for (int h0 = gk * G; h0 < gk * G + G; h0 += HPW) {
+      const int h = h0 + slot;
+      const bool ok = h < gk * G + G;
+      const long pi = (long)qi * p.nq + (ok ? h : h0);
+      float qv[4], dov[4];
+      load4<T>(reinterpret_cast<const T *>(p.q) + pi * HD + d0, qv);
+      load4<T>(reinterpret_cast<const T *>(p.dout) + pi * HD + d0, dov);
+      const float lse = p.lse[pi], Dv = p.D[pi];
+      float sp = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sp += qv[e] * kd[e];
+        dp += dov[e] * vd[e];
       }
-      for (int o = 32; o > 0; o >>= 1) {
+#pragma unroll
+      for (int o = LPH / 2; o > 0; o >>= 1) {
         sp += __shfl_xor(sp, o, 64);
         dp += __shfl_xor(dp, o, 64);
       }
-      const long pi = (long)qi * p.nq + h;
-      const float pr = fast_exp2(fmaf(sp, p.scale_log2, -p.lse[pi]));
-      const float dsv = pr * (dp - p.D[pi]);
+      const float pr = fast_exp2(fmaf(sp, p.scale_log2, -lse));
+      const float dsv = pr * (dp - Dv);
+      if (ok) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        dk[t] += dsv * qv[t];
-        dv[t] += pr * dov[t];
+        for (int e = 0; e < 4; ++e) {
+          dk[e] += dsv * qv[e];
+          dv[e] += pr * dov[e];
+        }
       }
     }
   }
+  // add the head slots' sums (lanes l, l + LPH, ..)
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int d = lane + 64 * t;
-    if (d < HD) {
-      p.dk[((long)c * p.nkv + gk) * HD + d] = dk[t] * p.scale;
-      p.dv[((long)c * p.nkv + gk) * HD + d] = dv[t];
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (HPW == 4) {
+      dk[e] = xor_sum<16>(dk[e]);
+      dv[e] = xor_sum<16>(dv[e]);
     }
+    dk[e] = xor_sum<32>(dk[e]);
+    dv[e] = xor_sum<32>(dv[e]);
+  }
+  if (slot == 0) {
+    const long o = ((long)c * p.nkv + gk) * HD + d0;
+    *reinterpret_cast<floatx4 *>(p.dk + o) = floatx4{dk[0] * p.scale, dk[1] * p.scale, dk[2] * p.scale, dk[3] * p.scale};
+    *reinterpret_cast<floatx4 *>(p.dv + o) = floatx4{dv[0], dv[1], dv[2], dv[3]};
   }
 }
 
@@ -1474,8 +1495,9 @@ hipError_t launch_attn_bwd(int dtype, const AttnBwdParams &p, hipStream_t s) {
   hipLaunchKernelGGL(k_attn_bwd_reduce, dim3(nblocks((long)p.n * p.nkv * p.hd, 256)), dim3(256), 0, s, p);
   {
     const unsigned b = nblocks((long)p.L * p.nkv, 4);
-    if (dtype == 1) hipLaunchKernelGGL(k_attn_bwd_chain<bf16_t>, dim3(b), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(k_attn_bwd_chain<float>, dim3(b), dim3(256), 0, s, p);
+    if (dtype == 1 && p.hd == 64) hipLaunchKernelGGL((k_attn_bwd_chain<bf16_t, 64>), dim3(b), dim3(256), 0, s, p);
+    else if (dtype == 1) hipLaunchKernelGGL((k_attn_bwd_chain<bf16_t, 128>), dim3(b), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((k_attn_bwd_chain<float, 64>), dim3(b), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }
