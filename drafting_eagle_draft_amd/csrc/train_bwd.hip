@@ -1182,7 +1182,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_reduce(AttnBwdParams p) {
 
 // dK, dV of the rollout cells (depth >= 1): cell c = (a + j, j) is seen by
 // the kept cells (a + d, d), j <= d < K, of its own rollout, each with the G
-// heads of the kv head.  One wave per (cell, kv head); lane = dimension.
+// heads of the kv head.  One wave per (cell, kv head).
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void k_attn_bwd_chain(AttnBwdParams p) {
   // A wave step covers HPW query heads of one deeper cell: LPH lanes per
