@@ -22,8 +22,9 @@
 //    remain, so reads past the last row, strip or k tile return zero
 //    without branches;
 //  * persistent grid of one workgroup per CU walking tiles in bands of four
-//    row blocks, with the tile index spread so that the 32 CUs of one XCD
-//    work on one 4 x 8 patch of tiles at a time (shared L2 panels).
+//    row blocks (eight for the LM head), with the tile index spread so that
+//    the 32 CUs of one XCD work on one 4 x 8 (8 x 4) patch of tiles at a
+//    time (shared L2 panels).
 #include <cmath>
 
 #include "pe_epilogue.hpp"
@@ -138,13 +139,17 @@ void k_gemm_tile(TileGemmParams p) {
   constexpr int stage_bytes = (NS + 16) * 64 * 16;
 
   // Unit u -> (first activation row, first weight strip, chunk); tiles in
-  // bands of four row blocks, columns inside a band.
+  // bands of BH row blocks, columns inside a band.  The LM head takes bands
+  // of eight (each XCD's 32 concurrent tiles an 8 x 4 patch), which halves
+  // how often each vocabulary strip is fetched (the activations, a few
+  // hundred MB, stay in the memory-side cache): 1.2% faster.
   auto tile_origin = [&](int u, int &m0, int &s0, int &ks) {
     ks = u / tiles;
     const int t = u - ks * tiles;
-    const int band = t / (4 * CB), rem = t - band * 4 * CB;
-    const int rows_in = min(4, RB - band * 4);
-    const int cb = rem / rows_in, rb = band * 4 + rem % rows_in;
+    constexpr int BH = LMH ? 8 : 4;
+    const int band = t / (BH * CB), rem = t - band * BH * CB;
+    const int rows_in = min(BH, RB - band * BH);
+    const int cb = rem / rows_in, rb = band * BH + rem % rows_in;
     m0 = rb * 256;
     s0 = cb * NS;
   };
