@@ -7,14 +7,16 @@
 // section "2. The P-EAGLE Parallel Drafter").
 //
 // Design (gfx950):
-//  * 256 x 256 output tiles (16 row groups x 16 weight strips), one
-//    workgroup of eight waves per CU (two per SIMD, so one wave's LDS and
-//    barrier waits are covered by the other's matrix work), each wave a
-//    128 x 64 block held in 128 fp32 accumulators (4 x 8 MFMA 16x16 tiles);
+//  * 256 x 256 output tiles (16 row groups x 16 weight strips), or 256 x
+//    320 (20 strips) for plain stores and accumulations where that pads
+//    less, one workgroup of eight waves per CU (two per SIMD, so one wave's
+//    LDS and barrier waits are covered by the other's matrix work), each
+//    wave a 128 x 64 (128 x 80) block held in 128 (160) fp32 accumulators
+//    (4 (5) x 8 MFMA 16x16 tiles);
 //  * operands move HBM/L2 -> LDS by buffer loads that write LDS directly
-//    (no staging registers), 32 fragments (32 KB) per k step, four LDS
-//    stages, issued three steps ahead of use; each wave then reads its 12
-//    fragments of the step and runs 32 MFMAs as they arrive;
+//    (no staging registers), 32 (36) fragments of 1 KB per k step, four
+//    LDS stages, issued three steps ahead of use; each wave then reads its
+//    12 (13) fragments of the step and runs 32 (40) MFMAs as they arrive;
 //  * the LM head stages its logits block through LDS and writes whole
 //    rows, and folds the argmax keys of the tile's four column quarters in
 //    LDS before one atomic maximum per row;
