@@ -189,16 +189,28 @@ GemmPlan plan_gemm(int cus, int NT, int KT, int Mv, int nf, int epi) {
       }
     }
   }
-  // Measured exception to the model (forward A/B on the MI355X): the
-  // in-kernel-finished 2880-wide projections of one 16-row group with
-  // 256-270 k tiles (fc and down of the GPT-OSS-20B-shaped drafter, which
-  // the model splits 11 and 7 ways) run fastest in 5 chunks: 4.4 us less
-  // per forward over the five launches; 4 chunks lose 2.4 us per launch.
-  if (nf == 1 && NT == 180 && KT >= 256 && KT <= 270 && finishes_in_kernel(epi)) {
-    const int kc = (KT + 4) / 5;
-    g.KS = (KT + kc - 1) / kc; g.kc = kc; g.nkw = (kc + W - 1) / W;
-    g.L.grid = std::min(NT, std::max(1, cus / g.KS));
-  }
+  // Measured exceptions to the model (forward A/B on the MI355X) for
+  // in-kernel-finished projections, keyed by 16-row groups, strips and k
+  // tiles: the model's split and its neighbours were timed in one process.
+  struct SplitOverride {
+    int nf, NT, KT_lo, KT_hi, KS;
+  };
+  static constexpr SplitOverride kOverrides[] = {
+      // GPT-OSS-20B shape, 16 rows: fc (model 11 ways) and down (model 7);
+      // 4.4 us less per forward over the five launches, 4 ways lose 2.4 us
+      // per launch, 6 ways 0.5 us
+      {1, 180, 256, 270, 5},
+      // Qwen3-Coder-30B shape, 32 rows: down (model 7 ways); 2.3 us less
+      // per forward, 5 ways lose 1 us per launch
+      {2, 128, 192, 192, 4},
+  };
+  if (finishes_in_kernel(epi))
+    for (const SplitOverride &o : kOverrides)
+      if (nf == o.nf && NT == o.NT && KT >= o.KT_lo && KT <= o.KT_hi) {
+        const int kc = (KT + o.KS - 1) / o.KS;
+        g.KS = (KT + kc - 1) / kc; g.kc = kc; g.nkw = (kc + W - 1) / W;
+        g.L.grid = std::min(NT, std::max(1, cus / g.KS));
+      }
   g.L.waves = W;
   g.L.lds = (size_t)W * nf * 1024 + 256;
   g.L.maxkw = g.nkw <= 2 ? 2 : g.nkw <= 4 ? 4 : g.nkw <= 8 ? 8 : g.nkw <= 12 ? 12 : 18;
