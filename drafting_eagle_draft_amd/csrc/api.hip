@@ -193,20 +193,23 @@ GemmPlan plan_gemm(int cus, int NT, int KT, int Mv, int nf, int epi) {
   // in-kernel-finished projections, keyed by 16-row groups, strips and k
   // tiles: the model's split and its neighbours were timed in one process.
   struct SplitOverride {
-    int nf, NT, KT_lo, KT_hi, KS;
+    int epi, nf, NT, KT_lo, KT_hi, KS;  // epi -1: any in-kernel-finished epilogue
   };
   static constexpr SplitOverride kOverrides[] = {
       // GPT-OSS-20B shape, 16 rows: fc (model 11 ways) and down (model 7);
       // 4.4 us less per forward over the five launches, 4 ways lose 2.4 us
       // per launch, 6 ways 0.5 us
-      {1, 180, 256, 270, 5},
+      {-1, 1, 180, 256, 270, 5},
       // Qwen3-Coder-30B shape, 32 rows: down (model 7 ways); 2.3 us less
       // per forward, 5 ways lose 1 us per launch
-      {2, 128, 192, 192, 4},
+      {EPI_RESID, 2, 128, 192, 192, 4},
+      // Qwen3-Coder-30B shape: fc of the 4 + 1 fused rows (model 7 ways);
+      // 0.9-1.9 us less per forward
+      {EPI_FC, 1, 128, 192, 192, 4},
   };
   if (finishes_in_kernel(epi))
     for (const SplitOverride &o : kOverrides)
-      if (nf == o.nf && NT == o.NT && KT >= o.KT_lo && KT <= o.KT_hi) {
+      if ((o.epi < 0 || o.epi == epi) && nf == o.nf && NT == o.NT && KT >= o.KT_lo && KT <= o.KT_hi) {
         const int kc = (KT + o.KS - 1) / o.KS;
         g.KS = (KT + kc - 1) / kc; g.kc = kc; g.nkw = (kc + W - 1) / W;
         g.L.grid = std::min(NT, std::max(1, cus / g.KS));
