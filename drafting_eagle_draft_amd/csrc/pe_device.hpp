@@ -101,6 +101,12 @@ __device__ __forceinline__ u32x4 ldg16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// The same load marked non-temporal (nt), for data read once that should
+// not displace lines other workgroups still use.
+__device__ __forceinline__ u32x4 ldg16_nt(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
 __device__ __forceinline__ void stg16(void *p, u32x4 v) {
   *reinterpret_cast<u32x4 *>(p) = v;
 }

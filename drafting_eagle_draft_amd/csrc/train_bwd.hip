@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void k_ce_lse(const T *logits, int L, int V, c
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const int v = v0 + u * 64 * E;
-        q[u] = v < V ? ldg16(row + v) : u32x4{0u, 0u, 0u, 0u};
+        q[u] = v < V ? ldg16_nt(row + v) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void k_ce_grad(const T *logits, int L, int V, 
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int idx = t + k * NTH, rr = idx / (CB / E), cc = (idx - rr * (CB / E)) * E, v = v0 + cc;
-      q[k] = s_lab[rr] >= 0 && v < V ? ldg16(logits + (long)(i0 + rr) * V + v) : u32x4{0u, 0u, 0u, 0u};
+      q[k] = s_lab[rr] >= 0 && v < V ? ldg16_nt(logits + (long)(i0 + rr) * V + v) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   const int KTA = (V + KTILE - 1) / KTILE, KTT = (L + KTILE - 1) / KTILE;
