@@ -30,8 +30,8 @@ namespace {
 // Cache policy of the weight-tile loads: non-temporal (the nt bit of the
 // gfx950 buffer load).  Every weight byte is read once per forward, so the
 // tiles should not displace the activations and partials that the
-// workgroups do share; measured on the MI355X, the LM head streams 6.8
-// instead of 6.2 TB/s and each projection gains 3-9%.
+// workgroups do share; measured on the MI355X, the LM head streams 6.9
+// instead of 6.3 TB/s and the layer projections gain 1-5%.
 constexpr int kWeightAux = 2;
 
 template <int MAXKW>
